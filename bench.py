@@ -1,0 +1,345 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA lightning-indexer hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config decode|prefill|long|
+                     tiny|index_cache] [--rotate R] [--no-cpu-baseline]
+
+One step = one pass of the whole hot path over one batch: IndexCache mask
+(host), q quantisation, paged FP8 logits, per-row top-k into the shared index
+buffer, each through the C ABI of libdsa_indexer.so.  The default workload is
+the decode batch: 64 requests with contexts uniform in [1024, 8192], one
+query each at the last position, 64 heads, head_dim 128, index_topk 2048,
+FP8 e4m3 K with one fp32 scale per token, 64-token pages drawn from a
+shuffled 16384-page pool (synthetic, seeded).
+
+Timing: inputs are resident in HBM before the timed region.  R copies of the
+K cache (and of q / weights) rotate across steps so that consecutive steps do
+not hit the 256 MB Infinity Cache.  The timed region replays one HIP graph
+that holds R steps (one per copy), so it measures GPU execution, not Python
+launch overhead; every replay is first checked bit-exactly against the eager
+result.  Per-kernel durations come from HIP events on the launch stream
+around every kernel of 64 eager steps, queued behind a GPU sleep so that no
+host gap falls inside a bracket.
+
+Prints ONE JSON line.  ``roofline`` is for the dominant kernel (the logits
+kernel): achieved = algorithmic bytes (or FLOPs) per launch / its average
+duration; ``cpu_baseline`` times the CPU oracle (numpy) on a bounded sample
+of the same workload on this host.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
+
+METRIC = ("indexer query-rows/sec (logits+top-k), HBM GB/s & FP8 MFMA util "
+          "vs peak")
+
+WORKLOADS = {
+    "decode": "decode batch: 64 requests, context U[1024,8192] (seed 1), 1 "
+              "query each at the last position, H=64, head_dim 128, "
+              "index_topk 2048, FP8 e4m3 K + fp32 scale per token (132 B), "
+              "64-token pages from a shuffled 16384-page pool",
+    "prefill": "prefill chunk: 1 request, 32768-token cached prefix + 8192 "
+               "new queries at positions 32768..40959, causal, H=64, "
+               "head_dim 128, index_topk 2048, FP8 K, shuffled 64-token pages",
+    "long": "long context: 1 request, 1048576-token FP8 K cache (16384 "
+            "shuffled pages, 1% of tokens x4), 16 decode rows at the tail, "
+            "H=64, head_dim 128, index_topk 2048",
+    "tiny": "tiny: 1 request, 256 cached tokens, 8 queries at 248..255, H=4, "
+            "index_topk 32",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="decode",
+                    choices=sorted(WORKLOADS) + ["index_cache"])
+    ap.add_argument("--rotate", type=int, default=8,
+                    help="K-cache copies rotated across steps (cold cache)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def make_batch(name):
+    from dsa_lightning_indexer_amd import synth
+    return {"decode": synth.decode, "prefill": synth.prefill,
+            "long": synth.long_context, "tiny": synth.tiny}[name]()
+
+
+def logits_work(b):
+    """Algorithmic bytes and FLOPs of one logits launch.
+
+    Per visible (row, token) pair: 132 B of K (128 FP8 key bytes + 4 B fp32
+    scale) read and 4 B of logit written, and 2 * H * 128 FLOPs.  Per row:
+    H * 128 B of FP8 q, H * 4 B of q scales and H * 4 B of weights.  A decode
+    row reads every visible key once; a prefill or long-context tile reads a
+    key once for all of its rows, so its bytes count the distinct keys.
+    """
+    H = b.H
+    pairs = b.visible_pairs
+    flops = 2.0 * H * 128 * pairs
+    per_row = b.T * H * (128 + 4 + 4)
+    if b.T == b.R:                                 # one row per request
+        kbytes = 132 * pairs
+    else:                                          # keys shared by a request
+        kbytes = 132 * sum(int(c) for c in b.contexts)
+    return kbytes + 4 * pairs + per_row, flops
+
+
+def cpu_baseline(b, seconds):
+    """Time the CPU oracle on the same workload (whole batches, repeated
+    until ``seconds`` of work; a bounded row sample for large batches)."""
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:                                   # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    from oracle import indexer as oi
+    rows = np.arange(b.T)
+    sample = "whole batch"
+    if b.visible_pairs > 2_000_000:                     # bound the sample
+        per_row = b.visible_pairs / b.T
+        nrows = max(1, int(2_000_000 / per_row))
+        rows = np.linspace(0, b.T - 1, nrows).round().astype(np.int64)
+        sample = f"{len(rows)} evenly spaced rows of {b.T}"
+    t0 = time.perf_counter()
+    done = 0
+    reps = 0
+    while True:
+        q = b.q_bf16[rows].float().numpy()
+        codes = np.zeros((b.T, b.H, 128), np.uint8)
+        sc = np.ones((b.T, b.H), np.float32)
+        codes[rows], sc[rows] = oi.quantize_q(q)
+        lg = oi.indexer_logits(codes, sc, b.weights, b.k_cache, b.block_table,
+                               b.query_start_loc, b.positions, b.ld, rows=rows)
+        oi.indexer_topk(lg, b.positions, b.k, rows=rows)
+        done += len(rows)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": done / el, "unit": "query-rows/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{sample}, {reps} pass(es), {done} rows in {el:.1f} s "
+                      "(numpy fp64 oracle: quantise q, logits, sort-based "
+                      "top-k)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; "
+                                   "--gpus N > 1 is not supported"}))
+        sys.exit(2)
+    if args.config == "index_cache":
+        return bench_index_cache(args)
+
+    import torch
+    from dsa_lightning_indexer_amd import binding
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    b = make_batch(args.config)
+    R = max(1, args.rotate if args.config in ("decode", "long") else 1)
+    bt = torch.from_numpy(b.block_table).to(dev)
+    qsl = torch.from_numpy(b.query_start_loc).to(dev)
+    pos = torch.from_numpy(b.positions).to(dev)
+    kcs = [torch.from_numpy(b.k_cache).to(dev) for _ in range(R)]
+    qs_in = [b.q_bf16.to(dev) for _ in range(R)]
+    ws_in = [torch.from_numpy(b.weights).to(dev) for _ in range(R)]
+    T, H, ld, k = b.T, b.H, b.ld, b.k
+    q8 = torch.empty((T, H, 128), dtype=torch.uint8, device=dev)
+    qsc = torch.empty((T, H), dtype=torch.float32, device=dev)
+    logits = torch.empty((T, ld), dtype=torch.float32, device=dev)
+    buf = torch.empty((T, k), dtype=torch.int32, device=dev)
+    tws_n = binding.dsa_topk_workspace_size(T, ld, k)
+    tws = torch.empty(max(tws_n, 1), dtype=torch.uint8, device=dev)
+
+    def step(i, ev=None):
+        r = i % R
+        binding.dsa_index_cache_mask(1)                       # one F layer
+        if ev is not None:
+            ev[0].record()
+        binding.dsa_quantize_q(qs_in[r], q8, qsc)
+        if ev is not None:
+            ev[1].record()
+        binding.dsa_indexer_logits(q8, qsc, ws_in[r], kcs[r], bt, qsl, pos,
+                                   ld, logits)
+        if ev is not None:
+            ev[2].record()
+        binding.dsa_indexer_topk(logits, pos, k, buf, tws)
+        if ev is not None:
+            ev[3].record()
+
+    # Eager warm-up; the last slot's output is the reference for the graph.
+    for i in range(max(args.warmup, R)):
+        step(i)
+    torch.cuda.synchronize()
+    assert binding.dsa_device_error_flags(reset=True) == 0
+    last = (max(args.warmup, R) - 1) % R
+    step(last)
+    torch.cuda.synchronize()
+    ref_buf = buf.clone()
+
+    # One HIP graph holds R steps (one per K-cache copy); the timed region
+    # replays it.  Every replay is checked against the eager result first.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for r in range(R):
+            step(r)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        buf.fill_(-7)
+        graph.replay()
+        torch.cuda.synchronize()
+        if (R - 1) != last:
+            step(last)                       # eager work between replays
+            torch.cuda.synchronize()
+        if not torch.equal(buf, ref_buf):
+            raise SystemExit("graph replay differs from the eager result")
+
+    reps = max(1, math.ceil(args.steps / R))
+    K = reps * R
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(20e6))
+    start.record()
+    for _ in range(reps):
+        graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / K
+
+    # Per-kernel durations: eager steps with HIP events around every kernel
+    # on the launch stream, enqueued behind a GPU sleep so that the host has
+    # queued them all before the GPU reaches them (no host gaps inside a
+    # bracket).
+    NK = min(64, K)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+           for _ in range(NK)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(50e6))
+    for i in range(NK):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    kq = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    kl = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    kt = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    eager_ms_step = evs[0][0].elapsed_time(evs[-1][3]) / NK
+    assert binding.dsa_device_error_flags(reset=True) == 0
+
+    alg_bytes, flops = logits_work(b)
+    gbs = alg_bytes / (kl * 1e-3) / 1e9
+    tfl = flops / (kl * 1e-3) / 1e12
+    if args.config in ("prefill", "long"):
+        roof = {"bound": "mfma", "achieved": round(tfl, 2),
+                "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tfl / FP8_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    roof["kernel"] = "logits"
+    roof["algorithmic_bytes"] = int(alg_bytes)
+    roof["algorithmic_flops"] = flops
+    roof["kernel_ms"] = round(kl, 5)
+
+    out = {
+        "metric": METRIC, "value": round(T / (ms_step * 1e-3), 1),
+        "unit": "query-rows/s", "n_gpus": 1, "steps": K,
+        "warmup": max(args.warmup, R), "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.config], "rows": T,
+                   "heads": H, "index_topk": k,
+                   "visible_pairs": b.visible_pairs,
+                   "kcache_copies_rotated": R},
+        "kernels_ms": {"quantize_q": round(kq, 5), "logits": round(kl, 5),
+                       "topk": round(kt, 5)},
+        "eager_ms_per_step": round(eager_ms_step, 5),
+        "logits_gbs": round(gbs, 1), "logits_tflops": round(tfl, 2),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def bench_index_cache(args):
+    """IndexCache stack: 61 layers, 32 decode requests x 16384 context,
+    freq=4 / offset=2 (16 F layers) against freq=1 (61 F layers); one step =
+    one dsa_index_cache_run over the whole stack."""
+    import torch
+    from dsa_lightning_indexer_amd import binding, synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    L = 61
+    full4 = [l for l, s in enumerate(binding.dsa_index_cache_mask(
+        L, freq=4, offset=2)) if not s]
+    layers_np = synth.index_cache_layers(list(range(L)))
+    ref = layers_np[0]
+    layers = []
+    for l in range(L):
+        b = layers_np[l]
+        layers.append({"q_bf16": b.q_bf16.to(dev),
+                       "weights": torch.from_numpy(b.weights).to(dev),
+                       "k_cache": torch.from_numpy(b.k_cache).to(dev)})
+    del layers_np
+    bt = torch.from_numpy(ref.block_table).to(dev)
+    qsl = torch.from_numpy(ref.query_start_loc).to(dev)
+    pos = torch.from_numpy(ref.positions).to(dev)
+    T, k, ld = ref.T, ref.k, ref.ld
+    buf = torch.empty((T, k), dtype=torch.int32, device=dev)
+    ws = torch.empty(binding.dsa_run_workspace_size(T, ref.H, ld, k),
+                     dtype=torch.uint8, device=dev)
+    res = {}
+    for freq in (4, 1):
+        def run():
+            binding.dsa_index_cache_run(layers, bt, qsl, pos, ld, k, buf,
+                                        freq=freq, offset=2, workspace=ws)
+        for _ in range(max(2, args.warmup // 10)):
+            run()
+        torch.cuda.synchronize()
+        n = max(3, args.steps // 20)
+        s, e = torch.cuda.Event(True), torch.cuda.Event(True)
+        torch.cuda._sleep(int(60e6))
+        s.record()
+        for _ in range(n):
+            run()
+        e.record()
+        torch.cuda.synchronize()
+        res[freq] = s.elapsed_time(e) / n
+    F = len(full4)
+    per_layer_bytes = 132 * 32 * 16384 + 4 * 32 * 16384 + 32 * 64 * 136
+    out = {
+        "metric": "IndexCache stack forward (61 DSA layers)",
+        "value": round(T / (res[4] * 1e-3), 1), "unit": "query-rows/s",
+        "n_gpus": 1, "steps": max(3, args.steps // 20),
+        "ms_per_step": round(res[4], 4), "higher_is_better": True,
+        "data": "synthetic", "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "config": {"workload": "IndexCache stack: 61 layers, freq 4 offset 2 "
+                               f"({F} F) vs freq 1 (61 F); 32 decode requests "
+                               "x 16384 context, H=64, index_topk 2048"},
+        "ms_freq4": round(res[4], 4), "ms_freq1": round(res[1], 4),
+        "speedup": round(res[1] / res[4], 3), "full_layers_freq4": F,
+        "hbm_gbs_freq1": round(61 * per_layer_bytes / (res[1] * 1e-3) / 1e9, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

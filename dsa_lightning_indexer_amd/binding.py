@@ -1,0 +1,254 @@
+"""Python binding of libdsa_indexer.so (ctypes).
+
+Argument marshalling only: every step of the hot path runs in the library's
+HIP kernels.  Tensors are torch tensors on the GPU (PyTorch provides device
+memory and the stream); each function passes ``data_ptr()``s, sizes and
+``torch.cuda.current_stream().cuda_stream`` to the C entry point of the same
+name (declared in include/dsa_indexer.h) and raises ``DsaError`` on a
+non-zero status.  There is no fallback: if the library is missing, the first
+call raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libdsa_indexer.so")
+
+DSA_OK = 0
+DSA_ERR_INVALID_ARG = -1
+DSA_ERR_UNSUPPORTED = -2
+DSA_ERR_WORKSPACE = -3
+DSA_ERR_HIP = -4
+
+HEAD_DIM = 128
+PAGE_TOKENS = 64
+PAGE_BYTES = 8448
+LOGITS_ROW_ALIGN = 256
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"dsa status {status}: {message}")
+        self.status = status
+
+
+class LayerInputs(ctypes.Structure):
+    _fields_ = [("q_bf16", ctypes.c_void_p), ("weights", ctypes.c_void_p),
+                ("k_cache", ctypes.c_void_p), ("num_pages", ctypes.c_int64)]
+
+
+LAYER_CALLBACK = ctypes.CFUNCTYPE(None, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p, ctypes.c_void_p)
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_L = ctypes.c_int64
+_S = ctypes.c_size_t
+_SIGNATURES = {
+    "dsa_last_error": (ctypes.c_char_p, []),
+    "dsa_version": (_I, []),
+    "dsa_quantize_q": (_I, [_P, _L, _I, _I, _P, _P, _P]),
+    "dsa_indexer_logits": (_I, [_P, _P, _P, _P, _L, _P, _L, _P, _P, _L, _I,
+                                _I, _I, _I, _P, _L, _P]),
+    "dsa_indexer_topk": (_I, [_P, _L, _P, _L, _I, _P, _L, _P, _S, _P]),
+    "dsa_topk_workspace_size": (_S, [_L, _L, _I]),
+    "dsa_index_cache_mask": (_I, [ctypes.c_char_p, _I, _I, _I, _I, _P]),
+    "dsa_index_cache_run": (_I, [ctypes.c_char_p, _I, _I, _I, _I, _P, _P, _L,
+                                 _P, _P, _L, _I, _I, _L, _I, _P, _L, _P, _P,
+                                 LAYER_CALLBACK, _P, _P, _S, _P]),
+    "dsa_run_workspace_size": (_S, [_L, _I, _L, _I]),
+    "dsa_device_error_flags": (_I, [_I]),
+    "dsa_set_option": (_I, [ctypes.c_char_p, _I]),
+}
+
+
+def lib():
+    """The loaded library (loads it on first use; raises if not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m dsa_lightning_indexer_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc < 0:
+        msg = lib().dsa_last_error()
+        raise DsaError(rc, msg.decode() if msg else "")
+    return rc
+
+
+def _dev_ptr(t, dtype, name):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def dsa_quantize_q(q_bf16, q_fp8=None, q_scale=None, stream=None):
+    """bf16 [T, H, 128] -> (uint8 codes [T, H, 128], fp32 scales [T, H])."""
+    T, H, D = q_bf16.shape
+    dev = q_bf16.device
+    if q_fp8 is None:
+        q_fp8 = torch.empty((T, H, D), dtype=torch.uint8, device=dev)
+    if q_scale is None:
+        q_scale = torch.empty((T, H), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().dsa_quantize_q(
+            _dev_ptr(q_bf16, torch.bfloat16, "q_bf16"), T, H, D,
+            _dev_ptr(q_fp8, torch.uint8, "q_fp8"),
+            _dev_ptr(q_scale, torch.float32, "q_scale"), _stream(stream, dev)))
+    return q_fp8, q_scale
+
+
+def dsa_indexer_logits(q_fp8, q_scale, weights, k_cache, block_table,
+                       query_start_loc, positions, ld, logits=None,
+                       stream=None):
+    """Causal indexer logits, fp32 [T, ld]."""
+    T, H, D = q_fp8.shape
+    R = block_table.shape[0]
+    dev = q_fp8.device
+    if logits is None:
+        logits = torch.empty((T, ld), dtype=torch.float32, device=dev)
+    if k_cache.dim() != 2 or k_cache.shape[1] != PAGE_BYTES:
+        raise ValueError("k_cache must be uint8 [num_pages, 8448]")
+    if query_start_loc.numel() != R + 1:
+        raise ValueError("query_start_loc must have R + 1 entries")
+    with torch.cuda.device(dev):
+        _check(lib().dsa_indexer_logits(
+            _dev_ptr(q_fp8, torch.uint8, "q_fp8"),
+            _dev_ptr(q_scale, torch.float32, "q_scale"),
+            _dev_ptr(weights, torch.float32, "weights"),
+            _dev_ptr(k_cache, torch.uint8, "k_cache"), k_cache.shape[0],
+            _dev_ptr(block_table, torch.int32, "block_table"),
+            block_table.shape[1],
+            _dev_ptr(query_start_loc, torch.int32, "query_start_loc"),
+            _dev_ptr(positions, torch.int32, "positions"), T, R, H, D,
+            PAGE_TOKENS, _dev_ptr(logits, torch.float32, "logits"),
+            logits.shape[1], _stream(stream, dev)))
+    return logits
+
+
+def dsa_topk_workspace_size(T, ld, k):
+    return lib().dsa_topk_workspace_size(T, ld, k)
+
+
+def dsa_indexer_topk(logits, positions, k, out=None, workspace=None,
+                     stream=None):
+    """Per-row causal top-k, int32 [T, k] (ascending positions, -1 padded)."""
+    T, ld = logits.shape
+    dev = logits.device
+    if out is None:
+        out = torch.empty((T, k), dtype=torch.int32, device=dev)
+    need = dsa_topk_workspace_size(T, ld, k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = _dev_ptr(workspace, torch.uint8, "workspace") if need > 0 else None
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    with torch.cuda.device(dev):
+        _check(lib().dsa_indexer_topk(
+            _dev_ptr(logits, torch.float32, "logits"), ld,
+            _dev_ptr(positions, torch.int32, "positions"), T, k,
+            _dev_ptr(out, torch.int32, "out"), out.shape[1], ws_ptr, ws_bytes,
+            _stream(stream, dev)))
+    return out
+
+
+def dsa_index_cache_mask(num_layers, pattern=None, freq=1, offset=2,
+                         num_hidden_layers=-1):
+    """IndexCache F/S mask (host): list of bools, True = S (reuse)."""
+    buf = (ctypes.c_uint8 * max(num_layers, 1))()
+    pat = pattern.encode() if pattern is not None else None
+    _check(lib().dsa_index_cache_mask(pat, freq, offset, num_layers,
+                                      num_hidden_layers, buf))
+    return [bool(buf[i]) for i in range(num_layers)]
+
+
+def dsa_run_workspace_size(T, H, ld, k):
+    return lib().dsa_run_workspace_size(T, H, ld, k)
+
+
+def dsa_index_cache_run(layers, block_table, query_start_loc, positions, ld,
+                        k, topk_buffer, pattern=None, freq=1, offset=2,
+                        num_hidden_layers=-1, H=None, snapshots=False,
+                        callback=None, workspace=None, stream=None):
+    """One forward pass over ``len(layers)`` DSA layers.
+
+    ``layers[l]`` is a dict with ``q_bf16`` (bf16 [T, H, 128]), ``weights``
+    (fp32 [T, H]) and ``k_cache`` (uint8 [pages, 8448]) for F layers, or None
+    (allowed for S layers).  Returns (is_skip list, snapshots tensor
+    [L, T, k] or None).
+    """
+    L = len(layers)
+    T = positions.numel()
+    R = block_table.shape[0]
+    dev = topk_buffer.device
+    if topk_buffer.dim() != 2 or topk_buffer.shape[1] != k:
+        raise ValueError("topk_buffer must be int32 [buffer_rows, k]")
+    if H is None:
+        H = next(l["q_bf16"].shape[1] for l in layers if l is not None)
+    arr = (LayerInputs * max(L, 1))()
+    for i, lay in enumerate(layers):
+        if lay is None:
+            arr[i] = LayerInputs(None, None, None, 0)
+        else:
+            arr[i] = LayerInputs(
+                _dev_ptr(lay["q_bf16"], torch.bfloat16, "q_bf16"),
+                _dev_ptr(lay["weights"], torch.float32, "weights"),
+                _dev_ptr(lay["k_cache"], torch.uint8, "k_cache"),
+                lay["k_cache"].shape[0])
+    snaps = torch.empty((L, T, k), dtype=torch.int32, device=dev) \
+        if snapshots else None
+    need = dsa_run_workspace_size(T, H, ld, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    skip = (ctypes.c_uint8 * max(L, 1))()
+    cb = LAYER_CALLBACK(0) if callback is None else LAYER_CALLBACK(
+        lambda layer, full, buf, user: callback(layer, bool(full)))
+    pat = pattern.encode() if pattern is not None else None
+    with torch.cuda.device(dev):
+        _check(lib().dsa_index_cache_run(
+            pat, freq, offset, L, num_hidden_layers, arr,
+            _dev_ptr(block_table, torch.int32, "block_table"),
+            block_table.shape[1],
+            _dev_ptr(query_start_loc, torch.int32, "query_start_loc"),
+            _dev_ptr(positions, torch.int32, "positions"), T, R, H, ld, k,
+            _dev_ptr(topk_buffer, torch.int32, "topk_buffer"),
+            topk_buffer.shape[0],
+            _dev_ptr(snaps, torch.int32, "snapshots") if snaps is not None
+            else None, skip, cb, None,
+            _dev_ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+            _stream(stream, dev)))
+    return [bool(skip[i]) for i in range(L)], snaps
+
+
+def dsa_device_error_flags(reset=True):
+    return _check(lib().dsa_device_error_flags(1 if reset else 0))
+
+
+def dsa_set_option(key, value):
+    return _check(lib().dsa_set_option(key.encode(), int(value)))

@@ -1,0 +1,109 @@
+// Device-side building blocks shared by the gfx950 kernels of the DSA
+// lightning-indexer library: fixed layout constants, the FP8 e4m3fn encoder,
+// the FP8 MFMA wrapper and wave-level reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// Indexer-K cache layout (GLM-5.3 KV/indexer cache budget article, SGLang
+// buffer-shape section and the IndexKeyCache.move comment in the eviction
+// section): one 128-dim K per token, FP8 e4m3fn, plus one fp32 scale per
+// 128-element block; a 64-token page stores 64 x 128 key bytes first, then
+// 64 x 4 scale bytes: 8448 bytes.
+constexpr int kPageTokens = 64;
+constexpr int kHeadDim = 128;
+constexpr int kPageKeyBytes = kPageTokens * kHeadDim;       // 8192
+constexpr int kPageBytes = kPageKeyBytes + kPageTokens * 4;  // 8448
+constexpr int kMaxHeads = 64;
+constexpr float kE4M3Max = 448.0f;
+
+// Device error flags (sticky, cleared by dsa_device_error_flags(reset=1)).
+constexpr unsigned kErrPageOutOfRange = 1u;   // block_table entry not in pool
+constexpr unsigned kErrPositionOutOfRange = 2u;  // p < 0, p >= ld or page past bt
+constexpr unsigned kErrCandidateOverflow = 4u;   // internal top-k list full
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// 16x16x128 FP8 (e4m3) x FP8 (e4m3) -> fp32 matrix FMA.  Operand format 0 on
+// both sides selects e4m3; zero scale operands make the compiler emit the
+// unscaled v_mfma_f32_16x16x128_f8f6f4.
+__device__ __forceinline__ f32x4 mfma16x16x128_fp8(const i32x8& a,
+                                                    const i32x8& b,
+                                                    const f32x4& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0,
+                                                          0, 0);
+}
+
+// float -> OCP e4m3fn byte: round to nearest, ties to even mantissa,
+// magnitudes >= 448 saturate to 448, NaN -> 0x7F.  Integer arithmetic on the
+// fp32 bit pattern.
+__device__ __forceinline__ uint32_t e4m3fn_encode(float x) {
+  const uint32_t b = __float_as_uint(x);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t a = b & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;               // NaN
+  uint32_t code;
+  if (a >= 0x43e00000u) {                          // |x| >= 448
+    code = 0x7eu;
+  } else if (a < 0x3c800000u) {                    // |x| < 2^-6: subnormal
+    // value = m * 2^-9; scaling by 2^9 is exact, rint rounds half to even
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  } else {
+    const uint32_t e = (a >> 23) - 120u;           // rebias 127 -> 7
+    const uint32_t mant = a & 0x7fffffu;
+    code = (e << 3) | (mant >> 20);
+    const uint32_t rem = mant & 0xfffffu;
+    if (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) code += 1u;
+    if (code > 0x7eu) code = 0x7eu;
+  }
+  return code | sign;
+}
+
+// Order-preserving map of an fp32 value to uint32 (larger float -> larger
+// key); -0 is folded onto +0 first so the two compare equal.
+__device__ __forceinline__ uint32_t float_to_ordered(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// The value of a wave-uniform expression, held in a scalar register.
+__device__ __forceinline__ int wave_uniform(int v) {
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+// Row -> request index by binary search over query_start_loc[0..R].
+__device__ __forceinline__ int request_of_row(const int32_t* qsl, int R,
+                                              int64_t t) {
+  int lo = 0, hi = R - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (qsl[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Sum over the 4 lane groups (lanes l, l^16, l^32, l^48) of four partial
+// values, scattered so that lane group g ends with the total of value g.
+__device__ __forceinline__ float reduce_scatter4(float v0, float v1, float v2,
+                                                 float v3) {
+  const int lane = lane_id();
+  const bool hi = lane >= 32;
+  float send0 = hi ? v0 : v2, send1 = hi ? v1 : v3;
+  float keep0 = hi ? v2 : v0, keep1 = hi ? v3 : v1;
+  keep0 += __shfl_xor(send0, 32);
+  keep1 += __shfl_xor(send1, 32);
+  const bool odd = (lane >> 4) & 1;
+  const float send = odd ? keep0 : keep1;
+  float keep = odd ? keep1 : keep0;
+  keep += __shfl_xor(send, 16);
+  return keep;
+}
+
+}  // namespace dsa

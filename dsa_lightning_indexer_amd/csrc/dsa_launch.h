@@ -1,0 +1,56 @@
+// Host-side launchers of the gfx950 kernels (internal to the library; the
+// public C ABI is include/dsa_indexer.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+struct LogitsArgs {
+  const uint8_t* q8;            // e4m3fn codes [T, H, 128]
+  const float* q_scale;         // [T, H]
+  const float* weights;         // [T, H]
+  const uint8_t* k_cache;       // [num_pages, 8448]
+  int64_t num_pages;
+  const int32_t* block_table;   // [R, bt_stride]
+  int64_t bt_stride;
+  const int32_t* qsl;           // query_start_loc [R + 1]
+  const int32_t* positions;     // [T]
+  int64_t T;
+  int R;
+  int H;
+  float* logits;                // [T, ld]
+  int64_t ld;
+};
+
+struct TopkArgs {
+  const float* logits;          // [T, ld]
+  int64_t ld;
+  const int32_t* positions;     // [T]
+  int64_t T;
+  int k;
+  int32_t* out;                 // [T, out_ld]
+  int64_t out_ld;
+  void* workspace;
+  size_t ws_bytes;
+};
+
+// Kernel-choice knobs (dsa_set_option); 0 = automatic.
+struct Options {
+  int logits_kernel = 0;        // 1 = row-wise, 2 = tiled
+  int row_pages_per_wave = 0;
+  int tile_pages_per_split = 0;
+  int topk_kernel = 0;          // 1 = one workgroup per row, 2 = multi-WG
+};
+Options& options();
+
+hipError_t launch_quantize_q(const uint16_t* q_bf16, int64_t blocks,
+                             uint8_t* q8, float* q_scale, hipStream_t stream);
+hipError_t launch_logits(const LogitsArgs& a, hipStream_t stream);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
+size_t topk_workspace_bytes(int64_t T, int64_t ld, int k);
+hipError_t read_error_flags(unsigned* flags, bool reset);
+
+}  // namespace dsa

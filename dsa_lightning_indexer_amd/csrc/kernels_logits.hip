@@ -1,0 +1,440 @@
+// gfx950 kernels for the first half of the lightning-indexer hot path:
+//   * q quantisation (bf16 -> e4m3fn codes + one fp32 scale per 128 block),
+//   * paged FP8 logits: per-head FP8 MFMA dot products q_h . k_s, ReLU, the
+//     per-head weighted sum, the K scale and the causal bound.
+//
+// Score: for query row t at position p and cached token s <= p,
+//   logit[t, s] = sum_h w[t,h] * max(qhat[t,h,:] . khat[s,:], 0)
+// (the DeepSeek Sparse Attention lightning-indexer score of DeepSeek-V3.2,
+// arXiv:2512.02556, which the GLM-5.3 cache-budget article cites; the pages
+// name the indexer and an fp8_index operator -- Ascend msmodeling DeepSeek-V3.2
+// RFC, section 2.1.3 -- but print no formula).  With qhat = code_q * s_q and
+// khat = code_k * s_k, s_q, s_k >= 0, this equals
+//   s_k[s] * sum_h (w[t,h] * s_q[t,h]) * max(code_q[t,h,:] . code_k[s,:], 0),
+// so the MFMA contracts raw FP8 codes and both scales are applied in the
+// fp32 epilogue.
+//
+// Paging (vLLM HBM-index notes, section 2.3; GLM-5.3 article, SGLang
+// buffer-shape section): token s of request r lives in physical page
+// block_table[r, s / 64], slot s % 64; the page holds 64 x 128 key bytes and
+// then 64 fp32 scales.
+#include <algorithm>
+
+#include "dsa_common.h"
+#include "dsa_launch.h"
+
+namespace dsa {
+
+__device__ unsigned g_err_logits = 0;
+
+__device__ __forceinline__ void raise_flag(unsigned f) {
+  atomicOr(&g_err_logits, f);
+}
+
+// ---------------------------------------------------------------------------
+// q quantisation: 16 lanes per (t, h) block of 128 bf16 values, 8 per lane.
+//   amax = max |q|;  s = amax / 448 (IEEE fp32 division; s = 1 if amax == 0)
+//   code = e4m3fn(q / s) (IEEE fp32 division, RNE, saturating)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quantize_q_kernel(
+    const uint16_t* __restrict__ q, int64_t blocks, uint8_t* __restrict__ q8,
+    float* __restrict__ q_scale) {
+  const int64_t blk = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  if (blk >= blocks) return;                 // whole 16-lane groups exit
+  const uint4 raw = *reinterpret_cast<const uint4*>(q + blk * 128 + sub * 8);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1)
+    amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+  const float s = (amax == 0.f) ? 1.0f : amax / kE4M3Max;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lo |= e4m3fn_encode(f[i] / s) << (8 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hi |= e4m3fn_encode(f[4 + i] / s) << (8 * i);
+  *reinterpret_cast<uint2*>(q8 + blk * 128 + sub * 8) = make_uint2(lo, hi);
+  if (sub == 0) q_scale[blk] = s;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA operand layout used below (v_mfma_f32_16x16x128_f8f6f4, wave64):
+//   A (16 x 128): lane l holds row (l % 16), 32 bytes of K-chunk (l / 16);
+//   B (128 x 16): lane l holds column (l % 16), the same 32-byte K-chunk;
+//   C (16 x 16):  lane l holds rows 4*(l/16) + j, j = 0..3, column (l % 16).
+// A and B place the 128-long reduction index identically, so loading q rows
+// and K rows with the same byte pattern gives the exact dot products.
+// Rows of A are heads (16 per M-tile), columns of B are tokens (16 per
+// N-tile); a 64-token page is 4 N-tiles.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ i32x8 load_frag_global(const uint8_t* row32) {
+  const uint4 x = *reinterpret_cast<const uint4*>(row32);
+  const uint4 y = *reinterpret_cast<const uint4*>(row32 + 16);
+  i32x8 v = {(int)x.x, (int)x.y, (int)x.z, (int)x.w,
+             (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+  return v;
+}
+
+// A fragments of one query row (MT M-tiles of 16 heads; heads >= H are 0).
+template <int MT>
+__device__ __forceinline__ void load_q_frags(const uint8_t* q8_row, int H,
+                                             i32x8 (&qa)[MT]) {
+  const int lane = lane_id();
+  const int i16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int head = 16 * m + i16;
+    if (head < H) {
+      qa[m] = load_frag_global(q8_row + head * kHeadDim + 32 * g);
+    } else {
+      qa[m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+}
+
+// Per-lane effective head weights w[h] * s_q[h] for the C rows this lane
+// holds: head 16*m + 4*(lane/16) + j.
+template <int MT>
+__device__ __forceinline__ void load_head_weights(const float* w_row,
+                                                  const float* s_row, int H,
+                                                  float (&w)[MT][4]) {
+  const int g = lane_id() >> 4;
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int head = 16 * m + 4 * g + j;
+      w[m][j] = head < H ? w_row[head] * s_row[head] : 0.f;
+    }
+}
+
+// sum over this lane's heads of w * ReLU(dot) for one N-tile.
+template <int MT>
+__device__ __forceinline__ float head_reduce(const f32x4 (&acc)[MT],
+                                             const float (&w)[MT][4]) {
+  float v = 0.f;
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v = fmaf(w[m][j], fmaxf(acc[m][j], 0.f), v);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Row-wise logits (decode shape: few query rows per request).  Grid:
+// x = query row, y = page group; 4 waves per workgroup, each wave scores
+// `ppw` consecutive pages of its row straight from HBM into MFMA registers
+// (each K byte is used by exactly one row, so there is nothing to share
+// through LDS).  Lane l stores the logit of token l of the page: one
+// coalesced 256-byte store per page.
+// ---------------------------------------------------------------------------
+template <int MT>
+__global__ __launch_bounds__(256) void logits_row_kernel(LogitsArgs a,
+                                                         int ppw) {
+  const int64_t t = blockIdx.x;
+  const int wave = wave_uniform(threadIdx.x >> 6);
+  const int lane = lane_id();
+  const int p = a.positions[t];
+  if (p < 0 || p >= a.ld || (int64_t)(p >> 6) >= a.bt_stride) {
+    if (threadIdx.x == 0 && blockIdx.y == 0) raise_flag(kErrPositionOutOfRange);
+    return;
+  }
+  const int npages = (p >> 6) + 1;
+  const int j0 = (blockIdx.y * 4 + wave) * ppw;
+  if (j0 >= npages) return;
+  const int j1 = min(j0 + ppw, npages);
+  const int r = wave_uniform(request_of_row(a.qsl, a.R, t));
+  const int32_t* bt = a.block_table + (int64_t)r * a.bt_stride;
+  const int i16 = lane & 15, g = lane >> 4;
+
+  i32x8 qa[MT];
+  load_q_frags<MT>(a.q8 + t * a.H * kHeadDim, a.H, qa);
+  float w[MT][4];
+  load_head_weights<MT>(a.weights + t * a.H, a.q_scale + t * a.H, a.H, w);
+  float* out = a.logits + t * a.ld;
+
+  for (int jp = j0; jp < j1; ++jp) {
+    const int page = wave_uniform(bt[jp]);
+    const int s = jp * kPageTokens + lane;
+    if (page < 0 || (int64_t)page >= a.num_pages) {
+      if (lane == 0) raise_flag(kErrPageOutOfRange);
+      out[s] = -INFINITY;
+      continue;
+    }
+    const uint8_t* pg = a.k_cache + (int64_t)page * kPageBytes;
+    i32x8 kb[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      kb[nt] = load_frag_global(pg + (16 * nt + i16) * kHeadDim + 32 * g);
+    const float kscale = reinterpret_cast<const float*>(pg + kPageKeyBytes)[lane];
+    float v[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      f32x4 acc[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        acc[m] = mfma16x16x128_fp8(qa[m], kb[nt], f32x4{0.f, 0.f, 0.f, 0.f});
+      v[nt] = head_reduce<MT>(acc, w);
+    }
+    const float tot = reduce_scatter4(v[0], v[1], v[2], v[3]);
+    out[s] = (s <= p) ? tot * kscale : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Tiled logits (several query rows of one request share every K page: the
+// prefill chunk and the long-context tail).  A workgroup of 8 waves owns a
+// tile of 16 consecutive rows of one request and a range of pages; each
+// page (8192 key bytes + 256 scale bytes) is read from HBM once per tile with
+// fully coalesced 16-byte loads, staged in LDS (double-buffered, rows padded
+// to 144 bytes so the MFMA-layout reads are bank-conflict free) and used by
+// all 8 waves; wave w scores rows 2w and 2w+1.  Grid: x = page split,
+// y = tile (tiles of request r are numbered after those of requests < r).
+// ---------------------------------------------------------------------------
+constexpr int kTileRows = 16;
+constexpr int kTileWaves = 8;
+constexpr int kLdsRow = 144;
+
+// Tile y -> (request, first row, rows).  One wave scans query_start_loc.
+__device__ void find_tile(const int32_t* qsl, int R, int y, int* s_info) {
+  const int lane = lane_id();
+  int base = 0;
+  for (int c = 0; c < R; c += 64) {
+    const int r = c + lane;
+    int n = 0;
+    if (r < R) n = (qsl[r + 1] - qsl[r] + kTileRows - 1) / kTileRows;
+    if (n < 0) n = 0;
+    int incl = n;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    const int excl = incl - n;
+    if (r < R && y >= base + excl && y < base + incl) {
+      s_info[0] = r;
+      s_info[1] = qsl[r] + (y - base - excl) * kTileRows;
+      s_info[2] = min(kTileRows, qsl[r + 1] - s_info[1]);
+    }
+    base += __shfl(incl, 63);
+  }
+}
+
+template <int MT>
+__global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a,
+                                                          int pages_per_split) {
+  __shared__ __align__(16) uint8_t s_keys[2][kPageTokens * kLdsRow];
+  __shared__ __align__(16) float s_scale[2][kPageTokens];
+  __shared__ int s_ok[2];
+  __shared__ int s_info[4];
+  __shared__ int s_pos[kTileRows];
+
+  const int tid = threadIdx.x;
+  const int wave = wave_uniform(tid >> 6);
+  const int lane = lane_id();
+  if (tid == 0) { s_info[0] = -1; s_info[1] = 0; s_info[2] = 0; }
+  __syncthreads();
+  if (wave == 0) find_tile(a.qsl, a.R, blockIdx.y, s_info);
+  __syncthreads();
+  const int r = s_info[0];
+  if (r < 0) return;                         // grid bound beyond last tile
+  const int64_t row0 = s_info[1];
+  const int nrows = s_info[2];
+  if (tid < kTileRows) {
+    int p = -1;
+    if (tid < nrows && row0 + tid >= 0 && row0 + tid < a.T) {
+      p = a.positions[row0 + tid];
+      if (p < 0 || p >= a.ld || (int64_t)(p >> 6) >= a.bt_stride) {
+        raise_flag(kErrPositionOutOfRange);
+        p = -1;
+      }
+    }
+    s_pos[tid] = p;
+  }
+  __syncthreads();
+  int maxp = -1;
+#pragma unroll
+  for (int i = 0; i < kTileRows; ++i) maxp = max(maxp, s_pos[i]);
+  const int npages = (maxp >> 6) + 1;        // 0 when no valid row
+  const int jb = blockIdx.x * pages_per_split;
+  const int je = min(jb + pages_per_split, npages);
+  if (jb >= je) return;
+
+  const int32_t* bt = a.block_table + (int64_t)r * a.bt_stride;
+  const int i16 = lane & 15, g = lane >> 4;
+
+  // This wave's two rows.
+  int prow[2];
+  i32x8 qa[2][MT];
+  float w[2][MT][4];
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int lr = 2 * wave + rr;
+    prow[rr] = s_pos[lr];
+    if (prow[rr] >= 0) {
+      const int64_t t = row0 + lr;
+      load_q_frags<MT>(a.q8 + t * a.H * kHeadDim, a.H, qa[rr]);
+      load_head_weights<MT>(a.weights + t * a.H, a.q_scale + t * a.H, a.H,
+                            w[rr]);
+    } else {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        qa[rr][m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[rr][m][j] = 0.f;
+      }
+    }
+  }
+
+  // Cooperative page copy: thread i moves key bytes [16 i, 16 i + 16)
+  // (token i / 8, chunk i % 8); threads 0..15 also move the 256 scale bytes.
+  const int ctok = tid >> 3, cchunk = tid & 7;
+  auto fetch = [&](int jp, uint4& kreg, uint4& sreg, bool& ok) {
+    const int page = bt[jp];
+    ok = page >= 0 && (int64_t)page < a.num_pages;
+    if (!ok) {
+      kreg = make_uint4(0, 0, 0, 0);
+      sreg = make_uint4(0, 0, 0, 0);
+      return;
+    }
+    const uint8_t* pg = a.k_cache + (int64_t)page * kPageBytes;
+    kreg = *reinterpret_cast<const uint4*>(pg + tid * 16);
+    if (tid < 16) sreg = *reinterpret_cast<const uint4*>(pg + kPageKeyBytes + tid * 16);
+  };
+  auto stash = [&](int buf, const uint4& kreg, const uint4& sreg, bool ok) {
+    *reinterpret_cast<uint4*>(&s_keys[buf][ctok * kLdsRow + cchunk * 16]) = kreg;
+    if (tid < 16) *reinterpret_cast<uint4*>(&s_scale[buf][tid * 4]) = sreg;
+    if (tid == 0) s_ok[buf] = ok;
+  };
+
+  uint4 kreg, sreg = make_uint4(0, 0, 0, 0);
+  bool ok;
+  fetch(jb, kreg, sreg, ok);
+  if (!ok && tid == 0) raise_flag(kErrPageOutOfRange);
+  stash(0, kreg, sreg, ok);
+
+  for (int jp = jb; jp < je; ++jp) {
+    const int buf = (jp - jb) & 1;
+    const bool more = jp + 1 < je;
+    if (more) {
+      fetch(jp + 1, kreg, sreg, ok);
+      if (!ok && tid == 0) raise_flag(kErrPageOutOfRange);
+    }
+    __syncthreads();
+    const uint8_t* kb_lds = s_keys[buf];
+    const bool page_ok = s_ok[buf] != 0;
+#pragma unroll
+    for (int ntp = 0; ntp < 2; ++ntp) {
+      i32x8 kb[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint8_t* src = kb_lds + (16 * (2 * ntp + q) + i16) * kLdsRow + 32 * g;
+        const uint4 x = *reinterpret_cast<const uint4*>(src);
+        const uint4 y = *reinterpret_cast<const uint4*>(src + 16);
+        kb[q] = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w,
+                      (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+      }
+      float v[2][2];
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          f32x4 acc[MT];
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+            acc[m] = mfma16x16x128_fp8(qa[rr][m], kb[q], f32x4{0.f, 0.f, 0.f, 0.f});
+          v[rr][q] = head_reduce<MT>(acc, w[rr]);
+        }
+      // lane group g ends with (row g >> 1, N-tile 2*ntp + (g & 1))
+      const float tot = reduce_scatter4(v[0][0], v[0][1], v[1][0], v[1][1]);
+      const int rr = g >> 1;
+      const int tok = 16 * (2 * ntp + (g & 1)) + i16;
+      const int pr = rr ? prow[1] : prow[0];
+      if (pr >= 0) {
+        const int s = jp * kPageTokens + tok;
+        const float val = (s <= pr && page_ok) ? tot * s_scale[buf][tok]
+                                               : -INFINITY;
+        a.logits[(row0 + 2 * wave + rr) * a.ld + s] = val;
+      }
+    }
+    if (more) stash(buf ^ 1, kreg, sreg, ok);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers.
+// ---------------------------------------------------------------------------
+hipError_t launch_quantize_q(const uint16_t* q_bf16, int64_t blocks,
+                             uint8_t* q8, float* q_scale, hipStream_t stream) {
+  if (blocks <= 0) return hipSuccess;
+  const int64_t grid = (blocks + 15) / 16;
+  hipLaunchKernelGGL(quantize_q_kernel, dim3((unsigned)grid), dim3(256), 0,
+                     stream, q_bf16, blocks, q8, q_scale);
+  return hipGetLastError();
+}
+
+template <int MT>
+static hipError_t launch_logits_mt(const LogitsArgs& a, hipStream_t stream,
+                                   bool tiled, int64_t max_pages) {
+  const Options& o = options();
+  if (!tiled) {
+    int ppw = o.row_pages_per_wave;
+    if (ppw <= 0) {
+      // aim for >= 2048 workgroups of 4 waves before giving a wave 2+ pages
+      const int64_t waves = a.T * max_pages;
+      ppw = (int)std::max<int64_t>(1, std::min<int64_t>(8, waves / (4 * 2048)));
+    }
+    const int64_t gy = (max_pages + 4 * ppw - 1) / (4 * ppw);
+    hipLaunchKernelGGL(logits_row_kernel<MT>, dim3((unsigned)a.T, (unsigned)gy),
+                       dim3(256), 0, stream, a, ppw);
+  } else {
+    const int64_t tiles = (a.T + kTileRows - 1) / kTileRows + a.R;
+    int pps = o.tile_pages_per_split;
+    if (pps <= 0) {
+      const int64_t real_tiles = (a.T + kTileRows - 1) / kTileRows;
+      int64_t splits = (2048 + real_tiles - 1) / real_tiles;
+      splits = std::max<int64_t>(1, std::min<int64_t>(splits, max_pages));
+      pps = (int)std::max<int64_t>(8, (max_pages + splits - 1) / splits);
+    }
+    const int64_t gx = (max_pages + pps - 1) / pps;
+    hipLaunchKernelGGL(logits_tile_kernel<MT>, dim3((unsigned)gx, (unsigned)tiles),
+                       dim3(kTileWaves * 64), 0, stream, a, pps);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_logits(const LogitsArgs& a, hipStream_t stream) {
+  if (a.T <= 0) return hipSuccess;
+  const int64_t max_pages = std::min<int64_t>(a.bt_stride, a.ld / kPageTokens);
+  const Options& o = options();
+  bool tiled = a.T > 2 * (int64_t)a.R;
+  if (o.logits_kernel == 1) tiled = false;
+  if (o.logits_kernel == 2) tiled = true;
+  const int mt = (a.H + 15) / 16;
+  switch (mt) {
+    case 1: return launch_logits_mt<1>(a, stream, tiled, max_pages);
+    case 2: return launch_logits_mt<2>(a, stream, tiled, max_pages);
+    case 3: return launch_logits_mt<3>(a, stream, tiled, max_pages);
+    default: return launch_logits_mt<4>(a, stream, tiled, max_pages);
+  }
+}
+
+hipError_t read_logits_flags(unsigned* flags, bool reset) {
+  hipError_t e = hipMemcpyFromSymbol(flags, HIP_SYMBOL(g_err_logits),
+                                     sizeof(unsigned), 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess || !reset) return e;
+  const unsigned zero = 0;
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_err_logits), &zero, sizeof(unsigned), 0,
+                           hipMemcpyHostToDevice);
+}
+
+}  // namespace dsa

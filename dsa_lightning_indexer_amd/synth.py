@@ -96,14 +96,15 @@ def write_pages(k_cache, pages, k32):
     """Store tokens 0..N-1 of one request into its physical pages."""
     n = k32.shape[0]
     codes, scale = _quantize_tokens_fp8(k32)
-    for j, P in enumerate(pages):
-        a, b = j * PAGE_TOKENS, min(n, (j + 1) * PAGE_TOKENS)
-        if a >= b:
-            break
-        cnt = b - a
-        k_cache[P, : cnt * HEAD_DIM] = codes[a:b].reshape(-1)
-        k_cache[P, PAGE_KEY_BYTES: PAGE_KEY_BYTES + 4 * cnt] = \
-            scale[a:b].astype("<f4").view(np.uint8)
+    npg = (n + PAGE_TOKENS - 1) // PAGE_TOKENS
+    pages = np.asarray(pages[:npg], dtype=np.int64)
+    pad = npg * PAGE_TOKENS - n
+    if pad:
+        codes = np.concatenate([codes, np.zeros((pad, HEAD_DIM), np.uint8)])
+        scale = np.concatenate([scale, np.zeros(pad, np.float32)])
+    k_cache[pages, :PAGE_KEY_BYTES] = codes.reshape(npg, PAGE_KEY_BYTES)
+    k_cache[pages, PAGE_KEY_BYTES:] = \
+        scale.astype("<f4").view(np.uint8).reshape(npg, PAGE_TOKENS * 4)
 
 
 def page_layout(rng, contexts, pool_pages=None, bt_width=None):

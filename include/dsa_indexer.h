@@ -1,0 +1,223 @@
+/*
+ * dsa_indexer.h -- C ABI of the MI355X (gfx950) DeepSeek Sparse Attention
+ * lightning-indexer library (libdsa_indexer.so).
+ *
+ * The library scores, for every query token, each earlier cached token of a
+ * paged FP8 indexer-K cache, selects the causal top-k token positions and
+ * writes them into a shared int32 index buffer; IndexCache "S" layers reuse
+ * the buffer written by the previous "F" layer of the same forward pass.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [KVB] GLM-5.3 inference pipeline (12): paging budget, prefix hits and
+ *        eviction of the main KV and indexer caches -- byte accounts (132 B per
+ *        token per layer: 128 FP8 key bytes + one fp32 scale per 128-element
+ *        block), SGLang buffer shape (64-token pages of 8448 bytes), eviction
+ *        (keys first, then scales, inside every page), top-k index buffer and
+ *        logits budget (fp32 [rows, cols], rows aligned to 256 columns).
+ *  [HBM] HBM index architecture design (vLLM research notes), sections 2.3
+ *        and 4.2 -- block_table / positions / query_start_loc and
+ *        slot = block_table[req, pos / 64] * 64 + pos % 64.
+ *  [IC]  vLLM IndexCache practical guide -- section 2 (F/S layers, shared
+ *        buffer, -1 clear, reuse within one pass), section 3 (index_topk_freq,
+ *        index_topk_pattern, index_skip_topk_offset and the skip rule),
+ *        section 4 (pattern semantics), section 5 item 3 (MTP layers).
+ *  [RFC] RFC: DeepseekV32 model support (Ascend msmodeling), section 2.1.3 --
+ *        the indexer path is FP8 (fp8_index operator).
+ * The score (per-head dot product q_h . k_s, ReLU, per-head weighted sum) is
+ * the lightning-indexer score of DeepSeek-V3.2 (arXiv:2512.02556, cited by
+ * [KVB]); the pages print no formula for it.
+ *
+ * Conventions for every entry point:
+ *  - Pointers documented "device" are device (HBM) addresses on the current
+ *    HIP device; "host" pointers are ordinary host memory.
+ *  - The caller owns every buffer.  No entry point allocates device memory;
+ *    scratch comes from a caller-provided workspace sized by the *_size
+ *    queries.
+ *  - `stream` is a hipStream_t passed as void* (NULL = default stream).  All
+ *    device work is enqueued asynchronously on it; nothing synchronises.
+ *  - Return value: DSA_OK (0) or a negative dsa_status.  Argument errors are
+ *    detected on the host before anything is enqueued; the message is
+ *    available from dsa_last_error() on the calling thread.
+ *  - Device-side range errors (a block_table entry outside the page pool, a
+ *    position outside the logits row or block-table row) never fault: the
+ *    affected logits become -inf and a sticky flag is raised, readable with
+ *    dsa_device_error_flags().
+ *  - Supported shapes: head_dim == 128, page_size == 64, 1 <= H <= 64.
+ */
+#ifndef DSA_INDEXER_H
+#define DSA_INDEXER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = -1,   /* null pointer, bad size, bad pattern, ...   */
+  DSA_ERR_UNSUPPORTED = -2,   /* head_dim != 128, page_size != 64, H > 64   */
+  DSA_ERR_WORKSPACE = -3,     /* workspace smaller than the size query      */
+  DSA_ERR_HIP = -4            /* a HIP runtime call or launch failed        */
+} dsa_status;
+
+#define DSA_HEAD_DIM 128
+#define DSA_PAGE_TOKENS 64
+#define DSA_PAGE_BYTES 8448          /* 64 x 128 key bytes, then 64 x fp32  */
+#define DSA_TOKEN_BYTES 132
+#define DSA_LOGITS_ROW_ALIGN 256     /* ld % 256 == 0 ([KVB] logits budget) */
+#define DSA_MAX_HEADS 64
+
+/* Device error flags (dsa_device_error_flags). */
+#define DSA_DEVERR_PAGE_OUT_OF_RANGE 1u
+#define DSA_DEVERR_POSITION_OUT_OF_RANGE 2u
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* dsa_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int dsa_version(void);
+
+/*
+ * dsa_quantize_q -- per (token, head) FP8 quantisation of the indexer query
+ * ([RFC] 2.1.3: FP8 indexer path; [KVB]: one fp32 scale per 128-element
+ * block, the granularity the K cache uses).
+ *   q_bf16   device, bf16 [T, H, 128], row-major, contiguous.
+ *   q_fp8    device, out: OCP e4m3fn codes [T, H, 128].
+ *   q_scale  device, out: fp32 [T, H].
+ * Per 128-element block: amax = max|q|, s = amax / 448 (IEEE fp32 division;
+ * s = 1 when amax == 0), code = e4m3fn(q / s) with IEEE fp32 division,
+ * round-to-nearest-even and saturation to +-448.  T == 0 is a no-op.
+ */
+int dsa_quantize_q(const void* q_bf16, int64_t T, int H, int head_dim,
+                   uint8_t* q_fp8, float* q_scale, void* stream);
+
+/*
+ * dsa_indexer_logits -- causal lightning-indexer logits over a paged FP8
+ * indexer-K cache.
+ *   q_fp8, q_scale   device, output of dsa_quantize_q: [T, H, 128], [T, H].
+ *   weights          device, fp32 [T, H]: per (token, head) weight.
+ *   k_cache          device, uint8 [num_pages, 8448]: page P holds the
+ *                    e4m3fn keys of its 64 tokens (64 x 128 bytes) followed
+ *                    by their 64 little-endian fp32 scales ([KVB]).
+ *   block_table      device, int32 [R, bt_stride]: physical page of logical
+ *                    page j of request r ([HBM] 2.3).
+ *   query_start_loc  device, int32 [R + 1]: rows of request r are
+ *                    [qsl[r], qsl[r+1]) ([HBM] 4.2).
+ *   positions        device, int32 [T]: absolute position p_t of row t.
+ *   logits           device, out: fp32 [T, ld], ld % 256 == 0 and
+ *                    ld > every p_t.
+ * Row t (request r, position p) gets, for every s <= p,
+ *   logits[t, s] = sum_h w[t,h] * max(qhat[t,h,:] . khat[s,:], 0)
+ * with qhat = code * q_scale and khat = code * k_scale, accumulated in fp32;
+ * columns p < s < 64 * ceil((p+1)/64) are written as -inf; later columns are
+ * not written.  Requires the block_table row to hold ceil((p+1)/64) valid
+ * pages.  head_dim must be 128, page_size 64, 1 <= H <= 64.
+ */
+int dsa_indexer_logits(const uint8_t* q_fp8, const float* q_scale,
+                       const float* weights, const uint8_t* k_cache,
+                       int64_t num_pages, const int32_t* block_table,
+                       int64_t bt_stride, const int32_t* query_start_loc,
+                       const int32_t* positions, int64_t T, int R, int H,
+                       int head_dim, int page_size, float* logits, int64_t ld,
+                       void* stream);
+
+/*
+ * dsa_indexer_topk -- per-row causal top-k into the shared index buffer
+ * ([IC] 2: rows cleared to -1, then the top-k scattered in; [KVB] top-k
+ * buffer: int32 [max_num_batched_tokens, index_topk]).
+ *   logits     device, fp32 [T, ld]; row t reads columns 0..p_t only.
+ *   positions  device, int32 [T].
+ *   out        device, out: int32 [T, out_ld], out_ld >= k; slots [0, k) of
+ *              every row are written.
+ * n = p_t + 1.  If n <= k the row is 0, 1, ..., n-1 followed by -1.
+ * Otherwise it holds the k token positions with the largest logits, ties at
+ * the k-th value broken toward the lower position, listed in ascending
+ * position order.  workspace/ws_bytes: dsa_topk_workspace_size() bytes of
+ * device memory (may be 0 / NULL when that size is 0).
+ */
+int dsa_indexer_topk(const float* logits, int64_t ld, const int32_t* positions,
+                     int64_t T, int k, int32_t* out, int64_t out_ld,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+size_t dsa_topk_workspace_size(int64_t T, int64_t ld, int k);
+
+/*
+ * dsa_index_cache_mask -- IndexCache layer rule ([IC] 3, 4, 5.3), host only.
+ *   pattern            host, nullable: one 'F'/'S' per DSA layer; overrides
+ *                      freq when non-NULL; layers past its end are F.
+ *   freq               index_topk_freq >= 1 (1 = every layer computes).
+ *   offset             index_skip_topk_offset (the pages' default is 2).
+ *   num_hidden_layers  layers >= this are MTP/nextn layers: always F; a
+ *                      negative value means there are none.
+ *   is_skip            host, out: uint8 [num_layers], 1 = S (reuse), 0 = F.
+ * Without a pattern: S iff max(layer - offset + 1, 0) % freq != 0.
+ * A pattern character other than 'F' or 'S' is an error.
+ */
+int dsa_index_cache_mask(const char* pattern, int freq, int offset,
+                         int num_layers, int num_hidden_layers,
+                         uint8_t* is_skip);
+
+/* Per-layer inputs of dsa_index_cache_run (ignored for S layers). */
+typedef struct {
+  const void* q_bf16;      /* device, bf16 [T, H, 128]                     */
+  const float* weights;    /* device, fp32 [T, H]                          */
+  const uint8_t* k_cache;  /* device, uint8 [num_pages, 8448]              */
+  int64_t num_pages;
+} dsa_layer_inputs;
+
+/* Called on the calling thread after layer `layer`'s work is enqueued on the
+ * stream (work the callback enqueues on the same stream runs after it). */
+typedef void (*dsa_layer_callback)(int layer, int is_full,
+                                   int32_t* topk_buffer, void* user);
+
+/*
+ * dsa_index_cache_run -- one forward pass over a stack of DSA layers ([IC] 2).
+ * F layers quantise q, score and write the top-k of rows [0, T) into
+ * topk_buffer (int32 [buffer_rows, k], device); S layers enqueue nothing and
+ * leave the buffer as the previous F layer wrote it.  Layer l's inputs are
+ * layers[l] (host array of num_layers entries); block_table,
+ * query_start_loc and positions (device) are shared by all layers.
+ *   snapshots    device, nullable: int32 [num_layers, T, k]; after layer l
+ *                rows [0, T) of the buffer are copied to snapshots[l].
+ *   is_skip_out  host, nullable: uint8 [num_layers], the mask used.
+ *   cb, cb_user  nullable per-layer callback.
+ *   workspace    device, dsa_run_workspace_size(T, H, ld, k) bytes.
+ * Rejects (DSA_ERR_INVALID_ARG) a mask whose first layer is S: it would read
+ * a buffer no layer has written in this pass ([IC] 5.3).
+ */
+int dsa_index_cache_run(const char* pattern, int freq, int offset,
+                        int num_layers, int num_hidden_layers,
+                        const dsa_layer_inputs* layers,
+                        const int32_t* block_table, int64_t bt_stride,
+                        const int32_t* query_start_loc,
+                        const int32_t* positions, int64_t T, int R, int H,
+                        int64_t ld, int k, int32_t* topk_buffer,
+                        int64_t buffer_rows, int32_t* snapshots,
+                        uint8_t* is_skip_out, dsa_layer_callback cb,
+                        void* cb_user, void* workspace, size_t ws_bytes,
+                        void* stream);
+
+size_t dsa_run_workspace_size(int64_t T, int H, int64_t ld, int k);
+
+/*
+ * dsa_device_error_flags -- sticky device-side range-error flags
+ * (DSA_DEVERR_*) raised since the last reset; synchronises the device.
+ * reset != 0 clears them.  Returns the flags, or a negative dsa_status.
+ */
+int dsa_device_error_flags(int reset);
+
+/*
+ * dsa_set_option -- tuning/testing knobs; returns the previous value or
+ * DSA_ERR_INVALID_ARG for an unknown key.  Value 0 restores the automatic
+ * choice.  Keys: "logits_kernel" (1 row-wise, 2 tiled), "row_pages_per_wave",
+ * "tile_pages_per_split", "topk_kernel" (1 one workgroup per row).
+ */
+int dsa_set_option(const char* key, int value);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_INDEXER_H */

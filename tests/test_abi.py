@@ -1,0 +1,203 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+include/dsa_indexer.h declares, and rejects bad arguments on the host before
+touching the device.  Host-only entry points (mask, sizes, options) run."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from dsa_lightning_indexer_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa_indexer.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(binding.LIB_PATH),
+                                reason="library not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(dsa_[a-z_0-9]+)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ["dsa_indexer_logits", "dsa_indexer_topk", "dsa_index_cache_run",
+                 "dsa_index_cache_mask", "dsa_quantize_q", "dsa_last_error"]:
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported():
+    L = binding.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(declared_functions()) == set(binding._SIGNATURES)
+
+
+def test_version_and_last_error():
+    L = binding.lib()
+    assert L.dsa_version() >= 100
+    assert isinstance(L.dsa_last_error(), bytes)
+
+
+def test_mask_via_abi_matches_pages_example(golden):
+    g = golden("index_cache_examples.json")
+    m = binding.dsa_index_cache_mask(61, freq=4, offset=2)
+    assert [i for i, s in enumerate(m) if not s] == \
+        g["freq4_offset2_61"]["full_layers"]
+    p = g["pattern_61"]["pattern"]
+    m = binding.dsa_index_cache_mask(61, pattern=p, freq=4, offset=2)
+    assert [i for i, s in enumerate(m) if not s] == g["pattern_61"]["full_layers"]
+    assert not any(binding.dsa_index_cache_mask(61))           # defaults
+    m = binding.dsa_index_cache_mask(64, pattern="F" + "S" * 63,
+                                     num_hidden_layers=61)
+    assert all(m[1:61]) and not any(m[61:])
+    assert binding.dsa_index_cache_mask(5, pattern="FS") == \
+        [False, True, False, False, False]
+
+
+@pytest.mark.parametrize("kw", [dict(freq=0), dict(pattern="FFX"),
+                                dict(pattern="fs"), dict(freq=-3)])
+def test_mask_rejects_bad_config(kw):
+    with pytest.raises(binding.DsaError) as e:
+        binding.dsa_index_cache_mask(8, **kw)
+    assert e.value.status == binding.DSA_ERR_INVALID_ARG
+
+
+def test_mask_matches_oracle_on_many_configs():
+    from oracle import index_cache
+    import numpy as np
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        L = int(rng.integers(0, 80))
+        freq = int(rng.integers(1, 9))
+        off = int(rng.integers(-3, 6))
+        nh = int(rng.integers(0, L + 1)) if rng.random() < 0.3 else None
+        pat = None
+        if rng.random() < 0.4:
+            pat = "".join(rng.choice(["F", "S"], size=int(rng.integers(0, 90))))
+        ours = binding.dsa_index_cache_mask(L, pattern=pat, freq=freq,
+                                            offset=off,
+                                            num_hidden_layers=-1 if nh is None else nh)
+        ref = index_cache.skip_mask(L, pattern=pat, freq=freq, offset=off,
+                                    num_hidden_layers=nh)
+        assert ours == ref.tolist()
+
+
+def _logits_call(**over):
+    args = dict(q_fp8=None, q_scale=None, weights=None, k_cache=None,
+                num_pages=4, block_table=None, bt_stride=4, qsl=None,
+                positions=None, T=8, R=1, H=4, head_dim=128, page_size=64,
+                logits=None, ld=256, stream=None)
+    args.update(over)
+    return binding.lib().dsa_indexer_logits(*args.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(head_dim=64), binding.DSA_ERR_UNSUPPORTED),
+    (dict(page_size=32), binding.DSA_ERR_UNSUPPORTED),
+    (dict(H=65), binding.DSA_ERR_UNSUPPORTED),
+    (dict(H=0), binding.DSA_ERR_UNSUPPORTED),
+    (dict(ld=100), binding.DSA_ERR_INVALID_ARG),
+    (dict(ld=0), binding.DSA_ERR_INVALID_ARG),
+    (dict(T=-1), binding.DSA_ERR_INVALID_ARG),
+    (dict(R=0), binding.DSA_ERR_INVALID_ARG),
+    (dict(bt_stride=0), binding.DSA_ERR_INVALID_ARG),
+    (dict(num_pages=0), binding.DSA_ERR_INVALID_ARG),
+    (dict(), binding.DSA_ERR_INVALID_ARG),          # null device pointers
+])
+def test_logits_rejects_bad_arguments(over, status):
+    assert _logits_call(**over) == status
+    assert binding.lib().dsa_last_error()
+
+
+def test_logits_empty_batch_is_noop():
+    assert _logits_call(T=0) == binding.DSA_OK
+
+
+def test_topk_rejects_bad_arguments():
+    L = binding.lib()
+    fake = ctypes.c_void_p(0x1000)
+    assert L.dsa_indexer_topk(fake, 100, fake, 4, 8, fake, 8, None, 0, None) \
+        == binding.DSA_ERR_INVALID_ARG                        # ld % 256
+    assert L.dsa_indexer_topk(fake, 256, fake, 4, 0, fake, 8, None, 0, None) \
+        == binding.DSA_ERR_INVALID_ARG                        # k < 1
+    assert L.dsa_indexer_topk(fake, 256, fake, 4, 8, fake, 4, None, 0, None) \
+        == binding.DSA_ERR_INVALID_ARG                        # out_ld < k
+    assert L.dsa_indexer_topk(None, 256, None, 4, 8, None, 8, None, 0, None) \
+        == binding.DSA_ERR_INVALID_ARG                        # nulls
+    assert L.dsa_indexer_topk(None, 256, None, 0, 8, None, 8, None, 0, None) \
+        == binding.DSA_OK                                     # empty
+
+
+def test_quantize_rejects_bad_arguments():
+    L = binding.lib()
+    assert L.dsa_quantize_q(None, 4, 4, 64, None, None, None) == \
+        binding.DSA_ERR_UNSUPPORTED
+    assert L.dsa_quantize_q(None, 4, 4, 128, None, None, None) == \
+        binding.DSA_ERR_INVALID_ARG
+    assert L.dsa_quantize_q(None, 0, 4, 128, None, None, None) == binding.DSA_OK
+
+
+def _fake_layers(n=3):
+    arr = (binding.LayerInputs * n)()
+    for i in range(n):
+        arr[i] = binding.LayerInputs(0x1000, 0x1000, 0x1000, 4)
+    return arr
+
+
+def _run_call(**over):
+    args = dict(pattern=None, freq=1, offset=2, L=3, nh=-1,
+                layers=_fake_layers(),
+                bt=ctypes.c_void_p(0x1000), bt_stride=4,
+                qsl=ctypes.c_void_p(0x1000), pos=ctypes.c_void_p(0x1000),
+                T=4, R=1, H=4, ld=256, k=8, buf=ctypes.c_void_p(0x1000),
+                buf_rows=4, snaps=None, skip=None,
+                cb=binding.LAYER_CALLBACK(0), user=None,
+                ws=ctypes.c_void_p(0x1000), ws_bytes=1 << 30, stream=None)
+    args.update(over)
+    return binding.lib().dsa_index_cache_run(*args.values())
+
+
+def test_run_rejects_first_layer_s():
+    assert _run_call(pattern=b"SFF") == binding.DSA_ERR_INVALID_ARG
+    assert b"layer 0" in binding.lib().dsa_last_error()
+    assert _run_call(freq=2, offset=0) == binding.DSA_ERR_INVALID_ARG
+
+
+def test_run_rejects_bad_arguments():
+    assert _run_call(pattern=b"FXF") == binding.DSA_ERR_INVALID_ARG
+    assert _run_call(freq=0) == binding.DSA_ERR_INVALID_ARG
+    assert _run_call(ws_bytes=16) == binding.DSA_ERR_WORKSPACE
+    assert _run_call(buf_rows=2) == binding.DSA_ERR_INVALID_ARG
+    assert _run_call(k=0) == binding.DSA_ERR_INVALID_ARG
+    assert _run_call(ld=300) == binding.DSA_ERR_INVALID_ARG
+    # F layer with null inputs
+    arr = (binding.LayerInputs * 3)()
+    assert _run_call(layers=arr) == binding.DSA_ERR_INVALID_ARG
+    assert b"layer 0" in binding.lib().dsa_last_error()
+
+
+def test_run_with_no_rows_only_reports_mask():
+    skip = (ctypes.c_uint8 * 5)()
+    assert _run_call(L=5, freq=2, offset=1, T=0, layers=_fake_layers(5),
+                     skip=skip, ws=None, ws_bytes=0) == binding.DSA_OK
+    assert list(skip) == [0, 1, 0, 1, 0]
+
+
+def test_workspace_sizes():
+    assert binding.dsa_run_workspace_size(64, 64, 8192, 2048) >= \
+        64 * 64 * 128 + 64 * 64 * 4 + 64 * 8192 * 4
+    assert binding.dsa_run_workspace_size(0, 64, 8192, 2048) == 0
+
+
+def test_set_option_roundtrip():
+    prev = binding.dsa_set_option("logits_kernel", 2)
+    assert binding.dsa_set_option("logits_kernel", prev) == 2
+    with pytest.raises(binding.DsaError):
+        binding.dsa_set_option("no_such_knob", 1)

@@ -1,0 +1,265 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Tolerances are documented in tests/parity.py."""
+
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from dsa_lightning_indexer_amd import binding, synth
+from oracle import indexer as oi
+from tests import parity
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(),
+                                 reason="needs a GPU")]
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _clear_flags():
+    binding.dsa_device_error_flags(reset=True)
+    yield
+    for key in ("logits_kernel", "row_pages_per_wave", "tile_pages_per_split",
+                "topk_kernel"):
+        binding.dsa_set_option(key, 0)
+
+
+def _assert_no_device_errors():
+    assert binding.dsa_device_error_flags(reset=True) == 0
+
+
+# ------------------------------------------------------------- quantise q --
+def _bf16(x):
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)) \
+        .to(torch.bfloat16)
+
+
+def test_quantize_q_bit_exact():
+    _say("case: quantize_q random + special blocks")
+    rng = np.random.default_rng(31)
+    q = rng.standard_normal((37, 8, 128)).astype(np.float32)
+    q[0, 0] = 0.0                                        # amax = 0
+    q[0, 1] = 2.0 ** -128                                # subnormal block
+    q[1, 0] *= 1e4                                       # large values
+    q[1, 1] = 0.0
+    q[1, 1, 5] = -3.0                                    # single nonzero
+    # amax 448 -> s = 1 exactly; entries at midpoints between FP8 codes
+    v = oi.fp8.positive_code_values()
+    mids = ((v[:-1] + v[1:]) / 2)[40:126]
+    q[2, 0, :] = 0.0
+    q[2, 0, 0] = 448.0
+    q[2, 0, 1:1 + 60] = mids[:60]
+    q[2, 1, :] = 0.0
+    q[2, 1, 0] = -448.0
+    q[2, 1, 1:1 + 26] = -mids[60:86]
+    qb = _bf16(q)
+    q8, qs = binding.dsa_quantize_q(qb.cuda())
+    torch.cuda.synchronize()
+    codes, s = oi.quantize_q(qb.float().numpy())
+    assert np.array_equal(qs.cpu().numpy().view(np.uint32), s.view(np.uint32))
+    assert np.array_equal(q8.cpu().numpy(), codes)
+
+
+def test_quantize_q_bit_exact_decode_shape():
+    _say("case: quantize_q decode batch")
+    b = synth.decode()
+    q8, qs = binding.dsa_quantize_q(b.q_bf16.cuda())
+    torch.cuda.synchronize()
+    codes, s = oi.quantize_q(b.q_f32)
+    assert np.array_equal(qs.cpu().numpy().view(np.uint32), s.view(np.uint32))
+    assert np.array_equal(q8.cpu().numpy(), codes)
+
+
+# ------------------------------------------------------------------- tiny --
+@pytest.mark.parametrize("kernel", [0, 1, 2])
+def test_tiny_logits_and_topk(kernel):
+    _say(f"case: tiny, logits kernel option {kernel}")
+    binding.dsa_set_option("logits_kernel", kernel)
+    b = synth.tiny()
+    _, _, lg, tk = parity.run_gpu(b)
+    lg, tk = lg.cpu().numpy(), tk.cpu().numpy()
+    ora = parity.oracle_logits(b)
+    mag = parity.magnitude(b)
+    for t in range(b.T):
+        p = int(b.positions[t])
+        parity.check_logits_row(lg[t], ora[t], p, f"tiny row {t}", mag[t])
+        assert np.all(np.isneginf(lg[t, p + 1: (p // 64 + 1) * 64]))
+        parity.check_topk_row(tk[t], ora[t, : p + 1], b.k, f"tiny row {t}")
+        parity.check_topk_exact_on_gpu_logits(tk[t], lg[t], p, b.k)
+    _assert_no_device_errors()
+
+
+# ----------------------------------------------------------------- decode --
+@pytest.mark.parametrize("kernel", [0, 2])
+def test_decode_batch_all_rows(kernel):
+    _say(f"case: decode batch (64 x U[1024,8192], H=64, k=2048), kernel {kernel}")
+    binding.dsa_set_option("logits_kernel", kernel)
+    b = synth.decode()
+    _, _, lg, tk = parity.run_gpu(b)
+    lg, tk = lg.cpu().numpy(), tk.cpu().numpy()
+    ora = parity.oracle_logits(b)
+    mag = parity.magnitude(b)
+    worst = 0.0
+    err_m = 0.0
+    padded = 0
+    for t in range(b.T):
+        p = int(b.positions[t])
+        worst = max(worst, parity.check_logits_row(lg[t], ora[t], p,
+                                                   f"decode row {t}", mag[t]))
+        parity.check_topk_row(tk[t], ora[t, : p + 1], b.k, f"decode row {t}")
+        parity.check_topk_exact_on_gpu_logits(tk[t], lg[t], p, b.k)
+        padded += p + 1 <= b.k
+        err_m = max(err_m, float(np.max(np.abs(lg[t, : p + 1] - ora[t, : p + 1])
+                                        / mag[t, : p + 1])))
+    _say(f"decode max rel logit err (|o| >= 1e-2 max) {worst:.3e}, "
+         f"max |err| / M = {err_m:.3e} (2^{np.log2(err_m):.1f}), "
+         f"padded rows {padded}")
+    assert padded > 0                 # the batch exercises -1 padding
+    _assert_no_device_errors()
+
+
+# ---------------------------------------------------------------- prefill --
+def test_prefill_chunk_sampled_rows():
+    _say("case: prefill chunk (8192 q x 40960 ctx, H=64, k=2048)")
+    b = synth.prefill()
+    _, _, lg, tk = parity.run_gpu(b)
+    rng = np.random.default_rng(2)
+    rows = sorted(set([0, 1, 15, 16, 17, 63, 64, 4095, 8190, 8191] +
+                      rng.choice(b.T, 14, replace=False).tolist()))
+    ora = parity.oracle_logits(b, rows=rows)
+    mag = parity.magnitude(b, rows=rows)
+    lg_rows = lg[rows].cpu().numpy()
+    tk_all = tk.cpu().numpy()
+    for i, t in enumerate(rows):
+        p = int(b.positions[t])
+        parity.check_logits_row(lg_rows[i], ora[i], p, f"prefill row {t}",
+                                mag[i])
+        parity.check_topk_row(tk_all[t], ora[i, : p + 1], b.k,
+                              f"prefill row {t}")
+        parity.check_topk_exact_on_gpu_logits(tk_all[t], lg_rows[i], p, b.k)
+    # every row: k distinct ascending indices within [0, p]
+    assert np.all(tk_all >= 0)
+    assert np.all(np.diff(tk_all, axis=1) > 0)
+    assert np.all(tk_all.max(axis=1) <= b.positions)
+    # exact top-k of the GPU logits on a wider sample of rows
+    more = rng.choice(b.T, 64, replace=False)
+    lg_more = lg[torch.from_numpy(np.sort(more)).cuda()].cpu().numpy()
+    for i, t in enumerate(np.sort(more)):
+        parity.check_topk_exact_on_gpu_logits(tk_all[t], lg_more[i],
+                                              int(b.positions[t]), b.k)
+    _assert_no_device_errors()
+
+
+# ----------------------------------------------------------- long context --
+def test_long_context_rows():
+    _say("case: long context (1M tokens, 16 rows, H=64, k=2048)")
+    b = synth.long_context()
+    _, _, lg, tk = parity.run_gpu(b)
+    tk = tk.cpu().numpy()
+    rows = [0, 15]
+    ora = parity.oracle_logits(b, rows=rows)
+    mag = parity.magnitude(b, rows=rows)
+    for i, t in enumerate(rows):
+        p = int(b.positions[t])
+        g = lg[t, : p + 1].cpu().numpy()
+        parity.check_logits_row(g, ora[i], p, f"long row {t}", mag[i])
+        parity.check_topk_row(tk[t], ora[i, : p + 1], b.k, f"long row {t}")
+    for t in range(b.T):
+        p = int(b.positions[t])
+        parity.check_topk_exact_on_gpu_logits(tk[t], lg[t].cpu().numpy(), p,
+                                              b.k, f"long row {t}")
+    _assert_no_device_errors()
+
+
+# ------------------------------------------------------------- edge cases --
+def _edge_batch(seed, contexts, positions, H, k, **kw):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return synth.build_batch(rng, contexts, positions, H=H, k=k, **kw)
+
+
+EDGE_CASES = {
+    "single_page": ([40], [[39]], 8, 16),
+    "one_token": ([1], [[0]], 4, 1),
+    "k1": ([300], [[299]], 16, 1),
+    "page_edges": ([127, 128, 129, 64, 63, 65], [[126], [127], [128], [63],
+                                                [62], [64]], 32, 64),
+    "context_below_k": ([100, 3000], [[99], [2999]], 64, 2048),
+    "h20_multi_rows": ([700, 333], [list(range(650, 700)),
+                                    [0, 1, 2, 100, 332]], 20, 96),
+    "ragged_prefill": ([1000], [list(range(0, 1000, 7))], 64, 128),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGE_CASES))
+@pytest.mark.parametrize("kernel", [1, 2])
+def test_edge_cases(name, kernel):
+    _say(f"case: edge {name}, logits kernel {kernel}")
+    binding.dsa_set_option("logits_kernel", kernel)
+    contexts, positions, H, k = EDGE_CASES[name]
+    b = _edge_batch(zlib.crc32(name.encode()) % 1000, contexts, positions, H, k,
+                    pool_pages=sum((c + 63) // 64 for c in contexts) + 3)
+    _, _, lg, tk = parity.run_gpu(b)
+    lg, tk = lg.cpu().numpy(), tk.cpu().numpy()
+    ora = parity.oracle_logits(b)
+    mag = parity.magnitude(b)
+    for t in range(b.T):
+        p = int(b.positions[t])
+        parity.check_logits_row(lg[t], ora[t], p, f"{name} row {t}", mag[t])
+        parity.check_topk_row(tk[t], ora[t, : p + 1], k, f"{name} row {t}")
+        parity.check_topk_exact_on_gpu_logits(tk[t], lg[t], p, k)
+    _assert_no_device_errors()
+
+
+def test_empty_batch_is_noop():
+    _say("case: T = 0")
+    d = torch.empty(0, 4, 128, dtype=torch.bfloat16, device="cuda")
+    q8, qs = binding.dsa_quantize_q(d)
+    assert q8.shape == (0, 4, 128)
+    lg = torch.empty(0, 256, device="cuda")
+    tk = binding.dsa_indexer_topk(lg, torch.empty(0, dtype=torch.int32,
+                                                  device="cuda"), 8)
+    assert tk.shape == (0, 8)
+
+
+def test_page_permutation_gives_identical_logits():
+    _say("case: page permutation invariance")
+    b = synth.decode(R=8)
+    perm = np.random.default_rng(9).permutation(b.k_cache.shape[0])
+    kc2 = np.empty_like(b.k_cache)
+    kc2[perm] = b.k_cache
+    bt2 = np.where(b.block_table >= 0, perm[np.maximum(b.block_table, 0)], -1)
+    b2 = synth.IndexerBatch(q_bf16=b.q_bf16, weights=b.weights, k_cache=kc2,
+                            block_table=bt2.astype(np.int32),
+                            query_start_loc=b.query_start_loc,
+                            positions=b.positions, k=b.k, ld=b.ld)
+    _, _, lg1, tk1 = parity.run_gpu(b)
+    _, _, lg2, tk2 = parity.run_gpu(b2)
+    for t in range(b.T):
+        p = int(b.positions[t])
+        assert torch.equal(lg1[t, : p + 1], lg2[t, : p + 1])
+    assert torch.equal(tk1, tk2)
+
+
+def test_topk_ties_and_constant_rows():
+    _say("case: top-k ties")
+    T, ld, k = 6, 4096, 100
+    rng = np.random.default_rng(12)
+    lg = rng.integers(-4, 5, size=(T, ld)).astype(np.float32)
+    lg[1] = 1.5                                           # constant row
+    lg[2, ::2] = -0.0                                     # -0 vs +0
+    lg[2, 1::2] = 0.0
+    lg[3] = rng.standard_normal(ld).astype(np.float32)
+    lg[3, 17] = np.inf
+    pos = np.array([4095, 3000, 999, 4095, 50, 2047], np.int32)
+    g = binding.dsa_indexer_topk(torch.from_numpy(lg).cuda(),
+                                 torch.from_numpy(pos).cuda(), k).cpu().numpy()
+    for t in range(T):
+        parity.check_topk_exact_on_gpu_logits(g[t], lg[t], int(pos[t]), k,
+                                              f"ties row {t}")
