@@ -18,8 +18,8 @@ not hit the 256 MB Infinity Cache.  The timed region replays one HIP graph
 that holds R steps (one per copy), so it measures GPU execution, not Python
 launch overhead; every replay is first checked bit-exactly against the eager
 result.  Per-kernel durations come from HIP events on the launch stream
-around every kernel of 64 eager steps, queued behind a GPU sleep so that no
-host gap falls inside a bracket.
+around 64 back-to-back launches of each kernel, queued behind a GPU sleep so
+that no host gap falls inside a bracket.
 
 Prints ONE JSON line.  ``roofline`` is for the dominant kernel (the logits
 kernel): achieved = algorithmic bytes (or FLOPs) per launch / its average
@@ -69,6 +69,11 @@ def parse():
                     help="K-cache copies rotated across steps (cold cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (for scaling "
+                         "hardware byte counters)")
+    ap.add_argument("--opt", action="append", default=[],
+                    help="library tuning knob key=value (dsa_set_option)")
     return ap.parse_args()
 
 
@@ -152,6 +157,9 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    for kv in args.opt:
+        key, val = kv.split("=")
+        binding.dsa_set_option(key, int(val))
     b = make_batch(args.config)
     R = max(1, args.rotate if args.config in ("decode", "long") else 1)
     bt = torch.from_numpy(b.block_table).to(dev)
@@ -168,21 +176,21 @@ def main():
     tws_n = binding.dsa_topk_workspace_size(T, ld, k)
     tws = torch.empty(max(tws_n, 1), dtype=torch.uint8, device=dev)
 
-    def step(i, ev=None):
+    def step(i):
         r = i % R
         binding.dsa_index_cache_mask(1)                       # one F layer
-        if ev is not None:
-            ev[0].record()
         binding.dsa_quantize_q(qs_in[r], q8, qsc)
-        if ev is not None:
-            ev[1].record()
         binding.dsa_indexer_logits(q8, qsc, ws_in[r], kcs[r], bt, qsl, pos,
                                    ld, logits)
-        if ev is not None:
-            ev[2].record()
         binding.dsa_indexer_topk(logits, pos, k, buf, tws)
-        if ev is not None:
-            ev[3].record()
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # Eager warm-up; the last slot's output is the reference for the graph.
     for i in range(max(args.warmup, R)):
@@ -223,22 +231,28 @@ def main():
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / K
 
-    # Per-kernel durations: eager steps with HIP events around every kernel
-    # on the launch stream, enqueued behind a GPU sleep so that the host has
-    # queued them all before the GPU reaches them (no host gaps inside a
-    # bracket).
-    NK = min(64, K)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
-           for _ in range(NK)]
-    torch.cuda.synchronize()
-    torch.cuda._sleep(int(50e6))
-    for i in range(NK):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    kq = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    kl = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    kt = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-    eager_ms_step = evs[0][0].elapsed_time(evs[-1][3]) / NK
+    # Per-kernel durations: for each kernel, NK back-to-back launches on the
+    # launch stream (rotating over the K-cache copies) between two HIP
+    # events, queued behind a GPU sleep so that the host has enqueued them
+    # all before the GPU reaches the first event.
+    NK = 64
+
+    def timed(fn):
+        a = torch.cuda.Event(enable_timing=True)
+        z = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(20e6))
+        a.record()
+        for i in range(NK):
+            fn(i % R)
+        z.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(z) / NK
+
+    kq = timed(lambda r: binding.dsa_quantize_q(qs_in[r], q8, qsc))
+    kl = timed(lambda r: binding.dsa_indexer_logits(
+        q8, qsc, ws_in[r], kcs[r], bt, qsl, pos, ld, logits))
+    kt = timed(lambda r: binding.dsa_indexer_topk(logits, pos, k, buf, tws))
     assert binding.dsa_device_error_flags(reset=True) == 0
 
     alg_bytes, flops = logits_work(b)
@@ -269,10 +283,11 @@ def main():
                    "kcache_copies_rotated": R},
         "kernels_ms": {"quantize_q": round(kq, 5), "logits": round(kl, 5),
                        "topk": round(kt, 5)},
-        "eager_ms_per_step": round(eager_ms_step, 5),
         "logits_gbs": round(gbs, 1), "logits_tflops": round(tfl, 2),
         "roofline": roof,
     }
+    if args.opt:
+        out["options"] = args.opt
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -85,7 +85,10 @@ __device__ __forceinline__ i32x8 load_frag_global(const uint8_t* row32) {
 }
 
 // A fragments of one query row (MT M-tiles of 16 heads; heads >= H are 0).
-template <int MT>
+// FULL (H == 16 * MT): plain loads.  Otherwise the head index is clamped so
+// every load stays in bounds and is issued unconditionally (no divergent
+// branch, so the loads overlap), and padded heads are zeroed afterwards.
+template <int MT, bool FULL>
 __device__ __forceinline__ void load_q_frags(const uint8_t* q8_row, int H,
                                              i32x8 (&qa)[MT]) {
   const int lane = lane_id();
@@ -93,28 +96,37 @@ __device__ __forceinline__ void load_q_frags(const uint8_t* q8_row, int H,
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     const int head = 16 * m + i16;
-    if (head < H) {
-      qa[m] = load_frag_global(q8_row + head * kHeadDim + 32 * g);
-    } else {
-      qa[m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
+    const int hh = FULL ? head : min(head, H - 1);
+    qa[m] = load_frag_global(q8_row + hh * kHeadDim + 32 * g);
+    if (!FULL && head >= H) qa[m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
   }
 }
 
 // Per-lane effective head weights w[h] * s_q[h] for the C rows this lane
-// holds: head 16*m + 4*(lane/16) + j.
-template <int MT>
+// holds: head 16*m + 4*(lane/16) + j, j = 0..3 (4 consecutive heads, one
+// 16-byte load each when FULL).
+template <int MT, bool FULL>
 __device__ __forceinline__ void load_head_weights(const float* w_row,
                                                   const float* s_row, int H,
                                                   float (&w)[MT][4]) {
   const int g = lane_id() >> 4;
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
+  for (int m = 0; m < MT; ++m) {
+    if (FULL) {
+      const float4 wv = *reinterpret_cast<const float4*>(w_row + 16 * m + 4 * g);
+      const float4 sv = *reinterpret_cast<const float4*>(s_row + 16 * m + 4 * g);
+      w[m][0] = wv.x * sv.x; w[m][1] = wv.y * sv.y;
+      w[m][2] = wv.z * sv.z; w[m][3] = wv.w * sv.w;
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int head = 16 * m + 4 * g + j;
-      w[m][j] = head < H ? w_row[head] * s_row[head] : 0.f;
+      for (int j = 0; j < 4; ++j) {
+        const int head = 16 * m + 4 * g + j;
+        const int hh = min(head, H - 1);
+        const float x = w_row[hh] * s_row[hh];
+        w[m][j] = head < H ? x : 0.f;
+      }
     }
+  }
 }
 
 // sum over this lane's heads of w * ReLU(dot) for one N-tile.
@@ -130,64 +142,139 @@ __device__ __forceinline__ float head_reduce(const f32x4 (&acc)[MT],
 }
 
 // ---------------------------------------------------------------------------
+// Request of row t: the number of requests r < R with qsl[r] <= t, minus 1
+// (query_start_loc is non-decreasing).  64 entries per wave-wide load and
+// ballot, so the lookup costs one memory round trip for R <= 64.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int request_of_row_wave(const int32_t* qsl, int R,
+                                                   int64_t t) {
+  const int lane = lane_id();
+  int count = 0;
+  for (int c = 0; c < R; c += 64) {
+    const int i = c + lane;
+    const bool le = i < R && (int64_t)qsl[i] <= t;
+    const uint64_t m = __ballot(le);
+    count += __popcll(m);
+    if (m != ~0ull) break;                     // later entries are > t
+  }
+  return count - 1;
+}
+
+// ---------------------------------------------------------------------------
 // Row-wise logits (decode shape: few query rows per request).  Grid:
 // x = query row, y = page group; 4 waves per workgroup, each wave scores
 // `ppw` consecutive pages of its row straight from HBM into MFMA registers
 // (each K byte is used by exactly one row, so there is nothing to share
-// through LDS).  Lane l stores the logit of token l of the page: one
-// coalesced 256-byte store per page.
+// through LDS).  Every load that does not depend on the page list (q
+// fragments, weights, the row's position and request) is issued before the
+// block-table lookup, and the next page is prefetched while the current one
+// is scored.  Lane l stores the logit of token l of the page: one coalesced
+// 256-byte store per page.
 // ---------------------------------------------------------------------------
-template <int MT>
-__global__ __launch_bounds__(256) void logits_row_kernel(LogitsArgs a,
-                                                         int ppw) {
+template <int MT, bool FULL, bool PREFETCH>
+__device__ __forceinline__ void logits_row_body(const LogitsArgs& a, int ppw) {
   const int64_t t = blockIdx.x;
   const int wave = wave_uniform(threadIdx.x >> 6);
   const int lane = lane_id();
+  const int i16 = lane & 15, g = lane >> 4;
+  const int j0 = (blockIdx.y * 4 + wave) * ppw;
+
+  // Everything below is issued before any of it is waited on: the q
+  // fragments, the weights, the position, the request lookup and -- on the
+  // guess that row t belongs to request t (one query row per request, the
+  // decode layout) -- the block-table entries of this wave's pages.
+  i32x8 qa[MT];
+  load_q_frags<MT, FULL>(a.q8 + t * a.H * kHeadDim, a.H, qa);
+  float w[MT][4];
+  load_head_weights<MT, FULL>(a.weights + t * a.H, a.q_scale + t * a.H, a.H,
+                              w);
   const int p = a.positions[t];
+  const int r_guess = (int)min<int64_t>(t, a.R - 1);
+  const bool in_row = lane < ppw && (int64_t)(j0 + lane) < a.bt_stride;
+  int my_page = in_row ? a.block_table[(int64_t)r_guess * a.bt_stride + j0 + lane]
+                       : -1;
+  const int r = wave_uniform(request_of_row_wave(a.qsl, a.R, t));
+
   if (p < 0 || p >= a.ld || (int64_t)(p >> 6) >= a.bt_stride) {
     if (threadIdx.x == 0 && blockIdx.y == 0) raise_flag(kErrPositionOutOfRange);
     return;
   }
   const int npages = (p >> 6) + 1;
-  const int j0 = (blockIdx.y * 4 + wave) * ppw;
   if (j0 >= npages) return;
   const int j1 = min(j0 + ppw, npages);
-  const int r = wave_uniform(request_of_row(a.qsl, a.R, t));
-  const int32_t* bt = a.block_table + (int64_t)r * a.bt_stride;
-  const int i16 = lane & 15, g = lane >> 4;
-
-  i32x8 qa[MT];
-  load_q_frags<MT>(a.q8 + t * a.H * kHeadDim, a.H, qa);
-  float w[MT][4];
-  load_head_weights<MT>(a.weights + t * a.H, a.q_scale + t * a.H, a.H, w);
+  if (r != r_guess)                           // rows are not one per request
+    my_page = in_row ? a.block_table[(int64_t)r * a.bt_stride + j0 + lane] : -1;
   float* out = a.logits + t * a.ld;
 
-  for (int jp = j0; jp < j1; ++jp) {
-    const int page = wave_uniform(bt[jp]);
-    const int s = jp * kPageTokens + lane;
-    if (page < 0 || (int64_t)page >= a.num_pages) {
-      if (lane == 0) raise_flag(kErrPageOutOfRange);
-      out[s] = -INFINITY;
-      continue;
-    }
+  auto load_page = [&](int page, i32x8 (&kb)[4], float& ks) {
     const uint8_t* pg = a.k_cache + (int64_t)page * kPageBytes;
-    i32x8 kb[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
       kb[nt] = load_frag_global(pg + (16 * nt + i16) * kHeadDim + 32 * g);
-    const float kscale = reinterpret_cast<const float*>(pg + kPageKeyBytes)[lane];
-    float v[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      f32x4 acc[MT];
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-        acc[m] = mfma16x16x128_fp8(qa[m], kb[nt], f32x4{0.f, 0.f, 0.f, 0.f});
-      v[nt] = head_reduce<MT>(acc, w);
+    ks = reinterpret_cast<const float*>(pg + kPageKeyBytes)[lane];
+  };
+  auto page_at = [&](int jp) {
+    return __builtin_amdgcn_readlane(my_page, jp - j0);
+  };
+  auto valid = [&](int page) {
+    return page >= 0 && (int64_t)page < a.num_pages;
+  };
+
+  i32x8 kb[4];
+  float ks = 0.f;
+  int cur = page_at(j0);
+  if (valid(cur)) load_page(cur, kb, ks);
+  for (int jp = j0; jp < j1; ++jp) {
+    i32x8 nb[4];
+    float nks = 0.f;
+    int nxt = -1;
+    if (PREFETCH && jp + 1 < j1) {
+      nxt = page_at(jp + 1);
+      if (valid(nxt)) load_page(nxt, nb, nks);
     }
-    const float tot = reduce_scatter4(v[0], v[1], v[2], v[3]);
-    out[s] = (s <= p) ? tot * kscale : -INFINITY;
+    const int s = jp * kPageTokens + lane;
+    if (!valid(cur)) {
+      if (lane == 0) raise_flag(kErrPageOutOfRange);
+      out[s] = -INFINITY;
+    } else {
+      float v[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        f32x4 acc[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          acc[m] = mfma16x16x128_fp8(qa[m], kb[nt], f32x4{0.f, 0.f, 0.f, 0.f});
+        v[nt] = head_reduce<MT>(acc, w);
+      }
+      const float tot = reduce_scatter4(v[0], v[1], v[2], v[3]);
+      out[s] = (s <= p) ? tot * ks : -INFINITY;
+    }
+    if (jp + 1 < j1) {
+      if (PREFETCH) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) kb[nt] = nb[nt];
+        ks = nks;
+        cur = nxt;
+      } else {
+        cur = page_at(jp + 1);
+        if (valid(cur)) load_page(cur, kb, ks);
+      }
+    }
   }
+}
+
+// One page per wave: at most 128 VGPRs so four waves share each SIMD.
+template <int MT, bool FULL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+void logits_row_kernel(LogitsArgs a, int ppw) {
+  logits_row_body<MT, FULL, false>(a, ppw);
+}
+
+// Several pages per wave with the next page prefetched.
+template <int MT, bool FULL>
+__global__ __launch_bounds__(256)
+void logits_row_prefetch_kernel(LogitsArgs a, int ppw) {
+  logits_row_body<MT, FULL, true>(a, ppw);
 }
 
 // ---------------------------------------------------------------------------
@@ -229,7 +316,7 @@ __device__ void find_tile(const int32_t* qsl, int R, int y, int* s_info) {
   }
 }
 
-template <int MT>
+template <int MT, bool FULL>
 __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a,
                                                           int pages_per_split) {
   __shared__ __align__(16) uint8_t s_keys[2][kPageTokens * kLdsRow];
@@ -282,9 +369,9 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a,
     prow[rr] = s_pos[lr];
     if (prow[rr] >= 0) {
       const int64_t t = row0 + lr;
-      load_q_frags<MT>(a.q8 + t * a.H * kHeadDim, a.H, qa[rr]);
-      load_head_weights<MT>(a.weights + t * a.H, a.q_scale + t * a.H, a.H,
-                            w[rr]);
+      load_q_frags<MT, FULL>(a.q8 + t * a.H * kHeadDim, a.H, qa[rr]);
+      load_head_weights<MT, FULL>(a.weights + t * a.H, a.q_scale + t * a.H,
+                                  a.H, w[rr]);
     } else {
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
@@ -382,20 +469,29 @@ hipError_t launch_quantize_q(const uint16_t* q_bf16, int64_t blocks,
   return hipGetLastError();
 }
 
-template <int MT>
+template <int MT, bool FULL>
 static hipError_t launch_logits_mt(const LogitsArgs& a, hipStream_t stream,
                                    bool tiled, int64_t max_pages) {
   const Options& o = options();
   if (!tiled) {
     int ppw = o.row_pages_per_wave;
     if (ppw <= 0) {
-      // aim for >= 2048 workgroups of 4 waves before giving a wave 2+ pages
-      const int64_t waves = a.T * max_pages;
-      ppw = (int)std::max<int64_t>(1, std::min<int64_t>(8, waves / (4 * 2048)));
+      // about 512 workgroups of 4 waves: enough waves in flight to keep
+      // HBM busy, few enough that each streams several pages with the next
+      // one prefetched (measured best on the decode batch)
+      const int64_t pages = a.T * max_pages;
+      ppw = (int)std::max<int64_t>(1, std::min<int64_t>(8, pages / (4 * 512)));
     }
+    if (ppw > 64) ppw = 64;
     const int64_t gy = (max_pages + 4 * ppw - 1) / (4 * ppw);
-    hipLaunchKernelGGL(logits_row_kernel<MT>, dim3((unsigned)a.T, (unsigned)gy),
-                       dim3(256), 0, stream, a, ppw);
+    if (ppw > 1)
+      hipLaunchKernelGGL((logits_row_prefetch_kernel<MT, FULL>),
+                         dim3((unsigned)a.T, (unsigned)gy), dim3(256), 0,
+                         stream, a, ppw);
+    else
+      hipLaunchKernelGGL((logits_row_kernel<MT, FULL>),
+                         dim3((unsigned)a.T, (unsigned)gy), dim3(256), 0,
+                         stream, a, ppw);
   } else {
     const int64_t tiles = (a.T + kTileRows - 1) / kTileRows + a.R;
     int pps = o.tile_pages_per_split;
@@ -406,7 +502,8 @@ static hipError_t launch_logits_mt(const LogitsArgs& a, hipStream_t stream,
       pps = (int)std::max<int64_t>(8, (max_pages + splits - 1) / splits);
     }
     const int64_t gx = (max_pages + pps - 1) / pps;
-    hipLaunchKernelGGL(logits_tile_kernel<MT>, dim3((unsigned)gx, (unsigned)tiles),
+    hipLaunchKernelGGL((logits_tile_kernel<MT, FULL>),
+                       dim3((unsigned)gx, (unsigned)tiles),
                        dim3(kTileWaves * 64), 0, stream, a, pps);
   }
   return hipGetLastError();
@@ -419,12 +516,18 @@ hipError_t launch_logits(const LogitsArgs& a, hipStream_t stream) {
   bool tiled = a.T > 2 * (int64_t)a.R;
   if (o.logits_kernel == 1) tiled = false;
   if (o.logits_kernel == 2) tiled = true;
-  const int mt = (a.H + 15) / 16;
-  switch (mt) {
-    case 1: return launch_logits_mt<1>(a, stream, tiled, max_pages);
-    case 2: return launch_logits_mt<2>(a, stream, tiled, max_pages);
-    case 3: return launch_logits_mt<3>(a, stream, tiled, max_pages);
-    default: return launch_logits_mt<4>(a, stream, tiled, max_pages);
+  switch (a.H) {
+    case 16: return launch_logits_mt<1, true>(a, stream, tiled, max_pages);
+    case 32: return launch_logits_mt<2, true>(a, stream, tiled, max_pages);
+    case 48: return launch_logits_mt<3, true>(a, stream, tiled, max_pages);
+    case 64: return launch_logits_mt<4, true>(a, stream, tiled, max_pages);
+    default: break;
+  }
+  switch ((a.H + 15) / 16) {
+    case 1: return launch_logits_mt<1, false>(a, stream, tiled, max_pages);
+    case 2: return launch_logits_mt<2, false>(a, stream, tiled, max_pages);
+    case 3: return launch_logits_mt<3, false>(a, stream, tiled, max_pages);
+    default: return launch_logits_mt<4, false>(a, stream, tiled, max_pages);
   }
 }
 

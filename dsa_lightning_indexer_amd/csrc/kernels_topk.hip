@@ -6,17 +6,29 @@
 // [max_num_batched_tokens, index_topk] int32).
 //
 // Row t reads columns 0..p_t (n = p_t + 1 logits).  If n <= k the row is
-// 0..n-1 followed by -1.  Otherwise the k largest logits are selected by a
-// radix select on order-preserving 32-bit keys: 12 + 12 + 8 bit digits, each
-// pass an LDS histogram (ds_add) followed by a workgroup scan that finds the
-// digit holding the k-th largest key.  Keys equal to the final threshold are
-// taken lowest index first.  The selected indices are then compacted in
-// ascending index order with wave ballots, so every row of the buffer is
-// deterministic and sorted by token position; slots [min(n,k), k) hold -1.
+// 0..n-1 followed by -1.  Otherwise the k largest logits are selected on
+// order-preserving 32-bit keys (larger float -> larger key, -0 folded onto
+// +0), ties at the k-th value taken lowest index first, and the selected
+// indices are written in ascending index order, so every row is
+// deterministic and sorted by token position.
 //
-// One workgroup (16 waves) per row.  The row's keys are cached in LDS when
-// they fit (dynamic shared memory sized by the host); longer rows are
-// re-read from global memory (L2) in every pass.
+// One workgroup (16 waves) per row:
+//   1. one sweep over the row builds a 4096-bin LDS histogram of the top 12
+//      key bits (and caches the keys in LDS while they fit);
+//   2. a two-barrier workgroup scan finds the bin d holding the k-th largest
+//      key;
+//   3. a second sweep counts, per wave segment, the keys whose top bits
+//      exceed d (all selected) and collects the keys of bin d (typically a
+//      few dozen to a few hundred) into an LDS candidate list;
+//   4. up to two more radix passes over the candidates only (bits 19..8,
+//      then 7..0) find the exact threshold key T; candidates above T are
+//      marked selected in an LDS bitmap, candidates equal to T marked as
+//      ties, of which the lowest-index ones are taken;
+//   5. each wave writes its segment's selected indices at the segment's
+//      offset, compacted with ballots.
+// When bin d holds more candidates than the list can take (heavy ties), or
+// the row is longer than the bitmaps cover, the row falls back to a full
+// 12+12+8-bit radix select over the row.
 #include <algorithm>
 
 #include "dsa_common.h"
@@ -27,15 +39,108 @@ namespace dsa {
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kHistBins = 4096;
-constexpr int kMaxCachedKeys = 35840;          // 140 KiB of LDS
+constexpr int kCandMax = 2048;
+constexpr int kMaxRowForBitmap = 65536;        // bitmap of 2048 words
+constexpr int kBitmapWords = kMaxRowForBitmap / 32;
+constexpr int kMaxCachedKeys = 24320;          // 95 KiB of LDS
 
 struct TopkShared {
-  uint32_t hist[kHistBins];
+  uint32_t hist[kHistBins];                    // pass 1 and fallback passes
+  uint32_t hist1[kHistBins];                   // candidate pass on bits 19..8
+  uint32_t cand_key[kCandMax];
+  uint32_t cand_idx[kCandMax];
+  uint32_t selbits[kBitmapWords];              // candidate above threshold
+  uint32_t tiebits[kBitmapWords];              // candidate equal to threshold
   uint32_t wave_sum[kTopkWaves];
-  uint32_t seg_gt[kTopkWaves];
+  uint32_t seg_cnt[kTopkWaves];
   uint32_t seg_eq[kTopkWaves];
-  uint32_t sel_digit, sel_above, sel_count;
+  uint32_t sel_digit, sel_above, sel_count, ncand;
 };
+
+// Two-barrier bin search on an LDS histogram: the bin where the count of
+// larger keys first reaches k_rem, scanning from the top.  4096 bins: wave
+// w owns bins 4095-256w down to 3840-256w, 4 per lane; 256 bins: wave 0
+// alone.  Results in sh.sel_*.  Call from all threads.
+template <int NBINS>
+__device__ void select_bin_fast(const uint32_t* hist, uint32_t k_rem,
+                                TopkShared& sh) {
+  static_assert(NBINS == 4096 || NBINS == 256, "bins");
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const bool active = NBINS == 4096 || wave == 0;
+  const int top = (NBINS == 4096) ? 4095 - 256 * wave - 4 * lane
+                                  : 255 - 4 * lane;
+  uint32_t c[4] = {0u, 0u, 0u, 0u};
+  uint32_t local = 0;
+  if (active) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { c[j] = hist[top - j]; local += c[j]; }
+  }
+  uint32_t incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  uint32_t above_w = 0;
+  if (NBINS == 4096) {
+    if (lane == 63) sh.wave_sum[wave] = incl;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) above_w += sh.wave_sum[w];
+  }
+  uint32_t above = above_w + incl - local;
+  if (active && above < k_rem && above + local >= k_rem) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (above + c[j] >= k_rem) {
+        sh.sel_digit = (uint32_t)(top - j);
+        sh.sel_above = above;
+        sh.sel_count = c[j];
+        break;
+      }
+      above += c[j];
+    }
+  }
+  __syncthreads();
+}
+
+// Strided sweep over [i0, i1) by all NT threads of the workgroup with U
+// loads in flight per thread: fn(i, value) for every element.  Indices past
+// the end are clamped to the last element, so every load is in bounds and
+// unconditional (no branch between issue and use).
+template <int U, int NT, typename Load, typename Fn>
+__device__ __forceinline__ void block_sweep(int i0, int i1, Load load, Fn fn) {
+  const int tid = threadIdx.x;
+  for (int base = i0; base < i1; base += NT * U) {
+    uint32_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = load(min(base + u * NT + tid, i1 - 1));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * NT + tid;
+      if (i < i1) fn(i, v[u]);
+    }
+  }
+}
+
+// In-order sweep of one wave's segment [s0, s1): U groups of 64 consecutive
+// elements are loaded (clamped, unconditional) before any is used;
+// fn(i, in_range, value) runs for every lane of every group (wave-uniform
+// control flow, so fn may ballot).
+template <int U, typename Load, typename Fn>
+__device__ __forceinline__ void wave_sweep(int s0, int s1, Load load, Fn fn) {
+  const int lane = lane_id();
+  for (int base = s0; base < s1; base += 64 * U) {
+    uint32_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = load(min(base + 64 * u + lane, s1 - 1));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + 64 * u + lane;
+      fn(i, i < s1, v[u]);
+    }
+  }
+}
 
 // Exclusive prefix sum of one value per thread over the workgroup; also
 // returns the total.  Contains barriers: call from all threads.
@@ -78,23 +183,11 @@ struct RowKeys {
   }
 };
 
-// One radix pass: histogram the digit at `shift` (nbins bins) of the keys
-// that match `prefix` under `mask`, then find the digit where the count of
-// larger keys first reaches k_rem.  Results land in sh.sel_*.
+// Given a filled histogram, find the bin where the count of larger keys
+// first reaches k_rem (bins scanned from the top).  Results in sh.sel_*.
 template <int NBINS>
-__device__ void radix_pass(const RowKeys& keys, int n, uint32_t prefix,
-                           uint32_t mask, int shift, uint32_t k_rem,
-                           TopkShared& sh) {
+__device__ void select_bin(uint32_t k_rem, TopkShared& sh) {
   const int tid = threadIdx.x;
-  for (int b = tid; b < NBINS; b += kTopkThreads) sh.hist[b] = 0u;
-  __syncthreads();
-  for (int i = tid; i < n; i += kTopkThreads) {
-    const uint32_t key = keys(i);
-    if ((key & mask) == prefix)
-      atomicAdd(&sh.hist[(key >> shift) & (NBINS - 1)], 1u);
-  }
-  __syncthreads();
-  // Thread t owns BPT bins in descending order starting at the top.
   constexpr int BPT = NBINS >= kTopkThreads ? NBINS / kTopkThreads : 1;
   constexpr int ACTIVE = NBINS / BPT;
   uint32_t local = 0;
@@ -122,50 +215,45 @@ __device__ void radix_pass(const RowKeys& keys, int n, uint32_t prefix,
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(
-    const float* __restrict__ logits, int64_t ld,
-    const int32_t* __restrict__ positions, int k, int32_t* __restrict__ out,
-    int64_t out_ld, int cache_cap) {
-  extern __shared__ uint32_t s_cache[];
-  __shared__ TopkShared sh;
-  const int64_t t = blockIdx.x;
+// Histogram the digit at `shift` of the keys matching prefix under mask.
+template <int NBINS>
+__device__ void radix_pass(const RowKeys& keys, int n, uint32_t prefix,
+                           uint32_t mask, int shift, uint32_t k_rem,
+                           TopkShared& sh) {
   const int tid = threadIdx.x;
-  const int lane = lane_id();
-  const int wave = tid >> 6;
-  int32_t* orow = out + t * out_ld;
-  int p = positions[t];
-  if (p >= ld) p = (int)ld - 1;              // logits past ld do not exist
-  const int n = p + 1;                       // p < 0 -> empty row
-  if (n <= k) {
-    for (int i = tid; i < k; i += kTopkThreads) orow[i] = i < n ? i : -1;
-    return;
-  }
-  const float* row = logits + t * ld;
-  const int cached = min(n, cache_cap);
-  for (int i = tid; i < cached; i += kTopkThreads)
-    s_cache[i] = float_to_ordered(row[i]);
+  for (int b = tid; b < NBINS; b += kTopkThreads) sh.hist[b] = 0u;
   __syncthreads();
-  const RowKeys keys{row, s_cache, cached};
+  for (int i = tid; i < n; i += kTopkThreads) {
+    const uint32_t key = keys(i);
+    if ((key & mask) == prefix)
+      atomicAdd(&sh.hist[(key >> shift) & (NBINS - 1)], 1u);
+  }
+  __syncthreads();
+  select_bin<NBINS>(k_rem, sh);
+}
 
-  uint32_t prefix = 0u, mask = 0u, k_rem = (uint32_t)k;
-  // pass 1: bits 31..20
-  radix_pass<4096>(keys, n, prefix, mask, 20, k_rem, sh);
-  prefix = sh.sel_digit << 20; mask = 0xfff00000u;
-  k_rem -= sh.sel_above;
+// Fallback: full radix select from pass 2 on (pass 1 already in sh.sel_*),
+// then ordered compaction taking equal keys lowest index first.
+__device__ void topk_radix_rest(const RowKeys& keys, int n, int k,
+                                int32_t* orow, TopkShared& sh) {
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  uint32_t prefix = sh.sel_digit << 20, mask = 0xfff00000u;
+  uint32_t k_rem = (uint32_t)k - sh.sel_above;
   bool done = sh.sel_count == k_rem;
-  if (!done) {                               // pass 2: bits 19..8
+  __syncthreads();
+  if (!done) {
     radix_pass<4096>(keys, n, prefix, mask, 8, k_rem, sh);
     prefix |= sh.sel_digit << 8; mask = 0xffffff00u;
     k_rem -= sh.sel_above;
     done = sh.sel_count == k_rem;
+    __syncthreads();
   }
-  if (!done) {                               // pass 3: bits 7..0
+  if (!done) {
     radix_pass<256>(keys, n, prefix, mask, 0, k_rem, sh);
     prefix |= sh.sel_digit; mask = 0xffffffffu;
     k_rem -= sh.sel_above;
   }
-  // Selected: (key & mask) > prefix, or (key & mask) == prefix among the
-  // first k_rem such keys in index order.  Contiguous per-wave segments.
   const int seg = ((n + kTopkWaves - 1) / kTopkWaves + 63) & ~63;
   const int b0 = min(n, wave * seg), b1 = min(n, b0 + seg);
   uint32_t gt = 0, eq = 0;
@@ -179,10 +267,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(
     gt += __shfl_xor(gt, off);
     eq += __shfl_xor(eq, off);
   }
-  if (lane == 0) { sh.seg_gt[wave] = gt; sh.seg_eq[wave] = eq; }
+  if (lane == 0) { sh.seg_cnt[wave] = gt; sh.seg_eq[wave] = eq; }
   __syncthreads();
   uint32_t gt_before = 0, eq_before = 0;
-  for (int w = 0; w < wave; ++w) { gt_before += sh.seg_gt[w]; eq_before += sh.seg_eq[w]; }
+  for (int w = 0; w < wave; ++w) { gt_before += sh.seg_cnt[w]; eq_before += sh.seg_eq[w]; }
   uint32_t pos = gt_before + min(eq_before, k_rem);
   uint32_t eq_seen = eq_before;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -203,13 +291,506 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(
   }
 }
 
-size_t topk_workspace_bytes(int64_t T, int64_t ld, int k) {
-  (void)T; (void)ld; (void)k;
-  return 0;
+__global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(
+    const float* __restrict__ logits, int64_t ld,
+    const int32_t* __restrict__ positions, int k, int32_t* __restrict__ out,
+    int64_t out_ld, int cache_cap) {
+  extern __shared__ uint32_t s_cache[];
+  __shared__ TopkShared sh;
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  int32_t* orow = out + t * out_ld;
+  int p = positions[t];
+  if (p >= ld) p = (int)ld - 1;              // logits past ld do not exist
+  const int n = p + 1;                       // p < 0 -> empty row
+  if (n <= k) {
+    for (int i = tid; i < k; i += kTopkThreads) orow[i] = i < n ? i : -1;
+    return;
+  }
+  const float* row = logits + t * ld;
+  const int cached = min(n, cache_cap);
+
+  // 0. clear
+  for (int b = tid; b < kHistBins; b += kTopkThreads) {
+    sh.hist[b] = 0u;
+    sh.hist1[b] = 0u;
+  }
+  for (int b = tid; b < kBitmapWords; b += kTopkThreads) {
+    sh.selbits[b] = 0u;
+    sh.tiebits[b] = 0u;
+  }
+  if (tid < kTopkWaves) { sh.seg_cnt[tid] = 0u; sh.seg_eq[tid] = 0u; }
+  if (tid == 0) sh.ncand = 0u;
+  __syncthreads();
+  // 1. histogram of the top 12 key bits; cache keys
+  block_sweep<8, kTopkThreads>(
+      0, n, [&](int i) { return float_to_ordered(row[i]); },
+      [&](int i, uint32_t key) {
+        if (i < cached) s_cache[i] = key;
+        atomicAdd(&sh.hist[key >> 20], 1u);
+      });
+  __syncthreads();
+  const RowKeys keys{row, s_cache, cached};
+  // 2. the bin holding the k-th largest key
+  select_bin_fast<kHistBins>(sh.hist, (uint32_t)k, sh);
+  const uint32_t d = sh.sel_digit;
+  const uint32_t k_rem = (uint32_t)k - sh.sel_above;
+  const uint32_t c = sh.sel_count;
+  if (c > (uint32_t)kCandMax || n > kMaxRowForBitmap) {
+    topk_radix_rest(keys, n, k, orow, sh);   // heavy ties or very long row
+    return;
+  }
+  // 3. per-segment counts of keys above bin d; collect bin d
+  const int seg = ((n + kTopkWaves - 1) / kTopkWaves + 63) & ~63;
+  const int b0 = min(n, wave * seg), b1 = min(n, b0 + seg);
+  uint32_t gt = 0;
+  auto lds_key = [&](int i) { return s_cache[i]; };
+  auto glb_key = [&](int i) { return float_to_ordered(row[i]); };
+  const int bm = min(max(b0, cached), b1);   // [b0, bm) cached, [bm, b1) not
+  auto collect = [&](int i, bool in, uint32_t key) {
+    if (!in) return;
+    const uint32_t dig = key >> 20;
+    gt += dig > d;
+    if (dig == d) {
+      const uint32_t slot = atomicAdd(&sh.ncand, 1u);
+      if (slot < (uint32_t)kCandMax) {
+        sh.cand_key[slot] = key;
+        sh.cand_idx[slot] = (uint32_t)i;
+      }
+    }
+  };
+  wave_sweep<8>(b0, bm, lds_key, collect);
+  wave_sweep<8>(bm, b1, glb_key, collect);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) gt += __shfl_xor(gt, off);
+  if (lane == 0) atomicAdd(&sh.seg_cnt[wave], gt);
+  __syncthreads();
+  // 4. exact threshold among the candidates: (key & mask) > thr is taken,
+  //    (key & mask) == thr is a tie, k_tie of the ties are taken by index.
+  const uint32_t nc = min(sh.ncand, (uint32_t)kCandMax);
+  uint32_t mask = 0u, thr = 0u, k_tie = k_rem;  // all candidates tie
+  if (k_rem < nc) {
+    for (uint32_t j = tid; j < nc; j += kTopkThreads)
+      atomicAdd(&sh.hist1[(sh.cand_key[j] >> 8) & 0xfffu], 1u);
+    for (int b = tid; b < 256; b += kTopkThreads) sh.hist[b] = 0u;
+    __syncthreads();
+    select_bin_fast<kHistBins>(sh.hist1, k_rem, sh);
+    const uint32_t p24 = (d << 12) | sh.sel_digit;
+    const uint32_t k2 = k_rem - sh.sel_above;
+    mask = 0xffffff00u; thr = p24 << 8; k_tie = k2;
+    if (sh.sel_count != k2) {
+      for (uint32_t j = tid; j < nc; j += kTopkThreads) {
+        const uint32_t key = sh.cand_key[j];
+        if ((key >> 8) == p24) atomicAdd(&sh.hist[key & 0xffu], 1u);
+      }
+      __syncthreads();
+      select_bin_fast<256>(sh.hist, k2, sh);
+      mask = 0xffffffffu; thr = (p24 << 8) | sh.sel_digit;
+      k_tie = k2 - sh.sel_above;
+    }
+  }
+  for (uint32_t j = tid; j < nc; j += kTopkThreads) {
+    const uint32_t km = sh.cand_key[j] & mask, ij = sh.cand_idx[j];
+    if (km > thr) {
+      atomicOr(&sh.selbits[ij >> 5], 1u << (ij & 31));
+      atomicAdd(&sh.seg_cnt[ij / (uint32_t)seg], 1u);
+    } else if (km == thr) {
+      atomicOr(&sh.tiebits[ij >> 5], 1u << (ij & 31));
+      atomicAdd(&sh.seg_eq[ij / (uint32_t)seg], 1u);
+    }
+  }
+  __syncthreads();
+  // 5. ordered write of this wave's segment
+  uint32_t pos = 0, tie_seen = 0;
+  for (int w = 0; w < wave; ++w) { pos += sh.seg_cnt[w]; tie_seen += sh.seg_eq[w]; }
+  pos += min(tie_seen, k_tie);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  auto emit = [&](int i, bool in, uint32_t key) {
+    bool sel = false, tie = false;
+    if (in) {
+      const uint32_t dig = key >> 20;
+      sel = dig > d;
+      if (dig == d) {
+        sel = (sh.selbits[i >> 5] >> (i & 31)) & 1u;
+        tie = (sh.tiebits[i >> 5] >> (i & 31)) & 1u;
+      }
+    }
+    const uint64_t tie_mask = __ballot(tie);
+    const uint32_t tie_rank = tie_seen + (uint32_t)__popcll(tie_mask & below);
+    sel = sel || (tie && tie_rank < k_tie);
+    const uint64_t sel_mask = __ballot(sel);
+    const uint32_t slot = pos + (uint32_t)__popcll(sel_mask & below);
+    if (sel && slot < (uint32_t)k) orow[slot] = i;
+    pos += (uint32_t)__popcll(sel_mask);
+    tie_seen += (uint32_t)__popcll(tie_mask);
+  };
+  wave_sweep<8>(b0, bm, lds_key, emit);
+  wave_sweep<8>(bm, b1, glb_key, emit);
 }
 
-hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
-  if (a.T <= 0) return hipSuccess;
+// ---------------------------------------------------------------------------
+// Multi-workgroup top-k for long rows (n > kMaxRowForBitmap, e.g. a 1M-token
+// context).  Each row is cut into chunks of kMwChunk keys, one 256-thread
+// workgroup per (chunk, row):
+//   pass 1  histogram of the top 12 key bits per chunk (LDS), added into a
+//           per-row global histogram; the last workgroup of the row to finish
+//           (a device-scope counter) finds the bin d of the k-th largest key;
+//   pass 2  per chunk: count the keys above bin d, append the keys of bin d
+//           to a per-row candidate list; the last workgroup resolves the
+//           exact threshold key T and the number of ties at T to take (two
+//           LDS radix passes over the candidates), adds the candidates above
+//           T to their chunks' counts, and scans the chunk counts into
+//           offsets;
+//   write   per chunk: keys > T and the lowest-index ties, written in
+//           ascending index order at the chunk's offset.
+// All cross-workgroup hand-offs are device-scope atomics with fences on
+// both sides; nothing waits on another workgroup.  A candidate list that
+// overflows (heavy ties) is resolved by the last workgroup sweeping the row.
+// ---------------------------------------------------------------------------
+constexpr int kMwThreads = 256;
+constexpr int kMwWaves = kMwThreads / 64;
+constexpr int kMwChunk = 16384;
+constexpr int kMwCandCap = 32768;
+
+struct MwState {
+  uint32_t d1, above1, count1, thr, k_tie, pad[3];
+};
+
+struct MwWorkspace {
+  uint32_t* hist;     // [T][4096]
+  uint32_t* done1;    // [T]
+  uint32_t* done2;    // [T]
+  uint32_t* ncand;    // [T]
+  MwState* state;     // [T]
+  uint32_t* ccnt;     // [T][C] keys > T per chunk (then exclusive prefix)
+  uint32_t* ctie;     // [T][C] keys == T per chunk (then exclusive prefix)
+  uint32_t* cand_key; // [T][cap]
+  uint32_t* cand_idx; // [T][cap]
+  int64_t C;          // chunks per row
+};
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static bool use_multi_wg(int64_t ld) { return ld > kMaxRowForBitmap; }
+
+static MwWorkspace carve(void* base, int64_t T, int64_t ld, size_t* total) {
+  MwWorkspace w{};
+  const int64_t C = (ld + kMwChunk - 1) / kMwChunk;
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { char* q = p ? p + off : nullptr; off += align256(bytes); return q; };
+  w.hist = reinterpret_cast<uint32_t*>(take((size_t)T * kHistBins * 4));
+  w.done1 = reinterpret_cast<uint32_t*>(take((size_t)T * 4));
+  w.done2 = reinterpret_cast<uint32_t*>(take((size_t)T * 4));
+  w.ncand = reinterpret_cast<uint32_t*>(take((size_t)T * 4));
+  w.ccnt = reinterpret_cast<uint32_t*>(take((size_t)T * C * 4));
+  w.ctie = reinterpret_cast<uint32_t*>(take((size_t)T * C * 4));
+  const size_t zero_bytes = off;                 // everything above starts at 0
+  w.state = reinterpret_cast<MwState*>(take((size_t)T * sizeof(MwState)));
+  w.cand_key = reinterpret_cast<uint32_t*>(take((size_t)T * kMwCandCap * 4));
+  w.cand_idx = reinterpret_cast<uint32_t*>(take((size_t)T * kMwCandCap * 4));
+  w.C = C;
+  if (total) *total = off;
+  (void)zero_bytes;
+  return w;
+}
+
+static size_t mw_zero_bytes(int64_t T, int64_t ld) {
+  const int64_t C = (ld + kMwChunk - 1) / kMwChunk;
+  return align256((size_t)T * kHistBins * 4) + 3 * align256((size_t)T * 4) +
+         2 * align256((size_t)T * C * 4);
+}
+
+__global__ void mw_clear_kernel(uint4* p, size_t n16) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+// Block-level bin search for a 256-thread workgroup over an LDS histogram:
+// the bin where the count of larger keys first reaches k_rem.  Thread i owns
+// BPL bins starting at the top.  Two barriers.
+template <int NBINS>
+__device__ void mw_select(const uint32_t* hist, uint32_t k_rem,
+                          uint32_t* wave_sum, uint32_t* out /*digit,above,count*/) {
+  constexpr int BPL = NBINS >= kMwThreads ? NBINS / kMwThreads : 1;
+  constexpr int ACTIVE = NBINS / BPL;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const bool active = tid < ACTIVE;
+  const int top = NBINS - 1 - tid * BPL;
+  uint32_t local = 0;
+  if (active)
+    for (int j = 0; j < BPL; ++j) local += hist[top - j];
+  uint32_t incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wave_sum[wave] = incl;
+  __syncthreads();
+  uint32_t above = incl - local;
+  for (int w = 0; w < wave; ++w) above += wave_sum[w];
+  if (active && above < k_rem && above + local >= k_rem) {
+    for (int j = 0; j < BPL; ++j) {
+      const uint32_t c = hist[top - j];
+      if (above + c >= k_rem) {
+        out[0] = (uint32_t)(top - j);
+        out[1] = above;
+        out[2] = c;
+        break;
+      }
+      above += c;
+    }
+  }
+  __syncthreads();
+}
+
+struct MwShared {
+  uint32_t hist[kHistBins];
+  uint32_t wave_sum[kMwWaves];
+  uint32_t sel[3];
+  uint32_t last;
+  uint32_t wcnt[kMwWaves], wtie[kMwWaves];
+};
+
+__device__ __forceinline__ int row_len(const int32_t* positions, int64_t t,
+                                       int64_t ld) {
+  int p = positions[t];
+  if (p >= ld) p = (int)ld - 1;
+  return p + 1;
+}
+
+// Becomes true in exactly one workgroup per row: the last of `parts`
+// workgroups to call it.  Publishes this workgroup's earlier global writes.
+__device__ bool mw_arrive_last(uint32_t* counter, uint32_t parts, MwShared& sh) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = atomicAdd(counter, 1u);
+    sh.last = (old == parts - 1) ? 1u : 0u;
+  }
+  __syncthreads();
+  const bool last = sh.last != 0;
+  if (last) __threadfence();
+  return last;
+}
+
+__global__ __launch_bounds__(kMwThreads) void mw_pass1_kernel(
+    const float* __restrict__ logits, int64_t ld, const int32_t* positions,
+    int k, MwWorkspace ws) {
+  __shared__ MwShared sh;
+  const int64_t t = blockIdx.y;
+  const int64_t c = blockIdx.x;
+  const int n = row_len(positions, t, ld);
+  if (n <= k) return;
+  const uint32_t parts = (uint32_t)((n + kMwChunk - 1) / kMwChunk);
+  if (c >= parts) return;
+  const int tid = threadIdx.x;
+  for (int b = tid; b < kHistBins; b += kMwThreads) sh.hist[b] = 0u;
+  __syncthreads();
+  const float* row = logits + t * ld;
+  const int i0 = (int)c * kMwChunk, i1 = min(n, i0 + kMwChunk);
+  block_sweep<8, kMwThreads>(
+      i0, i1, [&](int i) { return float_to_ordered(row[i]); },
+      [&](int, uint32_t key) { atomicAdd(&sh.hist[key >> 20], 1u); });
+  __syncthreads();
+  uint32_t* gh = ws.hist + t * kHistBins;
+  for (int b = tid; b < kHistBins; b += kMwThreads)
+    if (sh.hist[b]) atomicAdd(&gh[b], sh.hist[b]);
+  if (!mw_arrive_last(&ws.done1[t], parts, sh)) return;
+  for (int b = tid; b < kHistBins; b += kMwThreads)
+    sh.hist[b] = __atomic_load_n(&gh[b], __ATOMIC_RELAXED);
+  __syncthreads();
+  mw_select<kHistBins>(sh.hist, (uint32_t)k, sh.wave_sum, sh.sel);
+  if (tid == 0) {
+    ws.state[t].d1 = sh.sel[0];
+    ws.state[t].above1 = sh.sel[1];
+    ws.state[t].count1 = sh.sel[2];
+  }
+}
+
+// Last workgroup of pass 2: exact threshold among the keys of bin d1.
+// Candidate source: the candidate list, or (overflow) the whole row.
+__device__ void mw_resolve(const float* row, int n, int k, const MwState st,
+                           const uint32_t* ck, const uint32_t* ci, uint32_t nc,
+                           bool from_row, int64_t t, MwWorkspace& ws,
+                           MwShared& sh) {
+  const int tid = threadIdx.x;
+  const uint32_t d1 = st.d1;
+  uint32_t k_rem = (uint32_t)k - st.above1;
+  const uint32_t total = from_row ? st.count1 : nc;
+  auto for_each = [&](auto&& fn) {
+    if (from_row) {
+      for (int i = tid; i < n; i += kMwThreads) {
+        const uint32_t key = float_to_ordered(row[i]);
+        if ((key >> 20) == d1) fn(key, (uint32_t)i);
+      }
+    } else {
+      for (uint32_t j = tid; j < nc; j += kMwThreads) fn(ck[j], ci[j]);
+    }
+  };
+  uint32_t mask = 0xfff00000u, thr = d1 << 20, k_tie = k_rem;
+  if (k_rem < total) {
+    for (int b = tid; b < kHistBins; b += kMwThreads) sh.hist[b] = 0u;
+    __syncthreads();
+    for_each([&](uint32_t key, uint32_t) {
+      atomicAdd(&sh.hist[(key >> 8) & 0xfffu], 1u);
+    });
+    __syncthreads();
+    mw_select<kHistBins>(sh.hist, k_rem, sh.wave_sum, sh.sel);
+    const uint32_t p24 = (d1 << 12) | sh.sel[0];
+    const uint32_t k2 = k_rem - sh.sel[1];
+    mask = 0xffffff00u; thr = p24 << 8; k_tie = k2;
+    if (sh.sel[2] != k2) {
+      __syncthreads();
+      for (int b = tid; b < 256; b += kMwThreads) sh.hist[b] = 0u;
+      __syncthreads();
+      for_each([&](uint32_t key, uint32_t) {
+        if ((key >> 8) == p24) atomicAdd(&sh.hist[key & 0xffu], 1u);
+      });
+      __syncthreads();
+      mw_select<256>(sh.hist, k2, sh.wave_sum, sh.sel);
+      mask = 0xffffffffu; thr = (p24 << 8) | sh.sel[0];
+      k_tie = k2 - sh.sel[1];
+    }
+  }
+  // keys of bin d1 above the threshold join their chunk's count; ties
+  // at the threshold are counted per chunk
+  uint32_t* ccnt = ws.ccnt + t * ws.C;
+  uint32_t* ctie = ws.ctie + t * ws.C;
+  for_each([&](uint32_t key, uint32_t idx) {
+    const uint32_t km = key & mask;
+    if (km > thr) atomicAdd(&ccnt[idx / kMwChunk], 1u);
+    else if (km == thr) atomicAdd(&ctie[idx / kMwChunk], 1u);
+  });
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    ws.state[t].thr = thr;
+    ws.state[t].k_tie = k_tie;
+    ws.state[t].pad[0] = mask;
+    // exclusive prefixes over the chunks (few dozen)
+    const int parts = (n + kMwChunk - 1) / kMwChunk;
+    uint32_t a = 0, b = 0;
+    for (int q = 0; q < parts; ++q) {
+      const uint32_t x = __atomic_load_n(&ccnt[q], __ATOMIC_RELAXED);
+      const uint32_t y = __atomic_load_n(&ctie[q], __ATOMIC_RELAXED);
+      ccnt[q] = a; ctie[q] = b;
+      a += x; b += y;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kMwThreads) void mw_pass2_kernel(
+    const float* __restrict__ logits, int64_t ld, const int32_t* positions,
+    int k, MwWorkspace ws) {
+  __shared__ MwShared sh;
+  const int64_t t = blockIdx.y;
+  const int64_t c = blockIdx.x;
+  const int n = row_len(positions, t, ld);
+  if (n <= k) return;
+  const uint32_t parts = (uint32_t)((n + kMwChunk - 1) / kMwChunk);
+  if (c >= parts) return;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const MwState st = ws.state[t];
+  const float* row = logits + t * ld;
+  const int i0 = (int)c * kMwChunk, i1 = min(n, i0 + kMwChunk);
+  uint32_t* ck = ws.cand_key + t * kMwCandCap;
+  uint32_t* ci = ws.cand_idx + t * kMwCandCap;
+  uint32_t gt = 0;
+  block_sweep<8, kMwThreads>(
+      i0, i1, [&](int i) { return float_to_ordered(row[i]); },
+      [&](int i, uint32_t key) {
+        const uint32_t dig = key >> 20;
+        gt += dig > st.d1;
+        if (dig == st.d1) {
+          const uint32_t slot = atomicAdd(&ws.ncand[t], 1u);
+          if (slot < (uint32_t)kMwCandCap) {
+            ck[slot] = key;
+            ci[slot] = (uint32_t)i;
+          }
+        }
+      });
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) gt += __shfl_xor(gt, off);
+  if (lane == 0) sh.wcnt[wave] = gt;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t s = 0;
+    for (int w = 0; w < kMwWaves; ++w) s += sh.wcnt[w];
+    atomicAdd(&ws.ccnt[t * ws.C + c], s);
+  }
+  if (!mw_arrive_last(&ws.done2[t], parts, sh)) return;
+  const uint32_t nc = __atomic_load_n(&ws.ncand[t], __ATOMIC_RELAXED);
+  const bool overflow = nc > (uint32_t)kMwCandCap;
+  mw_resolve(row, n, k, st, ck, ci, overflow ? 0u : nc, overflow, t, ws, sh);
+}
+
+__global__ __launch_bounds__(kMwThreads) void mw_write_kernel(
+    const float* __restrict__ logits, int64_t ld, const int32_t* positions,
+    int k, int32_t* __restrict__ out, int64_t out_ld, MwWorkspace ws) {
+  __shared__ MwShared sh;
+  const int64_t t = blockIdx.y;
+  const int64_t c = blockIdx.x;
+  const int n = row_len(positions, t, ld);
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  int32_t* orow = out + t * out_ld;
+  if (n <= k) {
+    if (c == 0)
+      for (int i = tid; i < k; i += kMwThreads) orow[i] = i < n ? i : -1;
+    return;
+  }
+  const int parts = (n + kMwChunk - 1) / kMwChunk;
+  if (c >= parts) return;
+  const MwState st = ws.state[t];
+  const uint32_t mask = st.pad[0], thr = st.thr, k_tie = st.k_tie;
+  const float* row = logits + t * ld;
+  const int i0 = (int)c * kMwChunk, i1 = min(n, i0 + kMwChunk);
+  constexpr int kSub = kMwChunk / kMwWaves;
+  const int s0 = min(i1, i0 + wave * kSub), s1 = min(i1, s0 + kSub);
+  uint32_t gt = 0, eq = 0;
+  auto load = [&](int i) { return float_to_ordered(row[i]) & mask; };
+  wave_sweep<8>(s0, s1, load, [&](int, bool in, uint32_t km) {
+    gt += in && km > thr;
+    eq += in && km == thr;
+  });
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    gt += __shfl_xor(gt, off);
+    eq += __shfl_xor(eq, off);
+  }
+  if (lane == 0) { sh.wcnt[wave] = gt; sh.wtie[wave] = eq; }
+  __syncthreads();
+  uint32_t gt_before = ws.ccnt[t * ws.C + c], tie_seen = ws.ctie[t * ws.C + c];
+  for (int w = 0; w < wave; ++w) { gt_before += sh.wcnt[w]; tie_seen += sh.wtie[w]; }
+  uint32_t pos = gt_before + min(tie_seen, k_tie);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  wave_sweep<8>(s0, s1, load, [&](int i, bool in, uint32_t km) {
+    const bool is_gt = in && km > thr;
+    const bool is_eq = in && km == thr;
+    const uint64_t eq_mask = __ballot(is_eq);
+    const uint32_t eq_rank = tie_seen + (uint32_t)__popcll(eq_mask & below);
+    const bool sel = is_gt || (is_eq && eq_rank < k_tie);
+    const uint64_t sel_mask = __ballot(sel);
+    const uint32_t slot = pos + (uint32_t)__popcll(sel_mask & below);
+    if (sel && slot < (uint32_t)k) orow[slot] = i;
+    pos += (uint32_t)__popcll(sel_mask);
+    tie_seen += (uint32_t)__popcll(eq_mask);
+  });
+}
+
+size_t topk_workspace_bytes(int64_t T, int64_t ld, int k) {
+  (void)k;
+  if (T <= 0 || !use_multi_wg(ld)) return 0;
+  size_t total = 0;
+  carve(nullptr, T, ld, &total);
+  return total;
+}
+
+static hipError_t launch_topk_single(const TopkArgs& a, hipStream_t stream) {
   const int cap = (int)std::min<int64_t>(a.ld, kMaxCachedKeys);
   const size_t dyn = (size_t)cap * sizeof(uint32_t);
   static bool attr_set = false;
@@ -224,6 +805,25 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)a.T), dim3(kTopkThreads),
                      dyn, stream, a.logits, a.ld, a.positions, a.k, a.out,
                      a.out_ld, cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
+  if (a.T <= 0) return hipSuccess;
+  if (!use_multi_wg(a.ld)) return launch_topk_single(a, stream);
+  MwWorkspace ws = carve(a.workspace, a.T, a.ld, nullptr);
+  const size_t zb = mw_zero_bytes(a.T, a.ld);
+  const size_t n16 = zb / 16;
+  hipLaunchKernelGGL(mw_clear_kernel,
+                     dim3((unsigned)std::min<size_t>((n16 + 255) / 256, 1024)),
+                     dim3(256), 0, stream, static_cast<uint4*>(a.workspace), n16);
+  const dim3 grid((unsigned)ws.C, (unsigned)a.T);
+  hipLaunchKernelGGL(mw_pass1_kernel, grid, dim3(kMwThreads), 0, stream,
+                     a.logits, a.ld, a.positions, a.k, ws);
+  hipLaunchKernelGGL(mw_pass2_kernel, grid, dim3(kMwThreads), 0, stream,
+                     a.logits, a.ld, a.positions, a.k, ws);
+  hipLaunchKernelGGL(mw_write_kernel, grid, dim3(kMwThreads), 0, stream,
+                     a.logits, a.ld, a.positions, a.k, a.out, a.out_ld, ws);
   return hipGetLastError();
 }
 

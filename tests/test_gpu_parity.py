@@ -263,3 +263,22 @@ def test_topk_ties_and_constant_rows():
     for t in range(T):
         parity.check_topk_exact_on_gpu_logits(g[t], lg[t], int(pos[t]), k,
                                               f"ties row {t}")
+
+
+def test_topk_multi_workgroup_rows():
+    """Rows longer than 65536 columns take the multi-workgroup top-k; mix
+    long, short (padded) and constant rows (candidate-list overflow)."""
+    _say("case: multi-workgroup top-k")
+    T, ld, k = 6, 131072, 2048
+    rng = np.random.default_rng(44)
+    lg = rng.standard_normal((T, ld)).astype(np.float32)
+    lg[1] = 0.5                                   # all equal: overflow path
+    lg[3, :1000] = rng.integers(-2, 3, 1000)      # short row with ties
+    lg[4] = np.round(lg[4] * 4) / 4               # heavy near-ties
+    pos = np.array([ld - 1, 90000, 70000, 999, ld - 1, 65536], np.int32)
+    assert binding.dsa_topk_workspace_size(T, ld, k) > 0
+    g = binding.dsa_indexer_topk(torch.from_numpy(lg).cuda(),
+                                 torch.from_numpy(pos).cuda(), k).cpu().numpy()
+    for t in range(T):
+        parity.check_topk_exact_on_gpu_logits(g[t], lg[t], int(pos[t]), k,
+                                              f"multi-wg row {t}")
