@@ -102,9 +102,9 @@ __device__ __forceinline__ void load_q_frags(const uint8_t* q8_row, int H,
   }
 }
 
-// Per-lane effective head weights w[h] * s_q[h] for the C rows this lane
-// holds: head 16*m + 4*(lane/16) + j, j = 0..3 (4 consecutive heads, one
-// 16-byte load each when FULL).
+// Per-lane effective head weights w[h] * s_q[h] / 2 for the C rows this
+// lane holds: head 16*m + 4*(lane/16) + j, j = 0..3 (4 consecutive heads,
+// one 16-byte load each when FULL).  The 1/2 belongs to head_reduce's ReLU.
 template <int MT, bool FULL>
 __device__ __forceinline__ void load_head_weights(const float* w_row,
                                                   const float* s_row, int H,
@@ -115,29 +115,33 @@ __device__ __forceinline__ void load_head_weights(const float* w_row,
     if (FULL) {
       const float4 wv = *reinterpret_cast<const float4*>(w_row + 16 * m + 4 * g);
       const float4 sv = *reinterpret_cast<const float4*>(s_row + 16 * m + 4 * g);
-      w[m][0] = wv.x * sv.x; w[m][1] = wv.y * sv.y;
-      w[m][2] = wv.z * sv.z; w[m][3] = wv.w * sv.w;
+      w[m][0] = 0.5f * (wv.x * sv.x); w[m][1] = 0.5f * (wv.y * sv.y);
+      w[m][2] = 0.5f * (wv.z * sv.z); w[m][3] = 0.5f * (wv.w * sv.w);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int head = 16 * m + 4 * g + j;
         const int hh = min(head, H - 1);
-        const float x = w_row[hh] * s_row[hh];
+        const float x = 0.5f * (w_row[hh] * s_row[hh]);
         w[m][j] = head < H ? x : 0.f;
       }
     }
   }
 }
 
-// sum over this lane's heads of w * ReLU(dot) for one N-tile.
+// sum over this lane's heads of w * ReLU(dot) for one N-tile.  ReLU is
+// written as (x + |x|) / 2 with the 1/2 folded into the weights: one add
+// with an abs source modifier and one FMA per MFMA output (a plain fmaxf
+// costs an extra NaN-canonicalising max on gfx950).
 template <int MT>
 __device__ __forceinline__ float head_reduce(const f32x4 (&acc)[MT],
-                                             const float (&w)[MT][4]) {
+                                             const float (&w_half)[MT][4]) {
   float v = 0.f;
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v = fmaf(w[m][j], fmaxf(acc[m][j], 0.f), v);
+    for (int j = 0; j < 4; ++j)
+      v = fmaf(w_half[m][j], acc[m][j] + fabsf(acc[m][j]), v);
   return v;
 }
 
@@ -458,6 +462,142 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a,
 }
 
 // ---------------------------------------------------------------------------
+// Tiled logits without LDS staging: the same 16-row tile and page split,
+// but every wave streams the pages itself (16-byte loads straight into MFMA
+// B registers, next page prefetched); the 8 waves of a tile read the same
+// page within a few hundred cycles, so HBM sees it once and L2 serves the
+// rest.  No workgroup barrier inside the page loop, so the waves drift
+// apart and one wave's MFMAs overlap another's epilogue.
+// ---------------------------------------------------------------------------
+template <int MT, bool FULL>
+__global__ __launch_bounds__(512) void logits_tile_direct_kernel(
+    LogitsArgs a, int pages_per_split) {
+  __shared__ int s_info[4];
+  __shared__ int s_pos[kTileRows];
+  const int tid = threadIdx.x;
+  const int wave = wave_uniform(tid >> 6);
+  const int lane = lane_id();
+  if (tid == 0) { s_info[0] = -1; s_info[1] = 0; s_info[2] = 0; }
+  __syncthreads();
+  if (wave == 0) find_tile(a.qsl, a.R, blockIdx.y, s_info);
+  __syncthreads();
+  const int r = s_info[0];
+  if (r < 0) return;
+  const int64_t row0 = s_info[1];
+  const int nrows = s_info[2];
+  if (tid < kTileRows) {
+    int p = -1;
+    if (tid < nrows && row0 + tid >= 0 && row0 + tid < a.T) {
+      p = a.positions[row0 + tid];
+      if (p < 0 || p >= a.ld || (int64_t)(p >> 6) >= a.bt_stride) {
+        raise_flag(kErrPositionOutOfRange);
+        p = -1;
+      }
+    }
+    s_pos[tid] = p;
+  }
+  __syncthreads();
+  int maxp = -1;
+#pragma unroll
+  for (int i = 0; i < kTileRows; ++i) maxp = max(maxp, s_pos[i]);
+  const int npages = (maxp >> 6) + 1;
+  const int jb = blockIdx.x * pages_per_split;
+  const int je = min(jb + pages_per_split, npages);
+  if (jb >= je) return;
+  const int prow0 = s_pos[2 * wave], prow1 = s_pos[2 * wave + 1];
+  if (prow0 < 0 && prow1 < 0) return;        // this wave has no rows
+  // pages past both rows' positions are not needed by this wave
+  const int my_je = min(je, (max(prow0, prow1) >> 6) + 1);
+  if (jb >= my_je) return;
+
+  const int32_t* bt = a.block_table + (int64_t)r * a.bt_stride;
+  const int i16 = lane & 15, g = lane >> 4;
+  i32x8 qa[2][MT];
+  float w[2][MT][4];
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int pr = rr ? prow1 : prow0;
+    const int64_t t = row0 + 2 * wave + rr;
+    if (pr >= 0) {
+      load_q_frags<MT, FULL>(a.q8 + t * a.H * kHeadDim, a.H, qa[rr]);
+      load_head_weights<MT, FULL>(a.weights + t * a.H, a.q_scale + t * a.H,
+                                  a.H, w[rr]);
+    } else {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        qa[rr][m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[rr][m][j] = 0.f;
+      }
+    }
+  }
+
+  auto valid = [&](int page) {
+    return page >= 0 && (int64_t)page < a.num_pages;
+  };
+  // B fragments of one page plus the two k-scales this lane applies (token
+  // 16*(2*ntp + (g & 1)) + i16 for ntp = 0, 1).
+  auto load_page = [&](int page, i32x8 (&kb)[4], float (&ks)[2]) {
+    const uint8_t* pg = a.k_cache + (int64_t)page * kPageBytes;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      kb[nt] = load_frag_global(pg + (16 * nt + i16) * kHeadDim + 32 * g);
+    const float* sc = reinterpret_cast<const float*>(pg + kPageKeyBytes);
+    ks[0] = sc[16 * (g & 1) + i16];
+    ks[1] = sc[16 * (2 + (g & 1)) + i16];
+  };
+
+  i32x8 kb[4];
+  float ks[2] = {0.f, 0.f};
+  int cur = wave_uniform(bt[jb]);
+  if (valid(cur)) load_page(cur, kb, ks);
+  else if (lane == 0) raise_flag(kErrPageOutOfRange);
+  const int rr_out = g >> 1;
+  const int pr_out = rr_out ? prow1 : prow0;
+  float* orow = a.logits + (row0 + 2 * wave + rr_out) * a.ld;
+
+  for (int jp = jb; jp < my_je; ++jp) {
+    i32x8 nb[4];
+    float nks[2] = {0.f, 0.f};
+    int nxt = -1;
+    if (jp + 1 < my_je) {
+      nxt = wave_uniform(bt[jp + 1]);
+      if (valid(nxt)) load_page(nxt, nb, nks);
+      else if (lane == 0) raise_flag(kErrPageOutOfRange);
+    }
+    const bool ok = valid(cur);
+#pragma unroll
+    for (int ntp = 0; ntp < 2; ++ntp) {
+      float v[2][2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          f32x4 acc[MT];
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+            acc[m] = mfma16x16x128_fp8(qa[rr][m], kb[2 * ntp + q],
+                                       f32x4{0.f, 0.f, 0.f, 0.f});
+          v[rr][q] = head_reduce<MT>(acc, w[rr]);
+        }
+      }
+      // lane group g ends with (row g >> 1, N-tile 2*ntp + (g & 1))
+      const float tot = reduce_scatter4(v[0][0], v[0][1], v[1][0], v[1][1]);
+      if (pr_out >= 0) {
+        const int s = jp * kPageTokens + 16 * (2 * ntp + (g & 1)) + i16;
+        orow[s] = (s <= pr_out && ok) ? tot * ks[ntp] : -INFINITY;
+      }
+    }
+    if (jp + 1 < my_je) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) kb[nt] = nb[nt];
+      ks[0] = nks[0]; ks[1] = nks[1];
+      cur = nxt;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers.
 // ---------------------------------------------------------------------------
 hipError_t launch_quantize_q(const uint16_t* q_bf16, int64_t blocks,
@@ -502,9 +642,14 @@ static hipError_t launch_logits_mt(const LogitsArgs& a, hipStream_t stream,
       pps = (int)std::max<int64_t>(8, (max_pages + splits - 1) / splits);
     }
     const int64_t gx = (max_pages + pps - 1) / pps;
-    hipLaunchKernelGGL((logits_tile_kernel<MT, FULL>),
-                       dim3((unsigned)gx, (unsigned)tiles),
-                       dim3(kTileWaves * 64), 0, stream, a, pps);
+    if (o.logits_kernel == 3)
+      hipLaunchKernelGGL((logits_tile_direct_kernel<MT, FULL>),
+                         dim3((unsigned)gx, (unsigned)tiles),
+                         dim3(kTileWaves * 64), 0, stream, a, pps);
+    else
+      hipLaunchKernelGGL((logits_tile_kernel<MT, FULL>),
+                         dim3((unsigned)gx, (unsigned)tiles),
+                         dim3(kTileWaves * 64), 0, stream, a, pps);
   }
   return hipGetLastError();
 }
@@ -515,7 +660,7 @@ hipError_t launch_logits(const LogitsArgs& a, hipStream_t stream) {
   const Options& o = options();
   bool tiled = a.T > 2 * (int64_t)a.R;
   if (o.logits_kernel == 1) tiled = false;
-  if (o.logits_kernel == 2) tiled = true;
+  if (o.logits_kernel >= 2) tiled = true;
   switch (a.H) {
     case 16: return launch_logits_mt<1, true>(a, stream, tiled, max_pages);
     case 32: return launch_logits_mt<2, true>(a, stream, tiled, max_pages);

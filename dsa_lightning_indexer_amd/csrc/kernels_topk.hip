@@ -30,6 +30,7 @@
 // the row is longer than the bitmaps cover, the row falls back to a full
 // 12+12+8-bit radix select over the row.
 #include <algorithm>
+#include <type_traits>
 
 #include "dsa_common.h"
 #include "dsa_launch.h"
@@ -42,7 +43,8 @@ constexpr int kHistBins = 4096;
 constexpr int kCandMax = 2048;
 constexpr int kMaxRowForBitmap = 65536;        // bitmap of 2048 words
 constexpr int kBitmapWords = kMaxRowForBitmap / 32;
-constexpr int kMaxCachedKeys = 24320;          // 95 KiB of LDS
+constexpr int kMaxCachedHi = 48128;            // 94 KiB: top 16 key bits
+constexpr int kMaxCachedFull = 23552;          // 92 KiB: whole 32-bit keys
 
 struct TopkShared {
   uint32_t hist[kHistBins];                    // pass 1 and fallback passes
@@ -56,6 +58,19 @@ struct TopkShared {
   uint32_t seg_eq[kTopkWaves];
   uint32_t sel_digit, sel_above, sel_count, ncand;
 };
+
+// Inclusive prefix sum across the 64 lanes of a wave with DPP: four
+// row_shr steps within each 16-lane row, then row_bcast:15 / row_bcast:31
+// carry the row totals into the later rows.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false); // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false); // row_bcast:31
+  return x;
+}
 
 // Two-barrier bin search on an LDS histogram: the bin where the count of
 // larger keys first reaches k_rem, scanning from the top.  4096 bins: wave
@@ -76,12 +91,7 @@ __device__ void select_bin_fast(const uint32_t* hist, uint32_t k_rem,
 #pragma unroll
     for (int j = 0; j < 4; ++j) { c[j] = hist[top - j]; local += c[j]; }
   }
-  uint32_t incl = local;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
+  const uint32_t incl = wave_inclusive_scan(local);
   uint32_t above_w = 0;
   if (NBINS == 4096) {
     if (lane == 63) sh.wave_sum[wave] = incl;
@@ -179,7 +189,7 @@ struct RowKeys {
   const uint32_t* cache;
   int cached;
   __device__ __forceinline__ uint32_t operator()(int i) const {
-    return i < cached ? cache[i] : float_to_ordered(row[i]);
+    return (cache && i < cached) ? cache[i] : float_to_ordered(row[i]);
   }
 };
 
@@ -291,11 +301,17 @@ __device__ void topk_radix_rest(const RowKeys& keys, int n, int k,
   }
 }
 
+// KEY32: rows short enough to cache whole keys in LDS (no reload of the
+// candidates' keys); otherwise the top 16 key bits are cached.
+template <bool KEY32>
 __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(
     const float* __restrict__ logits, int64_t ld,
     const int32_t* __restrict__ positions, int k, int32_t* __restrict__ out,
     int64_t out_ld, int cache_cap) {
-  extern __shared__ uint32_t s_cache[];
+  using CacheT = typename std::conditional<KEY32, uint32_t, uint16_t>::type;
+  extern __shared__ __align__(16) unsigned char s_raw[];
+  CacheT* s_hi = reinterpret_cast<CacheT*>(s_raw);
+  constexpr int kDigShift = KEY32 ? 20 : 4;   // digit = top 12 key bits
   __shared__ TopkShared sh;
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x;
@@ -324,48 +340,60 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(
   if (tid < kTopkWaves) { sh.seg_cnt[tid] = 0u; sh.seg_eq[tid] = 0u; }
   if (tid == 0) sh.ncand = 0u;
   __syncthreads();
-  // 1. histogram of the top 12 key bits; cache keys
+  // 1. histogram of the top 12 key bits; cache the top 16 bits
   block_sweep<8, kTopkThreads>(
       0, n, [&](int i) { return float_to_ordered(row[i]); },
       [&](int i, uint32_t key) {
-        if (i < cached) s_cache[i] = key;
+        if (i < cached) s_hi[i] = (CacheT)(KEY32 ? key : key >> 16);
         atomicAdd(&sh.hist[key >> 20], 1u);
       });
   __syncthreads();
-  const RowKeys keys{row, s_cache, cached};
   // 2. the bin holding the k-th largest key
   select_bin_fast<kHistBins>(sh.hist, (uint32_t)k, sh);
   const uint32_t d = sh.sel_digit;
   const uint32_t k_rem = (uint32_t)k - sh.sel_above;
   const uint32_t c = sh.sel_count;
   if (c > (uint32_t)kCandMax || n > kMaxRowForBitmap) {
-    topk_radix_rest(keys, n, k, orow, sh);   // heavy ties or very long row
+    const RowKeys keys{row, nullptr, 0};       // full keys from global
+    topk_radix_rest(keys, n, k, orow, sh);     // heavy ties or very long row
     return;
   }
-  // 3. per-segment counts of keys above bin d; collect bin d
+  // 3. per-segment counts of keys above bin d; collect the indices of bin d
   const int seg = ((n + kTopkWaves - 1) / kTopkWaves + 63) & ~63;
   const int b0 = min(n, wave * seg), b1 = min(n, b0 + seg);
   uint32_t gt = 0;
-  auto lds_key = [&](int i) { return s_cache[i]; };
-  auto glb_key = [&](int i) { return float_to_ordered(row[i]); };
+  auto lds_hi = [&](int i) { return (uint32_t)s_hi[i]; };
+  auto glb_hi = [&](int i) {
+    return KEY32 ? float_to_ordered(row[i]) : float_to_ordered(row[i]) >> 16;
+  };
   const int bm = min(max(b0, cached), b1);   // [b0, bm) cached, [bm, b1) not
-  auto collect = [&](int i, bool in, uint32_t key) {
+  auto collect = [&](int i, bool in, uint32_t hi) {
     if (!in) return;
-    const uint32_t dig = key >> 20;
+    const uint32_t dig = hi >> kDigShift;
     gt += dig > d;
     if (dig == d) {
       const uint32_t slot = atomicAdd(&sh.ncand, 1u);
       if (slot < (uint32_t)kCandMax) {
-        sh.cand_key[slot] = key;
         sh.cand_idx[slot] = (uint32_t)i;
+        if (KEY32) sh.cand_key[slot] = hi;
       }
     }
   };
-  wave_sweep<8>(b0, bm, lds_key, collect);
-  wave_sweep<8>(bm, b1, glb_key, collect);
+  wave_sweep<8>(b0, bm, lds_hi, collect);
+  wave_sweep<8>(bm, b1, glb_hi, collect);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) gt += __shfl_xor(gt, off);
   if (lane == 0) atomicAdd(&sh.seg_cnt[wave], gt);
+  __syncthreads();
+  // full keys of the candidates, all loads in flight together
+  if (!KEY32) {
+    const uint32_t ncl = min(sh.ncand, (uint32_t)kCandMax);
+    const uint32_t j0 = tid, j1 = tid + kTopkThreads;
+    const float f0 = row[j0 < ncl ? sh.cand_idx[j0] : 0];
+    const float f1 = row[j1 < ncl ? sh.cand_idx[j1] : 0];
+    if (j0 < ncl) sh.cand_key[j0] = float_to_ordered(f0);
+    if (j1 < ncl) sh.cand_key[j1] = float_to_ordered(f1);
+  }
   __syncthreads();
   // 4. exact threshold among the candidates: (key & mask) > thr is taken,
   //    (key & mask) == thr is a tie, k_tie of the ties are taken by index.
@@ -407,10 +435,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(
   for (int w = 0; w < wave; ++w) { pos += sh.seg_cnt[w]; tie_seen += sh.seg_eq[w]; }
   pos += min(tie_seen, k_tie);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  auto emit = [&](int i, bool in, uint32_t key) {
+  auto emit = [&](int i, bool in, uint32_t hi) {
     bool sel = false, tie = false;
     if (in) {
-      const uint32_t dig = key >> 20;
+      const uint32_t dig = hi >> kDigShift;
       sel = dig > d;
       if (dig == d) {
         sel = (sh.selbits[i >> 5] >> (i & 31)) & 1u;
@@ -426,8 +454,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(
     pos += (uint32_t)__popcll(sel_mask);
     tie_seen += (uint32_t)__popcll(tie_mask);
   };
-  wave_sweep<8>(b0, bm, lds_key, emit);
-  wave_sweep<8>(bm, b1, glb_key, emit);
+  wave_sweep<8>(b0, bm, lds_hi, emit);
+  wave_sweep<8>(bm, b1, glb_hi, emit);
 }
 
 // ---------------------------------------------------------------------------
@@ -548,12 +576,16 @@ __device__ void mw_select(const uint32_t* hist, uint32_t k_rem,
   __syncthreads();
 }
 
+constexpr int kMwLocalCand = 1024;
+
 struct MwShared {
   uint32_t hist[kHistBins];
   uint32_t wave_sum[kMwWaves];
   uint32_t sel[3];
   uint32_t last;
   uint32_t wcnt[kMwWaves], wtie[kMwWaves];
+  uint32_t lkey[kMwLocalCand], lidx[kMwLocalCand];
+  uint32_t nloc, base;
 };
 
 __device__ __forceinline__ int row_len(const int32_t* positions, int64_t t,
@@ -700,6 +732,10 @@ __global__ __launch_bounds__(kMwThreads) void mw_pass2_kernel(
   const int i0 = (int)c * kMwChunk, i1 = min(n, i0 + kMwChunk);
   uint32_t* ck = ws.cand_key + t * kMwCandCap;
   uint32_t* ci = ws.cand_idx + t * kMwCandCap;
+  if (tid == 0) sh.nloc = 0u;
+  __syncthreads();
+  // keys above bin d1 are counted; keys in bin d1 are gathered in LDS and
+  // appended to the row's list with one global atomic per workgroup
   uint32_t gt = 0;
   block_sweep<8, kMwThreads>(
       i0, i1, [&](int i) { return float_to_ordered(row[i]); },
@@ -707,10 +743,13 @@ __global__ __launch_bounds__(kMwThreads) void mw_pass2_kernel(
         const uint32_t dig = key >> 20;
         gt += dig > st.d1;
         if (dig == st.d1) {
-          const uint32_t slot = atomicAdd(&ws.ncand[t], 1u);
-          if (slot < (uint32_t)kMwCandCap) {
-            ck[slot] = key;
-            ci[slot] = (uint32_t)i;
+          const uint32_t slot = atomicAdd(&sh.nloc, 1u);
+          if (slot < (uint32_t)kMwLocalCand) {
+            sh.lkey[slot] = key;
+            sh.lidx[slot] = (uint32_t)i;
+          } else {                                 // rare: straight to global
+            const uint32_t g = atomicAdd(&ws.ncand[t], 1u);
+            if (g < (uint32_t)kMwCandCap) { ck[g] = key; ci[g] = (uint32_t)i; }
           }
         }
       });
@@ -718,10 +757,17 @@ __global__ __launch_bounds__(kMwThreads) void mw_pass2_kernel(
   for (int off = 32; off >= 1; off >>= 1) gt += __shfl_xor(gt, off);
   if (lane == 0) sh.wcnt[wave] = gt;
   __syncthreads();
+  const uint32_t nl = min(sh.nloc, (uint32_t)kMwLocalCand);
   if (tid == 0) {
     uint32_t s = 0;
     for (int w = 0; w < kMwWaves; ++w) s += sh.wcnt[w];
     atomicAdd(&ws.ccnt[t * ws.C + c], s);
+    sh.base = nl ? atomicAdd(&ws.ncand[t], nl) : 0u;
+  }
+  __syncthreads();
+  for (uint32_t j = tid; j < nl; j += kMwThreads) {
+    const uint32_t g = sh.base + j;
+    if (g < (uint32_t)kMwCandCap) { ck[g] = sh.lkey[j]; ci[g] = sh.lidx[j]; }
   }
   if (!mw_arrive_last(&ws.done2[t], parts, sh)) return;
   const uint32_t nc = __atomic_load_n(&ws.ncand[t], __ATOMIC_RELAXED);
@@ -790,22 +836,29 @@ size_t topk_workspace_bytes(int64_t T, int64_t ld, int k) {
   return total;
 }
 
-static hipError_t launch_topk_single(const TopkArgs& a, hipStream_t stream) {
-  const int cap = (int)std::min<int64_t>(a.ld, kMaxCachedKeys);
-  const size_t dyn = (size_t)cap * sizeof(uint32_t);
+template <bool KEY32>
+static hipError_t launch_topk_single_t(const TopkArgs& a, hipStream_t stream,
+                                       int max_cache, size_t elem) {
+  const int cap = (int)std::min<int64_t>(a.ld, max_cache);
+  const size_t dyn = (size_t)cap * elem;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(topk_row_kernel),
-        hipFuncAttributeMaxDynamicSharedMemorySize,
-        (int)(kMaxCachedKeys * sizeof(uint32_t)));
+        reinterpret_cast<const void*>(topk_row_kernel<KEY32>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)(max_cache * elem));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)a.T), dim3(kTopkThreads),
-                     dyn, stream, a.logits, a.ld, a.positions, a.k, a.out,
-                     a.out_ld, cap);
+  hipLaunchKernelGGL(topk_row_kernel<KEY32>, dim3((unsigned)a.T),
+                     dim3(kTopkThreads), dyn, stream, a.logits, a.ld,
+                     a.positions, a.k, a.out, a.out_ld, cap);
   return hipGetLastError();
+}
+
+static hipError_t launch_topk_single(const TopkArgs& a, hipStream_t stream) {
+  if (a.ld <= kMaxCachedFull)
+    return launch_topk_single_t<true>(a, stream, kMaxCachedFull, 4);
+  return launch_topk_single_t<false>(a, stream, kMaxCachedHi, 2);
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {

@@ -78,7 +78,7 @@ def test_quantize_q_bit_exact_decode_shape():
 
 
 # ------------------------------------------------------------------- tiny --
-@pytest.mark.parametrize("kernel", [0, 1, 2])
+@pytest.mark.parametrize("kernel", [0, 1, 2, 3])
 def test_tiny_logits_and_topk(kernel):
     _say(f"case: tiny, logits kernel option {kernel}")
     binding.dsa_set_option("logits_kernel", kernel)
@@ -97,7 +97,7 @@ def test_tiny_logits_and_topk(kernel):
 
 
 # ----------------------------------------------------------------- decode --
-@pytest.mark.parametrize("kernel", [0, 2])
+@pytest.mark.parametrize("kernel", [0, 2, 3])
 def test_decode_batch_all_rows(kernel):
     _say(f"case: decode batch (64 x U[1024,8192], H=64, k=2048), kernel {kernel}")
     binding.dsa_set_option("logits_kernel", kernel)
@@ -198,7 +198,7 @@ EDGE_CASES = {
 
 
 @pytest.mark.parametrize("name", sorted(EDGE_CASES))
-@pytest.mark.parametrize("kernel", [1, 2])
+@pytest.mark.parametrize("kernel", [1, 2, 3])
 def test_edge_cases(name, kernel):
     _say(f"case: edge {name}, logits kernel {kernel}")
     binding.dsa_set_option("logits_kernel", kernel)
