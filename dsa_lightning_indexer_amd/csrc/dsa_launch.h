@@ -42,7 +42,7 @@ struct Options {
   int logits_kernel = 0;        // 1 = row-wise, 2 = tiled
   int row_pages_per_wave = 0;
   int tile_pages_per_split = 0;
-  int topk_kernel = 0;          // 1 = one workgroup per row, 2 = multi-WG
+  int topk_kernel = 0;          // 0/1 = register-resident rows, 2 = LDS-cached rows
 };
 Options& options();
 

@@ -76,9 +76,9 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
 // larger keys first reaches k_rem, scanning from the top.  4096 bins: wave
 // w owns bins 4095-256w down to 3840-256w, 4 per lane; 256 bins: wave 0
 // alone.  Results in sh.sel_*.  Call from all threads.
-template <int NBINS>
+template <int NBINS, typename Shared>
 __device__ void select_bin_fast(const uint32_t* hist, uint32_t k_rem,
-                                TopkShared& sh) {
+                                Shared& sh) {
   static_assert(NBINS == 4096 || NBINS == 256, "bins");
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
@@ -456,6 +456,176 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(
   };
   wave_sweep<8>(b0, bm, lds_hi, emit);
   wave_sweep<8>(bm, b1, glb_hi, emit);
+}
+
+// ---------------------------------------------------------------------------
+// Register-resident top-k for rows of up to kRegMaxRow columns (decode rows,
+// prefill rows).  Thread tid holds columns s*4096 + 4*tid + j (slice s,
+// j = 0..3) in registers: one coalesced 16-byte load per slice, no LDS copy
+// of the row.  The threshold key is found by up to three LDS histograms
+// (top 12 key bits over the row; bits 19..8 over the keys of the chosen
+// bin; bits 7..0 over the keys matching the 24-bit prefix), each followed by
+// the two-barrier bin search.  Selection: masked key > thr, or == thr for
+// the k_tie lowest-index ties.  The output slot of a selected column is the
+// number of selected columns before it: one packed (above, tie) count per
+// thread and slice, a DPP scan within the wave and a scan of the per-wave
+// totals give every thread its offsets, so the indices come out in
+// ascending order with no candidate list and no capacity limit.
+// ---------------------------------------------------------------------------
+constexpr int kRegSlice = 4 * kTopkThreads;     // columns per slice
+constexpr int kRegMaxSlices = 12;
+constexpr int kRegMaxRow = kRegSlice * kRegMaxSlices;   // 49152
+
+struct RegTopkShared {
+  uint32_t hist[kHistBins];
+  uint32_t hist2[kHistBins];
+  uint32_t tot[kRegMaxSlices * kTopkWaves];     // packed per (slice, wave)
+  uint32_t wave_sum[kTopkWaves];
+  uint32_t sel_digit, sel_above, sel_count;
+};
+
+template <int S>
+__global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(
+    const float* __restrict__ logits, int64_t ld,
+    const int32_t* __restrict__ positions, int k, int32_t* __restrict__ out,
+    int64_t out_ld) {
+  static_assert(S >= 1 && S <= kRegMaxSlices, "slices");
+  __shared__ RegTopkShared sh;
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  int32_t* orow = out + t * out_ld;
+  int p = positions[t];
+  if (p >= ld) p = (int)ld - 1;              // logits past ld do not exist
+  const int n = p + 1;                       // p < 0 -> empty row
+  if (n <= k) {
+    for (int i = tid; i < k; i += kTopkThreads) orow[i] = i < n ? i : -1;
+    return;
+  }
+  const float* row = logits + t * ld;
+
+  for (int b = tid; b < kHistBins; b += kTopkThreads) {
+    sh.hist[b] = 0u;
+    sh.hist2[b] = 0u;
+  }
+  // keys of this thread's columns; columns >= n are marked invalid
+  uint32_t key[S][4];
+  uint32_t valid[S];                          // bit j: column valid
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int c0 = s * kRegSlice + 4 * tid;
+    valid[s] = 0u;
+    key[s][0] = key[s][1] = key[s][2] = key[s][3] = 0u;
+    if (s * kRegSlice < n) {                  // workgroup-uniform
+      const float4 v =
+          *reinterpret_cast<const float4*>(row + min(c0, (int)ld - 4));
+      key[s][0] = float_to_ordered(v.x);
+      key[s][1] = float_to_ordered(v.y);
+      key[s][2] = float_to_ordered(v.z);
+      key[s][3] = float_to_ordered(v.w);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) valid[s] |= (c0 + j < n ? 1u : 0u) << j;
+    }
+  }
+  __syncthreads();
+  // pass 1: top 12 bits over the row
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if ((valid[s] >> j) & 1u) atomicAdd(&sh.hist[key[s][j] >> 20], 1u);
+  __syncthreads();
+  select_bin_fast<kHistBins>(sh.hist, (uint32_t)k, sh);
+  const uint32_t d = sh.sel_digit;
+  const uint32_t k_rem = (uint32_t)k - sh.sel_above;
+  uint32_t mask = 0xfff00000u, thr = d << 20, k_tie = k_rem;
+  if (k_rem < sh.sel_count) {
+    // pass 2: bits 19..8 of the keys in bin d; bins 0..255 of hist are
+    // cleared for pass 3 (the barrier after pass 2 orders the clear)
+    if (tid < 256) sh.hist[tid] = 0u;
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (((valid[s] >> j) & 1u) && (key[s][j] >> 20) == d)
+          atomicAdd(&sh.hist2[(key[s][j] >> 8) & 0xfffu], 1u);
+    __syncthreads();
+    select_bin_fast<kHistBins>(sh.hist2, k_rem, sh);
+    const uint32_t p24 = (d << 12) | sh.sel_digit;
+    const uint32_t k2 = k_rem - sh.sel_above;
+    mask = 0xffffff00u; thr = p24 << 8; k_tie = k2;
+    if (k2 < sh.sel_count) {
+      // pass 3: bits 7..0 of the keys matching the 24-bit prefix
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (((valid[s] >> j) & 1u) && (key[s][j] >> 8) == p24)
+            atomicAdd(&sh.hist[key[s][j] & 0xffu], 1u);
+      __syncthreads();
+      select_bin_fast<256>(sh.hist, k2, sh);
+      mask = 0xffffffffu; thr = (p24 << 8) | sh.sel_digit;
+      k_tie = k2 - sh.sel_above;
+    }
+  }
+  // packed per-slice counts: above in bits 0..15, ties in bits 16..31
+  uint32_t cnt[S], incl[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    uint32_t c = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = (valid[s] >> j) & 1u;
+      const uint32_t km = key[s][j] & mask;
+      c += (ok && km > thr) ? 1u : 0u;
+      c += (ok && km == thr) ? 0x10000u : 0u;
+    }
+    cnt[s] = c;
+    incl[s] = wave_inclusive_scan(c);
+    if (lane == 63) sh.tot[s * kTopkWaves + wave] = incl[s];
+  }
+  __syncthreads();
+  // exclusive scan of the S*16 (slice, wave) totals, in place, by wave 0
+  if (wave == 0) {
+    constexpr int kPer = (S * kTopkWaves + 63) / 64;
+    uint32_t v[kPer], local = 0u;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int idx = lane * kPer + i;
+      v[i] = idx < S * kTopkWaves ? sh.tot[idx] : 0u;
+      local += v[i];
+    }
+    uint32_t run = wave_inclusive_scan(local) - local;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int idx = lane * kPer + i;
+      if (idx < S * kTopkWaves) sh.tot[idx] = run;
+      run += v[i];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const uint32_t before = sh.tot[s * kTopkWaves + wave] + incl[s] - cnt[s];
+    uint32_t gt_b = before & 0xffffu, eq_b = before >> 16;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = (valid[s] >> j) & 1u;
+      const uint32_t km = key[s][j] & mask;
+      const int col = s * kRegSlice + 4 * tid + j;
+      // slots are < k by construction; the check keeps a row's writes
+      // inside the row whatever the counts
+      if (ok && km > thr) {
+        const uint32_t slot = gt_b + min(eq_b, k_tie);
+        if (slot < (uint32_t)k) orow[slot] = col;
+        ++gt_b;
+      } else if (ok && km == thr) {
+        if (eq_b < k_tie && gt_b + eq_b < (uint32_t)k) orow[gt_b + eq_b] = col;
+        ++eq_b;
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -855,7 +1025,37 @@ static hipError_t launch_topk_single_t(const TopkArgs& a, hipStream_t stream,
   return hipGetLastError();
 }
 
+template <int S>
+static hipError_t launch_topk_reg_t(const TopkArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(topk_reg_kernel<S>, dim3((unsigned)a.T),
+                     dim3(kTopkThreads), 0, stream, a.logits, a.ld,
+                     a.positions, a.k, a.out, a.out_ld);
+  return hipGetLastError();
+}
+
+static hipError_t launch_topk_reg(const TopkArgs& a, hipStream_t stream) {
+  switch ((a.ld + kRegSlice - 1) / kRegSlice) {
+    case 1: return launch_topk_reg_t<1>(a, stream);
+    case 2: return launch_topk_reg_t<2>(a, stream);
+    case 3: return launch_topk_reg_t<3>(a, stream);
+    case 4: return launch_topk_reg_t<4>(a, stream);
+    case 5: return launch_topk_reg_t<5>(a, stream);
+    case 6: return launch_topk_reg_t<6>(a, stream);
+    case 7: return launch_topk_reg_t<7>(a, stream);
+    case 8: return launch_topk_reg_t<8>(a, stream);
+    case 9: return launch_topk_reg_t<9>(a, stream);
+    case 10: return launch_topk_reg_t<10>(a, stream);
+    case 11: return launch_topk_reg_t<11>(a, stream);
+    default: return launch_topk_reg_t<12>(a, stream);
+  }
+}
+
 static hipError_t launch_topk_single(const TopkArgs& a, hipStream_t stream) {
+  // register-resident kernel unless disabled (option 2) or the row is too
+  // long for it; it needs 16-byte aligned rows (ld is a multiple of 256)
+  const bool aligned = (reinterpret_cast<uintptr_t>(a.logits) & 15u) == 0;
+  if (options().topk_kernel != 2 && a.ld <= kRegMaxRow && aligned)
+    return launch_topk_reg(a, stream);
   if (a.ld <= kMaxCachedFull)
     return launch_topk_single_t<true>(a, stream, kMaxCachedFull, 4);
   return launch_topk_single_t<false>(a, stream, kMaxCachedHi, 2);

@@ -211,8 +211,9 @@ int dsa_device_error_flags(int reset);
 /*
  * dsa_set_option -- tuning/testing knobs; returns the previous value or
  * DSA_ERR_INVALID_ARG for an unknown key.  Value 0 restores the automatic
- * choice.  Keys: "logits_kernel" (1 row-wise, 2 tiled), "row_pages_per_wave",
- * "tile_pages_per_split", "topk_kernel" (1 one workgroup per row).
+ * choice.  Keys: "logits_kernel" (1 row-wise, 2 tiled, 3 tiled with direct
+ * loads), "row_pages_per_wave", "tile_pages_per_split", "topk_kernel" (rows
+ * of up to 49152 columns: 1 register-resident keys, 2 keys cached in LDS).
  */
 int dsa_set_option(const char* key, int value);
 

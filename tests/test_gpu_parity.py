@@ -247,8 +247,10 @@ def test_page_permutation_gives_identical_logits():
     assert torch.equal(tk1, tk2)
 
 
-def test_topk_ties_and_constant_rows():
-    _say("case: top-k ties")
+@pytest.mark.parametrize("kernel", [1, 2])
+def test_topk_ties_and_constant_rows(kernel):
+    _say(f"case: top-k ties, top-k kernel {kernel}")
+    binding.dsa_set_option("topk_kernel", kernel)
     T, ld, k = 6, 4096, 100
     rng = np.random.default_rng(12)
     lg = rng.integers(-4, 5, size=(T, ld)).astype(np.float32)
@@ -263,6 +265,49 @@ def test_topk_ties_and_constant_rows():
     for t in range(T):
         parity.check_topk_exact_on_gpu_logits(g[t], lg[t], int(pos[t]), k,
                                               f"ties row {t}")
+
+
+@pytest.mark.parametrize("kernel", [1, 2])
+@pytest.mark.parametrize("ld", [256, 4096, 8192, 20480, 40960, 49152, 53248])
+def test_topk_row_lengths(ld, kernel):
+    """Single-workgroup top-k over row lengths that span one to twelve
+    4096-column slices (and one past the register-resident limit), with
+    random, integer-tied and constant rows, rows just above and below k,
+    and a row whose length is the whole ld."""
+    _say(f"case: top-k rows of ld {ld}, top-k kernel {kernel}")
+    binding.dsa_set_option("topk_kernel", kernel)
+    k = 2048 if ld >= 4096 else 64
+    rng = np.random.default_rng(ld + kernel)
+    T = 8
+    lg = (rng.standard_normal((T, ld)) * 5).astype(np.float32)
+    lg[1] = np.round(lg[1])                            # many ties
+    lg[2] = -3.25                                      # constant
+    lg[5, : ld // 2] = -np.inf
+    pos = np.array([ld - 1, ld - 1, ld // 2, k, k - 1, ld - 1,
+                    min(ld - 1, k + 4097), max(0, ld - 4093)], np.int32)
+    g = binding.dsa_indexer_topk(torch.from_numpy(lg).cuda(),
+                                 torch.from_numpy(pos).cuda(), k).cpu().numpy()
+    for t in range(T):
+        parity.check_topk_exact_on_gpu_logits(g[t], lg[t], int(pos[t]), k,
+                                              f"ld {ld} row {t}")
+
+
+def test_topk_unaligned_logits_rows():
+    """A logits pointer that is not 16-byte aligned takes the LDS-cached
+    kernel; results are the exact top-k either way."""
+    _say("case: top-k on an unaligned logits view")
+    T, ld, k = 4, 4096, 512
+    rng = np.random.default_rng(5)
+    base = torch.from_numpy(rng.standard_normal(T * ld + 1)
+                            .astype(np.float32)).cuda()
+    lg = base[1:].view(T, ld)
+    pos = torch.tensor([4095, 2000, 600, 511], dtype=torch.int32,
+                       device="cuda")
+    g = binding.dsa_indexer_topk(lg, pos, k).cpu().numpy()
+    lgh = lg.cpu().numpy()
+    for t in range(T):
+        parity.check_topk_exact_on_gpu_logits(g[t], lgh[t], int(pos[t]), k,
+                                              f"unaligned row {t}")
 
 
 def test_topk_multi_workgroup_rows():
