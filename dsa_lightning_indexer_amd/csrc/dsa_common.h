@@ -78,6 +78,37 @@ __device__ __forceinline__ int wave_uniform(int v) {
   return __builtin_amdgcn_readfirstlane(v);
 }
 
+// Inclusive prefix sum across the 64 lanes of a wave with DPP: four
+// row_shr steps within each 16-lane row, then row_bcast:15 / row_bcast:31
+// carry the row totals into the later rows.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false); // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false); // row_bcast:31
+  return x;
+}
+
+// Read-only metadata (positions, query_start_loc, block table) through the
+// constant address space: a wave-uniform index becomes a scalar load, which
+// travels on the scalar cache path instead of queueing behind the vector
+// loads in flight on the compute unit.
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+__device__ __forceinline__ int load_uniform(const int32_t* p, int64_t i) {
+  return ((const_i32*)(p))[i];
+}
+
+// Raw buffer resource over [base, base + bytes): loads past the end return
+// zero without touching memory and stores past the end are dropped, so a
+// load or store can be issued unconditionally and switched off by its size.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                            int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes,
+                                           0x00020000);
+}
+
 // Row -> request index by binary search over query_start_loc[0..R].
 __device__ __forceinline__ int request_of_row(const int32_t* qsl, int R,
                                               int64_t t) {

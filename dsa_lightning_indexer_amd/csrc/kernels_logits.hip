@@ -282,6 +282,195 @@ void logits_row_prefetch_kernel(LogitsArgs a, int ppw) {
 }
 
 // ---------------------------------------------------------------------------
+// Balanced row-wise logits for small decode batches (T <= 128 rows).  With
+// few rows of very different lengths, a grid of (row, page group) leaves
+// some compute units with several long groups and others idle, and a
+// compute unit's share of the bytes sets the kernel time.  Here the visible
+// pages of the whole batch are dealt out evenly: every wave (one per
+// workgroup) reads the positions of all rows with scalar loads, computes
+// P = the number of visible pages, a per-wave budget
+// ppw = max(D, ceil(P / waves in the grid)), gives row t ceil(n_t / ppw)
+// waves, and takes its own contiguous page range of one row from a prefix
+// sum over the rows.  Page ids and the request check are scalar loads too,
+// so the K loads are issued after two scalar round trips and never queue
+// behind vector loads.  K pages are read with buffer loads whose size is
+// zero for pages outside the range (no traffic, no branch), which keeps the
+// hardware wait counts exact: page q is scored as soon as its bytes arrive
+// while later pages are still in flight.
+// ---------------------------------------------------------------------------
+constexpr int kBalancedMaxRows = 128;
+
+// Positions of rows c0 .. c0+63 in lanes 0..63 (rows >= T repeat row T-1).
+__device__ __forceinline__ int positions_to_lanes(const int32_t* pos, int c0,
+                                                  int64_t T) {
+  int x[64];
+  if ((int64_t)c0 + 64 <= T) {
+    typedef int i32x16 __attribute__((ext_vector_type(16)));
+    typedef __attribute__((address_space(4))) const i32x16 const_i32x16;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const i32x16 v = ((const_i32x16*)(pos + c0))[k];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) x[16 * k + j] = v[j];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 64; ++i)
+      x[i] = load_uniform(pos, min<int64_t>(c0 + i, T - 1));
+  }
+  int v = 0;
+#pragma unroll
+  for (int i = 0; i < 64; ++i)
+    asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(x[i]), "i"(i));
+  return v;
+}
+
+struct RowSpan {
+  int row, jb, je, p;
+};
+
+// The page range [jb, je) of row `row` owned by wave `wv`; row = -1 when the
+// wave has no work.  With ppw >= P / budget, the rows need at most
+// budget + T waves (one partial wave per row), the grid size.  Rows whose
+// position is out of range own no pages (the row is left untouched and wave
+// 0 raises the flag).
+template <int NCH>
+__device__ __forceinline__ RowSpan balanced_span(const LogitsArgs& a, int D,
+                                                 int budget, int wv) {
+  const int lane = lane_id();
+  int pl[NCH], n[NCH];
+  uint32_t total = 0u;
+  bool bad = false;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    pl[c] = positions_to_lanes(a.positions, 64 * c, a.T);
+    const bool in = 64 * c + lane < a.T;
+    const bool ok = pl[c] >= 0 && pl[c] < a.ld &&
+                    (int64_t)(pl[c] >> 6) < a.bt_stride;
+    bad |= in && !ok;
+    n[c] = (in && ok) ? (pl[c] >> 6) + 1 : 0;
+    total += __builtin_amdgcn_readlane(wave_inclusive_scan((uint32_t)n[c]), 63);
+  }
+  if (wv == 0 && __ballot(bad) != 0ull && lane == 0)
+    raise_flag(kErrPositionOutOfRange);
+  const int ppw =
+      max(D, (int)((total + (uint32_t)budget - 1) / (uint32_t)budget));
+  RowSpan sp{-1, 0, 0, 0};
+  uint32_t base = 0u;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const uint32_t cnt = ((uint32_t)n[c] + ppw - 1) / (uint32_t)ppw;
+    const uint32_t incl = wave_inclusive_scan(cnt);
+    const uint64_t m = __ballot((uint32_t)wv < base + incl);
+    if (sp.row < 0 && m != 0ull) {
+      const int l = __builtin_ctzll(m);
+      const int ex = (int)(base + __builtin_amdgcn_readlane(incl - cnt, l));
+      const int cl = __builtin_amdgcn_readlane((int)cnt, l);
+      const int nl = __builtin_amdgcn_readlane(n[c], l);
+      // nl = cl * qd + rm: the first rm waves of the row take qd + 1 pages
+      const int i = wv - ex, qd = nl / cl, rm = nl - qd * cl;
+      sp.row = 64 * c + l;
+      sp.jb = i * qd + min(i, rm);
+      sp.je = sp.jb + qd + (i < rm ? 1 : 0);
+      sp.p = __builtin_amdgcn_readlane(pl[c], l);
+    }
+    base += __builtin_amdgcn_readlane(incl, 63);
+  }
+  sp.row = wave_uniform(sp.row);
+  sp.jb = wave_uniform(sp.jb);
+  sp.je = wave_uniform(sp.je);
+  sp.p = wave_uniform(sp.p);
+  return sp;
+}
+
+template <int MT, bool FULL, int D, int NCH>
+__global__ __launch_bounds__(64) void logits_balanced_kernel(LogitsArgs a,
+                                                             int budget) {
+  const int lane = lane_id();
+  const int i16 = lane & 15, g = lane >> 4;
+  const RowSpan sp = balanced_span<NCH>(a, D, budget, (int)blockIdx.x);
+  if (sp.row < 0) return;
+  const int64_t t = sp.row;
+  const int p = sp.p, jb = sp.jb, je = sp.je;
+
+  // request guess r = t (one query row per request), checked below; the
+  // page ids of the first chunk are fetched with it
+  int r = (int)min<int64_t>(t, a.R - 1);
+  const int q0 = load_uniform(a.qsl, r), q1 = load_uniform(a.qsl, r + 1);
+  const int32_t* btr = a.block_table + (int64_t)r * a.bt_stride;
+  const int last = (int)a.bt_stride - 1;
+  int pages[D];
+#pragma unroll
+  for (int q = 0; q < D; ++q) pages[q] = load_uniform(btr, min(jb + q, last));
+  i32x8 qa[MT];
+  load_q_frags<MT, FULL>(a.q8 + t * a.H * kHeadDim, a.H, qa);
+  float w[MT][4];
+  load_head_weights<MT, FULL>(a.weights + t * a.H, a.q_scale + t * a.H, a.H,
+                              w);
+  if (!(q0 <= t && t < q1)) {                 // rows are not one per request
+    r = wave_uniform(request_of_row_wave(a.qsl, a.R, t));
+    btr = a.block_table + (int64_t)r * a.bt_stride;
+#pragma unroll
+    for (int q = 0; q < D; ++q) pages[q] = load_uniform(btr, min(jb + q, last));
+  }
+  float* out = a.logits + t * a.ld;
+  bool bad_page = false;
+  for (int c = jb; c < je; c += D) {
+    if (c != jb) {
+#pragma unroll
+      for (int q = 0; q < D; ++q) pages[q] = load_uniform(btr, min(c + q, last));
+    }
+    i32x8 kb[D][4];
+    float ks[D];
+    bool ok[D];
+#pragma unroll
+    for (int q = 0; q < D; ++q) {
+      ok[q] = c + q < je && pages[q] >= 0 && (int64_t)pages[q] < a.num_pages;
+      bad_page |= c + q < je && !ok[q];
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(
+          a.k_cache + (int64_t)(ok[q] ? pages[q] : 0) * kPageBytes,
+          ok[q] ? kPageBytes : 0);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int off = (16 * nt + i16) * kHeadDim + 32 * g;
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        const auto y = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0);
+        kb[q][nt] = i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3],
+                          (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+      }
+      ks[q] = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(rs, kPageKeyBytes + 4 * lane, 0, 0));
+    }
+    // keep every load of the chunk ahead of the first MFMA
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < D; ++q) {
+      const int jp = c + q;
+      float res = -INFINITY;
+      if (ok[q]) {
+        float v[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          f32x4 acc[MT];
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+            acc[m] = mfma16x16x128_fp8(qa[m], kb[q][nt], f32x4{0.f, 0.f, 0.f, 0.f});
+          v[nt] = head_reduce<MT>(acc, w);
+        }
+        const float tot = reduce_scatter4(v[0], v[1], v[2], v[3]);
+        if (jp * kPageTokens + lane <= p) res = tot * ks[q];
+      }
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc(
+          out + (int64_t)min(jp, last) * kPageTokens,
+          jp < je ? kPageTokens * 4 : 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(res), ro, 4 * lane,
+                                            0, 0);
+    }
+  }
+  if (bad_page && lane == 0) raise_flag(kErrPageOutOfRange);
+}
+
+// ---------------------------------------------------------------------------
 // Tiled logits (several query rows of one request share every K page: the
 // prefill chunk and the long-context tail).  A workgroup of 8 waves owns a
 // tile of 16 consecutive rows of one request and a range of pages; each
@@ -613,7 +802,25 @@ template <int MT, bool FULL>
 static hipError_t launch_logits_mt(const LogitsArgs& a, hipStream_t stream,
                                    bool tiled, int64_t max_pages) {
   const Options& o = options();
-  if (!tiled) {
+  if (!tiled && a.T <= kBalancedMaxRows && o.logits_kernel != 4) {
+    // D pages per wave; enough waves that a batch whose rows all reach
+    // max_pages still gets about D pages per wave
+    int D = o.row_pages_per_wave;
+    D = D <= 0 ? 3 : std::min(D, 4);
+    if (D == 1) D = 2;
+    const int64_t pmax = a.T * max_pages;
+    const int64_t budget =
+        std::max<int64_t>(1, std::min<int64_t>((pmax + D - 1) / D, 1 << 16));
+    const dim3 grid((unsigned)(budget + a.T));
+    const bool two = a.T > 64;
+#define DSA_BAL(DD)                                                          \
+    if (two) hipLaunchKernelGGL((logits_balanced_kernel<MT, FULL, DD, 2>),    \
+                                grid, dim3(64), 0, stream, a, (int)budget);   \
+    else hipLaunchKernelGGL((logits_balanced_kernel<MT, FULL, DD, 1>),        \
+                            grid, dim3(64), 0, stream, a, (int)budget);
+    if (D == 2) { DSA_BAL(2) } else if (D == 3) { DSA_BAL(3) } else { DSA_BAL(4) }
+#undef DSA_BAL
+  } else if (!tiled) {
     int ppw = o.row_pages_per_wave;
     if (ppw <= 0) {
       // about 512 workgroups of 4 waves: enough waves in flight to keep
@@ -659,8 +866,8 @@ hipError_t launch_logits(const LogitsArgs& a, hipStream_t stream) {
   const int64_t max_pages = std::min<int64_t>(a.bt_stride, a.ld / kPageTokens);
   const Options& o = options();
   bool tiled = a.T > 2 * (int64_t)a.R;
-  if (o.logits_kernel == 1) tiled = false;
-  if (o.logits_kernel >= 2) tiled = true;
+  if (o.logits_kernel == 1 || o.logits_kernel == 4) tiled = false;
+  if (o.logits_kernel == 2 || o.logits_kernel == 3) tiled = true;
   switch (a.H) {
     case 16: return launch_logits_mt<1, true>(a, stream, tiled, max_pages);
     case 32: return launch_logits_mt<2, true>(a, stream, tiled, max_pages);

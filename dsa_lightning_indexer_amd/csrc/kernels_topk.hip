@@ -59,18 +59,6 @@ struct TopkShared {
   uint32_t sel_digit, sel_above, sel_count, ncand;
 };
 
-// Inclusive prefix sum across the 64 lanes of a wave with DPP: four
-// row_shr steps within each 16-lane row, then row_bcast:15 / row_bcast:31
-// carry the row totals into the later rows.
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, true);  // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, true);  // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, true);  // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, true);  // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false); // row_bcast:15
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false); // row_bcast:31
-  return x;
-}
 
 // Two-barrier bin search on an LDS histogram: the bin where the count of
 // larger keys first reaches k_rem, scanning from the top.  4096 bins: wave

@@ -78,7 +78,7 @@ def test_quantize_q_bit_exact_decode_shape():
 
 
 # ------------------------------------------------------------------- tiny --
-@pytest.mark.parametrize("kernel", [0, 1, 2, 3])
+@pytest.mark.parametrize("kernel", [0, 1, 2, 3, 4])
 def test_tiny_logits_and_topk(kernel):
     _say(f"case: tiny, logits kernel option {kernel}")
     binding.dsa_set_option("logits_kernel", kernel)
@@ -97,7 +97,7 @@ def test_tiny_logits_and_topk(kernel):
 
 
 # ----------------------------------------------------------------- decode --
-@pytest.mark.parametrize("kernel", [0, 2, 3])
+@pytest.mark.parametrize("kernel", [0, 2, 3, 4])
 def test_decode_batch_all_rows(kernel):
     _say(f"case: decode batch (64 x U[1024,8192], H=64, k=2048), kernel {kernel}")
     binding.dsa_set_option("logits_kernel", kernel)
@@ -122,6 +122,23 @@ def test_decode_batch_all_rows(kernel):
          f"max |err| / M = {err_m:.3e} (2^{np.log2(err_m):.1f}), "
          f"padded rows {padded}")
     assert padded > 0                 # the batch exercises -1 padding
+    _assert_no_device_errors()
+
+
+@pytest.mark.parametrize("rows", [100, 128])
+def test_decode_batch_two_position_chunks(rows):
+    """More than 64 decode rows: the balanced row kernel reads the positions
+    in two chunks of 64 lanes."""
+    _say(f"case: decode batch of {rows} rows")
+    b = synth.decode(R=rows)
+    _, _, lg, tk = parity.run_gpu(b)
+    lg, tk = lg.cpu().numpy(), tk.cpu().numpy()
+    ora = parity.oracle_logits(b)
+    mag = parity.magnitude(b)
+    for t in range(b.T):
+        p = int(b.positions[t])
+        parity.check_logits_row(lg[t], ora[t], p, f"decode row {t}", mag[t])
+        parity.check_topk_exact_on_gpu_logits(tk[t], lg[t], p, b.k)
     _assert_no_device_errors()
 
 
@@ -198,7 +215,7 @@ EDGE_CASES = {
 
 
 @pytest.mark.parametrize("name", sorted(EDGE_CASES))
-@pytest.mark.parametrize("kernel", [1, 2, 3])
+@pytest.mark.parametrize("kernel", [1, 2, 3, 4])
 def test_edge_cases(name, kernel):
     _say(f"case: edge {name}, logits kernel {kernel}")
     binding.dsa_set_option("logits_kernel", kernel)
