@@ -28,6 +28,9 @@ of the same workload on this host.
 """
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -36,6 +39,7 @@ import time
 
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
 
@@ -74,6 +78,16 @@ def parse():
                          "hardware byte counters)")
     ap.add_argument("--opt", action="append", default=[],
                     help="library tuning knob key=value (dsa_set_option)")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="summarise a rocprofv3 --kernel-trace --stats CSV "
+                         "directory as markdown (no GPU)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="per-dispatch FETCH_SIZE / WRITE_SIZE of the logits "
+                         "kernel from two rocprofv3 --pmc CSV directories, "
+                         "scaled by the 256 MiB calibration copy (no GPU)")
+    ap.add_argument("--bench-log", help="bench JSON line of the profiled run")
+    ap.add_argument("--command", action="append", default=[],
+                    help="command line(s) that produced the profile")
     return ap.parse_args()
 
 
@@ -143,8 +157,164 @@ def cpu_baseline(b, seconds):
                       "top-k)"}
 
 
+
+# ----------------------------------------------------------------------------
+# Profile summaries (run on the host over rocprofv3 CSV output).
+# ----------------------------------------------------------------------------
+LOGITS_SOURCES = ("dsa_lightning_indexer_amd/csrc/kernels_logits.hip",
+                  "dsa_lightning_indexer_amd/csrc/dsa_common.h",
+                  "dsa_lightning_indexer_amd/csrc/dsa_launch.h")
+CALIBRATION_BYTES = 1 << 28
+
+
+def logits_sources_digest():
+    """Digest of the sources the logits kernels are built from: byte counters
+    taken for another version of the kernel are not reported."""
+    h = hashlib.sha256()
+    for rel in LOGITS_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counters_path(config):
+    return os.path.join(ROOT, "profiles", f"{config}_logits_counters.json")
+
+
+def traffic_from_counters(config):
+    """HBM bytes per logits launch from the committed counter summary of this
+    workload, or None when there is none or the kernel has changed since."""
+    try:
+        with open(counters_path(config)) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("sources_digest") != logits_sources_digest():
+        return None
+    return int(d["traffic_bytes_per_launch"])
+
+
+def _csv_rows(directory, suffix):
+    rows = []
+    for path in sorted(glob.glob(os.path.join(directory, f"*{suffix}"))):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    return rows
+
+
+def _per_dispatch(rows):
+    """{dispatch id: (kernel name, summed counter value in KiB)}"""
+    out = {}
+    for r in rows:
+        key = r["Dispatch_Id"]
+        name, v = out.get(key, (r["Kernel_Name"], 0.0))
+        out[key] = (name, v + float(r["Counter_Value"]))
+    return out
+
+
+def _is_logits(name):
+    return "dsa::logits_" in name
+
+
+def pmc_summary(args):
+    fetch = _per_dispatch(_csv_rows(args.pmc_summary[0],
+                                    "counter_collection.csv"))
+    write = _per_dispatch(_csv_rows(args.pmc_summary[1],
+                                    "counter_collection.csv"))
+
+    def calib(d):
+        # the calibration copies are the largest copy dispatches
+        v = sorted((x for n, x in d.values() if "copyBuffer" in n),
+                   reverse=True)[:3]
+        if not v:
+            raise SystemExit("no calibration copy in the counter run")
+        return sum(v) / len(v)
+
+    def logits(d):
+        v = [x for n, x in d.values() if _is_logits(n)]
+        names = sorted({n for n, _ in d.values() if _is_logits(n)})
+        if not v:
+            raise SystemExit("no logits dispatch in the counter run")
+        return sum(v) / len(v), len(v), names
+
+    f_cal, w_cal = calib(fetch), calib(write)
+    f_ff = CALIBRATION_BYTES / (f_cal * 1024.0)
+    w_ff = CALIBRATION_BYTES / (w_cal * 1024.0)
+    f_kib, nf, names = logits(fetch)
+    w_kib, nw, _ = logits(write)
+    bench = None
+    if args.bench_log:
+        with open(args.bench_log) as f:
+            for line in f:
+                if line.startswith("{") and '"metric"' in line:
+                    bench = json.loads(line)
+    out = {
+        "config": args.config,
+        "kernel": names,
+        "sources_digest": logits_sources_digest(),
+        "fetch_kib_per_dispatch": round(f_kib, 1),
+        "write_kib_per_dispatch": round(w_kib, 1),
+        "dispatches": [nf, nw],
+        "calibration_copy_bytes": CALIBRATION_BYTES,
+        "calibration_fetch_kib": round(f_cal, 1),
+        "calibration_write_kib": round(w_cal, 1),
+        "fetch_scale": round(f_ff, 4),
+        "write_scale": round(w_ff, 4),
+        "traffic_bytes_per_launch": int(round(f_kib * 1024 * f_ff +
+                                              w_kib * 1024 * w_ff)),
+        "algorithmic_bytes_per_launch":
+            bench["roofline"]["algorithmic_bytes"] if bench else None,
+        "commands": args.command,
+    }
+    print(json.dumps(out, indent=1))
+
+
+def trace_summary(args):
+    stats = _csv_rows(args.trace_summary, "kernel_stats.csv")
+    trace = _csv_rows(args.trace_summary, "kernel_trace.csv")
+    durs = {}
+    for r in trace:
+        durs.setdefault(r["Kernel_Name"], []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = [f"# Kernel trace: {WORKLOADS.get(args.config, args.config)}", "",
+             "Commands (GPU box, from the repository root):", "", "```"]
+    lines += args.command + ["```", "",
+                             "Durations are per dispatch over every dispatch "
+                             "of the run (warm-up, graph replays and the "
+                             "per-kernel event loops).", "",
+                             "| kernel | calls | average (us) | median (us) "
+                             "| min (us) | max (us) | % |",
+                             "|---|---|---|---|---|---|---|"]
+    for r in stats:
+        name = r["Name"]
+        d = sorted(durs.get(name, [0.0]))
+        nm = name if len(name) <= 90 else name[:87] + "..."
+        lines.append(f"| `{nm}` | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.3f} | "
+                     f"{d[len(d) // 2]:.3f} | {d[0]:.3f} | {d[-1]:.3f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    if args.bench_log:
+        with open(args.bench_log) as f:
+            for line in f:
+                if line.startswith("{") and '"metric"' in line:
+                    b = json.loads(line)
+                    lines += ["", "Bench line of the same (profiled) run: "
+                              f"ms/step {b['ms_per_step']}, per-kernel HIP-"
+                              f"event averages (ms) {b['kernels_ms']}, "
+                              f"roofline {b['roofline']['achieved']} "
+                              f"{b['roofline']['unit']} (frac "
+                              f"{b['roofline']['frac']})."]
+    print("\n".join(lines))
+
+
 def main():
     args = parse()
+    if args.trace_summary:
+        return trace_summary(args)
+    if args.pmc_summary:
+        return pmc_summary(args)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; "
                                    "--gpus N > 1 is not supported"}))
@@ -266,6 +436,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    roof["traffic"] = traffic_from_counters(args.config)
     roof["kernel"] = "logits"
     roof["algorithmic_bytes"] = int(alg_bytes)
     roof["algorithmic_flops"] = flops
