@@ -57,6 +57,9 @@ _SIGNATURES = {
                                 _I, _I, _I, _P, _L, _P]),
     "dsa_indexer_topk": (_I, [_P, _L, _P, _L, _I, _P, _L, _P, _S, _P]),
     "dsa_topk_workspace_size": (_S, [_L, _L, _I]),
+    "dsa_indexer_forward": (_I, [_P, _P, _P, _L, _P, _L, _P, _P, _L, _I, _I,
+                                 _I, _I, _P, _L, _I, _P, _L, _P, _S, _P]),
+    "dsa_forward_workspace_size": (_S, [_L, _I, _L, _I]),
     "dsa_index_cache_mask": (_I, [ctypes.c_char_p, _I, _I, _I, _I, _P]),
     "dsa_index_cache_run": (_I, [ctypes.c_char_p, _I, _I, _I, _I, _P, _P, _L,
                                  _P, _P, _L, _I, _I, _L, _I, _P, _L, _P, _P,
@@ -176,6 +179,45 @@ def dsa_indexer_topk(logits, positions, k, out=None, workspace=None,
             _dev_ptr(out, torch.int32, "out"), out.shape[1], ws_ptr, ws_bytes,
             _stream(stream, dev)))
     return out
+
+
+def dsa_forward_workspace_size(T, H, ld, k):
+    return lib().dsa_forward_workspace_size(T, H, ld, k)
+
+
+def dsa_indexer_forward(q_bf16, weights, k_cache, block_table,
+                        query_start_loc, positions, ld, k, logits=None,
+                        out=None, workspace=None, stream=None):
+    """One layer's hot path: q quantisation, logits and top-k.  Returns
+    (logits fp32 [T, ld], top-k int32 [T, k])."""
+    T, H, D = q_bf16.shape
+    R = block_table.shape[0]
+    dev = q_bf16.device
+    if logits is None:
+        logits = torch.empty((T, ld), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if k_cache.dim() != 2 or k_cache.shape[1] != PAGE_BYTES:
+        raise ValueError("k_cache must be uint8 [num_pages, 8448]")
+    if query_start_loc.numel() != R + 1:
+        raise ValueError("query_start_loc must have R + 1 entries")
+    need = dsa_forward_workspace_size(T, H, logits.shape[1], k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().dsa_indexer_forward(
+            _dev_ptr(q_bf16, torch.bfloat16, "q_bf16"),
+            _dev_ptr(weights, torch.float32, "weights"),
+            _dev_ptr(k_cache, torch.uint8, "k_cache"), k_cache.shape[0],
+            _dev_ptr(block_table, torch.int32, "block_table"),
+            block_table.shape[1],
+            _dev_ptr(query_start_loc, torch.int32, "query_start_loc"),
+            _dev_ptr(positions, torch.int32, "positions"), T, R, H, D,
+            PAGE_TOKENS, _dev_ptr(logits, torch.float32, "logits"),
+            logits.shape[1], k, _dev_ptr(out, torch.int32, "out"),
+            out.shape[1], _dev_ptr(workspace, torch.uint8, "workspace"),
+            workspace.numel(), _stream(stream, dev)))
+    return logits, out
 
 
 def dsa_index_cache_mask(num_layers, pattern=None, freq=1, offset=2,

@@ -37,9 +37,18 @@ struct TopkArgs {
   size_t ws_bytes;
 };
 
+// One layer's hot path: q quantisation into q8 / q_scale, logits, top-k.
+struct ForwardArgs {
+  const uint16_t* q_bf16;       // [T, H, 128]
+  uint8_t* q8;                  // lg.q8
+  float* q_scale;               // lg.q_scale
+  LogitsArgs lg;
+  TopkArgs tk;                  // tk.logits == lg.logits
+};
+
 // Kernel-choice knobs (dsa_set_option); 0 = automatic.
 struct Options {
-  int logits_kernel = 0;        // 1 = row-wise, 2 = tiled
+  int logits_kernel = 0;        // 1 row-wise, 2 tiled, 3 tiled direct, 4 row grid
   int row_pages_per_wave = 0;
   int tile_pages_per_split = 0;
   int topk_kernel = 0;          // 0/1 = register-resident rows, 2 = LDS-cached rows
@@ -48,6 +57,7 @@ Options& options();
 
 hipError_t launch_quantize_q(const uint16_t* q_bf16, int64_t blocks,
                              uint8_t* q8, float* q_scale, hipStream_t stream);
+hipError_t launch_forward(const ForwardArgs& f, hipStream_t stream);
 hipError_t launch_logits(const LogitsArgs& a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 size_t topk_workspace_bytes(int64_t T, int64_t ld, int k);

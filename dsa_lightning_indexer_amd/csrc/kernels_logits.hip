@@ -329,16 +329,22 @@ struct RowSpan {
   int row, jb, je, p;
 };
 
-// The page range [jb, je) of row `row` owned by wave `wv`; row = -1 when the
-// wave has no work.  With ppw >= P / budget, the rows need at most
-// budget + T waves (one partial wave per row), the grid size.  Rows whose
-// position is out of range own no pages (the row is left untouched and wave
-// 0 raises the flag).
+// The page range [jb, je) of row `row` owned by wave li of XCD x; row = -1
+// when the wave has no work.  Workgroups are dealt to the 8 XCDs
+// round-robin, so wave (one workgroup) w runs on XCD w % 8: the flattened
+// page list (rows in order) is cut into 8 contiguous parts, part x goes to
+// the waves of XCD x, and a row's q is then fetched into one or two of the
+// XCD L2 caches instead of all eight.  Within a part every row fragment of f
+// pages gets ceil(f / ppw) waves, ppw = max(D, ceil(ceil(P / 8) /
+// per_xcd)), so a part needs at most per_xcd + T waves: the grid is 8
+// (per_xcd + T) waves.  Rows whose position is out of range own no pages
+// (the row is left untouched and wave 0 raises the flag).
 template <int NCH>
 __device__ __forceinline__ RowSpan balanced_span(const LogitsArgs& a, int D,
-                                                 int budget, int wv) {
+                                                 int per_xcd, int wv) {
   const int lane = lane_id();
   int pl[NCH], n[NCH];
+  uint32_t incl[NCH];                         // page prefix over the batch
   uint32_t total = 0u;
   bool bad = false;
 #pragma unroll
@@ -349,32 +355,42 @@ __device__ __forceinline__ RowSpan balanced_span(const LogitsArgs& a, int D,
                     (int64_t)(pl[c] >> 6) < a.bt_stride;
     bad |= in && !ok;
     n[c] = (in && ok) ? (pl[c] >> 6) + 1 : 0;
-    total += __builtin_amdgcn_readlane(wave_inclusive_scan((uint32_t)n[c]), 63);
+    incl[c] = total + wave_inclusive_scan((uint32_t)n[c]);
+    total = __builtin_amdgcn_readlane(incl[c], 63);
   }
   if (wv == 0 && __ballot(bad) != 0ull && lane == 0)
     raise_flag(kErrPositionOutOfRange);
+  const uint32_t x = (uint32_t)wv & 7u, li = (uint32_t)wv >> 3;
+  const uint32_t lo_x = (uint32_t)((uint64_t)total * x / 8u);
+  const uint32_t hi_x = (uint32_t)((uint64_t)total * (x + 1u) / 8u);
+  const uint32_t part = (total + 7u) / 8u;
   const int ppw =
-      max(D, (int)((total + (uint32_t)budget - 1) / (uint32_t)budget));
+      max(D, (int)((part + (uint32_t)per_xcd - 1) / (uint32_t)per_xcd));
   RowSpan sp{-1, 0, 0, 0};
   uint32_t base = 0u;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    const uint32_t cnt = ((uint32_t)n[c] + ppw - 1) / (uint32_t)ppw;
-    const uint32_t incl = wave_inclusive_scan(cnt);
-    const uint64_t m = __ballot((uint32_t)wv < base + incl);
+    // this row's fragment in part x: pages [lo, hi) of the flattened list
+    const uint32_t ex_pages = incl[c] - (uint32_t)n[c];
+    const uint32_t lo = max(ex_pages, lo_x), hi = min(incl[c], hi_x);
+    const uint32_t f = hi > lo ? hi - lo : 0u;
+    const uint32_t cnt = (f + ppw - 1) / (uint32_t)ppw;
+    const uint32_t wincl = wave_inclusive_scan(cnt);
+    const uint64_t m = __ballot(li < base + wincl);
     if (sp.row < 0 && m != 0ull) {
       const int l = __builtin_ctzll(m);
-      const int ex = (int)(base + __builtin_amdgcn_readlane(incl - cnt, l));
+      const int ex = (int)(base + __builtin_amdgcn_readlane(wincl - cnt, l));
       const int cl = __builtin_amdgcn_readlane((int)cnt, l);
-      const int nl = __builtin_amdgcn_readlane(n[c], l);
-      // nl = cl * qd + rm: the first rm waves of the row take qd + 1 pages
-      const int i = wv - ex, qd = nl / cl, rm = nl - qd * cl;
+      const int fl = __builtin_amdgcn_readlane((int)f, l);
+      const int first = __builtin_amdgcn_readlane((int)(lo - ex_pages), l);
+      // fl = cl * qd + rm: the first rm waves of the fragment take qd + 1
+      const int i = (int)li - ex, qd = fl / cl, rm = fl - qd * cl;
       sp.row = 64 * c + l;
-      sp.jb = i * qd + min(i, rm);
+      sp.jb = first + i * qd + min(i, rm);
       sp.je = sp.jb + qd + (i < rm ? 1 : 0);
       sp.p = __builtin_amdgcn_readlane(pl[c], l);
     }
-    base += __builtin_amdgcn_readlane(incl, 63);
+    base += __builtin_amdgcn_readlane(wincl, 63);
   }
   sp.row = wave_uniform(sp.row);
   sp.jb = wave_uniform(sp.jb);
@@ -385,10 +401,10 @@ __device__ __forceinline__ RowSpan balanced_span(const LogitsArgs& a, int D,
 
 template <int MT, bool FULL, int D, int NCH>
 __global__ __launch_bounds__(64) void logits_balanced_kernel(LogitsArgs a,
-                                                             int budget) {
+                                                             int per_xcd) {
   const int lane = lane_id();
   const int i16 = lane & 15, g = lane >> 4;
-  const RowSpan sp = balanced_span<NCH>(a, D, budget, (int)blockIdx.x);
+  const RowSpan sp = balanced_span<NCH>(a, D, per_xcd, (int)blockIdx.x);
   if (sp.row < 0) return;
   const int64_t t = sp.row;
   const int p = sp.p, jb = sp.jb, je = sp.je;
@@ -809,15 +825,16 @@ static hipError_t launch_logits_mt(const LogitsArgs& a, hipStream_t stream,
     D = D <= 0 ? 3 : std::min(D, 4);
     if (D == 1) D = 2;
     const int64_t pmax = a.T * max_pages;
-    const int64_t budget =
-        std::max<int64_t>(1, std::min<int64_t>((pmax + D - 1) / D, 1 << 16));
-    const dim3 grid((unsigned)(budget + a.T));
+    const int64_t part = (pmax + 7) / 8;
+    const int64_t per_xcd =
+        std::max<int64_t>(1, std::min<int64_t>((part + D - 1) / D, 1 << 13));
+    const dim3 grid((unsigned)(8 * (per_xcd + a.T)));
     const bool two = a.T > 64;
 #define DSA_BAL(DD)                                                          \
     if (two) hipLaunchKernelGGL((logits_balanced_kernel<MT, FULL, DD, 2>),    \
-                                grid, dim3(64), 0, stream, a, (int)budget);   \
+                                grid, dim3(64), 0, stream, a, (int)per_xcd);  \
     else hipLaunchKernelGGL((logits_balanced_kernel<MT, FULL, DD, 1>),        \
-                            grid, dim3(64), 0, stream, a, (int)budget);
+                            grid, dim3(64), 0, stream, a, (int)per_xcd);
     if (D == 2) { DSA_BAL(2) } else if (D == 3) { DSA_BAL(3) } else { DSA_BAL(4) }
 #undef DSA_BAL
   } else if (!tiled) {
@@ -881,6 +898,16 @@ hipError_t launch_logits(const LogitsArgs& a, hipStream_t stream) {
     case 3: return launch_logits_mt<3, false>(a, stream, tiled, max_pages);
     default: return launch_logits_mt<4, false>(a, stream, tiled, max_pages);
   }
+}
+
+// One layer's hot path: q quantisation, logits, top-k.
+hipError_t launch_forward(const ForwardArgs& f, hipStream_t stream) {
+  if (f.lg.T <= 0) return hipSuccess;
+  hipError_t e = launch_quantize_q(f.q_bf16, f.lg.T * f.lg.H, f.q8, f.q_scale,
+                                   stream);
+  if (e == hipSuccess) e = launch_logits(f.lg, stream);
+  if (e == hipSuccess) e = launch_topk(f.tk, stream);
+  return e;
 }
 
 hipError_t read_logits_flags(unsigned* flags, bool reset) {

@@ -60,28 +60,34 @@ struct TopkShared {
 };
 
 
-// Two-barrier bin search on an LDS histogram: the bin where the count of
-// larger keys first reaches k_rem, scanning from the top.  4096 bins: wave
-// w owns bins 4095-256w down to 3840-256w, 4 per lane; 256 bins: wave 0
-// alone.  Results in sh.sel_*.  Call from all threads.
-template <int NBINS, typename Shared>
-__device__ void select_bin_fast(const uint32_t* hist, uint32_t k_rem,
+// Bin search on an LDS histogram: the bin where the count of larger keys
+// first reaches k_rem, scanning from the top.  4096 bins: thread tid owns
+// 4096/NT consecutive bins from 4095 - (4096/NT) tid down; a DPP scan in
+// each wave and the per-wave totals in LDS give every thread the count
+// above its bins (two barriers).  256 bins: wave 0 alone, 4 per lane.
+// Results in sh.sel_digit / sel_above / sel_count.  Call from all threads.
+template <int NBINS, int NT, typename Shared>
+__device__ void topk_select_bin(const uint32_t* hist, uint32_t k_rem,
                                 Shared& sh) {
   static_assert(NBINS == 4096 || NBINS == 256, "bins");
+  static_assert(NBINS == 256 || NBINS % NT == 0, "threads");
+  constexpr int B = (NBINS == 4096) ? 4096 / NT : 4;
+  constexpr int NW = NT / 64;
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   const bool active = NBINS == 4096 || wave == 0;
-  const int top = (NBINS == 4096) ? 4095 - 256 * wave - 4 * lane
+  const int top = (NBINS == 4096) ? 4095 - B * (int)threadIdx.x
                                   : 255 - 4 * lane;
-  uint32_t c[4] = {0u, 0u, 0u, 0u};
-  uint32_t local = 0;
-  if (active) {
+  uint32_t c[B];
+  uint32_t local = 0u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) { c[j] = hist[top - j]; local += c[j]; }
+  for (int j = 0; j < B; ++j) {
+    c[j] = active ? hist[top - j] : 0u;
+    local += c[j];
   }
   const uint32_t incl = wave_inclusive_scan(local);
-  uint32_t above_w = 0;
-  if (NBINS == 4096) {
+  uint32_t above_w = 0u;
+  if (NBINS == 4096 && NW > 1) {
     if (lane == 63) sh.wave_sum[wave] = incl;
     __syncthreads();
     for (int w = 0; w < wave; ++w) above_w += sh.wave_sum[w];
@@ -89,7 +95,7 @@ __device__ void select_bin_fast(const uint32_t* hist, uint32_t k_rem,
   uint32_t above = above_w + incl - local;
   if (active && above < k_rem && above + local >= k_rem) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < B; ++j) {
       if (above + c[j] >= k_rem) {
         sh.sel_digit = (uint32_t)(top - j);
         sh.sel_above = above;
@@ -337,7 +343,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(
       });
   __syncthreads();
   // 2. the bin holding the k-th largest key
-  select_bin_fast<kHistBins>(sh.hist, (uint32_t)k, sh);
+  topk_select_bin<kHistBins, kTopkThreads>(sh.hist, (uint32_t)k, sh);
   const uint32_t d = sh.sel_digit;
   const uint32_t k_rem = (uint32_t)k - sh.sel_above;
   const uint32_t c = sh.sel_count;
@@ -392,7 +398,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(
       atomicAdd(&sh.hist1[(sh.cand_key[j] >> 8) & 0xfffu], 1u);
     for (int b = tid; b < 256; b += kTopkThreads) sh.hist[b] = 0u;
     __syncthreads();
-    select_bin_fast<kHistBins>(sh.hist1, k_rem, sh);
+    topk_select_bin<kHistBins, kTopkThreads>(sh.hist1, k_rem, sh);
     const uint32_t p24 = (d << 12) | sh.sel_digit;
     const uint32_t k2 = k_rem - sh.sel_above;
     mask = 0xffffff00u; thr = p24 << 8; k_tie = k2;
@@ -402,7 +408,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(
         if ((key >> 8) == p24) atomicAdd(&sh.hist[key & 0xffu], 1u);
       }
       __syncthreads();
-      select_bin_fast<256>(sh.hist, k2, sh);
+      topk_select_bin<256, kTopkThreads>(sh.hist, k2, sh);
       mask = 0xffffffffu; thr = (p24 << 8) | sh.sel_digit;
       k_tie = k2 - sh.sel_above;
     }
@@ -448,52 +454,39 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(
 
 // ---------------------------------------------------------------------------
 // Register-resident top-k for rows of up to kRegMaxRow columns (decode rows,
-// prefill rows).  Thread tid holds columns s*4096 + 4*tid + j (slice s,
-// j = 0..3) in registers: one coalesced 16-byte load per slice, no LDS copy
-// of the row.  The threshold key is found by up to three LDS histograms
-// (top 12 key bits over the row; bits 19..8 over the keys of the chosen
-// bin; bits 7..0 over the keys matching the 24-bit prefix), each followed by
-// the two-barrier bin search.  Selection: masked key > thr, or == thr for
-// the k_tie lowest-index ties.  The output slot of a selected column is the
-// number of selected columns before it: one packed (above, tie) count per
-// thread and slice, a DPP scan within the wave and a scan of the per-wave
-// totals give every thread its offsets, so the indices come out in
-// ascending order with no candidate list and no capacity limit.
+// prefill rows): one workgroup of 1024 threads per row, the row's keys in
+// registers.
 // ---------------------------------------------------------------------------
-constexpr int kRegSlice = 4 * kTopkThreads;     // columns per slice
-constexpr int kRegMaxSlices = 12;
-constexpr int kRegMaxRow = kRegSlice * kRegMaxSlices;   // 49152
-
+template <int NT, int S>
 struct RegTopkShared {
   uint32_t hist[kHistBins];
   uint32_t hist2[kHistBins];
-  uint32_t tot[kRegMaxSlices * kTopkWaves];     // packed per (slice, wave)
-  uint32_t wave_sum[kTopkWaves];
+  uint32_t tot[S * (NT / 64)];                 // packed per (slice, wave)
+  uint32_t wave_sum[NT / 64];
   uint32_t sel_digit, sel_above, sel_count;
 };
 
-template <int S>
-__global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(
-    const float* __restrict__ logits, int64_t ld,
-    const int32_t* __restrict__ positions, int k, int32_t* __restrict__ out,
-    int64_t out_ld) {
-  static_assert(S >= 1 && S <= kRegMaxSlices, "slices");
-  __shared__ RegTopkShared sh;
-  const int64_t t = blockIdx.x;
+// Top-k of row[0..n) (k < n <= S * 4 * NT <= ld) into orow[0..k).  Thread
+// tid holds columns s * 4 NT + 4 tid + j (slice s, j = 0..3): one 16-byte
+// load per slice, no LDS copy of the row.  The threshold key comes from up
+// to three LDS histograms (top 12 key bits over the row; bits 19..8 over the
+// keys of the chosen bin; bits 7..0 over the keys matching the 24-bit
+// prefix).  A column is selected when its masked key is above the threshold
+// or equal to it and among the k_tie lowest-index ties; its output slot is
+// the number of selected columns before it, from packed (above, tie) counts
+// per thread and slice, a DPP scan within the wave and a scan of the
+// per-wave totals.  `row` must be 16-byte aligned and ld a multiple of 4.
+// Call from all NT threads.
+template <int NT, int S>
+__device__ void topk_row_registers(const float* row, int64_t ld, int n, int k,
+                                   int32_t* orow, RegTopkShared<NT, S>& sh) {
+  constexpr int NW = NT / 64;
+  constexpr int kSlice = 4 * NT;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
-  int32_t* orow = out + t * out_ld;
-  int p = positions[t];
-  if (p >= ld) p = (int)ld - 1;              // logits past ld do not exist
-  const int n = p + 1;                       // p < 0 -> empty row
-  if (n <= k) {
-    for (int i = tid; i < k; i += kTopkThreads) orow[i] = i < n ? i : -1;
-    return;
-  }
-  const float* row = logits + t * ld;
 
-  for (int b = tid; b < kHistBins; b += kTopkThreads) {
+  for (int b = tid; b < kHistBins; b += NT) {
     sh.hist[b] = 0u;
     sh.hist2[b] = 0u;
   }
@@ -502,10 +495,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(
   uint32_t valid[S];                          // bit j: column valid
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    const int c0 = s * kRegSlice + 4 * tid;
+    const int c0 = s * kSlice + 4 * tid;
     valid[s] = 0u;
     key[s][0] = key[s][1] = key[s][2] = key[s][3] = 0u;
-    if (s * kRegSlice < n) {                  // workgroup-uniform
+    if (s * kSlice < n) {                     // workgroup-uniform
       const float4 v =
           *reinterpret_cast<const float4*>(row + min(c0, (int)ld - 4));
       key[s][0] = float_to_ordered(v.x);
@@ -524,14 +517,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(
     for (int j = 0; j < 4; ++j)
       if ((valid[s] >> j) & 1u) atomicAdd(&sh.hist[key[s][j] >> 20], 1u);
   __syncthreads();
-  select_bin_fast<kHistBins>(sh.hist, (uint32_t)k, sh);
+  topk_select_bin<kHistBins, NT>(sh.hist, (uint32_t)k, sh);
   const uint32_t d = sh.sel_digit;
   const uint32_t k_rem = (uint32_t)k - sh.sel_above;
   uint32_t mask = 0xfff00000u, thr = d << 20, k_tie = k_rem;
   if (k_rem < sh.sel_count) {
     // pass 2: bits 19..8 of the keys in bin d; bins 0..255 of hist are
     // cleared for pass 3 (the barrier after pass 2 orders the clear)
-    if (tid < 256) sh.hist[tid] = 0u;
+    for (int b = tid; b < 256; b += NT) sh.hist[b] = 0u;
 #pragma unroll
     for (int s = 0; s < S; ++s)
 #pragma unroll
@@ -539,7 +532,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(
         if (((valid[s] >> j) & 1u) && (key[s][j] >> 20) == d)
           atomicAdd(&sh.hist2[(key[s][j] >> 8) & 0xfffu], 1u);
     __syncthreads();
-    select_bin_fast<kHistBins>(sh.hist2, k_rem, sh);
+    topk_select_bin<kHistBins, NT>(sh.hist2, k_rem, sh);
     const uint32_t p24 = (d << 12) | sh.sel_digit;
     const uint32_t k2 = k_rem - sh.sel_above;
     mask = 0xffffff00u; thr = p24 << 8; k_tie = k2;
@@ -552,7 +545,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(
           if (((valid[s] >> j) & 1u) && (key[s][j] >> 8) == p24)
             atomicAdd(&sh.hist[key[s][j] & 0xffu], 1u);
       __syncthreads();
-      select_bin_fast<256>(sh.hist, k2, sh);
+      topk_select_bin<256, NT>(sh.hist, k2, sh);
       mask = 0xffffffffu; thr = (p24 << 8) | sh.sel_digit;
       k_tie = k2 - sh.sel_above;
     }
@@ -571,37 +564,37 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(
     }
     cnt[s] = c;
     incl[s] = wave_inclusive_scan(c);
-    if (lane == 63) sh.tot[s * kTopkWaves + wave] = incl[s];
+    if (lane == 63) sh.tot[s * NW + wave] = incl[s];
   }
   __syncthreads();
-  // exclusive scan of the S*16 (slice, wave) totals, in place, by wave 0
+  // exclusive scan of the S * NW (slice, wave) totals, in place, by wave 0
   if (wave == 0) {
-    constexpr int kPer = (S * kTopkWaves + 63) / 64;
+    constexpr int kPer = (S * NW + 63) / 64;
     uint32_t v[kPer], local = 0u;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int idx = lane * kPer + i;
-      v[i] = idx < S * kTopkWaves ? sh.tot[idx] : 0u;
+      v[i] = idx < S * NW ? sh.tot[idx] : 0u;
       local += v[i];
     }
     uint32_t run = wave_inclusive_scan(local) - local;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int idx = lane * kPer + i;
-      if (idx < S * kTopkWaves) sh.tot[idx] = run;
+      if (idx < S * NW) sh.tot[idx] = run;
       run += v[i];
     }
   }
   __syncthreads();
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    const uint32_t before = sh.tot[s * kTopkWaves + wave] + incl[s] - cnt[s];
+    const uint32_t before = sh.tot[s * NW + wave] + incl[s] - cnt[s];
     uint32_t gt_b = before & 0xffffu, eq_b = before >> 16;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const bool ok = (valid[s] >> j) & 1u;
       const uint32_t km = key[s][j] & mask;
-      const int col = s * kRegSlice + 4 * tid + j;
+      const int col = s * kSlice + 4 * tid + j;
       // slots are < k by construction; the check keeps a row's writes
       // inside the row whatever the counts
       if (ok && km > thr) {
@@ -614,6 +607,35 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(
       }
     }
   }
+}
+
+// Row with n <= k columns: 0..n-1, then -1 (n <= 0: all -1).
+template <int NT>
+__device__ __forceinline__ void topk_row_short(int n, int k, int32_t* orow) {
+  for (int i = threadIdx.x; i < k; i += NT) orow[i] = i < n ? i : -1;
+}
+
+constexpr int kRegSlice = 4 * kTopkThreads;     // columns per slice
+constexpr int kRegMaxSlices = 12;
+constexpr int kRegMaxRow = kRegSlice * kRegMaxSlices;   // 49152
+
+template <int S>
+__global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(
+    const float* __restrict__ logits, int64_t ld,
+    const int32_t* __restrict__ positions, int k, int32_t* __restrict__ out,
+    int64_t out_ld) {
+  static_assert(S >= 1 && S <= kRegMaxSlices, "slices");
+  __shared__ RegTopkShared<kTopkThreads, S> sh;
+  const int64_t t = blockIdx.x;
+  int32_t* orow = out + t * out_ld;
+  int p = positions[t];
+  if (p >= ld) p = (int)ld - 1;              // logits past ld do not exist
+  const int n = p + 1;                       // p < 0 -> empty row
+  if (n <= k) {
+    topk_row_short<kTopkThreads>(n, k, orow);
+    return;
+  }
+  topk_row_registers<kTopkThreads, S>(logits + t * ld, ld, n, k, orow, sh);
 }
 
 // ---------------------------------------------------------------------------

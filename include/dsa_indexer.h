@@ -144,6 +144,30 @@ int dsa_indexer_topk(const float* logits, int64_t ld, const int32_t* positions,
 size_t dsa_topk_workspace_size(int64_t T, int64_t ld, int k);
 
 /*
+ * dsa_indexer_forward -- the whole indexer hot path of one layer for one
+ * batch: dsa_quantize_q, dsa_indexer_logits and dsa_indexer_topk in one
+ * call, with the same arguments, layouts and results (logits are written to
+ * `logits` as by dsa_indexer_logits, the top-k rows to `out` as by
+ * dsa_indexer_topk; [KVB], [HBM] 2.3 and 4.2, [IC] 2).
+ *   q_bf16     device, bf16 [T, H, 128].
+ *   workspace  device, dsa_forward_workspace_size(T, H, ld, k) bytes (q
+ *              codes and scales, top-k scratch); contents on entry do not
+ *              matter.
+ * The three kernels run in turn on `stream`; the result equals the three
+ * separate calls bit for bit.
+ */
+int dsa_indexer_forward(const void* q_bf16, const float* weights,
+                        const uint8_t* k_cache, int64_t num_pages,
+                        const int32_t* block_table, int64_t bt_stride,
+                        const int32_t* query_start_loc,
+                        const int32_t* positions, int64_t T, int R, int H,
+                        int head_dim, int page_size, float* logits,
+                        int64_t ld, int k, int32_t* out, int64_t out_ld,
+                        void* workspace, size_t ws_bytes, void* stream);
+
+size_t dsa_forward_workspace_size(int64_t T, int H, int64_t ld, int k);
+
+/*
  * dsa_index_cache_mask -- IndexCache layer rule ([IC] 3, 4, 5.3), host only.
  *   pattern            host, nullable: one 'F'/'S' per DSA layer; overrides
  *                      freq when non-NULL; layers past its end are F.
@@ -212,8 +236,9 @@ int dsa_device_error_flags(int reset);
  * dsa_set_option -- tuning/testing knobs; returns the previous value or
  * DSA_ERR_INVALID_ARG for an unknown key.  Value 0 restores the automatic
  * choice.  Keys: "logits_kernel" (1 row-wise, 2 tiled, 3 tiled with direct
- * loads), "row_pages_per_wave", "tile_pages_per_split", "topk_kernel" (rows
- * of up to 49152 columns: 1 register-resident keys, 2 keys cached in LDS).
+ * loads, 4 row-wise on a (row, page group) grid), "row_pages_per_wave",
+ * "tile_pages_per_split", "topk_kernel" (rows of up to 49152 columns: 1
+ * register-resident keys, 2 keys cached in LDS).
  */
 int dsa_set_option(const char* key, int value);
 

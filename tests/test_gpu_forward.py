@@ -1,0 +1,152 @@
+"""GPU tests of dsa_indexer_forward (q quantisation, logits and top-k in one
+call) through the C ABI: against the separate entry points bit for bit."""
+
+import sys
+
+import pytest
+import torch
+
+from dsa_lightning_indexer_amd import binding, synth
+from tests import parity
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(),
+                                 reason="needs a GPU")]
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _reset():
+    binding.dsa_device_error_flags(reset=True)
+    yield
+    for key in ("logits_kernel", "topk_kernel", "row_pages_per_wave"):
+        binding.dsa_set_option(key, 0)
+
+
+def _forward(b, d, k=None, **kw):
+    k = b.k if k is None else k
+    return binding.dsa_indexer_forward(d["q_bf16"], d["weights"], d["k_cache"],
+                                       d["block_table"], d["qsl"],
+                                       d["positions"], b.ld, k, **kw)
+
+
+def _batches():
+    return {
+        "decode64": lambda: synth.decode(),
+        "decode100": lambda: synth.decode(R=100),
+        "decode_short": lambda: synth.decode(R=24, lo=100, hi=3000, k=256),
+        "tiny": lambda: synth.tiny(),
+    }
+
+
+@pytest.mark.parametrize("name", sorted(_batches()))
+def test_forward_equals_separate_calls(name):
+    _say(f"case: forward vs separate calls, {name}")
+    b = _batches()[name]()
+    d = parity.upload(b)
+    _, _, lg_ref, tk_ref = parity.run_gpu(b, d)
+    lg, tk = _forward(b, d)
+    torch.cuda.synchronize()
+    for t in range(b.T):
+        p = int(b.positions[t])
+        assert torch.equal(lg[t, : p + 1], lg_ref[t, : p + 1]), f"row {t}"
+    assert torch.equal(tk, tk_ref)
+    assert binding.dsa_device_error_flags(reset=True) == 0
+
+
+@pytest.mark.parametrize("H", [20, 48])
+def test_forward_partial_heads(H):
+    """Head counts that are not a multiple of 16 (padded A rows) and 48."""
+    _say(f"case: forward, H={H}")
+    b = synth.decode(R=12, H=H, k=512, seed=5)
+    d = parity.upload(b)
+    lg, tk = _forward(b, d)
+    _, _, lg_ref, tk_ref = parity.run_gpu(b, d)
+    for t in range(b.T):
+        p = int(b.positions[t])
+        assert torch.equal(lg[t, : p + 1], lg_ref[t, : p + 1]), f"row {t}"
+    assert torch.equal(tk, tk_ref)
+
+
+def test_forward_repeated_calls_and_workspace_reuse():
+    """Dirty workspace, repeated calls, a smaller batch through the same
+    workspace: all equal to a fresh call."""
+    _say("case: forward repeated calls on one dirty workspace")
+    b = synth.decode()
+    d = parity.upload(b)
+    need = binding.dsa_forward_workspace_size(b.T, b.H, b.ld, b.k)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+    lg0, tk0 = _forward(b, d)
+    for _ in range(3):
+        lg, tk = _forward(b, d, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(tk, tk0)
+    small = synth.decode(R=9, seed=31)
+    ds = parity.upload(small)
+    _, _, _, tk_small_ref = parity.run_gpu(small, ds)
+    _, tk_small = _forward(small, ds, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(tk_small, tk_small_ref)
+
+
+def test_forward_graph_replays():
+    """The forward call captured in a HIP graph: every replay equals the
+    eager result."""
+    _say("case: forward in a HIP graph")
+    b = synth.decode()
+    d = parity.upload(b)
+    need = binding.dsa_forward_workspace_size(b.T, b.H, b.ld, b.k)
+    ws = torch.empty((need,), dtype=torch.uint8, device="cuda")
+    lg = torch.empty((b.T, b.ld), dtype=torch.float32, device="cuda")
+    tk = torch.empty((b.T, b.k), dtype=torch.int32, device="cuda")
+    _forward(b, d, logits=lg, out=tk, workspace=ws)
+    torch.cuda.synchronize()
+    ref = tk.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        _forward(b, d, logits=lg, out=tk, workspace=ws)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            _forward(b, d, logits=lg, out=tk, workspace=ws)
+    torch.cuda.synchronize()
+    for i in range(4):
+        tk.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(tk, ref), f"replay {i}"
+
+
+def test_forward_out_of_range_position_row():
+    """A position past the logits row: flagged, its logits row untouched,
+    every other row as from the separate calls."""
+    _say("case: forward with an out-of-range position (host-forced)")
+    b = synth.decode(R=16, seed=77)
+    d = parity.upload(b)
+    _, _, lg_ref, tk_ref = parity.run_gpu(b, d)
+    pos = d["positions"].clone()
+    pos[5] = b.ld + 100
+    d2 = dict(d, positions=pos)
+    lg = torch.full((b.T, b.ld), 3.0, device="cuda")
+    _, tk = _forward(b, d2, logits=lg)
+    torch.cuda.synchronize()
+    assert binding.dsa_device_error_flags(reset=True) & 2
+    assert torch.all(lg[5] == 3.0)
+    keep = [t for t in range(b.T) if t != 5]
+    assert torch.equal(tk[keep], tk_ref[keep])
+
+
+def test_forward_rejects_small_workspace():
+    b = synth.tiny()
+    d = parity.upload(b)
+    need = binding.dsa_forward_workspace_size(b.T, b.H, b.ld, b.k)
+    ws = torch.empty((need - 1,), dtype=torch.uint8, device="cuda")
+    with pytest.raises(binding.DsaError) as e:
+        _forward(b, d, workspace=ws)
+    assert e.value.status == binding.DSA_ERR_WORKSPACE
