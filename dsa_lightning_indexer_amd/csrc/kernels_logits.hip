@@ -667,6 +667,163 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a,
 }
 
 // ---------------------------------------------------------------------------
+// Tiled logits, one row per wave.  A workgroup of 16 waves owns a tile of 16
+// consecutive rows of one request and a range of pages; wave w scores row
+// w.  With one row per wave a wave holds 16 heads x 128 q codes (32 VGPRs)
+// instead of two rows, so it fits in 128 VGPRs and four waves share each
+// SIMD: the MFMAs of one wave overlap the ReLU / weight VALU work of the
+// others (the two compete for the SIMD's issue slots otherwise).  Pages are
+// staged in LDS two at a time (double-buffered pairs, 144-byte padded rows)
+// with one barrier per pair; the page copy is a branch-free buffer load
+// (16 bytes of keys per thread, zero-size for a page outside the pool) so
+// that the loop carries no divergent control flow.  Each page: 4 N-tiles x
+// MT MFMAs, the head reduction in registers, one reduce-scatter across the
+// 4 lane groups, and one 256-byte logit store.
+// ---------------------------------------------------------------------------
+constexpr int kT16Waves = 16;
+constexpr int kT16Threads = 64 * kT16Waves;
+
+template <int MT, bool FULL>
+__global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
+    LogitsArgs a, int pages_per_split) {
+  // [buffer][page of the pair][64 tokens x 144 B], scales likewise
+  __shared__ __align__(16) uint8_t s_keys[2][2][kPageTokens * kLdsRow];
+  __shared__ __align__(16) float s_scale[2][2][kPageTokens];
+  __shared__ int s_info[4];
+  __shared__ int s_pos[kTileRows];
+
+  const int tid = threadIdx.x;
+  const int wave = wave_uniform(tid >> 6);
+  const int lane = lane_id();
+  if (tid == 0) { s_info[0] = -1; s_info[1] = 0; s_info[2] = 0; }
+  __syncthreads();
+  if (wave == 0) find_tile(a.qsl, a.R, blockIdx.y, s_info);
+  __syncthreads();
+  const int r = s_info[0];
+  if (r < 0) return;                         // grid bound beyond last tile
+  const int64_t row0 = s_info[1];
+  const int nrows = s_info[2];
+  if (tid < kTileRows) {
+    int p = -1;
+    if (tid < nrows && row0 + tid >= 0 && row0 + tid < a.T) {
+      p = a.positions[row0 + tid];
+      if (p < 0 || p >= a.ld || (int64_t)(p >> 6) >= a.bt_stride) {
+        raise_flag(kErrPositionOutOfRange);
+        p = -1;
+      }
+    }
+    s_pos[tid] = p;
+  }
+  __syncthreads();
+  int maxp = -1;
+#pragma unroll
+  for (int i = 0; i < kTileRows; ++i) maxp = max(maxp, s_pos[i]);
+  const int npages = (maxp >> 6) + 1;        // 0 when no valid row
+  const int jb = blockIdx.x * pages_per_split;
+  const int je = min(jb + pages_per_split, npages);
+  if (jb >= je) return;
+
+  const int32_t* bt = a.block_table + (int64_t)r * a.bt_stride;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int prow = wave_uniform(s_pos[wave]);
+  const int64_t t = row0 + wave;
+  i32x8 qa[MT];
+  float w[MT][4];
+  if (prow >= 0) {
+    load_q_frags<MT, FULL>(a.q8 + t * a.H * kHeadDim, a.H, qa);
+    load_head_weights<MT, FULL>(a.weights + t * a.H, a.q_scale + t * a.H,
+                                a.H, w);
+  } else {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      qa[m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[m][j] = 0.f;
+    }
+  }
+
+  // Page pair copy: thread i moves 16 key bytes of page (i >> 9) of the
+  // pair (token (i & 511) / 8, chunk i % 8); threads with (i & 511) < 16
+  // also move 16 scale bytes.  Pages past the range or outside the pool
+  // are zero-size buffers: the loads return 0 without touching memory.
+  const int half = wave_uniform(wave >> 3), sub = tid & 511;
+  const int ctok = sub >> 3, cchunk = sub & 7;
+  bool bad_page = false;
+  const int last = (int)a.bt_stride - 1;
+  auto page_id = [&](int jp) {
+    const int page = load_uniform(bt, min(jp, last));
+    return jp < je ? page : -1;
+  };
+  auto page_rsrc = [&](int jp) {
+    const int page = page_id(jp);
+    const bool ok = page >= 0 && (int64_t)page < a.num_pages;
+    bad_page |= jp < je && !ok;
+    return make_rsrc(a.k_cache + (int64_t)(ok ? page : 0) * kPageBytes,
+                     ok ? kPageBytes : 0);
+  };
+  auto fetch = [&](int jp, uint4& kreg, uint4& sreg) {
+    const __amdgpu_buffer_rsrc_t r0 = page_rsrc(jp);
+    const __amdgpu_buffer_rsrc_t r1 = page_rsrc(jp + 1);
+    const __amdgpu_buffer_rsrc_t rs = half ? r1 : r0;
+    const auto k4 = __builtin_amdgcn_raw_buffer_load_b128(rs, sub * 16, 0, 0);
+    // threads with sub >= 16 read past the page end: zero, no traffic
+    const auto s4 = __builtin_amdgcn_raw_buffer_load_b128(
+        rs, sub < 16 ? kPageKeyBytes + sub * 16 : kPageBytes, 0, 0);
+    kreg = make_uint4(k4[0], k4[1], k4[2], k4[3]);
+    sreg = make_uint4(s4[0], s4[1], s4[2], s4[3]);
+  };
+  auto stash = [&](int buf, const uint4& kreg, const uint4& sreg) {
+    *reinterpret_cast<uint4*>(&s_keys[buf][half][ctok * kLdsRow + cchunk * 16]) =
+        kreg;
+    if (sub < 16)
+      *reinterpret_cast<uint4*>(&s_scale[buf][half][sub * 4]) = sreg;
+  };
+
+  uint4 kreg, sreg;
+  fetch(jb, kreg, sreg);
+  stash(0, kreg, sreg);
+  float* orow = a.logits + t * a.ld;
+
+  for (int jp = jb; jp < je; jp += 2) {
+    const int buf = ((jp - jb) >> 1) & 1;
+    const bool more = jp + 2 < je;
+    if (more) fetch(jp + 2, kreg, sreg);
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int pj = jp + h;
+      const uint8_t* kb_lds = s_keys[buf][h];
+      float v[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const uint8_t* src = kb_lds + (16 * nt + i16) * kLdsRow + 32 * g;
+        const uint4 x = *reinterpret_cast<const uint4*>(src);
+        const uint4 y = *reinterpret_cast<const uint4*>(src + 16);
+        const i32x8 kb = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w,
+                               (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+        f32x4 acc[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          acc[m] = mfma16x16x128_fp8(qa[m], kb, f32x4{0.f, 0.f, 0.f, 0.f});
+        v[nt] = head_reduce<MT>(acc, w);
+      }
+      // lane group g ends with N-tile g
+      const float tot = reduce_scatter4(v[0], v[1], v[2], v[3]);
+      const int tok = 16 * g + i16;
+      const int s = pj * kPageTokens + tok;
+      // a page outside the pool scores -inf (its loads returned 0)
+      const int page = page_id(pj);
+      const bool page_ok = page >= 0 && (int64_t)page < a.num_pages;
+      const float val = (s <= prow && page_ok) ? tot * s_scale[buf][h][tok]
+                                               : -INFINITY;
+      if (prow >= 0 && pj < je) orow[s] = val;
+    }
+    if (more) stash(buf ^ 1, kreg, sreg);
+  }
+  if (bad_page && tid == 0) raise_flag(kErrPageOutOfRange);
+}
+
+// ---------------------------------------------------------------------------
 // Tiled logits without LDS staging: the same 16-row tile and page split,
 // but every wave streams the pages itself (16-byte loads straight into MFMA
 // B registers, next page prefetched); the 8 waves of a tile read the same
@@ -863,10 +1020,17 @@ static hipError_t launch_logits_mt(const LogitsArgs& a, hipStream_t stream,
       const int64_t real_tiles = (a.T + kTileRows - 1) / kTileRows;
       int64_t splits = (2048 + real_tiles - 1) / real_tiles;
       splits = std::max<int64_t>(1, std::min<int64_t>(splits, max_pages));
-      pps = (int)std::max<int64_t>(8, (max_pages + splits - 1) / splits);
+      // at least 64 pages per workgroup: a 16-wave workgroup has a
+      // noticeable start (tile lookup, q fragments, first page pair); the
+      // 1M-token tail (one tile) measured best at 64 (256 workgroups)
+      pps = (int)std::max<int64_t>(64, (max_pages + splits - 1) / splits);
     }
     const int64_t gx = (max_pages + pps - 1) / pps;
-    if (o.logits_kernel == 3)
+    if (o.logits_kernel != 2 && o.logits_kernel != 3)
+      hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL>),
+                         dim3((unsigned)gx, (unsigned)tiles),
+                         dim3(kT16Threads), 0, stream, a, pps);
+    else if (o.logits_kernel == 3)
       hipLaunchKernelGGL((logits_tile_direct_kernel<MT, FULL>),
                          dim3((unsigned)gx, (unsigned)tiles),
                          dim3(kTileWaves * 64), 0, stream, a, pps);
@@ -884,7 +1048,8 @@ hipError_t launch_logits(const LogitsArgs& a, hipStream_t stream) {
   const Options& o = options();
   bool tiled = a.T > 2 * (int64_t)a.R;
   if (o.logits_kernel == 1 || o.logits_kernel == 4) tiled = false;
-  if (o.logits_kernel == 2 || o.logits_kernel == 3) tiled = true;
+  if (o.logits_kernel == 2 || o.logits_kernel == 3 || o.logits_kernel == 5)
+    tiled = true;
   switch (a.H) {
     case 16: return launch_logits_mt<1, true>(a, stream, tiled, max_pages);
     case 32: return launch_logits_mt<2, true>(a, stream, tiled, max_pages);

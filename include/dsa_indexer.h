@@ -235,8 +235,9 @@ int dsa_device_error_flags(int reset);
 /*
  * dsa_set_option -- tuning/testing knobs; returns the previous value or
  * DSA_ERR_INVALID_ARG for an unknown key.  Value 0 restores the automatic
- * choice.  Keys: "logits_kernel" (1 row-wise, 2 tiled, 3 tiled with direct
- * loads, 4 row-wise on a (row, page group) grid), "row_pages_per_wave",
+ * choice.  Keys: "logits_kernel" (1 row-wise, 2 tiled with 8 waves x 2 rows,
+ * 3 tiled with direct loads, 4 row-wise on a (row, page group) grid, 5 tiled
+ * with 16 waves x 1 row), "row_pages_per_wave",
  * "tile_pages_per_split", "topk_kernel" (rows of up to 49152 columns: 1
  * register-resident keys, 2 keys cached in LDS).
  */

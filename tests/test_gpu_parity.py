@@ -78,7 +78,7 @@ def test_quantize_q_bit_exact_decode_shape():
 
 
 # ------------------------------------------------------------------- tiny --
-@pytest.mark.parametrize("kernel", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("kernel", [0, 1, 2, 3, 4, 5])
 def test_tiny_logits_and_topk(kernel):
     _say(f"case: tiny, logits kernel option {kernel}")
     binding.dsa_set_option("logits_kernel", kernel)
@@ -143,8 +143,11 @@ def test_decode_batch_two_position_chunks(rows):
 
 
 # ---------------------------------------------------------------- prefill --
-def test_prefill_chunk_sampled_rows():
-    _say("case: prefill chunk (8192 q x 40960 ctx, H=64, k=2048)")
+@pytest.mark.parametrize("kernel", [0, 5])
+def test_prefill_chunk_sampled_rows(kernel):
+    _say(f"case: prefill chunk (8192 q x 40960 ctx, H=64, k=2048), "
+         f"logits kernel {kernel}")
+    binding.dsa_set_option("logits_kernel", kernel)
     b = synth.prefill()
     _, _, lg, tk = parity.run_gpu(b)
     rng = np.random.default_rng(2)
@@ -175,8 +178,11 @@ def test_prefill_chunk_sampled_rows():
 
 
 # ----------------------------------------------------------- long context --
-def test_long_context_rows():
-    _say("case: long context (1M tokens, 16 rows, H=64, k=2048)")
+@pytest.mark.parametrize("kernel", [0, 5])
+def test_long_context_rows(kernel):
+    _say(f"case: long context (1M tokens, 16 rows, H=64, k=2048), "
+         f"logits kernel {kernel}")
+    binding.dsa_set_option("logits_kernel", kernel)
     b = synth.long_context()
     _, _, lg, tk = parity.run_gpu(b)
     tk = tk.cpu().numpy()
@@ -215,7 +221,7 @@ EDGE_CASES = {
 
 
 @pytest.mark.parametrize("name", sorted(EDGE_CASES))
-@pytest.mark.parametrize("kernel", [1, 2, 3, 4])
+@pytest.mark.parametrize("kernel", [1, 2, 3, 4, 5])
 def test_edge_cases(name, kernel):
     _say(f"case: edge {name}, logits kernel {kernel}")
     binding.dsa_set_option("logits_kernel", kernel)
