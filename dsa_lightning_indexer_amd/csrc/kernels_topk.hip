@@ -466,61 +466,36 @@ struct RegTopkShared {
   uint32_t sel_digit, sel_above, sel_count;
 };
 
-// Top-k of row[0..n) (k < n <= S * 4 * NT <= ld) into orow[0..k).  Thread
-// tid holds columns s * 4 NT + 4 tid + j (slice s, j = 0..3): one 16-byte
-// load per slice, no LDS copy of the row.  The threshold key comes from up
-// to three LDS histograms (top 12 key bits over the row; bits 19..8 over the
-// keys of the chosen bin; bits 7..0 over the keys matching the 24-bit
-// prefix).  A column is selected when its masked key is above the threshold
-// or equal to it and among the k_tie lowest-index ties; its output slot is
-// the number of selected columns before it, from packed (above, tie) counts
-// per thread and slice, a DPP scan within the wave and a scan of the
-// per-wave totals.  `row` must be 16-byte aligned and ld a multiple of 4.
-// Call from all NT threads.
-template <int NT, int S>
-__device__ void topk_row_registers(const float* row, int64_t ld, int n, int k,
-                                   int32_t* orow, RegTopkShared<NT, S>& sh) {
-  constexpr int NW = NT / 64;
-  constexpr int kSlice = 4 * NT;
-  const int tid = threadIdx.x;
-  const int lane = lane_id();
-  const int wave = tid >> 6;
-
-  for (int b = tid; b < kHistBins; b += NT) {
-    sh.hist[b] = 0u;
-    sh.hist2[b] = 0u;
-  }
-  // keys of this thread's columns; columns >= n are marked invalid
+// Keys held in registers: item s * 4 NT + 4 tid + j of a list in key[s][j]
+// (slice s, j = 0..3), valid when bit j of valid[s] is set.
+template <int S>
+struct RegKeys {
   uint32_t key[S][4];
-  uint32_t valid[S];                          // bit j: column valid
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const int c0 = s * kSlice + 4 * tid;
-    valid[s] = 0u;
-    key[s][0] = key[s][1] = key[s][2] = key[s][3] = 0u;
-    if (s * kSlice < n) {                     // workgroup-uniform
-      const float4 v =
-          *reinterpret_cast<const float4*>(row + min(c0, (int)ld - 4));
-      key[s][0] = float_to_ordered(v.x);
-      key[s][1] = float_to_ordered(v.y);
-      key[s][2] = float_to_ordered(v.z);
-      key[s][3] = float_to_ordered(v.w);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) valid[s] |= (c0 + j < n ? 1u : 0u) << j;
-    }
-  }
-  __syncthreads();
-  // pass 1: top 12 bits over the row
+  uint32_t valid[S];
+};
+
+// Threshold of the k largest valid keys (k < number of valid keys): a key
+// is selected when (key & mask) > thr, or (key & mask) == thr and it is
+// among the k_tie lowest-position such keys.  Up to three LDS histograms
+// (top 12 key bits over the list; bits 19..8 over the keys of the chosen
+// bin; bits 7..0 over the keys matching the 24-bit prefix), each followed
+// by the two-barrier bin search.  sh.hist and sh.hist2 must be zero and a
+// barrier passed before the call.  Call from all NT threads.
+template <int NT, int S>
+__device__ void reg_threshold(const RegKeys<S>& r, int k,
+                              RegTopkShared<NT, S>& sh, uint32_t& mask,
+                              uint32_t& thr, uint32_t& k_tie) {
+  const int tid = threadIdx.x;
 #pragma unroll
   for (int s = 0; s < S; ++s)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if ((valid[s] >> j) & 1u) atomicAdd(&sh.hist[key[s][j] >> 20], 1u);
+      if ((r.valid[s] >> j) & 1u) atomicAdd(&sh.hist[r.key[s][j] >> 20], 1u);
   __syncthreads();
   topk_select_bin<kHistBins, NT>(sh.hist, (uint32_t)k, sh);
   const uint32_t d = sh.sel_digit;
   const uint32_t k_rem = (uint32_t)k - sh.sel_above;
-  uint32_t mask = 0xfff00000u, thr = d << 20, k_tie = k_rem;
+  mask = 0xfff00000u; thr = d << 20; k_tie = k_rem;
   if (k_rem < sh.sel_count) {
     // pass 2: bits 19..8 of the keys in bin d; bins 0..255 of hist are
     // cleared for pass 3 (the barrier after pass 2 orders the clear)
@@ -529,8 +504,8 @@ __device__ void topk_row_registers(const float* row, int64_t ld, int n, int k,
     for (int s = 0; s < S; ++s)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (((valid[s] >> j) & 1u) && (key[s][j] >> 20) == d)
-          atomicAdd(&sh.hist2[(key[s][j] >> 8) & 0xfffu], 1u);
+        if (((r.valid[s] >> j) & 1u) && (r.key[s][j] >> 20) == d)
+          atomicAdd(&sh.hist2[(r.key[s][j] >> 8) & 0xfffu], 1u);
     __syncthreads();
     topk_select_bin<kHistBins, NT>(sh.hist2, k_rem, sh);
     const uint32_t p24 = (d << 12) | sh.sel_digit;
@@ -542,14 +517,29 @@ __device__ void topk_row_registers(const float* row, int64_t ld, int n, int k,
       for (int s = 0; s < S; ++s)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (((valid[s] >> j) & 1u) && (key[s][j] >> 8) == p24)
-            atomicAdd(&sh.hist[key[s][j] & 0xffu], 1u);
+          if (((r.valid[s] >> j) & 1u) && (r.key[s][j] >> 8) == p24)
+            atomicAdd(&sh.hist[r.key[s][j] & 0xffu], 1u);
       __syncthreads();
       topk_select_bin<256, NT>(sh.hist, k2, sh);
       mask = 0xffffffffu; thr = (p24 << 8) | sh.sel_digit;
       k_tie = k2 - sh.sel_above;
     }
   }
+}
+
+// Writes the selected items in list order: the output slot of an item is
+// the number of selected items before it, from packed (above, tie) counts
+// per thread and slice, a DPP scan within the wave and a scan of the
+// per-wave totals; orow[slot] = index_of(s, j, position in the list).
+template <int NT, int S, typename IndexOf>
+__device__ void reg_emit(const RegKeys<S>& r, int k, uint32_t mask,
+                         uint32_t thr, uint32_t k_tie, int32_t* orow,
+                         RegTopkShared<NT, S>& sh, IndexOf index_of) {
+  constexpr int NW = NT / 64;
+  constexpr int kSlice = 4 * NT;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
   // packed per-slice counts: above in bits 0..15, ties in bits 16..31
   uint32_t cnt[S], incl[S];
 #pragma unroll
@@ -557,8 +547,8 @@ __device__ void topk_row_registers(const float* row, int64_t ld, int n, int k,
     uint32_t c = 0u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bool ok = (valid[s] >> j) & 1u;
-      const uint32_t km = key[s][j] & mask;
+      const bool ok = (r.valid[s] >> j) & 1u;
+      const uint32_t km = r.key[s][j] & mask;
       c += (ok && km > thr) ? 1u : 0u;
       c += (ok && km == thr) ? 0x10000u : 0u;
     }
@@ -592,21 +582,60 @@ __device__ void topk_row_registers(const float* row, int64_t ld, int n, int k,
     uint32_t gt_b = before & 0xffffu, eq_b = before >> 16;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bool ok = (valid[s] >> j) & 1u;
-      const uint32_t km = key[s][j] & mask;
-      const int col = s * kSlice + 4 * tid + j;
+      const bool ok = (r.valid[s] >> j) & 1u;
+      const uint32_t km = r.key[s][j] & mask;
+      const int pos = s * kSlice + 4 * tid + j;
       // slots are < k by construction; the check keeps a row's writes
       // inside the row whatever the counts
       if (ok && km > thr) {
         const uint32_t slot = gt_b + min(eq_b, k_tie);
-        if (slot < (uint32_t)k) orow[slot] = col;
+        if (slot < (uint32_t)k) orow[slot] = index_of(s, j, pos);
         ++gt_b;
       } else if (ok && km == thr) {
-        if (eq_b < k_tie && gt_b + eq_b < (uint32_t)k) orow[gt_b + eq_b] = col;
+        if (eq_b < k_tie && gt_b + eq_b < (uint32_t)k)
+          orow[gt_b + eq_b] = index_of(s, j, pos);
         ++eq_b;
       }
     }
   }
+}
+
+// Top-k of row[0..n) (k < n <= S * 4 * NT <= ld) into orow[0..k), in
+// ascending column order.  Thread tid holds columns s * 4 NT + 4 tid + j in
+// registers: one 16-byte load per slice, no LDS copy of the row.  `row`
+// must be 16-byte aligned and ld a multiple of 4.  Call from all NT
+// threads.
+template <int NT, int S>
+__device__ void topk_row_registers(const float* row, int64_t ld, int n, int k,
+                                   int32_t* orow, RegTopkShared<NT, S>& sh) {
+  constexpr int kSlice = 4 * NT;
+  const int tid = threadIdx.x;
+  for (int b = tid; b < kHistBins; b += NT) {
+    sh.hist[b] = 0u;
+    sh.hist2[b] = 0u;
+  }
+  RegKeys<S> r;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int c0 = s * kSlice + 4 * tid;
+    r.valid[s] = 0u;
+    r.key[s][0] = r.key[s][1] = r.key[s][2] = r.key[s][3] = 0u;
+    if (s * kSlice < n) {                     // workgroup-uniform
+      const float4 v =
+          *reinterpret_cast<const float4*>(row + min(c0, (int)ld - 4));
+      r.key[s][0] = float_to_ordered(v.x);
+      r.key[s][1] = float_to_ordered(v.y);
+      r.key[s][2] = float_to_ordered(v.z);
+      r.key[s][3] = float_to_ordered(v.w);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r.valid[s] |= (c0 + j < n ? 1u : 0u) << j;
+    }
+  }
+  __syncthreads();
+  uint32_t mask, thr, k_tie;
+  reg_threshold<NT, S>(r, k, sh, mask, thr, k_tie);
+  reg_emit<NT, S>(r, k, mask, thr, k_tie, orow, sh,
+                  [](int, int, int pos) { return pos; });
 }
 
 // Row with n <= k columns: 0..n-1, then -1 (n <= 0: all -1).
@@ -1008,12 +1037,255 @@ __global__ __launch_bounds__(kMwThreads) void mw_write_kernel(
   });
 }
 
+// ---------------------------------------------------------------------------
+// Sample-select top-k for long rows (16384 < n, rows of up to 16M columns).
+// A key below the k-th largest can never be selected, so any lower bound
+// T_lo of the k-th largest key turns the row into a short candidate list
+// {key >= T_lo} that still holds the whole answer:
+//   sample   one 1024-thread workgroup per row reads 16384 keys at jittered
+//            stride n / 16384 and takes the m-th largest sample key as T_lo,
+//            m = k * 16384 / n + 4 sqrt(k * 16384 / n) + 16: about m n /
+//            16384 keys of the row (k plus a few standard deviations) are
+//            then at or above T_lo;
+//   collect  one 256-thread workgroup per 16384-key chunk writes its keys
+//            >= T_lo, in column order, to the chunk's slot of 512 (one
+//            fully coalesced pass over the row, the HBM-bound part);
+//   select   one 1024-thread workgroup per row gathers the candidates (a scan
+//            of the chunk counts, a binary search per item) into registers
+//            and runs the register top-k on them, writing their columns in
+//            ascending order.
+// The sample decides only the speed, never the result: when the candidates
+// number fewer than k (T_lo above the k-th key) or more than 16384, or a
+// chunk overflows its slot (heavy ties), the select workgroup runs an exact
+// radix select over the whole row instead.
+// ---------------------------------------------------------------------------
+constexpr int kSsSample = 16384;
+constexpr int kSsThreads = 256;
+constexpr int kSsChunk = 16384;
+constexpr int kSsChunkCap = 512;
+constexpr int kSsCandMax = 4 * 4 * kTopkThreads;   // 16384 (RegKeys<4>)
+constexpr int64_t kSsMaxChunks = 1024;             // rows up to 16M columns
+
+struct SsWorkspace {
+  uint32_t* thr;      // [T] T_lo
+  uint32_t* count;    // [T][C] candidates per chunk (> cap: overflow)
+  uint2* cand;        // [T][C][cap] (key, column)
+  int64_t C;
+};
+
+static bool use_sample_select(int64_t ld) {
+  return ld > kMaxRowForBitmap &&
+         (ld + kSsChunk - 1) / kSsChunk <= kSsMaxChunks;
+}
+
+static SsWorkspace ss_carve(void* base, int64_t T, int64_t ld,
+                            size_t* total) {
+  SsWorkspace w{};
+  const int64_t C = (ld + kSsChunk - 1) / kSsChunk;
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* q = p ? p + off : nullptr;
+    off += align256(bytes);
+    return q;
+  };
+  w.thr = reinterpret_cast<uint32_t*>(take((size_t)T * 4));
+  w.count = reinterpret_cast<uint32_t*>(take((size_t)T * C * 4));
+  w.cand = reinterpret_cast<uint2*>(take((size_t)T * C * kSsChunkCap * 8));
+  w.C = C;
+  if (total) *total = off;
+  return w;
+}
+
+__device__ __forceinline__ uint32_t ss_hash(uint32_t x) {
+  x ^= x >> 16; x *= 0x7feb352du; x ^= x >> 15; x *= 0x846ca68bu;
+  return x ^ (x >> 16);
+}
+
+__global__ __launch_bounds__(kTopkThreads) void ss_sample_kernel(
+    const float* __restrict__ logits, int64_t ld, const int32_t* positions,
+    int k, SsWorkspace ws) {
+  __shared__ RegTopkShared<kTopkThreads, 4> sh;
+  const int64_t t = blockIdx.x;
+  const int n = row_len(positions, t, ld);
+  if (n <= kSsCandMax || n <= k) return;
+  const int tid = threadIdx.x;
+  for (int b = tid; b < kHistBins; b += kTopkThreads) {
+    sh.hist[b] = 0u;
+    sh.hist2[b] = 0u;
+  }
+  const float* row = logits + t * ld;
+  const uint32_t stride = (uint32_t)n / kSsSample;     // >= 1
+  RegKeys<4> r;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    r.valid[s] = 0xfu;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t q = (uint32_t)(s * 4 * kTopkThreads + 4 * tid + j);
+      const uint32_t col = q * stride + ss_hash(q) % stride;   // < n
+      r.key[s][j] = float_to_ordered(row[col]);
+    }
+  }
+  __syncthreads();
+  const float e = (float)k * (float)kSsSample / (float)n;
+  const int m = min(kSsSample - 1, (int)(e + 4.f * sqrtf(e)) + 16);
+  uint32_t mask, thr, k_tie;
+  reg_threshold<kTopkThreads, 4>(r, m, sh, mask, thr, k_tie);
+  if (tid == 0) ws.thr[t] = thr & mask;
+}
+
+__global__ __launch_bounds__(kSsThreads) void ss_collect_kernel(
+    const float* __restrict__ logits, int64_t ld, const int32_t* positions,
+    int k, SsWorkspace ws) {
+  constexpr int kWaves = kSsThreads / 64;
+  constexpr int kSlices = kSsChunk / (4 * kSsThreads);   // 16
+  __shared__ uint32_t s_tot[kSlices * kWaves];
+  const int64_t t = blockIdx.y;
+  const int64_t c = blockIdx.x;
+  const int n = row_len(positions, t, ld);
+  if (n <= kSsCandMax || n <= k) return;
+  const int parts = (n + kSsChunk - 1) / kSsChunk;
+  if (c >= parts) return;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const uint32_t thr = ws.thr[t];
+  const float* row = logits + t * ld;
+  const int i0 = (int)c * kSsChunk;
+  uint32_t key[kSlices][4], cnt[kSlices], incl[kSlices];
+#pragma unroll
+  for (int s = 0; s < kSlices; ++s) {
+    const int c0 = i0 + s * 4 * kSsThreads + 4 * tid;
+    const float4 v =
+        *reinterpret_cast<const float4*>(row + min(c0, (int)ld - 4));
+    key[s][0] = float_to_ordered(v.x);
+    key[s][1] = float_to_ordered(v.y);
+    key[s][2] = float_to_ordered(v.z);
+    key[s][3] = float_to_ordered(v.w);
+    uint32_t m = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m += (c0 + j < n && key[s][j] >= thr) ? 1u : 0u;
+    cnt[s] = m;
+    incl[s] = wave_inclusive_scan(m);
+    if (lane == 63) s_tot[s * kWaves + wave] = incl[s];
+  }
+  __syncthreads();
+  if (wave == 0) {                           // 64 (slice, wave) totals
+    const uint32_t v = s_tot[lane];
+    const uint32_t sc = wave_inclusive_scan(v);
+    s_tot[lane] = sc - v;
+    if (lane == 63 && tid == 63)
+      ws.count[t * ws.C + c] = sc;            // may exceed the slot: overflow
+  }
+  __syncthreads();
+  uint2* slot = ws.cand + (t * ws.C + c) * kSsChunkCap;
+#pragma unroll
+  for (int s = 0; s < kSlices; ++s) {
+    uint32_t o = s_tot[s * kWaves + wave] + incl[s] - cnt[s];
+    const int c0 = i0 + s * 4 * kSsThreads + 4 * tid;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (c0 + j < n && key[s][j] >= thr) {
+        if (o < (uint32_t)kSsChunkCap)
+          slot[o] = make_uint2(key[s][j], (uint32_t)(c0 + j));
+        ++o;
+      }
+    }
+  }
+}
+
+union SsSelectShared {
+  RegTopkShared<kTopkThreads, 4> reg;
+  TopkShared full;
+};
+
+__global__ __launch_bounds__(kTopkThreads) void ss_select_kernel(
+    const float* __restrict__ logits, int64_t ld, const int32_t* positions,
+    int k, int32_t* __restrict__ out, int64_t out_ld, SsWorkspace ws) {
+  __shared__ SsSelectShared sh;
+  __shared__ uint32_t s_pre[kSsMaxChunks + 1];
+  __shared__ uint32_t s_flag[2];
+  const int64_t t = blockIdx.x;
+  const int n = row_len(positions, t, ld);
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  int32_t* orow = out + t * out_ld;
+  if (n <= k) {
+    topk_row_short<kTopkThreads>(n, k, orow);
+    return;
+  }
+  const float* row = logits + t * ld;
+  if (n <= kSsCandMax) {                     // the whole row fits
+    topk_row_registers<kTopkThreads, 4>(row, ld, n, k, orow, sh.reg);
+    return;
+  }
+  // candidates per chunk -> exclusive prefix (at most 1024 chunks)
+  const int parts = (n + kSsChunk - 1) / kSsChunk;
+  const uint32_t cc = tid < parts ? ws.count[t * ws.C + tid] : 0u;
+  if (tid == 0) { s_flag[0] = 0u; s_flag[1] = 0u; }
+  __syncthreads();
+  if (cc > (uint32_t)kSsChunkCap) s_flag[0] = 1u;           // overflow
+  const uint32_t wi = wave_inclusive_scan(cc);
+  if (lane == 63) sh.reg.wave_sum[wave] = wi;
+  __syncthreads();
+  uint32_t before = wi - cc;
+  for (int w = 0; w < wave; ++w) before += sh.reg.wave_sum[w];
+  if (tid < parts) s_pre[tid] = before;
+  if (tid == parts - 1) { s_pre[parts] = before + cc; s_flag[1] = before + cc; }
+  __syncthreads();
+  const uint32_t total = s_flag[1];
+  const bool exact_path = s_flag[0] != 0u || total < (uint32_t)k ||
+                          total > (uint32_t)kSsCandMax;
+  __syncthreads();
+  if (exact_path) {
+    // exact radix select over the whole row (keys from global)
+    const RowKeys keys{row, nullptr, 0};
+    radix_pass<kHistBins>(keys, n, 0u, 0u, 20, (uint32_t)k, sh.full);
+    topk_radix_rest(keys, n, k, orow, sh.full);
+    return;
+  }
+  for (int b = tid; b < kHistBins; b += kTopkThreads) {
+    sh.reg.hist[b] = 0u;
+    sh.reg.hist2[b] = 0u;
+  }
+  // gather: item x (list order = column order) lives in chunk q with
+  // s_pre[q] <= x < s_pre[q + 1]
+  RegKeys<4> r;
+  uint32_t col[4][4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    r.valid[s] = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t x = (uint32_t)(s * 4 * kTopkThreads + 4 * tid + j);
+      r.key[s][j] = 0u;
+      col[s][j] = 0u;
+      if (x < total) {
+        int lo = 0, hi = parts - 1;           // last chunk with s_pre <= x
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_pre[mid] <= x) lo = mid; else hi = mid - 1;
+        }
+        const uint2 e = ws.cand[(t * ws.C + lo) * kSsChunkCap + (x - s_pre[lo])];
+        r.key[s][j] = e.x;
+        col[s][j] = e.y;
+        r.valid[s] |= 1u << j;
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t mask, thr, k_tie;
+  reg_threshold<kTopkThreads, 4>(r, k, sh.reg, mask, thr, k_tie);
+  reg_emit<kTopkThreads, 4>(r, k, mask, thr, k_tie, orow, sh.reg,
+                            [&](int s, int j, int) { return (int)col[s][j]; });
+}
+
 size_t topk_workspace_bytes(int64_t T, int64_t ld, int k) {
   (void)k;
   if (T <= 0 || !use_multi_wg(ld)) return 0;
-  size_t total = 0;
-  carve(nullptr, T, ld, &total);
-  return total;
+  // room for either long-row path (the option can switch between them)
+  size_t mw = 0, ss = 0;
+  carve(nullptr, T, ld, &mw);
+  if (use_sample_select(ld)) ss_carve(nullptr, T, ld, &ss);
+  return std::max(mw, ss);
 }
 
 template <bool KEY32>
@@ -1074,6 +1346,20 @@ static hipError_t launch_topk_single(const TopkArgs& a, hipStream_t stream) {
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   if (a.T <= 0) return hipSuccess;
   if (!use_multi_wg(a.ld)) return launch_topk_single(a, stream);
+  const bool aligned = (reinterpret_cast<uintptr_t>(a.logits) & 15u) == 0;
+  if (use_sample_select(a.ld) && aligned && options().topk_kernel != 3) {
+    const SsWorkspace ss = ss_carve(a.workspace, a.T, a.ld, nullptr);
+    hipLaunchKernelGGL(ss_sample_kernel, dim3((unsigned)a.T),
+                       dim3(kTopkThreads), 0, stream, a.logits, a.ld,
+                       a.positions, a.k, ss);
+    hipLaunchKernelGGL(ss_collect_kernel, dim3((unsigned)ss.C, (unsigned)a.T),
+                       dim3(kSsThreads), 0, stream, a.logits, a.ld,
+                       a.positions, a.k, ss);
+    hipLaunchKernelGGL(ss_select_kernel, dim3((unsigned)a.T),
+                       dim3(kTopkThreads), 0, stream, a.logits, a.ld,
+                       a.positions, a.k, a.out, a.out_ld, ss);
+    return hipGetLastError();
+  }
   MwWorkspace ws = carve(a.workspace, a.T, a.ld, nullptr);
   const size_t zb = mw_zero_bytes(a.T, a.ld);
   const size_t n16 = zb / 16;

@@ -239,7 +239,8 @@ int dsa_device_error_flags(int reset);
  * 3 tiled with direct loads, 4 row-wise on a (row, page group) grid, 5 tiled
  * with 16 waves x 1 row), "row_pages_per_wave",
  * "tile_pages_per_split", "topk_kernel" (rows of up to 49152 columns: 1
- * register-resident keys, 2 keys cached in LDS).
+ * register-resident keys, 2 keys cached in LDS; rows longer than 65536
+ * columns: 3 multi-workgroup radix select instead of sample select).
  */
 int dsa_set_option(const char* key, int value);
 

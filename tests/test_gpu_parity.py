@@ -333,17 +333,26 @@ def test_topk_unaligned_logits_rows():
                                               f"unaligned row {t}")
 
 
-def test_topk_multi_workgroup_rows():
-    """Rows longer than 65536 columns take the multi-workgroup top-k; mix
-    long, short (padded) and constant rows (candidate-list overflow)."""
-    _say("case: multi-workgroup top-k")
-    T, ld, k = 6, 131072, 2048
+@pytest.mark.parametrize("kernel", [0, 3])
+def test_topk_multi_workgroup_rows(kernel):
+    """Rows in a batch wider than 65536 columns: sample select (0) or the
+    multi-workgroup radix select (3).  Long, mid-length, short (padded) and
+    constant rows (candidate overflow -> exact fallback), heavy near-ties,
+    a row whose top keys sit in one narrow run of columns, a row of -inf
+    with a few finite keys."""
+    _say(f"case: long-row top-k, kernel {kernel}")
+    binding.dsa_set_option("topk_kernel", kernel)
+    T, ld, k = 10, 131072, 2048
     rng = np.random.default_rng(44)
     lg = rng.standard_normal((T, ld)).astype(np.float32)
     lg[1] = 0.5                                   # all equal: overflow path
     lg[3, :1000] = rng.integers(-2, 3, 1000)      # short row with ties
     lg[4] = np.round(lg[4] * 4) / 4               # heavy near-ties
-    pos = np.array([ld - 1, 90000, 70000, 999, ld - 1, 65536], np.int32)
+    lg[6, 50000:52100] += 30.0                    # answer in one narrow run
+    lg[7] = -np.inf
+    lg[7, rng.choice(ld, 3000, replace=False)] = rng.standard_normal(3000)
+    pos = np.array([ld - 1, 90000, 70000, 999, ld - 1, 65536, ld - 1, ld - 1,
+                    10000, 20000], np.int32)
     assert binding.dsa_topk_workspace_size(T, ld, k) > 0
     g = binding.dsa_indexer_topk(torch.from_numpy(lg).cuda(),
                                  torch.from_numpy(pos).cuda(), k).cpu().numpy()
