@@ -123,7 +123,7 @@ def dominant_kernel(b):
         return "logits_balanced_kernel<", ""
     if b.T <= 2 * b.R:
         return "logits_row_prefetch_kernel<", ""
-    return "logits_tile_kernel<", ""
+    return "logits_tile16_kernel<", ""
 
 
 def cpu_baseline(b, seconds):
@@ -172,8 +172,7 @@ def cpu_baseline(b, seconds):
 # ----------------------------------------------------------------------------
 LOGITS_SOURCES = ("dsa_lightning_indexer_amd/csrc/kernels_logits.hip",
                   "dsa_lightning_indexer_amd/csrc/dsa_common.h",
-                  "dsa_lightning_indexer_amd/csrc/dsa_launch.h",
-                  "dsa_lightning_indexer_amd/csrc/dsa_topk_rows.h")
+                  "dsa_lightning_indexer_amd/csrc/dsa_launch.h")
 CALIBRATION_BYTES = 1 << 28
 
 
