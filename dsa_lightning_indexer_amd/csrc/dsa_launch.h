@@ -48,7 +48,7 @@ struct ForwardArgs {
 
 // Kernel-choice knobs (dsa_set_option); 0 = automatic.
 struct Options {
-  int logits_kernel = 0;        // 1 row-wise, 2 tiled 8x2, 3 tiled direct, 4 row grid, 5 tiled 16x1
+  int logits_kernel = 0;        // 1 row-wise, 2 tiled 8x2, 3 tiled direct, 4 row grid, 5 tiled 16x1 with the two-op epilogue
   int row_pages_per_wave = 0;
   int tile_pages_per_split = 0;
   int topk_kernel = 0;          // 0/1 register rows, 2 LDS-cached rows, 3 long rows by multi-WG radix

@@ -102,6 +102,28 @@ __device__ __forceinline__ void load_q_frags(const uint8_t* q8_row, int H,
   }
 }
 
+// The same fragments in the chunk-major K order of the 16-row tile kernel:
+// lane l holds bytes [16 (l / 16), + 16) and [64 + 16 (l / 16), + 16) of its
+// row (a permutation of the 128-long reduction index; A and B use the same
+// one, so the dot products are unchanged).
+template <int MT, bool FULL>
+__device__ __forceinline__ void load_q_frags_cm(const uint8_t* q8_row, int H,
+                                                i32x8 (&qa)[MT]) {
+  const int lane = lane_id();
+  const int i16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int head = 16 * m + i16;
+    const int hh = FULL ? head : min(head, H - 1);
+    const uint8_t* row = q8_row + hh * kHeadDim + 16 * g;
+    const uint4 x = *reinterpret_cast<const uint4*>(row);
+    const uint4 y = *reinterpret_cast<const uint4*>(row + 64);
+    qa[m] = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w,
+                  (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+    if (!FULL && head >= H) qa[m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+}
+
 // Per-lane effective head weights w[h] * s_q[h] / 2 for the C rows this
 // lane holds: head 16*m + 4*(lane/16) + j, j = 0..3 (4 consecutive heads,
 // one 16-byte load each when FULL).  The 1/2 belongs to head_reduce's ReLU.
@@ -142,6 +164,20 @@ __device__ __forceinline__ float head_reduce(const f32x4 (&acc)[MT],
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       v = fmaf(w_half[m][j], acc[m][j] + fabsf(acc[m][j]), v);
+  return v;
+}
+
+// The same sum without the linear part: sum over this lane's heads of
+// w * |dot| (one FMA with an abs source modifier per MFMA output).  The
+// tile kernels add sum_h w * dot, computed once for four rows, afterwards.
+template <int MT>
+__device__ __forceinline__ float head_reduce_abs(const f32x4 (&acc)[MT],
+                                                 const float (&w_half)[MT][4]) {
+  float v = 0.f;
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v = fmaf(w_half[m][j], fabsf(acc[m][j]), v);
   return v;
 }
 
@@ -667,28 +703,186 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a,
 }
 
 // ---------------------------------------------------------------------------
+// Linear part of the head reduction, shared by four rows (tile kernel).
+// With ReLU written as (x + |x|) / 2 and the 1/2 folded into the weights,
+//   sum_h w_h (x_h + |x_h|) = L + sum_h w_h |x_h|,
+//   L = sum_h w_h x_h = qlin . code_k,   qlin = sum_h w_h code_q[h, :],
+// so the per-output epilogue is a single FMA, and L costs one more FP8
+// MFMA per 16 keys for four rows together.  qlin (fp32) is split into
+// kLinPieces FP8 pieces, qlin ~= sum_p s_p c_p: s_p an fp32 scale, c_p the
+// e4m3 rounding of what the earlier pieces left over.  Each piece shrinks
+// the largest residual at least 28-fold (half an e4m3 step at the top of
+// the range is 1/28 of it), so four pieces leave at most ~1.6e-6 max|qlin|
+// per element, far inside the fp32 accumulation error of the dot products.
+// The A operand of that MFMA has rows 4 q + p = (row q of the group, piece
+// p), so lane group q of its output holds the four pieces of row q.
+// ---------------------------------------------------------------------------
+constexpr int kLinPieces = 4;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// One reduce-scatter step over v[0..N): lanes paired by the DPP pattern
+// CTRL differ in `bit`; a lane keeps half `bit` of the list and adds the
+// partner's copy of that half.
+template <int CTRL, int N>
+__device__ __forceinline__ void rs_step(float* v, bool bit) {
+#pragma unroll
+  for (int j = 0; j < N / 2; ++j) {
+    const float send = bit ? v[j] : v[j + N / 2];
+    const float keep = bit ? v[j + N / 2] : v[j];
+    v[j] = keep + dpp_f<CTRL>(send);
+  }
+}
+
+// Maximum over the wave of x >= 0 (wave-uniform result).
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));    // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f<0x4E>(x));    // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f<0x141>(x));   // row_half_mirror
+  x = fmaxf(x, dpp_f<0x140>(x));   // row_mirror
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// qlin of one row from its chunk-major A fragments (lane l: head 16 m +
+// l % 16; byte j of qa[m] is dim 16 (l / 16) + j for j < 16 and 64 + 16 (l
+// / 16) + j - 16 after; wa[m] the folded weight of that head), summed over
+// the 16 lanes of each lane row by a reduce-scatter (row_mirror,
+// row_half_mirror, then two quad permutations): lane l ends with bytes
+// 2 (l % 16) and + 1 of that list.  The hardware fp8 -> f32 conversion
+// decodes e4m3fn exactly.
+template <int MT>
+__device__ __forceinline__ float2 row_qlin(const i32x8 (&qa)[MT],
+                                           const float (&wa)[MT]) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  float v[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) v[j] = 0.f;
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(qa[m][k], false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(qa[m][k], true);
+      v[4 * k + 0] = fmaf(wa[m], lo[0], v[4 * k + 0]);
+      v[4 * k + 1] = fmaf(wa[m], lo[1], v[4 * k + 1]);
+      v[4 * k + 2] = fmaf(wa[m], hi[0], v[4 * k + 2]);
+      v[4 * k + 3] = fmaf(wa[m], hi[1], v[4 * k + 3]);
+    }
+  const int i16 = lane_id() & 15;
+  rs_step<0x140, 32>(v, (i16 >> 3) & 1);
+  rs_step<0x141, 16>(v, (i16 >> 2) & 1);
+  rs_step<0x4E, 8>(v, (i16 >> 1) & 1);
+  rs_step<0xB1, 4>(v, i16 & 1);
+  return make_float2(v[0], v[1]);
+}
+
+// Splits qlin (this lane's dims d, d + 1 as left by row_qlin) into
+// kLinPieces e4m3 pieces, A row a = 4 q + p of the group's operand (q = the
+// row within the group), stored chunk-major like the keys: byte d of A row
+// a at group[(d / 64) * 1024 + (d / 16 % 4) * 256 + a * 16 + d % 16], so
+// lane l reads its fragment at group + 16 l (+ 1024).  The scale of piece p
+// goes to scales[p].  qlin is first brought to max|qlin| in [1, 2) by a
+// power of two (exact), so a residual below 2^-60 -- nothing left that
+// matters -- ends the split without dividing by a denormal.
+__device__ __forceinline__ void split_pieces(float r0, float r1, int q,
+                                             uint8_t* group, float* scales) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const int lane = lane_id();
+  const int i16 = lane & 15, g = lane >> 4;
+  const int d = (i16 < 8 ? 16 * g : 64 + 16 * g - 16) + 2 * i16;
+  const float amax0 = wave_max_nonneg(fmaxf(fabsf(r0), fabsf(r1)));
+  int e = 0;
+  if (amax0 > 0.f) (void)frexpf(amax0, &e);
+  const int E = amax0 > 0.f ? 1 - e : 0;          // amax0 * 2^E in [1, 2)
+  r0 = __builtin_amdgcn_ldexpf(r0, E);
+  r1 = __builtin_amdgcn_ldexpf(r1, E);
+#pragma unroll
+  for (int p = 0; p < kLinPieces; ++p) {
+    const float amax = wave_max_nonneg(fmaxf(fabsf(r0), fabsf(r1)));
+    const bool live = amax > 0x1p-60f;
+    const float inv = live ? kE4M3Max / amax : 0.f;
+    const float sc = live ? amax / kE4M3Max : 0.f;
+    const uint32_t c0 = e4m3fn_encode(r0 * inv);
+    const uint32_t c1 = e4m3fn_encode(r1 * inv);
+    const uint32_t pk = c0 | (c1 << 8);
+    const f32x2 dec = __builtin_amdgcn_cvt_pk_f32_fp8((int)pk, false);
+    r0 = fmaf(-sc, dec[0], r0);
+    r1 = fmaf(-sc, dec[1], r1);
+    *reinterpret_cast<uint16_t*>(group + (d >> 6) * 1024 + ((d >> 4) & 3) * 256 +
+                                 (4 * q + p) * 16 + (d & 15)) = (uint16_t)pk;
+    if (lane == 0) scales[p] = __builtin_amdgcn_ldexpf(sc, -E);
+  }
+}
+
+// Folded weights w[h] * s_q[h] / 2 of the A-fragment heads of this lane:
+// head 16 m + l % 16 (0 for heads >= H).
+template <int MT, bool FULL>
+__device__ __forceinline__ void load_a_weights(const float* w_row,
+                                               const float* s_row, int H,
+                                               float (&wa)[MT]) {
+  const int i16 = lane_id() & 15;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int head = 16 * m + i16;
+    const int hh = FULL ? head : min(head, H - 1);
+    const float x = 0.5f * (w_row[hh] * s_row[hh]);
+    wa[m] = (FULL || head < H) ? x : 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Tiled logits, one row per wave.  A workgroup of 16 waves owns a tile of 16
 // consecutive rows of one request and a range of pages; wave w scores row
 // w.  With one row per wave a wave holds 16 heads x 128 q codes (32 VGPRs)
 // instead of two rows, so it fits in 128 VGPRs and four waves share each
-// SIMD: the MFMAs of one wave overlap the ReLU / weight VALU work of the
-// others (the two compete for the SIMD's issue slots otherwise).  Pages are
-// staged in LDS two at a time (double-buffered pairs, 144-byte padded rows)
-// with one barrier per pair; the page copy is a branch-free buffer load
-// (16 bytes of keys per thread, zero-size for a page outside the pool) so
-// that the loop carries no divergent control flow.  Each page: 4 N-tiles x
-// MT MFMAs, the head reduction in registers, one reduce-scatter across the
-// 4 lane groups, and one 256-byte logit store.
+// SIMD: the MFMAs of one wave overlap the VALU work of the others.
+//
+// Pages are staged in LDS two at a time (double-buffered pairs, one barrier
+// per pair) by direct-to-LDS buffer loads: no staging registers, no LDS
+// store instructions.  A page's keys sit in LDS chunk-major: 16-byte chunk
+// (N-tile n, half r, chunk g, token t) at n * 2048 + r * 1024 + g * 256 +
+// t * 16, holding bytes [64 r + 16 g, + 16) of token 16 n + t.  The B
+// operand of N-tile n is then two fully contiguous 1 KB reads (lane l at
+// n * 2048 + r * 1024 + 16 l), which the LDS serves at full rate; the
+// padded token-row layout costs ~1.7x that in bank conflicts.  q uses the
+// same permutation of the reduction index (load_q_frags_cm).  A page
+// outside the pool is a zero-size buffer: its loads touch no memory and its
+// logits are -inf.  Each page: 4 N-tiles x MT MFMAs, the head reduction in
+// registers, one reduce-scatter across the 4 lane groups, one 256-byte
+// logit store.
+//
+// LIN: the epilogue is w * |dot| (one FMA per output) and the linear part L
+// comes from the shared MFMA described above: wave 4 G + i computes it for
+// N-tile i of every page for rows 4 G .. 4 G + 3 and leaves it in LDS; the
+// logits of a page pair are completed and stored in the next pass of the
+// loop, after the barrier that publishes L.
 // ---------------------------------------------------------------------------
 constexpr int kT16Waves = 16;
 constexpr int kT16Threads = 64 * kT16Waves;
 
-template <int MT, bool FULL>
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int MT, bool FULL, bool LIN, int PP>
 __global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
     LogitsArgs a, int pages_per_split) {
-  // [buffer][page of the pair][64 tokens x 144 B], scales likewise
-  __shared__ __align__(16) uint8_t s_keys[2][2][kPageTokens * kLdsRow];
-  __shared__ __align__(16) float s_scale[2][2][kPageTokens];
+  static_assert(PP == 2 || PP == 4, "pages per step");
+  constexpr int kLs = PP * kPageTokens + 16;     // s_lin row stride (banks)
+  // [buffer][page of the step][8192 key bytes, chunk-major]; the scales
+  // have a third buffer: a step's scales are still read after the barrier
+  // that lets the next-but-one step's copy start
+  __shared__ __align__(16) uint8_t s_keys[2][PP][kPageKeyBytes];
+  __shared__ __align__(16) float s_scale[3][PP][kPageTokens];
+  __shared__ __align__(16) uint8_t s_alin[LIN ? kTileRows / 4 : 1][2048];
+  __shared__ __align__(16) float s_ascale[LIN ? kTileRows : 1][kLinPieces];
+  __shared__ __align__(16) float s_lin[2][LIN ? kTileRows : 1][kLs];
   __shared__ int s_info[4];
   __shared__ int s_pos[kTileRows];
 
@@ -727,27 +921,16 @@ __global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
   const int i16 = lane & 15, g = lane >> 4;
   const int prow = wave_uniform(s_pos[wave]);
   const int64_t t = row0 + wave;
-  i32x8 qa[MT];
-  float w[MT][4];
-  if (prow >= 0) {
-    load_q_frags<MT, FULL>(a.q8 + t * a.H * kHeadDim, a.H, qa);
-    load_head_weights<MT, FULL>(a.weights + t * a.H, a.q_scale + t * a.H,
-                                a.H, w);
-  } else {
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      qa[m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) w[m][j] = 0.f;
-    }
-  }
 
-  // Page pair copy: thread i moves 16 key bytes of page (i >> 9) of the
-  // pair (token (i & 511) / 8, chunk i % 8); threads with (i & 511) < 16
-  // also move 16 scale bytes.  Pages past the range or outside the pool
-  // are zero-size buffers: the loads return 0 without touching memory.
-  const int half = wave_uniform(wave >> 3), sub = tid & 511;
-  const int ctok = sub >> 3, cchunk = sub & 7;
+  // Page copy of a step, issued right after the barrier that frees the
+  // buffer: wave w moves LDS chunks 64 (w & 7) .. + 63 of pages (w >> 3) +
+  // 2 k of the step (lane l -> chunk q = 64 (w & 7) + l: N-tile q >> 7,
+  // half (q >> 6) & 1, chunk (q >> 4) & 3, token q & 15); waves 0 and 8
+  // also move those pages' 64 scales.
+  const int half = wave_uniform(wave >> 3);
+  const int cq = 64 * (wave & 7) + lane;
+  const int csrc = (16 * (cq >> 7) + (cq & 15)) * kHeadDim +
+                   64 * ((cq >> 6) & 1) + 16 * ((cq >> 4) & 3);
   bool bad_page = false;
   const int last = (int)a.bt_stride - 1;
   auto page_id = [&](int jp) {
@@ -761,66 +944,155 @@ __global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
     return make_rsrc(a.k_cache + (int64_t)(ok ? page : 0) * kPageBytes,
                      ok ? kPageBytes : 0);
   };
-  auto fetch = [&](int jp, uint4& kreg, uint4& sreg) {
-    const __amdgpu_buffer_rsrc_t r0 = page_rsrc(jp);
-    const __amdgpu_buffer_rsrc_t r1 = page_rsrc(jp + 1);
-    const __amdgpu_buffer_rsrc_t rs = half ? r1 : r0;
-    const auto k4 = __builtin_amdgcn_raw_buffer_load_b128(rs, sub * 16, 0, 0);
-    // threads with sub >= 16 read past the page end: zero, no traffic
-    const auto s4 = __builtin_amdgcn_raw_buffer_load_b128(
-        rs, sub < 16 ? kPageKeyBytes + sub * 16 : kPageBytes, 0, 0);
-    kreg = make_uint4(k4[0], k4[1], k4[2], k4[3]);
-    sreg = make_uint4(s4[0], s4[1], s4[2], s4[3]);
-  };
-  auto stash = [&](int buf, const uint4& kreg, const uint4& sreg) {
-    *reinterpret_cast<uint4*>(&s_keys[buf][half][ctok * kLdsRow + cchunk * 16]) =
-        kreg;
-    if (sub < 16)
-      *reinterpret_cast<uint4*>(&s_scale[buf][half][sub * 4]) = sreg;
+  auto fetch = [&](int jp, int buf, int sbuf) {
+#pragma unroll
+    for (int k = 0; k < PP / 2; ++k) {
+      const int ph = half + 2 * k;
+      const __amdgpu_buffer_rsrc_t rs = page_rsrc(jp + ph);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (lds_void*)&s_keys[buf][ph][64 * 16 * (wave & 7)], 16, csrc, 0,
+          0, 0);
+      if ((wave & 7) == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (lds_void*)&s_scale[sbuf][ph][0], 4, kPageKeyBytes + 4 * lane,
+            0, 0, 0);
+    }
   };
 
-  uint4 kreg, sreg;
-  fetch(jb, kreg, sreg);
-  stash(0, kreg, sreg);
+  i32x8 qa[MT];
+  if (prow >= 0) {
+    load_q_frags_cm<MT, FULL>(a.q8 + t * a.H * kHeadDim, a.H, qa);
+  } else {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) qa[m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  fetch(jb, 0, 0);
+
+  // Shared linear part: this wave's qlin pieces to LDS, then the A operand
+  // of its group (rows 4 G .. 4 G + 3, G = wave / 4).  The piece scales of
+  // the row a lane group receives are read from LDS where they are used.
+  const int G = wave >> 2;
+  auto load_alin = [&]() {
+    const uint8_t* src = &s_alin[G][16 * lane];
+    const uint4 x = *reinterpret_cast<const uint4*>(src);
+    const uint4 y = *reinterpret_cast<const uint4*>(src + 1024);
+    return i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w,
+                 (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+  };
+  i32x8 alin = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+  if (LIN) {
+    float wa[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) wa[m] = 0.f;
+    if (prow >= 0)
+      load_a_weights<MT, FULL>(a.weights + t * a.H, a.q_scale + t * a.H, a.H,
+                               wa);
+    const float2 ql = row_qlin<MT>(qa, wa);
+    split_pieces(ql.x, ql.y, wave & 3, &s_alin[G][0], &s_ascale[wave][0]);
+    __syncthreads();
+    alin = load_alin();
+  }
+  float w[MT][4];
+  if (prow >= 0) {
+    load_head_weights<MT, FULL>(a.weights + t * a.H, a.q_scale + t * a.H,
+                                a.H, w);
+  } else {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[m][j] = 0.f;
+  }
   float* orow = a.logits + t * a.ld;
 
-  for (int jp = jb; jp < je; jp += 2) {
-    const int buf = ((jp - jb) >> 1) & 1;
-    const bool more = jp + 2 < je;
-    if (more) fetch(jp + 2, kreg, sreg);
-    __syncthreads();
+  // LIN: wave 4 G + wq takes the N-tiles of a page in the order wq, wq + 1,
+  // ... (mod 4), so the tile it computes L for is always its first one and
+  // the loop carries no wave-dependent branch; lane group g then ends with
+  // N-tile (wq + g) mod 4.  The head sums of a step wait in registers for L
+  // until after the next barrier, and take their k-scales then.
+  const int wq = LIN ? (wave & 3) : 0;
+  const int tok = 16 * ((wq + g) & 3) + i16;
+  float pt[PP];
+  bool pok[PP];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < PP; ++h) { pt[h] = 0.f; pok[h] = false; }
+  int pjp = -1, pbuf = 0, psbuf = 0;
+  auto complete = [&]() {
+#pragma unroll
+    for (int h = 0; h < PP; ++h) {
+      const int pj = pjp + h;
+      const int s = pj * kPageTokens + tok;
+      const float lv = s_lin[pbuf][wave][kPageTokens * h + tok];
+      const float ks = s_scale[psbuf][h][tok];
+      const float val = (s <= prow && pok[h]) ? (pt[h] + lv) * ks : -INFINITY;
+      if (prow >= 0 && pj < je) orow[s] = val;
+    }
+  };
+
+  for (int jp = jb, si = 0; jp < je; jp += PP, ++si) {
+    const int buf = si & 1, sbuf = si % 3;
+    const bool more = jp + PP < je;
+    // this wave's copy of the pair has landed in LDS (the direct loads
+    // count in vmcnt); the barrier then publishes every wave's copy
+    __builtin_amdgcn_s_waitcnt(0x0f70);        // vmcnt(0)
+    __syncthreads();
+    if (LIN && jp != jb) complete();
+    if (more) fetch(jp + PP, buf ^ 1, sbuf == 2 ? 0 : sbuf + 1);
+#pragma unroll
+    for (int h = 0; h < PP; ++h) {
       const int pj = jp + h;
       const uint8_t* kb_lds = s_keys[buf][h];
       float v[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const uint8_t* src = kb_lds + (16 * nt + i16) * kLdsRow + 32 * g;
+        const int n = (wq + nt) & 3;
+        const uint8_t* src = kb_lds + 2048 * n + 16 * lane;
         const uint4 x = *reinterpret_cast<const uint4*>(src);
-        const uint4 y = *reinterpret_cast<const uint4*>(src + 16);
+        const uint4 y = *reinterpret_cast<const uint4*>(src + 1024);
         const i32x8 kb = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w,
                                (int)y.x, (int)y.y, (int)y.z, (int)y.w};
         f32x4 acc[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m)
           acc[m] = mfma16x16x128_fp8(qa[m], kb, f32x4{0.f, 0.f, 0.f, 0.f});
-        v[nt] = head_reduce<MT>(acc, w);
+        if (LIN) {
+          v[nt] = head_reduce_abs<MT>(acc, w);
+          if (nt == 0) {
+            // L of rows 4 G + g, keys of N-tile wq
+            const f32x4 lin = mfma16x16x128_fp8(alin, kb, f32x4{0.f, 0.f, 0.f, 0.f});
+            const float4 lsc =
+                *reinterpret_cast<const float4*>(&s_ascale[4 * G + g][0]);
+            const float lval = fmaf(lsc.w, lin[3],
+                               fmaf(lsc.z, lin[2],
+                               fmaf(lsc.y, lin[1], lsc.x * lin[0])));
+            s_lin[buf][4 * G + g][kPageTokens * h + 16 * wq + i16] = lval;
+          }
+        } else {
+          v[nt] = head_reduce<MT>(acc, w);
+        }
       }
-      // lane group g ends with N-tile g
+      // lane group g ends with N-tile (wq + g) mod 4: token tok of the page
       const float tot = reduce_scatter4(v[0], v[1], v[2], v[3]);
-      const int tok = 16 * g + i16;
       const int s = pj * kPageTokens + tok;
-      // a page outside the pool scores -inf (its loads returned 0)
+      // a page outside the pool scores -inf
       const int page = page_id(pj);
       const bool page_ok = page >= 0 && (int64_t)page < a.num_pages;
-      const float val = (s <= prow && page_ok) ? tot * s_scale[buf][h][tok]
-                                               : -INFINITY;
-      if (prow >= 0 && pj < je) orow[s] = val;
+      if (LIN) {
+        pt[h] = tot;
+        pok[h] = page_ok;
+      } else {
+        const float val = (s <= prow && page_ok) ? tot * s_scale[sbuf][h][tok]
+                                                 : -INFINITY;
+        if (prow >= 0 && pj < je) orow[s] = val;
+      }
     }
-    if (more) stash(buf ^ 1, kreg, sreg);
+    if (LIN) { pjp = jp; pbuf = buf; psbuf = sbuf; }
   }
-  if (bad_page && tid == 0) raise_flag(kErrPageOutOfRange);
+  if (LIN) {
+    __syncthreads();
+    complete();
+  }
+  // each half of the workgroup checks the pages it copies
+  if (bad_page && lane == 0) raise_flag(kErrPageOutOfRange);
 }
 
 // ---------------------------------------------------------------------------
@@ -1026,10 +1298,13 @@ static hipError_t launch_logits_mt(const LogitsArgs& a, hipStream_t stream,
       pps = (int)std::max<int64_t>(64, (max_pages + splits - 1) / splits);
     }
     const int64_t gx = (max_pages + pps - 1) / pps;
-    if (o.logits_kernel != 2 && o.logits_kernel != 3)
-      hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL>),
-                         dim3((unsigned)gx, (unsigned)tiles),
-                         dim3(kT16Threads), 0, stream, a, pps);
+    const dim3 g3((unsigned)gx, (unsigned)tiles);
+    if (o.logits_kernel == 5)
+      hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL, false, 2>),
+                         g3, dim3(kT16Threads), 0, stream, a, pps);
+    else if (o.logits_kernel != 2 && o.logits_kernel != 3)
+      hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL, true, 2>),
+                         g3, dim3(kT16Threads), 0, stream, a, pps);
     else if (o.logits_kernel == 3)
       hipLaunchKernelGGL((logits_tile_direct_kernel<MT, FULL>),
                          dim3((unsigned)gx, (unsigned)tiles),

@@ -237,7 +237,8 @@ int dsa_device_error_flags(int reset);
  * DSA_ERR_INVALID_ARG for an unknown key.  Value 0 restores the automatic
  * choice.  Keys: "logits_kernel" (1 row-wise, 2 tiled with 8 waves x 2 rows,
  * 3 tiled with direct loads, 4 row-wise on a (row, page group) grid, 5 tiled
- * with 16 waves x 1 row), "row_pages_per_wave",
+ * with 16 waves x 1 row but ReLU as an add and an FMA per MFMA output
+ * instead of the default's shared linear term), "row_pages_per_wave",
  * "tile_pages_per_split", "topk_kernel" (rows of up to 49152 columns: 1
  * register-resident keys, 2 keys cached in LDS; rows longer than 65536
  * columns: 3 multi-workgroup radix select instead of sample select).

@@ -144,9 +144,9 @@ def test_out_of_range_block_table_entry_is_flagged_not_faulting():
     b = synth.tiny()
     d = parity.upload(b)
     binding.dsa_device_error_flags(reset=True)
-    _, _, lg_ok, _ = parity.run_gpu(b, d)
-    for kernel in (1, 2, 4, 5):
+    for kernel in (0, 1, 2, 4, 5):
         binding.dsa_set_option("logits_kernel", kernel)
+        _, _, lg_ok, _ = parity.run_gpu(b, d)     # this kernel, good table
         bad = d["block_table"].clone()
         bad[0, 1] = 1 << 20                       # page id beyond the pool
         d2 = dict(d, block_table=bad)
