@@ -122,19 +122,23 @@ __device__ __forceinline__ int request_of_row(const int32_t* qsl, int R,
 
 // Sum over the 4 lane groups (lanes l, l^16, l^32, l^48) of four partial
 // values, scattered so that lane group g ends with the total of value g.
+// gfx950's permlane swaps do the exchange in VALU: the 32-lane swap of
+// (v0, v2) leaves lanes < 32 with v0 of lanes l and l + 32 and lanes >= 32
+// with v2 of lanes l - 32 and l (likewise (v1, v3)); the 16-lane swap of the
+// two sums then pairs 16-lane rows 0/1 and 2/3.  Each total is the same two
+// additions in the same order as an exchange through lane shuffles.
 __device__ __forceinline__ float reduce_scatter4(float v0, float v1, float v2,
                                                  float v3) {
-  const int lane = lane_id();
-  const bool hi = lane >= 32;
-  float send0 = hi ? v0 : v2, send1 = hi ? v1 : v3;
-  float keep0 = hi ? v2 : v0, keep1 = hi ? v3 : v1;
-  keep0 += __shfl_xor(send0, 32);
-  keep1 += __shfl_xor(send1, 32);
-  const bool odd = (lane >> 4) & 1;
-  const float send = odd ? keep0 : keep1;
-  float keep = odd ? keep1 : keep0;
-  keep += __shfl_xor(send, 16);
-  return keep;
+  const auto p02 = __builtin_amdgcn_permlane32_swap(
+      __float_as_uint(v0), __float_as_uint(v2), false, false);
+  const auto p13 = __builtin_amdgcn_permlane32_swap(
+      __float_as_uint(v1), __float_as_uint(v3), false, false);
+  const float a = __uint_as_float(p02[0]) + __uint_as_float(p02[1]);
+  const float b = __uint_as_float(p13[0]) + __uint_as_float(p13[1]);
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(a),
+                                                  __float_as_uint(b), false,
+                                                  false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 }  // namespace dsa

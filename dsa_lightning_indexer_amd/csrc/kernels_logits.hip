@@ -19,6 +19,7 @@
 // block_table[r, s / 64], slot s % 64; the page holds 64 x 128 key bytes and
 // then 64 fp32 scales.
 #include <algorithm>
+#include <type_traits>
 
 #include "dsa_common.h"
 #include "dsa_launch.h"
@@ -845,9 +846,11 @@ __device__ __forceinline__ void load_a_weights(const float* w_row,
 // instead of two rows, so it fits in 128 VGPRs and four waves share each
 // SIMD: the MFMAs of one wave overlap the VALU work of the others.
 //
-// Pages are staged in LDS two at a time (double-buffered pairs, one barrier
-// per pair) by direct-to-LDS buffer loads: no staging registers, no LDS
-// store instructions.  A page's keys sit in LDS chunk-major: 16-byte chunk
+// A tile's pages are cut into gridDim.x equal ranges (at least 64 pages),
+// so all splits of a tile take the same time and the last wave of
+// workgroups does not leave compute units idle.  Pages are staged in LDS PP
+// at a time (double-buffered, one barrier per step) by direct-to-LDS buffer
+// loads: no staging registers, no LDS store instructions.  A page's keys sit in LDS chunk-major: 16-byte chunk
 // (N-tile n, half r, chunk g, token t) at n * 2048 + r * 1024 + g * 256 +
 // t * 16, holding bytes [64 r + 16 g, + 16) of token 16 n + t.  The B
 // operand of N-tile n is then two fully contiguous 1 KB reads (lane l at
@@ -868,17 +871,47 @@ __device__ __forceinline__ void load_a_weights(const float* w_row,
 constexpr int kT16Waves = 16;
 constexpr int kT16Threads = 64 * kT16Waves;
 
-typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Direct-to-LDS buffer loads (lane l's SIZE bytes from base + voff land at
+// LDS address lds + SIZE * l), issued through inline assembly so that the
+// compiler does not track them: it cannot tell a copy into one LDS buffer
+// from reads of the other and would wait for the copy before every read.
+// The caller makes the data visible itself (vmcnt(0), then a barrier).
+// base, bytes and lds are wave-uniform; reads at or past `bytes` return 0.
+template <int SIZE>
+__device__ __forceinline__ void lds_copy(const void* base, int bytes,
+                                         const void* lds, int voff) {
+  static_assert(SIZE == 4 || SIZE == 16, "copy size");
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  u32x4 d;                                   // raw buffer resource
+  d[0] = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  d[1] = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xffffu);
+  d[2] = __builtin_amdgcn_readfirstlane((uint32_t)bytes);
+  d[3] = 0x00020000u;
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const lds_u8*)lds);
+  if (SIZE == 16)
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(d), "s"(m0) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(d), "s"(m0) : "memory", "m0");
+}
 
 template <int MT, bool FULL, bool LIN, int PP>
 __global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
-    LogitsArgs a, int pages_per_split) {
+    LogitsArgs a, int pages_per_split, int min_pages) {
   static_assert(PP == 2 || PP == 4, "pages per step");
   constexpr int kLs = PP * kPageTokens + 16;     // s_lin row stride (banks)
-  // [buffer][page of the step][8192 key bytes, chunk-major]; the scales
-  // have a third buffer: a step's scales are still read after the barrier
-  // that lets the next-but-one step's copy start
-  __shared__ __align__(16) uint8_t s_keys[2][PP][kPageKeyBytes];
+  // two key buffers [page of the step][8192 key bytes, chunk-major], as two
+  // objects so the compiler can tell the reads of one from the direct-to-LDS
+  // copy into the other (it would otherwise wait for the copy before every
+  // read); the scales have a third buffer: a step's scales are still read
+  // after the barrier that lets the next-but-one step's copy start
+  __shared__ __align__(16) uint8_t s_keys0[PP][kPageKeyBytes];
+  __shared__ __align__(16) uint8_t s_keys1[PP][kPageKeyBytes];
   __shared__ __align__(16) float s_scale[3][PP][kPageTokens];
   __shared__ __align__(16) uint8_t s_alin[LIN ? kTileRows / 4 : 1][2048];
   __shared__ __align__(16) float s_ascale[LIN ? kTileRows : 1][kLinPieces];
@@ -913,8 +946,14 @@ __global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
 #pragma unroll
   for (int i = 0; i < kTileRows; ++i) maxp = max(maxp, s_pos[i]);
   const int npages = (maxp >> 6) + 1;        // 0 when no valid row
-  const int jb = blockIdx.x * pages_per_split;
-  const int je = min(jb + pages_per_split, npages);
+  // pages_per_split > 0: fixed ranges; otherwise this tile's pages are cut
+  // into gridDim.x equal ranges of at least min_pages (the splits of a
+  // tile then take the same time whatever its length)
+  const int per = pages_per_split > 0
+                      ? pages_per_split
+                      : max(min_pages, (npages + (int)gridDim.x - 1) / (int)gridDim.x);
+  const int jb = blockIdx.x * per;
+  const int je = min(jb + per, npages);
   if (jb >= je) return;
 
   const int32_t* bt = a.block_table + (int64_t)r * a.bt_stride;
@@ -937,25 +976,20 @@ __global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
     const int page = load_uniform(bt, min(jp, last));
     return jp < je ? page : -1;
   };
-  auto page_rsrc = [&](int jp) {
-    const int page = page_id(jp);
-    const bool ok = page >= 0 && (int64_t)page < a.num_pages;
-    bad_page |= jp < je && !ok;
-    return make_rsrc(a.k_cache + (int64_t)(ok ? page : 0) * kPageBytes,
-                     ok ? kPageBytes : 0);
-  };
-  auto fetch = [&](int jp, int buf, int sbuf) {
+  auto fetch = [&](int jp, auto buf_, int sbuf) {
+    constexpr int B = decltype(buf_)::value;
+    auto& keys = *(B ? &s_keys1 : &s_keys0);
 #pragma unroll
     for (int k = 0; k < PP / 2; ++k) {
       const int ph = half + 2 * k;
-      const __amdgpu_buffer_rsrc_t rs = page_rsrc(jp + ph);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (lds_void*)&s_keys[buf][ph][64 * 16 * (wave & 7)], 16, csrc, 0,
-          0, 0);
+      const int page = page_id(jp + ph);
+      const bool ok = page >= 0 && (int64_t)page < a.num_pages;
+      bad_page |= jp + ph < je && !ok;
+      const uint8_t* pg = a.k_cache + (int64_t)(ok ? page : 0) * kPageBytes;
+      const int bytes = ok ? kPageBytes : 0;
+      lds_copy<16>(pg, bytes, &keys[ph][64 * 16 * (wave & 7)], csrc);
       if ((wave & 7) == 0)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (lds_void*)&s_scale[sbuf][ph][0], 4, kPageKeyBytes + 4 * lane,
-            0, 0, 0);
+        lds_copy<4>(pg, bytes, &s_scale[sbuf][ph][0], kPageKeyBytes + 4 * lane);
     }
   };
 
@@ -966,7 +1000,7 @@ __global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
 #pragma unroll
     for (int m = 0; m < MT; ++m) qa[m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
   }
-  fetch(jb, 0, 0);
+  fetch(jb, std::integral_constant<int, 0>(), 0);
 
   // Shared linear part: this wave's qlin pieces to LDS, then the A operand
   // of its group (rows 4 G .. 4 G + 3, G = wave / 4).  The piece scales of
@@ -1024,23 +1058,36 @@ __global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
       const float lv = s_lin[pbuf][wave][kPageTokens * h + tok];
       const float ks = s_scale[psbuf][h][tok];
       const float val = (s <= prow && pok[h]) ? (pt[h] + lv) * ks : -INFINITY;
-      if (prow >= 0 && pj < je) orow[s] = val;
+      // the page's 64 logits as a buffer, empty for a padding row or a page
+      // past the range: an unconditional store, no 64-bit address math
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc(
+          orow + (int64_t)min(pj, npages - 1) * kPageTokens,
+          prow >= 0 && pj < je ? kPageTokens * 4 : 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, 4 * tok,
+                                            0, 0);
     }
   };
 
-  for (int jp = jb, si = 0; jp < je; jp += PP, ++si) {
-    const int buf = si & 1, sbuf = si % 3;
+  // One step: the pages [jp, jp + PP) from key buffer B, the next step's
+  // copy into the other one.  The loop below alternates B = 0, 1 so that
+  // each buffer is a fixed object in each half.
+  auto step = [&](int jp, int si, auto buf_) {
+    constexpr int buf = decltype(buf_)::value;
+    auto& keys = *(buf ? &s_keys1 : &s_keys0);
+    const int sbuf = si % 3;
     const bool more = jp + PP < je;
-    // this wave's copy of the pair has landed in LDS (the direct loads
+    // this wave's copy of the step has landed in LDS (the direct loads
     // count in vmcnt); the barrier then publishes every wave's copy
     __builtin_amdgcn_s_waitcnt(0x0f70);        // vmcnt(0)
     __syncthreads();
     if (LIN && jp != jb) complete();
-    if (more) fetch(jp + PP, buf ^ 1, sbuf == 2 ? 0 : sbuf + 1);
+    if (more)
+      fetch(jp + PP, std::integral_constant<int, buf ^ 1>(),
+            sbuf == 2 ? 0 : sbuf + 1);
 #pragma unroll
     for (int h = 0; h < PP; ++h) {
       const int pj = jp + h;
-      const uint8_t* kb_lds = s_keys[buf][h];
+      const uint8_t* kb_lds = keys[h];
       float v[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
@@ -1086,6 +1133,14 @@ __global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
       }
     }
     if (LIN) { pjp = jp; pbuf = buf; psbuf = sbuf; }
+  };
+  for (int jp = jb, si = 0;;) {
+    step(jp, si, std::integral_constant<int, 0>());
+    jp += PP; ++si;
+    if (jp >= je) break;
+    step(jp, si, std::integral_constant<int, 1>());
+    jp += PP; ++si;
+    if (jp >= je) break;
   }
   if (LIN) {
     __syncthreads();
@@ -1298,13 +1353,16 @@ static hipError_t launch_logits_mt(const LogitsArgs& a, hipStream_t stream,
       pps = (int)std::max<int64_t>(64, (max_pages + splits - 1) / splits);
     }
     const int64_t gx = (max_pages + pps - 1) / pps;
+    // the 16-row kernel re-cuts each tile's own pages into gx equal ranges
+    // unless the split size is forced
+    const int pps16 = o.tile_pages_per_split > 0 ? pps : 0;
     const dim3 g3((unsigned)gx, (unsigned)tiles);
     if (o.logits_kernel == 5)
-      hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL, false, 2>),
-                         g3, dim3(kT16Threads), 0, stream, a, pps);
+      hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL, false, 2>), g3,
+                         dim3(kT16Threads), 0, stream, a, pps16, 64);
     else if (o.logits_kernel != 2 && o.logits_kernel != 3)
-      hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL, true, 2>),
-                         g3, dim3(kT16Threads), 0, stream, a, pps);
+      hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL, true, 2>), g3,
+                         dim3(kT16Threads), 0, stream, a, pps16, 64);
     else if (o.logits_kernel == 3)
       hipLaunchKernelGGL((logits_tile_direct_kernel<MT, FULL>),
                          dim3((unsigned)gx, (unsigned)tiles),
