@@ -467,11 +467,17 @@ struct RegTopkShared {
 };
 
 // Keys held in registers: item s * 4 NT + 4 tid + j of a list in key[s][j]
-// (slice s, j = 0..3), valid when bit j of valid[s] is set.
+// (slice s, j = 0..3, NT = kTopkThreads), valid when that item index is
+// below n (no per-key mask registers).
 template <int S>
 struct RegKeys {
   uint32_t key[S][4];
-  uint32_t valid[S];
+  int n;
+  // written as (per-lane offset) < (uniform bound) so that only 4 *
+  // threadIdx.x + j lives in vector registers
+  __device__ __forceinline__ bool ok(int s, int j) const {
+    return 4 * (int)threadIdx.x + j < n - s * 4 * kTopkThreads;
+  }
 };
 
 // Threshold of the k largest valid keys (k < number of valid keys): a key
@@ -490,7 +496,7 @@ __device__ void reg_threshold(const RegKeys<S>& r, int k,
   for (int s = 0; s < S; ++s)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if ((r.valid[s] >> j) & 1u) atomicAdd(&sh.hist[r.key[s][j] >> 20], 1u);
+      if (r.ok(s, j)) atomicAdd(&sh.hist[r.key[s][j] >> 20], 1u);
   __syncthreads();
   topk_select_bin<kHistBins, NT>(sh.hist, (uint32_t)k, sh);
   const uint32_t d = sh.sel_digit;
@@ -504,7 +510,7 @@ __device__ void reg_threshold(const RegKeys<S>& r, int k,
     for (int s = 0; s < S; ++s)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (((r.valid[s] >> j) & 1u) && (r.key[s][j] >> 20) == d)
+        if (r.ok(s, j) && (r.key[s][j] >> 20) == d)
           atomicAdd(&sh.hist2[(r.key[s][j] >> 8) & 0xfffu], 1u);
     __syncthreads();
     topk_select_bin<kHistBins, NT>(sh.hist2, k_rem, sh);
@@ -517,7 +523,7 @@ __device__ void reg_threshold(const RegKeys<S>& r, int k,
       for (int s = 0; s < S; ++s)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (((r.valid[s] >> j) & 1u) && (r.key[s][j] >> 8) == p24)
+          if (r.ok(s, j) && (r.key[s][j] >> 8) == p24)
             atomicAdd(&sh.hist[r.key[s][j] & 0xffu], 1u);
       __syncthreads();
       topk_select_bin<256, NT>(sh.hist, k2, sh);
@@ -540,21 +546,22 @@ __device__ void reg_emit(const RegKeys<S>& r, int k, uint32_t mask,
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
-  // packed per-slice counts: above in bits 0..15, ties in bits 16..31
-  uint32_t cnt[S], incl[S];
+  // packed per-slice counts: above in bits 0..15, ties in bits 16..31; only
+  // the exclusive prefix within the wave is kept
+  uint32_t excl[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     uint32_t c = 0u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bool ok = (r.valid[s] >> j) & 1u;
+      const bool ok = r.ok(s, j);
       const uint32_t km = r.key[s][j] & mask;
       c += (ok && km > thr) ? 1u : 0u;
       c += (ok && km == thr) ? 0x10000u : 0u;
     }
-    cnt[s] = c;
-    incl[s] = wave_inclusive_scan(c);
-    if (lane == 63) sh.tot[s * NW + wave] = incl[s];
+    const uint32_t incl = wave_inclusive_scan(c);
+    excl[s] = incl - c;
+    if (lane == 63) sh.tot[s * NW + wave] = incl;
   }
   __syncthreads();
   // exclusive scan of the S * NW (slice, wave) totals, in place, by wave 0
@@ -576,15 +583,20 @@ __device__ void reg_emit(const RegKeys<S>& r, int k, uint32_t mask,
     }
   }
   __syncthreads();
+  // 4 tid through an empty asm: the column indices below are then computed
+  // where they are used instead of being hoisted out of a caller's row loop
+  // as S x 4 loop-invariant registers
+  int tid4 = 4 * tid;
+  asm volatile("" : "+v"(tid4));
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    const uint32_t before = sh.tot[s * NW + wave] + incl[s] - cnt[s];
+    const uint32_t before = sh.tot[s * NW + wave] + excl[s];
     uint32_t gt_b = before & 0xffffu, eq_b = before >> 16;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bool ok = (r.valid[s] >> j) & 1u;
+      const bool ok = r.ok(s, j);
       const uint32_t km = r.key[s][j] & mask;
-      const int pos = s * kSlice + 4 * tid + j;
+      const int pos = s * kSlice + tid4 + j;
       // slots are < k by construction; the check keeps a row's writes
       // inside the row whatever the counts
       if (ok && km > thr) {
@@ -615,10 +627,10 @@ __device__ void topk_row_registers(const float* row, int64_t ld, int n, int k,
     sh.hist2[b] = 0u;
   }
   RegKeys<S> r;
+  r.n = n;
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int c0 = s * kSlice + 4 * tid;
-    r.valid[s] = 0u;
     r.key[s][0] = r.key[s][1] = r.key[s][2] = r.key[s][3] = 0u;
     if (s * kSlice < n) {                     // workgroup-uniform
       const float4 v =
@@ -627,8 +639,6 @@ __device__ void topk_row_registers(const float* row, int64_t ld, int n, int k,
       r.key[s][1] = float_to_ordered(v.y);
       r.key[s][2] = float_to_ordered(v.z);
       r.key[s][3] = float_to_ordered(v.w);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) r.valid[s] |= (c0 + j < n ? 1u : 0u) << j;
     }
   }
   __syncthreads();
@@ -648,23 +658,76 @@ constexpr int kRegSlice = 4 * kTopkThreads;     // columns per slice
 constexpr int kRegMaxSlices = 12;
 constexpr int kRegMaxRow = kRegSlice * kRegMaxSlices;   // 49152
 
+// Rows t = blockIdx.x, blockIdx.x + gridDim.x, ...: one workgroup of 1024
+// threads per compute unit (the keys fill the registers), so the loads of a
+// row would otherwise leave HBM idle while the previous row is selected.
+// The next row's keys are loaded into registers before the current row is
+// processed and only converted when its turn comes.
 template <int S>
 __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(
     const float* __restrict__ logits, int64_t ld,
     const int32_t* __restrict__ positions, int k, int32_t* __restrict__ out,
-    int64_t out_ld) {
+    int64_t out_ld, int64_t T) {
   static_assert(S >= 1 && S <= kRegMaxSlices, "slices");
+  constexpr int kSlice = 4 * kTopkThreads;
   __shared__ RegTopkShared<kTopkThreads, S> sh;
-  const int64_t t = blockIdx.x;
-  int32_t* orow = out + t * out_ld;
-  int p = positions[t];
-  if (p >= ld) p = (int)ld - 1;              // logits past ld do not exist
-  const int n = p + 1;                       // p < 0 -> empty row
-  if (n <= k) {
-    topk_row_short<kTopkThreads>(n, k, orow);
-    return;
+  const int tid = threadIdx.x;
+  // n = p + 1 columns (p < 0: empty row; logits past ld do not exist)
+  auto row_len = [&](int64_t t) {
+    return min(load_uniform(positions, t), (int)ld - 1) + 1;
+  };
+  // buffer loads over the row (one offset register for all slices; reads
+  // past the row's n columns return 0 and are masked out anyway)
+  auto issue = [&](int64_t t, int n, float4 (&v)[S]) {
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(logits + t * ld, n > k ? n * 4 : 0);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const auto x =
+          __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * tid, s * kSlice * 4, 0);
+      v[s] = make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]),
+                         __uint_as_float(x[2]), __uint_as_float(x[3]));
+    }
+  };
+  int64_t t = blockIdx.x;
+  if (t >= T) return;
+  int n = row_len(t);
+  float4 cur[S];
+  issue(t, n, cur);
+  for (;;) {
+    const int64_t tn = t + gridDim.x;
+    const int nn = tn < T ? row_len(tn) : 0;
+    float4 nxt[S];
+    issue(tn < T ? tn : t, tn < T ? nn : 0, nxt);
+    int32_t* orow = out + t * out_ld;
+    if (n <= k) {
+      topk_row_short<kTopkThreads>(n, k, orow);
+    } else {
+      for (int b = tid; b < kHistBins; b += kTopkThreads) {
+        sh.hist[b] = 0u;
+        sh.hist2[b] = 0u;
+      }
+      RegKeys<S> r;
+      r.n = n;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        r.key[s][0] = float_to_ordered(cur[s].x);
+        r.key[s][1] = float_to_ordered(cur[s].y);
+        r.key[s][2] = float_to_ordered(cur[s].z);
+        r.key[s][3] = float_to_ordered(cur[s].w);
+      }
+      __syncthreads();
+      uint32_t mask, thr, k_tie;
+      reg_threshold<kTopkThreads, S>(r, k, sh, mask, thr, k_tie);
+      reg_emit<kTopkThreads, S>(r, k, mask, thr, k_tie, orow, sh,
+                                [](int, int, int pos) { return pos; });
+    }
+    if (tn >= T) break;
+    t = tn;
+    n = nn;
+#pragma unroll
+    for (int s = 0; s < S; ++s) cur[s] = nxt[s];
   }
-  topk_row_registers<kTopkThreads, S>(logits + t * ld, ld, n, k, orow, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -1117,9 +1180,9 @@ __global__ __launch_bounds__(kTopkThreads) void ss_sample_kernel(
   const float* row = logits + t * ld;
   const uint32_t stride = (uint32_t)n / kSsSample;     // >= 1
   RegKeys<4> r;
+  r.n = kSsSample;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    r.valid[s] = 0xfu;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t q = (uint32_t)(s * 4 * kTopkThreads + 4 * tid + j);
@@ -1249,10 +1312,10 @@ __global__ __launch_bounds__(kTopkThreads) void ss_select_kernel(
   // gather: item x (list order = column order) lives in chunk q with
   // s_pre[q] <= x < s_pre[q + 1]
   RegKeys<4> r;
+  r.n = (int)total;
   uint32_t col[4][4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    r.valid[s] = 0u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t x = (uint32_t)(s * 4 * kTopkThreads + 4 * tid + j);
@@ -1267,7 +1330,6 @@ __global__ __launch_bounds__(kTopkThreads) void ss_select_kernel(
         const uint2 e = ws.cand[(t * ws.C + lo) * kSsChunkCap + (x - s_pre[lo])];
         r.key[s][j] = e.x;
         col[s][j] = e.y;
-        r.valid[s] |= 1u << j;
       }
     }
   }
@@ -1307,11 +1369,28 @@ static hipError_t launch_topk_single_t(const TopkArgs& a, hipStream_t stream,
   return hipGetLastError();
 }
 
+// Compute units of the current device (queried once per device).
+static int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+            hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <int S>
 static hipError_t launch_topk_reg_t(const TopkArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(topk_reg_kernel<S>, dim3((unsigned)a.T),
+  // one resident workgroup per compute unit; each loops over its rows
+  const int64_t grid = std::min<int64_t>(a.T, device_cu_count());
+  hipLaunchKernelGGL(topk_reg_kernel<S>, dim3((unsigned)grid),
                      dim3(kTopkThreads), 0, stream, a.logits, a.ld,
-                     a.positions, a.k, a.out, a.out_ld);
+                     a.positions, a.k, a.out, a.out_ld, a.T);
   return hipGetLastError();
 }
 
