@@ -588,6 +588,13 @@ __device__ void reg_emit(const RegKeys<S>& r, int k, uint32_t mask,
   // as S x 4 loop-invariant registers
   int tid4 = 4 * tid;
   asm volatile("" : "+v"(tid4));
+  // Branch-free: a key above the threshold, or one of the first k_tie keys
+  // equal to it, goes to slot gt_b + min(eq_b, k_tie) (for a taken tie
+  // eq_b < k_tie, so this is gt_b + eq_b); every key issues a store, and
+  // one not taken is pushed past the end of the row's k-slot buffer and
+  // dropped.  Slots are < k by construction; the buffer bound keeps a
+  // row's writes inside the row whatever the counts.
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(orow, k * 4);
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const uint32_t before = sh.tot[s * NW + wave] + excl[s];
@@ -597,17 +604,15 @@ __device__ void reg_emit(const RegKeys<S>& r, int k, uint32_t mask,
       const bool ok = r.ok(s, j);
       const uint32_t km = r.key[s][j] & mask;
       const int pos = s * kSlice + tid4 + j;
-      // slots are < k by construction; the check keeps a row's writes
-      // inside the row whatever the counts
-      if (ok && km > thr) {
-        const uint32_t slot = gt_b + min(eq_b, k_tie);
-        if (slot < (uint32_t)k) orow[slot] = index_of(s, j, pos);
-        ++gt_b;
-      } else if (ok && km == thr) {
-        if (eq_b < k_tie && gt_b + eq_b < (uint32_t)k)
-          orow[gt_b + eq_b] = index_of(s, j, pos);
-        ++eq_b;
-      }
+      const bool gt = ok && km > thr;
+      const bool eq = ok && km == thr;
+      const bool take = gt || (eq && eq_b < k_tie);
+      const uint32_t slot = gt_b + min(eq_b, k_tie);
+      __builtin_amdgcn_raw_buffer_store_b32((uint32_t)index_of(s, j, pos), ro,
+                                            take ? (int)(4 * slot) : 4 * k, 0,
+                                            0);
+      gt_b += gt ? 1u : 0u;
+      eq_b += eq ? 1u : 0u;
     }
   }
 }
