@@ -464,6 +464,9 @@ struct RegTopkShared {
   uint32_t tot[S * (NT / 64)];                 // packed per (slice, wave)
   uint32_t wave_sum[NT / 64];
   uint32_t sel_digit, sel_above, sel_count;
+  // column bitmaps of the keys above the threshold and of the ties
+  uint32_t selw[S * NT / 8];
+  uint32_t tiew[S * NT / 8];
 };
 
 // Keys held in registers: item s * 4 NT + 4 tid + j of a list in key[s][j]
@@ -617,6 +620,81 @@ __device__ void reg_emit(const RegKeys<S>& r, int k, uint32_t mask,
   }
 }
 
+// The same output for a list whose item index is its column: the selected
+// and tied keys go into column bitmaps (a thread's 4 keys of slice s are the
+// nibble 4 (tid % 8) of word s NT / 8 + tid / 8; 8 lanes OR-combine their
+// nibbles with DPP and one writes the word, so every word of the row is
+// written once, no atomics), one workgroup scan over the words' packed
+// (selected, tie) counts gives every word its first slot, and each lane
+// expands only the set bits of its two words.  Ties are taken lowest column
+// first up to k_tie.
+template <int NT, int S>
+__device__ void reg_emit_columns(const RegKeys<S>& r, int k, uint32_t mask,
+                                 uint32_t thr, uint32_t k_tie, int32_t* orow,
+                                 RegTopkShared<NT, S>& sh) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  auto or8 = [](uint32_t x) {
+    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xf, 0xf, false);
+    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xf, 0xf, false);
+    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xf, 0xf, false);
+    return x;
+  };
+  const int sh4 = 4 * (tid & 7);
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    uint32_t sel = 0u, tie = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = r.ok(s, j);
+      const uint32_t km = r.key[s][j] & mask;
+      sel |= (ok && km > thr) ? (1u << j) : 0u;
+      tie |= (ok && km == thr) ? (1u << j) : 0u;
+    }
+    sel = or8(sel << sh4);
+    tie = or8(tie << sh4);
+    if ((tid & 7) == 0) {
+      sh.selw[s * (NT / 8) + (tid >> 3)] = sel;
+      sh.tiew[s * (NT / 8) + (tid >> 3)] = tie;
+    }
+  }
+  __syncthreads();
+  // thread tid owns words 2 tid, 2 tid + 1 of the row's ceil(n / 32)
+  const int nw = (r.n + 31) >> 5;
+  const int w0 = 2 * tid;
+  uint32_t s0 = 0u, s1 = 0u, t0 = 0u, t1 = 0u;
+  if (w0 < nw) { s0 = sh.selw[w0]; t0 = sh.tiew[w0]; }
+  if (w0 + 1 < nw) { s1 = sh.selw[w0 + 1]; t1 = sh.tiew[w0 + 1]; }
+  const uint32_t c = (uint32_t)(__builtin_popcount(s0) + __builtin_popcount(s1)) |
+                     ((uint32_t)(__builtin_popcount(t0) + __builtin_popcount(t1)) << 16);
+  const uint32_t incl = wave_inclusive_scan(c);
+  if (lane == 63) sh.wave_sum[wave] = incl;
+  __syncthreads();
+  uint32_t before = incl - c;
+  for (int w = 0; w < wave; ++w) before += sh.wave_sum[w];
+  uint32_t gt_b = before & 0xffffu, eq_b = before >> 16;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(orow, k * 4);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t sw = h ? s1 : s0, tw = h ? t1 : t0;
+    uint32_t any = sw | tw;
+    while (any) {
+      const int b = __builtin_ctz(any);
+      any &= any - 1u;
+      const bool is_sel = (sw >> b) & 1u;
+      const bool take = is_sel || eq_b < k_tie;
+      const uint32_t slot = gt_b + min(eq_b, k_tie);
+      __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(32 * (w0 + h) + b), ro,
+                                            take ? (int)(4 * slot) : 4 * k, 0,
+                                            0);
+      gt_b += is_sel ? 1u : 0u;
+      eq_b += is_sel ? 0u : 1u;
+    }
+  }
+}
+
 // Top-k of row[0..n) (k < n <= S * 4 * NT <= ld) into orow[0..k), in
 // ascending column order.  Thread tid holds columns s * 4 NT + 4 tid + j in
 // registers: one 16-byte load per slice, no LDS copy of the row.  `row`
@@ -667,8 +745,11 @@ constexpr int kRegMaxRow = kRegSlice * kRegMaxSlices;   // 49152
 // threads per compute unit (the keys fill the registers), so the loads of a
 // row would otherwise leave HBM idle while the previous row is selected.
 // The next row's keys are loaded into registers before the current row is
-// processed and only converted when its turn comes.
-template <int S>
+// processed and only converted when its turn comes.  BITMAP selects the
+// column-bitmap emit (sparse selections: prefill-length rows) instead of
+// the per-slice scans, whose cost does not grow with the number of keys
+// taken (dense selections: a quarter or more of a decode row).
+template <int S, bool BITMAP>
 __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(
     const float* __restrict__ logits, int64_t ld,
     const int32_t* __restrict__ positions, int k, int32_t* __restrict__ out,
@@ -724,8 +805,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(
       __syncthreads();
       uint32_t mask, thr, k_tie;
       reg_threshold<kTopkThreads, S>(r, k, sh, mask, thr, k_tie);
-      reg_emit<kTopkThreads, S>(r, k, mask, thr, k_tie, orow, sh,
-                                [](int, int, int pos) { return pos; });
+      if (BITMAP)
+        reg_emit_columns<kTopkThreads, S>(r, k, mask, thr, k_tie, orow, sh);
+      else
+        reg_emit<kTopkThreads, S>(r, k, mask, thr, k_tie, orow, sh,
+                                  [](int, int, int pos) { return pos; });
     }
     if (tn >= T) break;
     t = tn;
@@ -1393,9 +1477,15 @@ template <int S>
 static hipError_t launch_topk_reg_t(const TopkArgs& a, hipStream_t stream) {
   // one resident workgroup per compute unit; each loops over its rows
   const int64_t grid = std::min<int64_t>(a.T, device_cu_count());
-  hipLaunchKernelGGL(topk_reg_kernel<S>, dim3((unsigned)grid),
-                     dim3(kTopkThreads), 0, stream, a.logits, a.ld,
-                     a.positions, a.k, a.out, a.out_ld, a.T);
+  // the bitmap emit when the longest rows take fewer than 1/8 of their keys
+  if ((int64_t)a.k * 8 < a.ld)
+    hipLaunchKernelGGL((topk_reg_kernel<S, true>), dim3((unsigned)grid),
+                       dim3(kTopkThreads), 0, stream, a.logits, a.ld,
+                       a.positions, a.k, a.out, a.out_ld, a.T);
+  else
+    hipLaunchKernelGGL((topk_reg_kernel<S, false>), dim3((unsigned)grid),
+                       dim3(kTopkThreads), 0, stream, a.logits, a.ld,
+                       a.positions, a.k, a.out, a.out_ld, a.T);
   return hipGetLastError();
 }
 

@@ -315,6 +315,30 @@ def test_topk_row_lengths(ld, kernel):
                                               f"ld {ld} row {t}")
 
 
+@pytest.mark.parametrize("k", [512, 2048])
+def test_topk_rows_looped_per_workgroup(k):
+    """More rows than compute units: each resident workgroup takes several
+    rows in turn with the next row's keys prefetched, so consecutive rows of
+    one workgroup mix random, tied, constant, short (<= k) and empty rows.
+    k = 512 of 8192 columns takes the column-bitmap emit, k = 2048 the
+    per-slice one."""
+    _say(f"case: top-k, 700 rows looped over resident workgroups, k={k}")
+    T, ld = 700, 8192
+    rng = np.random.default_rng(k)
+    lg = (rng.standard_normal((T, ld)) * 3).astype(np.float32)
+    kind = np.arange(T) % 5
+    lg[kind == 1] = np.round(lg[kind == 1])                 # many ties
+    lg[kind == 2] = 0.75                                    # constant
+    pos = rng.integers(k + 1, ld, size=T).astype(np.int32)
+    pos[kind == 3] = rng.integers(0, k + 1, size=int((kind == 3).sum()))
+    pos[np.arange(T) % 97 == 5] = -1                        # empty rows
+    g = binding.dsa_indexer_topk(torch.from_numpy(lg).cuda(),
+                                 torch.from_numpy(pos).cuda(), k).cpu().numpy()
+    for t in range(T):
+        parity.check_topk_exact_on_gpu_logits(g[t], lg[t], int(pos[t]), k,
+                                              f"looped row {t}")
+
+
 def test_topk_unaligned_logits_rows():
     """A logits pointer that is not 16-byte aligned takes the LDS-cached
     kernel; results are the exact top-k either way."""
