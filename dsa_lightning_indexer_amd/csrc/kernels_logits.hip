@@ -900,7 +900,7 @@ __device__ __forceinline__ void lds_copy(const void* base, int bytes,
                  :: "v"(voff), "s"(d), "s"(m0) : "memory", "m0");
 }
 
-template <int MT, bool FULL, bool LIN, int PP>
+template <int MT, bool FULL, bool LIN, int PP, bool PF>
 __global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
     LogitsArgs a, int pages_per_split, int min_pages) {
   static_assert(PP == 2 || PP == 4, "pages per step");
@@ -1068,6 +1068,16 @@ __global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
     }
   };
 
+  // B operand of N-tile (wq + nt) mod 4 of page h of a step: two contiguous
+  // 1 KB reads (chunk-major layout)
+  auto load_kb = [&](auto& keys, int h, int nt) {
+    const int n = (wq + nt) & 3;
+    const uint8_t* src = &keys[h][0] + 2048 * n + 16 * lane;
+    const uint4 x = *reinterpret_cast<const uint4*>(src);
+    const uint4 y = *reinterpret_cast<const uint4*>(src + 1024);
+    return i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w,
+                 (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+  };
   // One step: the pages [jp, jp + PP) from key buffer B, the next step's
   // copy into the other one.  The loop below alternates B = 0, 1 so that
   // each buffer is a fixed object in each half.
@@ -1084,19 +1094,24 @@ __global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
     if (more)
       fetch(jp + PP, std::integral_constant<int, buf ^ 1>(),
             sbuf == 2 ? 0 : sbuf + 1);
+    i32x8 kb_next;
+    if (PF) kb_next = load_kb(keys, 0, 0);
 #pragma unroll
     for (int h = 0; h < PP; ++h) {
       const int pj = jp + h;
-      const uint8_t* kb_lds = keys[h];
       float v[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const int n = (wq + nt) & 3;
-        const uint8_t* src = kb_lds + 2048 * n + 16 * lane;
-        const uint4 x = *reinterpret_cast<const uint4*>(src);
-        const uint4 y = *reinterpret_cast<const uint4*>(src + 1024);
-        const i32x8 kb = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w,
-                               (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+        // B operand of this N-tile; with PF the next N-tile's is read from
+        // LDS before this one's MFMAs are issued
+        i32x8 kb;
+        if (PF) {
+          kb = kb_next;
+          if (!(h == PP - 1 && nt == 3))
+            kb_next = load_kb(keys, nt == 3 ? h + 1 : h, (nt + 1) & 3);
+        } else {
+          kb = load_kb(keys, h, nt);
+        }
         f32x4 acc[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m)
@@ -1358,10 +1373,10 @@ static hipError_t launch_logits_mt(const LogitsArgs& a, hipStream_t stream,
     const int pps16 = o.tile_pages_per_split > 0 ? pps : 0;
     const dim3 g3((unsigned)gx, (unsigned)tiles);
     if (o.logits_kernel == 5)
-      hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL, false, 2>), g3,
+      hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL, false, 2, false>), g3,
                          dim3(kT16Threads), 0, stream, a, pps16, 64);
     else if (o.logits_kernel != 2 && o.logits_kernel != 3)
-      hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL, true, 2>), g3,
+      hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL, true, 2, true>), g3,
                          dim3(kT16Threads), 0, stream, a, pps16, 64);
     else if (o.logits_kernel == 3)
       hipLaunchKernelGGL((logits_tile_direct_kernel<MT, FULL>),
