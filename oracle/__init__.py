@@ -14,10 +14,12 @@ fp8          OCP FP8 e4m3fn codec written from the bit definition.
 indexer      q quantisation, paged K dequantisation, logits, causal mask,
              exact sort-based top-k, shared-buffer write.
 index_cache  IndexCache F/S layer rule and the layer loop.
+k_write      indexer-K write path: slot mapping, per-token FP8 quantisation
+             of new keys, scatter into 8448-byte pages.
 
 Pins (what each function is checked against, other than itself) are listed in
 each module's docstring.  Functions with no external pin say
 "parity unpinned" there.
 """
 
-from . import fp8, indexer, index_cache  # noqa: F401
+from . import fp8, indexer, index_cache, k_write  # noqa: F401
