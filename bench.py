@@ -439,6 +439,14 @@ def main():
         q8, qsc, ws_in[r], kcs[r], bt, qsl, pos, ld, logits))
     kt = timed(lambda r: binding.dsa_indexer_topk(logits, pos, k, buf, tws))
     kf = timed(forward)
+    # The indexer-K write path (the step before the hot path): the rows'
+    # own tokens as new keys, quantised and stored at their slots of a copy
+    # of the cache.
+    new_k = torch.randn((T, 128), dtype=torch.bfloat16, device=dev)
+    slots = binding.dsa_slot_mapping(bt, qsl, pos)
+    kw_cache = kcs[0].clone()
+    kkw = timed(lambda r: binding.dsa_indexer_k_write(new_k, slots, kw_cache))
+    del kw_cache
     assert binding.dsa_device_error_flags(reset=True) == 0
 
     alg_bytes, flops = logits_work(b)
@@ -470,7 +478,9 @@ def main():
                    "visible_pairs": b.visible_pairs,
                    "kcache_copies_rotated": R},
         "kernels_ms": {"quantize_q": round(kq, 5), "logits": round(kl, 5),
-                       "topk": round(kt, 5), "forward": round(kf, 5)},
+                       "topk": round(kt, 5), "forward": round(kf, 5),
+                       "k_write": round(kkw, 5)},
+        "k_write_gbs": round(T * (2 * 128 + 8 + 132) / (kkw * 1e-3) / 1e9, 1),
         "logits_gbs": round(gbs, 1), "logits_tflops": round(tfl, 2),
         "roofline": roof,
     }

@@ -65,6 +65,8 @@ _SIGNATURES = {
                                  _P, _P, _L, _I, _I, _L, _I, _P, _L, _P, _P,
                                  LAYER_CALLBACK, _P, _P, _S, _P]),
     "dsa_run_workspace_size": (_S, [_L, _I, _L, _I]),
+    "dsa_slot_mapping": (_I, [_P, _L, _P, _I, _P, _L, _P, _P]),
+    "dsa_indexer_k_write": (_I, [_P, _L, _I, _P, _P, _L, _P]),
     "dsa_device_error_flags": (_I, [_I]),
     "dsa_set_option": (_I, [ctypes.c_char_p, _I]),
 }
@@ -286,6 +288,44 @@ def dsa_index_cache_run(layers, block_table, query_start_loc, positions, ld,
             _dev_ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
             _stream(stream, dev)))
     return [bool(skip[i]) for i in range(L)], snaps
+
+
+def dsa_slot_mapping(block_table, query_start_loc, positions, slots=None,
+                     stream=None):
+    """int64 [T] physical slot of every row's token (-1: no page)."""
+    T = positions.shape[0]
+    R = block_table.shape[0]
+    dev = positions.device
+    if query_start_loc.numel() != R + 1:
+        raise ValueError("query_start_loc must have R + 1 entries")
+    if slots is None:
+        slots = torch.empty((T,), dtype=torch.int64, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().dsa_slot_mapping(
+            _dev_ptr(block_table, torch.int32, "block_table"),
+            block_table.shape[1],
+            _dev_ptr(query_start_loc, torch.int32, "query_start_loc"), R,
+            _dev_ptr(positions, torch.int32, "positions"), T,
+            _dev_ptr(slots, torch.int64, "slots"), _stream(stream, dev)))
+    return slots
+
+
+def dsa_indexer_k_write(k_bf16, slot_mapping, k_cache, stream=None):
+    """Quantise bf16 keys [N, 128] and store them at their slots of
+    k_cache (uint8 [num_pages, 8448], modified in place)."""
+    N, D = k_bf16.shape
+    dev = k_bf16.device
+    if k_cache.dim() != 2 or k_cache.shape[1] != PAGE_BYTES:
+        raise ValueError("k_cache must be uint8 [num_pages, 8448]")
+    if slot_mapping.numel() != N:
+        raise ValueError("slot_mapping must have one entry per key")
+    with torch.cuda.device(dev):
+        _check(lib().dsa_indexer_k_write(
+            _dev_ptr(k_bf16, torch.bfloat16, "k_bf16"), N, D,
+            _dev_ptr(slot_mapping, torch.int64, "slot_mapping"),
+            _dev_ptr(k_cache, torch.uint8, "k_cache"), k_cache.shape[0],
+            _stream(stream, dev)))
+    return k_cache
 
 
 def dsa_device_error_flags(reset=True):

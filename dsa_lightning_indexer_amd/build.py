@@ -19,7 +19,8 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libdsa_indexer.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "kernels_logits.hip", "kernels_topk.hip"]
+SOURCES = ["api.cpp", "kernels_logits.hip", "kernels_topk.hip",
+           "kernels_kwrite.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -58,6 +58,13 @@ Options& options();
 hipError_t launch_quantize_q(const uint16_t* q_bf16, int64_t blocks,
                              uint8_t* q8, float* q_scale, hipStream_t stream);
 hipError_t launch_forward(const ForwardArgs& f, hipStream_t stream);
+hipError_t launch_slot_mapping(const int32_t* block_table, int64_t bt_stride,
+                               const int32_t* qsl, int R,
+                               const int32_t* positions, int64_t T,
+                               int64_t* slots, hipStream_t stream);
+hipError_t launch_k_write(const uint16_t* k, int64_t N, const int64_t* slots,
+                          uint8_t* k_cache, int64_t num_pages,
+                          hipStream_t stream);
 hipError_t launch_logits(const LogitsArgs& a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 size_t topk_workspace_bytes(int64_t T, int64_t ld, int k);

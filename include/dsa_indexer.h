@@ -226,6 +226,42 @@ int dsa_index_cache_run(const char* pattern, int freq, int offset,
 size_t dsa_run_workspace_size(int64_t T, int H, int64_t ld, int k);
 
 /*
+ * dsa_slot_mapping -- physical cache slot of every query row's token
+ * ([HBM] 2.3: slot = block_table[r, p / 64] * 64 + p % 64, r the request
+ * of row t from query_start_loc).
+ *   block_table      device, int32 [R, bt_stride].
+ *   query_start_loc  device, int32 [R + 1], non-decreasing.
+ *   positions        device, int32 [T].
+ *   slots            device, out: int64 [T]; -1 where p < 0, p / 64 >=
+ *                    bt_stride or the block-table entry is negative.
+ * The slots are what dsa_indexer_k_write takes.  T == 0 is a no-op.
+ */
+int dsa_slot_mapping(const int32_t* block_table, int64_t bt_stride,
+                     const int32_t* query_start_loc, int R,
+                     const int32_t* positions, int64_t T, int64_t* slots,
+                     void* stream);
+
+/*
+ * dsa_indexer_k_write -- the indexer-K write path: quantise N new keys and
+ * store each at its slot of the paged cache ([KVB] section on the indexer
+ * cache's write path: FP8 key and FP32 scale at the token's in-page
+ * offset; page layout as for dsa_indexer_logits).
+ *   k_bf16        device, bf16 [N, 128], contiguous.
+ *   slot_mapping  device, int64 [N]: slot of token i (page slot / 64, row
+ *                 slot % 64); a negative slot writes nothing (padding).
+ *   k_cache       device, in/out: uint8 [num_pages, 8448].
+ * Per token: amax = max|k|, s = amax / 448 (IEEE fp32 division), code =
+ * e4m3fn(k / s) (IEEE division, round to nearest even, saturating at 448);
+ * an all-zero key stores s = 0 and zero codes.  Key bytes go to page * 8448
+ * + row * 128, the scale to page * 8448 + 8192 + row * 4.  A slot >=
+ * num_pages * 64 writes nothing and raises DSA_DEVERR_PAGE_OUT_OF_RANGE.
+ * Two tokens with the same slot in one call: unspecified which is stored.
+ */
+int dsa_indexer_k_write(const void* k_bf16, int64_t N, int head_dim,
+                        const int64_t* slot_mapping, uint8_t* k_cache,
+                        int64_t num_pages, void* stream);
+
+/*
  * dsa_device_error_flags -- sticky device-side range-error flags
  * (DSA_DEVERR_*) raised since the last reset; synchronises the device.
  * reset != 0 clears them.  Returns the flags, or a negative dsa_status.

@@ -144,6 +144,24 @@ def test_quantize_rejects_bad_arguments():
     assert L.dsa_quantize_q(None, 0, 4, 128, None, None, None) == binding.DSA_OK
 
 
+def test_k_write_and_slot_mapping_reject_bad_arguments():
+    L = binding.lib()
+    assert L.dsa_indexer_k_write(None, 4, 64, None, None, 4, None) == \
+        binding.DSA_ERR_UNSUPPORTED
+    assert L.dsa_indexer_k_write(None, 4, 128, None, None, 4, None) == \
+        binding.DSA_ERR_INVALID_ARG
+    assert L.dsa_indexer_k_write(None, -1, 128, None, None, 4, None) == \
+        binding.DSA_ERR_INVALID_ARG
+    assert L.dsa_indexer_k_write(None, 0, 128, None, None, 4, None) == \
+        binding.DSA_OK
+    assert L.dsa_slot_mapping(None, 4, None, 1, None, 4, None, None) == \
+        binding.DSA_ERR_INVALID_ARG
+    assert L.dsa_slot_mapping(None, 0, None, 1, None, 4, None, None) == \
+        binding.DSA_ERR_INVALID_ARG
+    assert L.dsa_slot_mapping(None, 4, None, 1, None, 0, None, None) == \
+        binding.DSA_OK
+
+
 def _fake_layers(n=3):
     arr = (binding.LayerInputs * n)()
     for i in range(n):
