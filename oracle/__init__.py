@@ -16,10 +16,12 @@ indexer      q quantisation, paged K dequantisation, logits, causal mask,
 index_cache  IndexCache F/S layer rule and the layer loop.
 k_write      indexer-K write path: slot mapping, per-token FP8 quantisation
              of new keys, scatter into 8448-byte pages.
+handoff      sparse-attention hand-off: top-k rows as physical slots and as
+             the additive 0 / -inf score mask.
 
 Pins (what each function is checked against, other than itself) are listed in
 each module's docstring.  Functions with no external pin say
 "parity unpinned" there.
 """
 
-from . import fp8, indexer, index_cache, k_write  # noqa: F401
+from . import fp8, indexer, index_cache, k_write, handoff  # noqa: F401
