@@ -447,6 +447,14 @@ def main():
     kw_cache = kcs[0].clone()
     kkw = timed(lambda r: binding.dsa_indexer_k_write(new_k, slots, kw_cache))
     del kw_cache
+    # The sparse-attention hand-off (the step after the hot path): the top-k
+    # rows as physical slots and as the fp32 0 / -inf score mask.
+    ho_slots = torch.empty((T, k), dtype=torch.int64, device=dev)
+    kho = timed(lambda r: binding.dsa_topk_to_slots(buf, bt, qsl,
+                                                    slots=ho_slots))
+    ho_mask = torch.empty((T, ld), dtype=torch.float32, device=dev)
+    kmask = timed(lambda r: binding.dsa_topk_mask(buf, ld, mask=ho_mask))
+    del ho_mask
     assert binding.dsa_device_error_flags(reset=True) == 0
 
     alg_bytes, flops = logits_work(b)
@@ -479,7 +487,9 @@ def main():
                    "kcache_copies_rotated": R},
         "kernels_ms": {"quantize_q": round(kq, 5), "logits": round(kl, 5),
                        "topk": round(kt, 5), "forward": round(kf, 5),
-                       "k_write": round(kkw, 5)},
+                       "k_write": round(kkw, 5), "topk_to_slots": round(kho, 5),
+                       "topk_mask": round(kmask, 5)},
+        "topk_mask_gbs": round(T * ld * 4 / (kmask * 1e-3) / 1e9, 1),
         "k_write_gbs": round(T * (2 * 128 + 8 + 132) / (kkw * 1e-3) / 1e9, 1),
         "logits_gbs": round(gbs, 1), "logits_tflops": round(tfl, 2),
         "roofline": roof,

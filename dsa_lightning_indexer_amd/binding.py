@@ -67,6 +67,8 @@ _SIGNATURES = {
     "dsa_run_workspace_size": (_S, [_L, _I, _L, _I]),
     "dsa_slot_mapping": (_I, [_P, _L, _P, _I, _P, _L, _P, _P]),
     "dsa_indexer_k_write": (_I, [_P, _L, _I, _P, _P, _L, _P]),
+    "dsa_topk_to_slots": (_I, [_P, _L, _I, _L, _P, _L, _P, _I, _P, _P]),
+    "dsa_topk_mask": (_I, [_P, _L, _I, _L, _P, _L, _P]),
     "dsa_device_error_flags": (_I, [_I]),
     "dsa_set_option": (_I, [ctypes.c_char_p, _I]),
 }
@@ -326,6 +328,39 @@ def dsa_indexer_k_write(k_bf16, slot_mapping, k_cache, stream=None):
             _dev_ptr(k_cache, torch.uint8, "k_cache"), k_cache.shape[0],
             _stream(stream, dev)))
     return k_cache
+
+
+def dsa_topk_to_slots(topk, block_table, query_start_loc, slots=None,
+                      stream=None):
+    """int64 [T, k] physical slot of every top-k entry (-1 stays -1)."""
+    T, k = topk.shape
+    R = block_table.shape[0]
+    dev = topk.device
+    if query_start_loc.numel() != R + 1:
+        raise ValueError("query_start_loc must have R + 1 entries")
+    if slots is None:
+        slots = torch.empty((T, k), dtype=torch.int64, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().dsa_topk_to_slots(
+            _dev_ptr(topk, torch.int32, "topk"), T, k, k,
+            _dev_ptr(block_table, torch.int32, "block_table"),
+            block_table.shape[1],
+            _dev_ptr(query_start_loc, torch.int32, "query_start_loc"), R,
+            _dev_ptr(slots, torch.int64, "slots"), _stream(stream, dev)))
+    return slots
+
+
+def dsa_topk_mask(topk, ld, mask=None, stream=None):
+    """fp32 [T, ld]: 0 at the selected columns, -inf elsewhere."""
+    T, k = topk.shape
+    dev = topk.device
+    if mask is None:
+        mask = torch.empty((T, ld), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().dsa_topk_mask(
+            _dev_ptr(topk, torch.int32, "topk"), T, k, k,
+            _dev_ptr(mask, torch.float32, "mask"), ld, _stream(stream, dev)))
+    return mask
 
 
 def dsa_device_error_flags(reset=True):

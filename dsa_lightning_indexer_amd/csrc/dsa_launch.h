@@ -65,6 +65,13 @@ hipError_t launch_slot_mapping(const int32_t* block_table, int64_t bt_stride,
 hipError_t launch_k_write(const uint16_t* k, int64_t N, const int64_t* slots,
                           uint8_t* k_cache, int64_t num_pages,
                           hipStream_t stream);
+hipError_t launch_topk_to_slots(const int32_t* topk, int64_t T, int k,
+                                int64_t topk_ld, const int32_t* block_table,
+                                int64_t bt_stride, const int32_t* qsl, int R,
+                                int64_t* slots, hipStream_t stream);
+hipError_t launch_topk_mask(const int32_t* topk, int64_t T, int k,
+                            int64_t topk_ld, float* mask, int64_t ld,
+                            hipStream_t stream);
 hipError_t launch_logits(const LogitsArgs& a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 size_t topk_workspace_bytes(int64_t T, int64_t ld, int k);

@@ -262,6 +262,33 @@ int dsa_indexer_k_write(const void* k_bf16, int64_t N, int head_dim,
                         int64_t num_pages, void* stream);
 
 /*
+ * dsa_topk_to_slots -- the sparse-attention hand-off in slot form: every
+ * entry of the top-k rows (logical positions, as dsa_indexer_topk writes
+ * them) as the physical cache slot of that token ([HBM] 2.3: block_table[r,
+ * s / 64] * 64 + s % 64, r the request of the row) -- the slot the write
+ * path stored its key at.
+ *   topk         device, int32 [T, topk_ld], k entries used per row.
+ *   block_table  device, int32 [R, bt_stride]; query_start_loc int32 [R+1].
+ *   slots        device, out: int64 [T, k] (row stride k); -1 for a -1
+ *                entry or an index without a block-table page.
+ */
+int dsa_topk_to_slots(const int32_t* topk, int64_t T, int k, int64_t topk_ld,
+                      const int32_t* block_table, int64_t bt_stride,
+                      const int32_t* query_start_loc, int R, int64_t* slots,
+                      void* stream);
+
+/*
+ * dsa_topk_mask -- the sparse-attention hand-off in mask form ([RFC] 2.1.3,
+ * sparse MLA: a tensor of the score's shape with 0 at the selected tokens
+ * and -inf elsewhere, added to q k^T).
+ *   topk  device, int32 [T, topk_ld], k entries used per row (-1 ignored).
+ *   mask  device, out: fp32 [T, ld], ld % 256 == 0; every column written:
+ *         0 if the row selects it, -inf otherwise.
+ */
+int dsa_topk_mask(const int32_t* topk, int64_t T, int k, int64_t topk_ld,
+                  float* mask, int64_t ld, void* stream);
+
+/*
  * dsa_device_error_flags -- sticky device-side range-error flags
  * (DSA_DEVERR_*) raised since the last reset; synchronises the device.
  * reset != 0 clears them.  Returns the flags, or a negative dsa_status.

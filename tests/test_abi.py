@@ -162,6 +162,22 @@ def test_k_write_and_slot_mapping_reject_bad_arguments():
         binding.DSA_OK
 
 
+def test_handoff_rejects_bad_arguments():
+    L = binding.lib()
+    P = ctypes.c_void_p(0x1000)
+    assert L.dsa_topk_to_slots(P, 4, 8, 4, P, 4, P, 1, P, None) == \
+        binding.DSA_ERR_INVALID_ARG                       # topk_ld < k
+    assert L.dsa_topk_to_slots(None, 4, 8, 8, P, 4, P, 1, P, None) == \
+        binding.DSA_ERR_INVALID_ARG
+    assert L.dsa_topk_to_slots(None, 0, 8, 8, None, 4, None, 1, None,
+                               None) == binding.DSA_OK
+    assert L.dsa_topk_mask(P, 4, 8, 8, P, 100, None) == \
+        binding.DSA_ERR_INVALID_ARG                       # ld % 256
+    assert L.dsa_topk_mask(None, 4, 8, 8, None, 256, None) == \
+        binding.DSA_ERR_INVALID_ARG
+    assert L.dsa_topk_mask(None, 0, 8, 8, None, 256, None) == binding.DSA_OK
+
+
 def _fake_layers(n=3):
     arr = (binding.LayerInputs * n)()
     for i in range(n):
