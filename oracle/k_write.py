@@ -18,7 +18,9 @@ Sources (web pages; cited by title and section):
 * [HBM] "HBM index architecture design" (vLLM research notes), section 2.3
   (virtual-to-physical translation): slot = block_table[req, pos // 64] * 64
   + pos % 64; section 2.5 (scheduler / worker contract) prints the example
-  block row [3, 7, 12].
+  block row [3, 7, 12]; section 5.1 (DeepSeek-V4 main MLA cache): a
+  256-token host block stores 256 // compress_ratio entries (64 at ratio 4,
+  2 at ratio 128); section 5.2: the compressed slot mapping.
 
 Readings where the pages are silent (listed in the design doc):
 * the key arrives as bf16 [N, 128] (the indexer's projection output, like q)
@@ -31,7 +33,9 @@ Readings where the pages are silent (listed in the design doc):
   never produces them).
 
 Pins: tests/test_oracle_k_write.py -- the [HBM] section 2.5 block row and the
-section 2.3 formula on hand positions (golden fixture), byte offsets of a
+section 2.3 formula on hand positions (golden fixture); the compressed
+mapping on hand positions at ratio 4 and 128 (the 5.1 per-block counts) and
+its reduction to the plain mapping at ratio 1; byte offsets of a
 hand-built write against the [KVB] page layout, the e4m3 error bound of the
 round trip, agreement of the codes with torch's float8_e4m3fn cast (a library
 routine), the zero-key and padding-slot cases.
@@ -59,6 +63,31 @@ def slot_mapping(block_table, query_start_loc, positions):
         page = int(bt[req[t], p // PAGE_TOKENS])
         if page >= 0:
             out[t] = page * PAGE_TOKENS + p % PAGE_TOKENS
+    return out
+
+
+def compressed_slot_mapping(block_table, query_start_loc, positions,
+                            compress_ratio, block_size):
+    """Slots of a compressed cache ([HBM] 5.2, DeepSeek-V4 compressed slot
+    mapping): only a token with (p + 1) % ratio == 0 has a slot; it is entry
+    c = p // ratio of its request, stored at block_table[r, c // block_size]
+    * block_size + c % block_size (block_size = entries per storage block,
+    the host block's tokens // ratio, [HBM] 5.1); every other token gets -1.
+    ratio 1 with block_size 64 is ``slot_mapping``."""
+    bt = np.asarray(block_table, dtype=np.int64)
+    pos = np.asarray(positions, dtype=np.int64)
+    req = request_of_rows(query_start_loc, pos.shape[0])
+    out = np.full(pos.shape[0], -1, dtype=np.int64)
+    for t in range(pos.shape[0]):
+        p = int(pos[t])
+        if p < 0 or (p + 1) % compress_ratio != 0:
+            continue
+        c = p // compress_ratio
+        if c // block_size >= bt.shape[1]:
+            continue
+        blk = int(bt[req[t], c // block_size])
+        if blk >= 0:
+            out[t] = blk * block_size + c % block_size
     return out
 
 

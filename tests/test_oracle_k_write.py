@@ -104,3 +104,32 @@ def test_written_cache_feeds_the_logits_definition():
     got = oi.gather_k(cache, bt[0], 0, L)
     assert np.array_equal(got, fp8.decode(codes) * s.astype(np.float64)[:, None])
     assert PAGE_KEY_BYTES == 8192
+
+
+def test_compressed_slot_mapping_by_hand():
+    """[HBM] 5.1/5.2: at ratio 4 a 256-token host block stores 64 entries
+    (block_size 64), at ratio 128 two; only (p + 1) % ratio == 0 has a slot,
+    entry p // ratio, -1 elsewhere."""
+    bt = np.array([[3, 7, 12]], dtype=np.int32)
+    qsl = np.array([0, 9], dtype=np.int32)
+    pos = np.array([0, 2, 3, 7, 255, 256, 259, 511, 767], dtype=np.int32)
+    got = k_write.compressed_slot_mapping(bt, qsl, pos, 4, 256 // 4)
+    # entries 0, 1, 63, 64 (block 1), 127 (block 1 row 63), 191 (block 2)
+    assert list(got) == [-1, -1, 3 * 64 + 0, 3 * 64 + 1, 3 * 64 + 63, -1,
+                         7 * 64 + 0, 7 * 64 + 63, 12 * 64 + 63]
+    got = k_write.compressed_slot_mapping(bt, qsl, pos, 128, 256 // 128)
+    # entries: p = 255 -> 1 (block 0 row 1); 511 -> 3 (block 1 row 1);
+    # 767 -> 5 (block 2 row 1)
+    assert list(got) == [-1, -1, -1, -1, 3 * 2 + 1, -1, -1, 7 * 2 + 1,
+                         12 * 2 + 1]
+
+
+def test_compressed_slot_mapping_ratio_one_is_plain():
+    rng = np.random.default_rng(6)
+    bt = rng.permutation(50).astype(np.int32)[:40].reshape(4, 10)
+    bt[3, 5:] = -1
+    qsl = np.array([0, 30, 30, 70, 100], dtype=np.int32)
+    pos = rng.integers(-1, 700, size=100).astype(np.int32)
+    assert np.array_equal(
+        k_write.compressed_slot_mapping(bt, qsl, pos, 1, PAGE_TOKENS),
+        k_write.slot_mapping(bt, qsl, pos))
