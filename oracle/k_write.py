@@ -30,12 +30,15 @@ Readings where the pages are silent (listed in the design doc):
   matters for its own division);
 * slot -1 (a padding token) writes nothing;
 * two tokens with the same slot in one call are not defined (the write path
-  never produces them).
+  never produces them);
+* compressed cache: a row sees the entries whose tokens all lie at or before
+  its position (compressed_positions).
 
 Pins: tests/test_oracle_k_write.py -- the [HBM] section 2.5 block row and the
 section 2.3 formula on hand positions (golden fixture); the compressed
 mapping on hand positions at ratio 4 and 128 (the 5.1 per-block counts) and
-its reduction to the plain mapping at ratio 1; byte offsets of a
+its reduction to the plain mapping at ratio 1; the compressed positions
+against a brute-force count of fully covered entries; byte offsets of a
 hand-built write against the [KVB] page layout, the e4m3 error bound of the
 round trip, agreement of the codes with torch's float8_e4m3fn cast (a library
 routine), the zero-key and padding-slot cases.
@@ -89,6 +92,16 @@ def compressed_slot_mapping(block_table, query_start_loc, positions,
         if blk >= 0:
             out[t] = blk * block_size + c % block_size
     return out
+
+
+def compressed_positions(positions, compress_ratio):
+    """Reading (the pages give no causal rule for compressed entries): a row
+    at position p sees entry c when every token it covers, c * ratio ..
+    c * ratio + ratio - 1, is at or before p; its position in the compressed
+    cache is the last such c, (p + 1) // ratio - 1 (-1: none, or p < 0)."""
+    pos = np.asarray(positions, dtype=np.int64)
+    out = np.where(pos >= 0, (pos + 1) // compress_ratio - 1, -1)
+    return out.astype(np.int64)
 
 
 def quantize_k(k):

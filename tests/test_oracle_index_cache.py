@@ -97,3 +97,57 @@ def test_run_s_layers_reuse_previous_full_layer():
             assert np.array_equal(snaps[l], snaps[last_full])
     # distinct layers really give distinct selections
     assert not np.array_equal(snaps[0], snaps[3])
+
+
+def test_mtp_draft_step_switch():
+    """[IC] 5 item 3 and [KVB] engineering judgement item 4: an MTP layer
+    computes at draft step 0 whatever the switch and the pattern; at a later
+    step it reuses only with the switch on; trunk layers ignore both."""
+    kw = dict(pattern="F" + "S" * 60, num_hidden_layers=61)
+    for step in (0, 1, 2):
+        for reuse in (False, True):
+            m = index_cache.skip_mask(63, mtp_draft_step=step, mtp_reuse=reuse,
+                                      **kw)
+            assert m[1:61].all() and not m[0]          # trunk unchanged
+            assert list(m[61:]) == [reuse and step > 0] * 2
+    # an MTP-only pass (layer ids 61, 62) starting at layer 61
+    m = index_cache.skip_mask(2, first_layer=61, mtp_draft_step=1,
+                              mtp_reuse=True, **kw)
+    assert m.tolist() == [True, True]
+    assert index_cache.skip_mask(2, first_layer=61, **kw).tolist() == \
+        [False, False]
+    # without MTP layers the switch changes nothing
+    assert not index_cache.skip_mask(61, freq=1, mtp_draft_step=3,
+                                     mtp_reuse=True).any()
+    with pytest.raises(ValueError):
+        index_cache.is_skip(61, num_hidden_layers=61, mtp_draft_step=-1)
+
+
+def test_mtp_reuse_pass_keeps_draft_step0_rows():
+    """Draft step 0 over the MTP layer computes and writes the buffer; a
+    later step with the switch on starts with an S layer (allowed only
+    there) and leaves step 0's rows; with the switch off it recomputes."""
+    rng = np.random.Generator(np.random.PCG64(5))
+    b = synth.build_batch(rng, [150, 80], [[149], [79]], H=4, k=8)
+    lay = [{"q": b.q_f32, "weights": b.weights, "k_cache": b.k_cache}]
+    buf0 = np.full((3, 8), 77, np.int32)
+    args = (b.block_table, b.query_start_loc, b.positions, b.ld, 8)
+    kw = dict(num_hidden_layers=4, first_layer=4)
+    m0, B0, _ = index_cache.run(lay, *args, buf0, mtp_draft_step=0,
+                                mtp_reuse=True, **kw)
+    assert m0.tolist() == [False]
+    codes, sc = indexer.quantize_q(b.q_f32)
+    lg = indexer.indexer_logits(codes, sc, b.weights, b.k_cache,
+                                b.block_table, b.query_start_loc,
+                                b.positions, b.ld)
+    assert np.array_equal(B0[:2], indexer.indexer_topk(lg, b.positions, 8))
+    m1, B1, _ = index_cache.run([None], *args, B0, mtp_draft_step=1,
+                                mtp_reuse=True, **kw)
+    assert m1.tolist() == [True] and np.array_equal(B1, B0)
+    m2, B2, _ = index_cache.run(lay, *args, buf0, mtp_draft_step=1,
+                                mtp_reuse=False, **kw)
+    assert m2.tolist() == [False] and np.array_equal(B2, B0)
+    # a trunk pass may still not start with S
+    with pytest.raises(ValueError):
+        index_cache.run([None], *args, buf0, pattern="SF",
+                        num_hidden_layers=4, mtp_draft_step=1, mtp_reuse=True)

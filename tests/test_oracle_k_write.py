@@ -133,3 +133,19 @@ def test_compressed_slot_mapping_ratio_one_is_plain():
     assert np.array_equal(
         k_write.compressed_slot_mapping(bt, qsl, pos, 1, PAGE_TOKENS),
         k_write.slot_mapping(bt, qsl, pos))
+
+
+def test_compressed_positions_brute_force():
+    """The last entry all of whose ratio tokens are at or before p, by
+    enumeration of entries."""
+    for ratio in (1, 2, 3, 4, 128):
+        pos = np.arange(-1, 700)
+        got = k_write.compressed_positions(pos, ratio)
+        for p, g in zip(pos, got):
+            seen = [c for c in range(800)
+                    if c * ratio + ratio - 1 <= p] if p >= 0 else []
+            assert g == (max(seen) if seen else -1), (ratio, p)
+    # a boundary token's slot holds exactly the row's last visible entry
+    pos = np.array([3, 7, 11, 255], dtype=np.int32)
+    assert list(k_write.compressed_positions(pos, 4)) == \
+        [int(p) // 4 for p in pos]
