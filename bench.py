@@ -444,6 +444,12 @@ def main():
     # of the cache.
     new_k = torch.randn((T, 128), dtype=torch.bfloat16, device=dev)
     slots = binding.dsa_slot_mapping(bt, qsl, pos)
+    # DeepSeek-V4 compressed variant (ratio 4, 64-entry storage blocks): the
+    # same rows' slots and compressed positions.
+    c_slots = torch.empty((T,), dtype=torch.int64, device=dev)
+    c_pos = torch.empty((T,), dtype=torch.int32, device=dev)
+    kcs_map = timed(lambda r: binding.dsa_compressed_slot_mapping(
+        bt, qsl, pos, 4, 64, slots=c_slots, positions_c=c_pos))
     kw_cache = kcs[0].clone()
     kkw = timed(lambda r: binding.dsa_indexer_k_write(new_k, slots, kw_cache))
     del kw_cache
@@ -488,7 +494,8 @@ def main():
         "kernels_ms": {"quantize_q": round(kq, 5), "logits": round(kl, 5),
                        "topk": round(kt, 5), "forward": round(kf, 5),
                        "k_write": round(kkw, 5), "topk_to_slots": round(kho, 5),
-                       "topk_mask": round(kmask, 5)},
+                       "topk_mask": round(kmask, 5),
+                       "compressed_slot_mapping": round(kcs_map, 5)},
         "topk_mask_gbs": round(T * ld * 4 / (kmask * 1e-3) / 1e9, 1),
         "k_write_gbs": round(T * (2 * 128 + 8 + 132) / (kkw * 1e-3) / 1e9, 1),
         "logits_gbs": round(gbs, 1), "logits_tflops": round(tfl, 2),

@@ -60,12 +60,16 @@ _SIGNATURES = {
     "dsa_indexer_forward": (_I, [_P, _P, _P, _L, _P, _L, _P, _P, _L, _I, _I,
                                  _I, _I, _P, _L, _I, _P, _L, _P, _S, _P]),
     "dsa_forward_workspace_size": (_S, [_L, _I, _L, _I]),
-    "dsa_index_cache_mask": (_I, [ctypes.c_char_p, _I, _I, _I, _I, _P]),
-    "dsa_index_cache_run": (_I, [ctypes.c_char_p, _I, _I, _I, _I, _P, _P, _L,
+    "dsa_index_cache_mask": (_I, [ctypes.c_char_p, _I, _I, _I, _I, _I, _I,
+                                  _I, _P]),
+    "dsa_index_cache_run": (_I, [ctypes.c_char_p, _I, _I, _I, _I, _I, _I, _I,
+                                 _P, _P, _L,
                                  _P, _P, _L, _I, _I, _L, _I, _P, _L, _P, _P,
                                  LAYER_CALLBACK, _P, _P, _S, _P]),
     "dsa_run_workspace_size": (_S, [_L, _I, _L, _I]),
     "dsa_slot_mapping": (_I, [_P, _L, _P, _I, _P, _L, _P, _P]),
+    "dsa_compressed_slot_mapping": (_I, [_P, _L, _P, _I, _P, _L, _I, _I, _P,
+                                         _P, _P]),
     "dsa_indexer_k_write": (_I, [_P, _L, _I, _P, _P, _L, _P]),
     "dsa_topk_to_slots": (_I, [_P, _L, _I, _L, _P, _L, _P, _I, _P, _P]),
     "dsa_topk_mask": (_I, [_P, _L, _I, _L, _P, _L, _P]),
@@ -225,12 +229,16 @@ def dsa_indexer_forward(q_bf16, weights, k_cache, block_table,
 
 
 def dsa_index_cache_mask(num_layers, pattern=None, freq=1, offset=2,
-                         num_hidden_layers=-1):
-    """IndexCache F/S mask (host): list of bools, True = S (reuse)."""
+                         num_hidden_layers=-1, first_layer=0,
+                         mtp_draft_step=0, mtp_reuse=False):
+    """IndexCache F/S mask (host) of layer ids first_layer ..
+    first_layer + num_layers - 1: list of bools, True = S (reuse)."""
     buf = (ctypes.c_uint8 * max(num_layers, 1))()
     pat = pattern.encode() if pattern is not None else None
-    _check(lib().dsa_index_cache_mask(pat, freq, offset, num_layers,
-                                      num_hidden_layers, buf))
+    _check(lib().dsa_index_cache_mask(pat, freq, offset, first_layer,
+                                      num_layers, num_hidden_layers,
+                                      mtp_draft_step, int(bool(mtp_reuse)),
+                                      buf))
     return [bool(buf[i]) for i in range(num_layers)]
 
 
@@ -241,8 +249,9 @@ def dsa_run_workspace_size(T, H, ld, k):
 def dsa_index_cache_run(layers, block_table, query_start_loc, positions, ld,
                         k, topk_buffer, pattern=None, freq=1, offset=2,
                         num_hidden_layers=-1, H=None, snapshots=False,
-                        callback=None, workspace=None, stream=None):
-    """One forward pass over ``len(layers)`` DSA layers.
+                        callback=None, workspace=None, stream=None,
+                        first_layer=0, mtp_draft_step=0, mtp_reuse=False):
+    """One forward pass over ``len(layers)`` DSA layers (ids first_layer ..).
 
     ``layers[l]`` is a dict with ``q_bf16`` (bf16 [T, H, 128]), ``weights``
     (fp32 [T, H]) and ``k_cache`` (uint8 [pages, 8448]) for F layers, or None
@@ -256,7 +265,7 @@ def dsa_index_cache_run(layers, block_table, query_start_loc, positions, ld,
     if topk_buffer.dim() != 2 or topk_buffer.shape[1] != k:
         raise ValueError("topk_buffer must be int32 [buffer_rows, k]")
     if H is None:
-        H = next(l["q_bf16"].shape[1] for l in layers if l is not None)
+        H = next((l["q_bf16"].shape[1] for l in layers if l is not None), 1)
     arr = (LayerInputs * max(L, 1))()
     for i, lay in enumerate(layers):
         if lay is None:
@@ -278,7 +287,8 @@ def dsa_index_cache_run(layers, block_table, query_start_loc, positions, ld,
     pat = pattern.encode() if pattern is not None else None
     with torch.cuda.device(dev):
         _check(lib().dsa_index_cache_run(
-            pat, freq, offset, L, num_hidden_layers, arr,
+            pat, freq, offset, first_layer, L, num_hidden_layers,
+            mtp_draft_step, int(bool(mtp_reuse)), arr,
             _dev_ptr(block_table, torch.int32, "block_table"),
             block_table.shape[1],
             _dev_ptr(query_start_loc, torch.int32, "query_start_loc"),
@@ -310,6 +320,34 @@ def dsa_slot_mapping(block_table, query_start_loc, positions, slots=None,
             _dev_ptr(positions, torch.int32, "positions"), T,
             _dev_ptr(slots, torch.int64, "slots"), _stream(stream, dev)))
     return slots
+
+
+def dsa_compressed_slot_mapping(block_table, query_start_loc, positions,
+                                compress_ratio, block_size, slots=None,
+                                positions_c=None, want_positions_c=True,
+                                stream=None):
+    """(int64 [T] compressed-cache slots, -1 off the ratio boundary;
+    int32 [T] compressed positions or None)."""
+    T = positions.shape[0]
+    R = block_table.shape[0]
+    dev = positions.device
+    if query_start_loc.numel() != R + 1:
+        raise ValueError("query_start_loc must have R + 1 entries")
+    if slots is None:
+        slots = torch.empty((T,), dtype=torch.int64, device=dev)
+    if positions_c is None and want_positions_c:
+        positions_c = torch.empty((T,), dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().dsa_compressed_slot_mapping(
+            _dev_ptr(block_table, torch.int32, "block_table"),
+            block_table.shape[1],
+            _dev_ptr(query_start_loc, torch.int32, "query_start_loc"), R,
+            _dev_ptr(positions, torch.int32, "positions"), T,
+            int(compress_ratio), int(block_size),
+            _dev_ptr(slots, torch.int64, "slots"),
+            _dev_ptr(positions_c, torch.int32, "positions_c"),
+            _stream(stream, dev)))
+    return slots, positions_c
 
 
 def dsa_indexer_k_write(k_bf16, slot_mapping, k_cache, stream=None):

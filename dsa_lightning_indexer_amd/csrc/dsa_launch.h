@@ -62,6 +62,10 @@ hipError_t launch_slot_mapping(const int32_t* block_table, int64_t bt_stride,
                                const int32_t* qsl, int R,
                                const int32_t* positions, int64_t T,
                                int64_t* slots, hipStream_t stream);
+hipError_t launch_compressed_slot_mapping(
+    const int32_t* block_table, int64_t bt_stride, const int32_t* qsl, int R,
+    const int32_t* positions, int64_t T, int ratio, int block_size,
+    int64_t* slots, int32_t* positions_c, hipStream_t stream);
 hipError_t launch_k_write(const uint16_t* k, int64_t N, const int64_t* slots,
                           uint8_t* k_cache, int64_t num_pages,
                           hipStream_t stream);

@@ -3,7 +3,8 @@
 // quantisation of its key scattered into the paged cache.
 //
 // Slot (vLLM HBM-index notes, section 2.3): token of request r at position p
-// lives at slot block_table[r, p / 64] * 64 + p % 64.  Write (GLM-5.3
+// lives at slot block_table[r, p / 64] * 64 + p % 64; the compressed
+// variant of a DeepSeek-V4 cache is described at its kernel.  Write (GLM-5.3
 // indexer-cache article, section on the indexer cache's write path, and the
 // page layout of its eviction section): a token's 128 e4m3fn key bytes go to
 // page slot / 64 at row slot % 64, its fp32 scale to byte 8192 + 4 * row of
@@ -31,6 +32,33 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(
     if (page >= 0) slot = (int64_t)page * kPageTokens + p % kPageTokens;
   }
   slots[t] = slot;
+}
+
+// Compressed slots (vLLM HBM-index notes, sections 5.1-5.2, DeepSeek-V4):
+// a token at position p has a slot only when (p + 1) % ratio == 0; it is
+// entry c = p / ratio of its request, stored at block_table[r, c / bs] * bs
+// + c % bs with bs the entries per storage block (host block / ratio); any
+// other token gets -1.  Optionally also the last entry a row can see, the
+// row's position in the compressed cache: (p + 1) / ratio - 1 (-1 for p < 0).
+__global__ __launch_bounds__(256) void compressed_slot_mapping_kernel(
+    const int32_t* __restrict__ block_table, int64_t bt_stride,
+    const int32_t* __restrict__ qsl, int R,
+    const int32_t* __restrict__ positions, int64_t T, int ratio, int bs,
+    int64_t* __restrict__ slots, int32_t* __restrict__ positions_c) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  const int p = positions[t];
+  int64_t slot = -1;
+  if (p >= 0 && (p + 1) % ratio == 0) {
+    const int c = p / ratio;
+    if ((int64_t)(c / bs) < bt_stride) {
+      const int r = request_of_row(qsl, R, t);
+      const int blk = block_table[(int64_t)r * bt_stride + c / bs];
+      if (blk >= 0) slot = (int64_t)blk * bs + c % bs;
+    }
+  }
+  slots[t] = slot;
+  if (positions_c) positions_c[t] = p >= 0 ? (p + 1) / ratio - 1 : -1;
 }
 
 // 16 lanes per token, 8 bf16 values per lane (one 16-byte load):
@@ -91,6 +119,18 @@ hipError_t launch_slot_mapping(const int32_t* block_table, int64_t bt_stride,
   hipLaunchKernelGGL(slot_mapping_kernel, dim3((unsigned)grid), dim3(256), 0,
                      stream, block_table, bt_stride, qsl, R, positions, T,
                      slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_compressed_slot_mapping(
+    const int32_t* block_table, int64_t bt_stride, const int32_t* qsl, int R,
+    const int32_t* positions, int64_t T, int ratio, int block_size,
+    int64_t* slots, int32_t* positions_c, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  const int64_t grid = (T + 255) / 256;
+  hipLaunchKernelGGL(compressed_slot_mapping_kernel, dim3((unsigned)grid),
+                     dim3(256), 0, stream, block_table, bt_stride, qsl, R,
+                     positions, T, ratio, block_size, slots, positions_c);
   return hipGetLastError();
 }
 

@@ -173,15 +173,26 @@ size_t dsa_forward_workspace_size(int64_t T, int H, int64_t ld, int k);
  *                      freq when non-NULL; layers past its end are F.
  *   freq               index_topk_freq >= 1 (1 = every layer computes).
  *   offset             index_skip_topk_offset (the pages' default is 2).
- *   num_hidden_layers  layers >= this are MTP/nextn layers: always F; a
- *                      negative value means there are none.
+ *   first_layer        layer id of is_skip[0] (0 for a trunk pass; the
+ *                      first MTP layer's id for a draft pass), >= 0.
+ *   num_hidden_layers  layers >= this are MTP/nextn layers; a negative
+ *                      value means there are none.
+ *   mtp_draft_step     draft step of the pass (0 = the step that computes).
+ *   mtp_reuse          nonzero when index_share_for_mtp_iteration is on and
+ *                      each draft position has one token (eagle topk 1;
+ *                      [KVB] engineering judgement, item 4).
  *   is_skip            host, out: uint8 [num_layers], 1 = S (reuse), 0 = F.
- * Without a pattern: S iff max(layer - offset + 1, 0) % freq != 0.
- * A pattern character other than 'F' or 'S' is an error.
+ * Layer l = first_layer + i.  An MTP layer is S iff mtp_reuse and
+ * mtp_draft_step > 0 ([IC] 5 item 3: full indexer, computes at draft step
+ * 0, the runtime switch turns on reuse).  Otherwise, with a pattern: S iff
+ * l < strlen(pattern) and pattern[l] == 'S'; without: S iff max(l - offset
+ * + 1, 0) % freq != 0.  A pattern character other than 'F' or 'S' is an
+ * error.
  */
 int dsa_index_cache_mask(const char* pattern, int freq, int offset,
-                         int num_layers, int num_hidden_layers,
-                         uint8_t* is_skip);
+                         int first_layer, int num_layers,
+                         int num_hidden_layers, int mtp_draft_step,
+                         int mtp_reuse, uint8_t* is_skip);
 
 /* Per-layer inputs of dsa_index_cache_run (ignored for S layers). */
 typedef struct {
@@ -191,8 +202,9 @@ typedef struct {
   int64_t num_pages;
 } dsa_layer_inputs;
 
-/* Called on the calling thread after layer `layer`'s work is enqueued on the
- * stream (work the callback enqueues on the same stream runs after it). */
+/* Called on the calling thread after the work of layer id `layer`
+ * (first_layer + its index) is enqueued on the stream (work the callback
+ * enqueues on the same stream runs after it). */
 typedef void (*dsa_layer_callback)(int layer, int is_full,
                                    int32_t* topk_buffer, void* user);
 
@@ -200,20 +212,25 @@ typedef void (*dsa_layer_callback)(int layer, int is_full,
  * dsa_index_cache_run -- one forward pass over a stack of DSA layers ([IC] 2).
  * F layers quantise q, score and write the top-k of rows [0, T) into
  * topk_buffer (int32 [buffer_rows, k], device); S layers enqueue nothing and
- * leave the buffer as the previous F layer wrote it.  Layer l's inputs are
- * layers[l] (host array of num_layers entries); block_table,
- * query_start_loc and positions (device) are shared by all layers.
- *   snapshots    device, nullable: int32 [num_layers, T, k]; after layer l
- *                rows [0, T) of the buffer are copied to snapshots[l].
+ * leave the buffer as the previous F layer wrote it.  layers[i] (host array
+ * of num_layers entries) holds the inputs of layer id first_layer + i;
+ * block_table, query_start_loc and positions (device) are shared by all
+ * layers.  pattern .. mtp_reuse: the rule of dsa_index_cache_mask.
+ *   snapshots    device, nullable: int32 [num_layers, T, k]; after layer i
+ *                rows [0, T) of the buffer are copied to snapshots[i].
  *   is_skip_out  host, nullable: uint8 [num_layers], the mask used.
  *   cb, cb_user  nullable per-layer callback.
  *   workspace    device, dsa_run_workspace_size(T, H, ld, k) bytes.
- * Rejects (DSA_ERR_INVALID_ARG) a mask whose first layer is S: it would read
- * a buffer no layer has written in this pass ([IC] 5.3).
+ * Rejects (DSA_ERR_INVALID_ARG) a mask whose first layer is S ([IC] 5.3:
+ * it would read a buffer no layer has written in this pass), except in an
+ * MTP draft pass that reuses (first_layer >= num_hidden_layers >= 0,
+ * mtp_reuse, mtp_draft_step > 0): the buffer then holds the rows that draft
+ * step 0 wrote, which the caller keeps between the passes.
  */
 int dsa_index_cache_run(const char* pattern, int freq, int offset,
-                        int num_layers, int num_hidden_layers,
-                        const dsa_layer_inputs* layers,
+                        int first_layer, int num_layers,
+                        int num_hidden_layers, int mtp_draft_step,
+                        int mtp_reuse, const dsa_layer_inputs* layers,
                         const int32_t* block_table, int64_t bt_stride,
                         const int32_t* query_start_loc,
                         const int32_t* positions, int64_t T, int R, int H,
@@ -240,6 +257,35 @@ int dsa_slot_mapping(const int32_t* block_table, int64_t bt_stride,
                      const int32_t* query_start_loc, int R,
                      const int32_t* positions, int64_t T, int64_t* slots,
                      void* stream);
+
+/*
+ * dsa_compressed_slot_mapping -- slots of a compressed cache ([HBM] 5.1,
+ * 5.2, DeepSeek-V4): only a token whose position p has (p + 1) %
+ * compress_ratio == 0 gets a slot; it is entry c = p / compress_ratio of its
+ * request, stored at block_table[r, c / block_size] * block_size + c %
+ * block_size.  block_size is the entries per storage block, the host
+ * block's tokens / compress_ratio (256 / 4 = 64: the 64-entry, 8448-byte
+ * page of dsa_indexer_k_write and dsa_indexer_logits).
+ *   block_table, query_start_loc, positions  as for dsa_slot_mapping.
+ *   slots        device, out: int64 [T]; -1 for a non-boundary token, p <
+ *                0, c / block_size >= bt_stride or a negative entry.
+ *   positions_c  device, out, nullable: int32 [T], the row's position in
+ *                the compressed cache, (p + 1) / compress_ratio - 1 (the
+ *                last entry whose tokens are all at or before p; -1 when
+ *                none is, or p < 0) -- the positions dsa_indexer_logits
+ *                and dsa_indexer_topk take over a compressed cache (a row
+ *                with -1 sees no entry and is left out of those calls:
+ *                the logits kernel flags a negative position).
+ * compress_ratio 1 with block_size 64 equals dsa_slot_mapping.  Rejects
+ * compress_ratio < 1 or block_size < 1.  T == 0 is a no-op.
+ */
+int dsa_compressed_slot_mapping(const int32_t* block_table,
+                                int64_t bt_stride,
+                                const int32_t* query_start_loc, int R,
+                                const int32_t* positions, int64_t T,
+                                int compress_ratio, int block_size,
+                                int64_t* slots, int32_t* positions_c,
+                                void* stream);
 
 /*
  * dsa_indexer_k_write -- the indexer-K write path: quantise N new keys and

@@ -81,11 +81,16 @@ def test_mask_matches_oracle_on_many_configs():
         pat = None
         if rng.random() < 0.4:
             pat = "".join(rng.choice(["F", "S"], size=int(rng.integers(0, 90))))
-        ours = binding.dsa_index_cache_mask(L, pattern=pat, freq=freq,
-                                            offset=off,
-                                            num_hidden_layers=-1 if nh is None else nh)
+        first = int(rng.integers(0, 70)) if rng.random() < 0.3 else 0
+        step = int(rng.integers(0, 3))
+        reuse = bool(rng.random() < 0.5)
+        ours = binding.dsa_index_cache_mask(
+            L, pattern=pat, freq=freq, offset=off,
+            num_hidden_layers=-1 if nh is None else nh, first_layer=first,
+            mtp_draft_step=step, mtp_reuse=reuse)
         ref = index_cache.skip_mask(L, pattern=pat, freq=freq, offset=off,
-                                    num_hidden_layers=nh)
+                                    num_hidden_layers=nh, first_layer=first,
+                                    mtp_draft_step=step, mtp_reuse=reuse)
         assert ours == ref.tolist()
 
 
@@ -162,6 +167,22 @@ def test_k_write_and_slot_mapping_reject_bad_arguments():
         binding.DSA_OK
 
 
+def test_compressed_slot_mapping_rejects_bad_arguments():
+    L = binding.lib()
+    P = ctypes.c_void_p(0x1000)
+    f = L.dsa_compressed_slot_mapping
+    assert f(P, 4, P, 1, P, 4, 0, 64, P, None, None) == \
+        binding.DSA_ERR_INVALID_ARG                       # ratio < 1
+    assert f(P, 4, P, 1, P, 4, 4, 0, P, None, None) == \
+        binding.DSA_ERR_INVALID_ARG                       # block_size < 1
+    assert f(P, 0, P, 1, P, 4, 4, 64, P, None, None) == \
+        binding.DSA_ERR_INVALID_ARG                       # bt_stride < 1
+    assert f(None, 4, P, 1, P, 4, 4, 64, P, None, None) == \
+        binding.DSA_ERR_INVALID_ARG                       # null pointer
+    assert f(None, 4, None, 1, None, 0, 4, 64, None, None, None) == \
+        binding.DSA_OK                                    # T == 0
+
+
 def test_handoff_rejects_bad_arguments():
     L = binding.lib()
     P = ctypes.c_void_p(0x1000)
@@ -186,8 +207,8 @@ def _fake_layers(n=3):
 
 
 def _run_call(**over):
-    args = dict(pattern=None, freq=1, offset=2, L=3, nh=-1,
-                layers=_fake_layers(),
+    args = dict(pattern=None, freq=1, offset=2, first=0, L=3, nh=-1,
+                step=0, reuse=0, layers=_fake_layers(),
                 bt=ctypes.c_void_p(0x1000), bt_stride=4,
                 qsl=ctypes.c_void_p(0x1000), pos=ctypes.c_void_p(0x1000),
                 T=4, R=1, H=4, ld=256, k=8, buf=ctypes.c_void_p(0x1000),
@@ -202,6 +223,23 @@ def test_run_rejects_first_layer_s():
     assert _run_call(pattern=b"SFF") == binding.DSA_ERR_INVALID_ARG
     assert b"layer 0" in binding.lib().dsa_last_error()
     assert _run_call(freq=2, offset=0) == binding.DSA_ERR_INVALID_ARG
+
+
+def test_run_mtp_reuse_pass_may_start_with_s():
+    """An MTP draft pass at step > 0 with the reuse switch is all S and is
+    accepted (no layer input is read); the same pass at step 0, or a trunk
+    pass, with S first is still refused."""
+    skip = (ctypes.c_uint8 * 2)()
+    none = (binding.LayerInputs * 2)()
+    assert _run_call(first=61, L=2, nh=61, step=1, reuse=1, layers=none,
+                     skip=skip) == binding.DSA_OK
+    assert list(skip) == [1, 1]
+    assert _run_call(first=61, L=2, nh=61, step=0, reuse=1, layers=none) == \
+        binding.DSA_ERR_INVALID_ARG                      # F with null inputs
+    assert _run_call(pattern=b"SF", nh=61, step=1, reuse=1, L=2,
+                     layers=_fake_layers(2)) == binding.DSA_ERR_INVALID_ARG
+    assert _run_call(first=-1) == binding.DSA_ERR_INVALID_ARG
+    assert _run_call(step=-1) == binding.DSA_ERR_INVALID_ARG
 
 
 def test_run_rejects_bad_arguments():
