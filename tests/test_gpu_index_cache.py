@@ -117,6 +117,52 @@ def test_index_cache_run_reduced(cfg):
     assert binding.dsa_device_error_flags(reset=True) == 0
 
 
+def test_mtp_draft_passes():
+    """A trunk pass (4 layers, freq 2), then MTP draft passes over the one
+    MTP layer (id 4) through the C ABI: step 0 computes (the oracle's
+    top-k of that layer), step 1 with the reuse switch is all S and keeps
+    step 0's rows bit-exactly, step 1 without it recomputes the same rows."""
+    _say("case: MTP draft passes (trunk freq 2, one MTP layer)")
+    nh, R, context, H, k = 4, 4, 2000, 16, 128
+    trunk_mask = binding.dsa_index_cache_mask(nh, freq=2, offset=1,
+                                              num_hidden_layers=nh)
+    full = [l for l in range(nh) if not trunk_mask[l]] + [nh]
+    batches, ref = _stack(full, R, context, H, k, seed=8)
+    dev = _dev_layers(batches, nh + 1)
+    geo = (torch.from_numpy(ref.block_table).cuda(),
+           torch.from_numpy(ref.query_start_loc).cuda(),
+           torch.from_numpy(ref.positions).cuda(), ref.ld, k)
+    buf = torch.full((R, k), 5, dtype=torch.int32, device="cuda")
+    skip, _ = binding.dsa_index_cache_run(dev[:nh], *geo, buf, freq=2,
+                                          offset=1, num_hidden_layers=nh)
+    assert skip == trunk_mask
+    calls = []
+    skip0, _ = binding.dsa_index_cache_run(
+        dev[nh:], *geo, buf, num_hidden_layers=nh, first_layer=nh,
+        mtp_draft_step=0, mtp_reuse=True,
+        callback=lambda layer, is_full: calls.append((layer, is_full)))
+    torch.cuda.synchronize()
+    assert skip0 == [False] and calls == [(nh, True)]
+    step0 = buf.cpu().numpy().copy()
+    b = batches[nh]
+    ora = parity.oracle_logits(b)
+    for t in range(b.T):
+        p = int(b.positions[t])
+        parity.check_topk_row(step0[t], ora[t, : p + 1], k, f"mtp row {t}")
+    skip1, _ = binding.dsa_index_cache_run(
+        [None], *geo, buf, num_hidden_layers=nh, first_layer=nh,
+        mtp_draft_step=1, mtp_reuse=True, H=H)
+    torch.cuda.synchronize()
+    assert skip1 == [True] and np.array_equal(buf.cpu().numpy(), step0)
+    buf.fill_(5)
+    skip2, _ = binding.dsa_index_cache_run(
+        dev[nh:], *geo, buf, num_hidden_layers=nh, first_layer=nh,
+        mtp_draft_step=1, mtp_reuse=False)
+    torch.cuda.synchronize()
+    assert skip2 == [False] and np.array_equal(buf.cpu().numpy(), step0)
+    assert binding.dsa_device_error_flags(reset=True) == 0
+
+
 def test_index_cache_run_full_size_freq4():
     _say("case: index cache full size (61 layers, 32 x 16384, freq 4)")
     L = 61
