@@ -18,10 +18,11 @@ k_write      indexer-K write path: slot mapping, per-token FP8 quantisation
              of new keys, scatter into 8448-byte pages.
 handoff      sparse-attention hand-off: top-k rows as physical slots and as
              the additive 0 / -inf score mask.
+chunking     logits budget and the forward pass over row chunks.
 
 Pins (what each function is checked against, other than itself) are listed in
 each module's docstring.  Functions with no external pin say
 "parity unpinned" there.
 """
 
-from . import fp8, indexer, index_cache, k_write, handoff  # noqa: F401
+from . import fp8, indexer, index_cache, k_write, handoff, chunking  # noqa: F401

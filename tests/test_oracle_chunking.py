@@ -1,0 +1,80 @@
+"""Pins for the oracle's logits budget and row chunking (CPU only), against
+the figures of the GLM-5.3 article's SGLang logits-budget section
+(tests/golden/logits_budget_example.json) and the rule's invariants."""
+
+import numpy as np
+import pytest
+
+from dsa_lightning_indexer_amd import synth
+from oracle import chunking, indexer
+
+
+def test_printed_figures(golden):
+    g = golden("logits_budget_example.json")
+    assert chunking.BYTES_PER_ELEM == g["bytes_per_elem"]
+    assert chunking.STATIC_SKIP_ELEMS == g["static_skip_elems"]
+    assert chunking.TOTAL_MEM_FRACTION == g["total_mem_fraction"]
+    assert chunking.ROW_ALIGN_ELEMS * 4 == g["row_stride_bytes"]
+    assert g["context_1m"] * chunking.BYTES_PER_ELEM == g["row_bytes_1m"]
+    assert g["row_bytes_1m"] == 4 << 20                          # "4MB"
+    assert g["prefill_rows_32k"] * g["row_bytes_1m"] == \
+        g["prefill_bytes_32k_by_1m"] == 128 << 30                  # "128GB"
+    assert g["mtp_row_factor"] == g["mtp_draft_tokens"] + 1
+    assert g["mtp_row_factor"] * g["row_bytes_1m"] == \
+        g["mtp_row_bytes_1m_per_request"] == 24 << 20              # "24MB"
+    assert abs(g["static_skip_elems"] * 4 - g["static_skip_bytes_about"]) \
+        < 1e6                                                      # "~32MB"
+
+
+def test_budget_cases():
+    G = 288 * 10**9
+    assert chunking.budget_bytes(G) == int(G * 0.3)
+    # a static fraction leaves less than 30 % outside it: that part rules
+    assert chunking.budget_bytes(G, 0.85) == int(G * (1 - 0.85)) < G * 0.3
+    assert chunking.budget_bytes(G, 0.5) == int(G * 0.3)        # cap rules
+    assert chunking.budget_bytes(G, 0.5, 0.2) == int(int(G * 0.5) * 0.2)
+    assert chunking.budget_bytes(G, 1.2) == 1                   # at least 1
+    assert chunking.budget_bytes(0) == 1
+
+
+def test_chunk_rows_rule(golden):
+    g = golden("logits_budget_example.json")
+    ld = g["context_1m"]
+    budget = chunking.budget_bytes(288 * 10**9)
+    # 32K prefill rows over 1M columns: over the budget, cut to what fits
+    r = chunking.chunk_rows(g["prefill_rows_32k"], ld, budget)
+    assert r == budget // g["row_bytes_1m"] and r * g["row_bytes_1m"] <= budget
+    assert (r + 1) * g["row_bytes_1m"] > budget
+    # under the static threshold: never cut, whatever the budget
+    assert chunking.chunk_rows(7, 1 << 20, 1) == 7              # 7.3M elems
+    assert chunking.chunk_rows(8, 1 << 20, 1) == 1              # 8.4M elems
+    # within the budget: one piece
+    assert chunking.chunk_rows(64, 8192, 64 * 8192 * 4) == 64
+    assert chunking.chunk_rows(0, 256, 10) == 0
+    # one row larger than the budget still makes progress
+    assert chunking.chunk_rows(100, 1 << 24, 1000) == 1
+
+
+@pytest.mark.parametrize("T,rows", [(1, 1), (10, 3), (64, 64), (65, 16),
+                                    (100, 1)])
+def test_pieces_cover_rows_once(T, rows):
+    p = chunking.pieces(T, rows)
+    flat = [i for a, b in p for i in range(a, b)]
+    assert flat == list(range(T))
+    assert all(0 < b - a <= rows for a, b in p)
+
+
+def test_chunked_forward_equals_unchunked():
+    """Rows are independent: every piece size gives the unchunked top-k."""
+    rng = np.random.Generator(np.random.PCG64(3))
+    b = synth.build_batch(rng, [300, 150], [[299, 200, 17], [149, 3]], H=4,
+                          k=16)
+    codes, s = indexer.quantize_q(b.q_f32)
+    lg = indexer.indexer_logits(codes, s, b.weights, b.k_cache, b.block_table,
+                                b.query_start_loc, b.positions, b.ld)
+    want = indexer.indexer_topk(lg, b.positions, 16)
+    for rows in (1, 2, 4, 5):
+        got = chunking.forward_chunked(b.q_f32, b.weights, b.k_cache,
+                                       b.block_table, b.query_start_loc,
+                                       b.positions, b.ld, 16, rows)
+        assert np.array_equal(got, want), rows
