@@ -439,6 +439,18 @@ def main():
         q8, qsc, ws_in[r], kcs[r], bt, qsl, pos, ld, logits))
     kt = timed(lambda r: binding.dsa_indexer_topk(logits, pos, k, buf, tws))
     kf = timed(forward)
+    # Row-chunked forward under a 256 MiB logits budget (the prefill chunk's
+    # 1.34 GB of logits become 6 chunks of 1638 rows; decode and the 1M
+    # tail fit in one chunk).
+    ch_budget = 256 << 20
+    ch_rows = binding.dsa_logits_chunk_rows(T, ld, ch_budget)
+    ch_ws = torch.empty(max(1, binding.dsa_forward_chunked_workspace_size(
+        T, b.R, H, ld, k, ch_rows)), dtype=torch.uint8, device=dev)
+    ch_out = torch.empty((T, k), dtype=torch.int32, device=dev)
+    kch = timed(lambda r: binding.dsa_indexer_forward_chunked(
+        qs_in[r], ws_in[r], kcs[r], bt, qsl, pos, ld, k,
+        rows_per_chunk=ch_rows, out=ch_out, workspace=ch_ws))
+    del ch_ws
     # The indexer-K write path (the step before the hot path): the rows'
     # own tokens as new keys, quantised and stored at their slots of a copy
     # of the cache.
@@ -495,7 +507,9 @@ def main():
                        "topk": round(kt, 5), "forward": round(kf, 5),
                        "k_write": round(kkw, 5), "topk_to_slots": round(kho, 5),
                        "topk_mask": round(kmask, 5),
-                       "compressed_slot_mapping": round(kcs_map, 5)},
+                       "compressed_slot_mapping": round(kcs_map, 5),
+                       "forward_chunked_256MiB": round(kch, 5)},
+        "chunked_rows_per_chunk": int(ch_rows),
         "topk_mask_gbs": round(T * ld * 4 / (kmask * 1e-3) / 1e9, 1),
         "k_write_gbs": round(T * (2 * 128 + 8 + 132) / (kkw * 1e-3) / 1e9, 1),
         "logits_gbs": round(gbs, 1), "logits_tflops": round(tfl, 2),

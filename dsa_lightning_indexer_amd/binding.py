@@ -60,6 +60,12 @@ _SIGNATURES = {
     "dsa_indexer_forward": (_I, [_P, _P, _P, _L, _P, _L, _P, _P, _L, _I, _I,
                                  _I, _I, _P, _L, _I, _P, _L, _P, _S, _P]),
     "dsa_forward_workspace_size": (_S, [_L, _I, _L, _I]),
+    "dsa_logits_budget_bytes": (_S, [_S, ctypes.c_double, ctypes.c_double]),
+    "dsa_logits_chunk_rows": (_L, [_L, _L, _S]),
+    "dsa_indexer_forward_chunked": (_I, [_P, _P, _P, _L, _P, _L, _P, _P, _L,
+                                         _I, _I, _I, _I, _L, _I, _P, _L, _L,
+                                         _P, _S, _P]),
+    "dsa_forward_chunked_workspace_size": (_S, [_L, _I, _I, _L, _I, _L]),
     "dsa_index_cache_mask": (_I, [ctypes.c_char_p, _I, _I, _I, _I, _I, _I,
                                   _I, _P]),
     "dsa_index_cache_run": (_I, [ctypes.c_char_p, _I, _I, _I, _I, _I, _I, _I,
@@ -226,6 +232,64 @@ def dsa_indexer_forward(q_bf16, weights, k_cache, block_table,
             out.shape[1], _dev_ptr(workspace, torch.uint8, "workspace"),
             workspace.numel(), _stream(stream, dev)))
     return logits, out
+
+
+def dsa_logits_budget_bytes(total_mem, mem_fraction_static=None,
+                            free_mem_fraction=1.0):
+    return lib().dsa_logits_budget_bytes(
+        int(total_mem),
+        -1.0 if mem_fraction_static is None else float(mem_fraction_static),
+        float(free_mem_fraction))
+
+
+def dsa_logits_chunk_rows(T, ld, budget_bytes):
+    return lib().dsa_logits_chunk_rows(T, ld, int(budget_bytes))
+
+
+def dsa_forward_chunked_workspace_size(T, R, H, ld, k, rows_per_chunk):
+    return lib().dsa_forward_chunked_workspace_size(T, R, H, ld, k,
+                                                    rows_per_chunk)
+
+
+def dsa_indexer_forward_chunked(q_bf16, weights, k_cache, block_table,
+                                query_start_loc, positions, ld, k,
+                                rows_per_chunk=None, budget_bytes=None,
+                                out=None, workspace=None, stream=None):
+    """The forward pass over row chunks that share one logits buffer of
+    ``rows_per_chunk`` rows (default: the rows ``budget_bytes`` allows, and
+    the budget defaults to 30 % of the device's memory).  Returns the top-k
+    int32 [T, k]."""
+    T, H, D = q_bf16.shape
+    R = block_table.shape[0]
+    dev = q_bf16.device
+    if out is None:
+        out = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if k_cache.dim() != 2 or k_cache.shape[1] != PAGE_BYTES:
+        raise ValueError("k_cache must be uint8 [num_pages, 8448]")
+    if query_start_loc.numel() != R + 1:
+        raise ValueError("query_start_loc must have R + 1 entries")
+    if rows_per_chunk is None:
+        if budget_bytes is None:
+            total = torch.cuda.get_device_properties(dev).total_memory
+            budget_bytes = dsa_logits_budget_bytes(total)
+        rows_per_chunk = max(1, dsa_logits_chunk_rows(T, ld, budget_bytes))
+    need = dsa_forward_chunked_workspace_size(T, R, H, ld, k, rows_per_chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().dsa_indexer_forward_chunked(
+            _dev_ptr(q_bf16, torch.bfloat16, "q_bf16"),
+            _dev_ptr(weights, torch.float32, "weights"),
+            _dev_ptr(k_cache, torch.uint8, "k_cache"), k_cache.shape[0],
+            _dev_ptr(block_table, torch.int32, "block_table"),
+            block_table.shape[1],
+            _dev_ptr(query_start_loc, torch.int32, "query_start_loc"),
+            _dev_ptr(positions, torch.int32, "positions"), T, R, H, D,
+            PAGE_TOKENS, ld, k, _dev_ptr(out, torch.int32, "out"),
+            out.shape[1], rows_per_chunk,
+            _dev_ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+            _stream(stream, dev)))
+    return out
 
 
 def dsa_index_cache_mask(num_layers, pattern=None, freq=1, offset=2,

@@ -76,7 +76,30 @@ hipError_t launch_topk_to_slots(const int32_t* topk, int64_t T, int k,
 hipError_t launch_topk_mask(const int32_t* topk, int64_t T, int k,
                             int64_t topk_ld, float* mask, int64_t ld,
                             hipStream_t stream);
-hipError_t launch_logits(const LogitsArgs& a, hipStream_t stream);
+// Logits kernel class.  Every class computes each (row, token) logit with
+// one fixed sequence of operations, so a row's logits depend on its class
+// only, not on which other rows share the launch.
+enum class LogitsPlan {
+  Auto,      // logits_plan(T, R) of this launch
+  Balanced,  // decode: pages dealt out evenly over waves (T <= 128)
+  Rowwise,   // one row per workgroup column
+  Tiled,     // 16-row tiles of one request through LDS
+};
+LogitsPlan logits_plan(int64_t T, int R);
+int device_cu_count();            // compute units of the current device
+hipError_t launch_logits(const LogitsArgs& a, hipStream_t stream,
+                         LogitsPlan plan = LogitsPlan::Auto);
+// The forward pass over row chunks [a, a + rows) that reuse one logits
+// buffer: q quantised once, then per chunk query_start_loc rebased into
+// qsl_chunk, logits of the chunk's rows (the class of the whole batch) and
+// their top-k into rows a.. of the output.
+struct ChunkedForwardArgs {
+  ForwardArgs f;                // whole batch; f.lg.logits / f.tk.* = chunk
+  int64_t rows;                 // rows per chunk (>= 1)
+  int32_t* qsl_chunk;           // [R + 1] scratch
+};
+hipError_t launch_forward_chunked(const ChunkedForwardArgs& c,
+                                  hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 size_t topk_workspace_bytes(int64_t T, int64_t ld, int k);
 hipError_t read_error_flags(unsigned* flags, bool reset);

@@ -1313,11 +1313,23 @@ hipError_t launch_quantize_q(const uint16_t* q_bf16, int64_t blocks,
   return hipGetLastError();
 }
 
+LogitsPlan logits_plan(int64_t T, int R) {
+  const Options& o = options();
+  bool tiled = T > 2 * (int64_t)R;
+  if (o.logits_kernel == 1 || o.logits_kernel == 4) tiled = false;
+  if (o.logits_kernel == 2 || o.logits_kernel == 3 || o.logits_kernel == 5)
+    tiled = true;
+  if (tiled) return LogitsPlan::Tiled;
+  return T <= kBalancedMaxRows && o.logits_kernel != 4 ? LogitsPlan::Balanced
+                                                       : LogitsPlan::Rowwise;
+}
+
 template <int MT, bool FULL>
 static hipError_t launch_logits_mt(const LogitsArgs& a, hipStream_t stream,
-                                   bool tiled, int64_t max_pages) {
+                                   LogitsPlan plan, int64_t max_pages) {
   const Options& o = options();
-  if (!tiled && a.T <= kBalancedMaxRows && o.logits_kernel != 4) {
+  const bool tiled = plan == LogitsPlan::Tiled;
+  if (plan == LogitsPlan::Balanced && a.T <= kBalancedMaxRows) {
     // D pages per wave; enough waves that a batch whose rows all reach
     // max_pages still gets about D pages per wave
     int D = o.row_pages_per_wave;
@@ -1366,6 +1378,20 @@ static hipError_t launch_logits_mt(const LogitsArgs& a, hipStream_t stream,
       // noticeable start (tile lookup, q fragments, first page pair); the
       // 1M-token tail (one tile) measured best at 64 (256 workgroups)
       pps = (int)std::max<int64_t>(64, (max_pages + splits - 1) / splits);
+      // One 16-wave workgroup fills a compute unit, so the grid runs in
+      // rounds of `cus` workgroups and a last round that is barely used
+      // costs a whole round (a 103-tile launch with 10 splits is 4 rounds
+      // and 6 workgroups).  Among 1/2 .. 1 times the splits chosen above,
+      // take the one with the fewest rounds per unit of work, the nearest
+      // to that choice on a tie.
+      const int64_t g0 = (max_pages + pps - 1) / pps;
+      const int64_t cus = device_cu_count();
+      int64_t best = g0, br = (g0 * real_tiles + cus - 1) / cus;
+      for (int64_t g = g0 - 1; g >= (g0 + 1) / 2; --g) {
+        const int64_t r = (g * real_tiles + cus - 1) / cus;
+        if (r * best < br * g) { best = g; br = r; }   // r / g < br / best
+      }
+      if (best != g0) pps = (int)((max_pages + best - 1) / best);
     }
     const int64_t gx = (max_pages + pps - 1) / pps;
     // the 16-row kernel re-cuts each tile's own pages into gx equal ranges
@@ -1390,26 +1416,23 @@ static hipError_t launch_logits_mt(const LogitsArgs& a, hipStream_t stream,
   return hipGetLastError();
 }
 
-hipError_t launch_logits(const LogitsArgs& a, hipStream_t stream) {
+hipError_t launch_logits(const LogitsArgs& a, hipStream_t stream,
+                         LogitsPlan plan) {
   if (a.T <= 0) return hipSuccess;
   const int64_t max_pages = std::min<int64_t>(a.bt_stride, a.ld / kPageTokens);
-  const Options& o = options();
-  bool tiled = a.T > 2 * (int64_t)a.R;
-  if (o.logits_kernel == 1 || o.logits_kernel == 4) tiled = false;
-  if (o.logits_kernel == 2 || o.logits_kernel == 3 || o.logits_kernel == 5)
-    tiled = true;
+  if (plan == LogitsPlan::Auto) plan = logits_plan(a.T, a.R);
   switch (a.H) {
-    case 16: return launch_logits_mt<1, true>(a, stream, tiled, max_pages);
-    case 32: return launch_logits_mt<2, true>(a, stream, tiled, max_pages);
-    case 48: return launch_logits_mt<3, true>(a, stream, tiled, max_pages);
-    case 64: return launch_logits_mt<4, true>(a, stream, tiled, max_pages);
+    case 16: return launch_logits_mt<1, true>(a, stream, plan, max_pages);
+    case 32: return launch_logits_mt<2, true>(a, stream, plan, max_pages);
+    case 48: return launch_logits_mt<3, true>(a, stream, plan, max_pages);
+    case 64: return launch_logits_mt<4, true>(a, stream, plan, max_pages);
     default: break;
   }
   switch ((a.H + 15) / 16) {
-    case 1: return launch_logits_mt<1, false>(a, stream, tiled, max_pages);
-    case 2: return launch_logits_mt<2, false>(a, stream, tiled, max_pages);
-    case 3: return launch_logits_mt<3, false>(a, stream, tiled, max_pages);
-    default: return launch_logits_mt<4, false>(a, stream, tiled, max_pages);
+    case 1: return launch_logits_mt<1, false>(a, stream, plan, max_pages);
+    case 2: return launch_logits_mt<2, false>(a, stream, plan, max_pages);
+    case 3: return launch_logits_mt<3, false>(a, stream, plan, max_pages);
+    default: return launch_logits_mt<4, false>(a, stream, plan, max_pages);
   }
 }
 

@@ -1459,7 +1459,7 @@ static hipError_t launch_topk_single_t(const TopkArgs& a, hipStream_t stream,
 }
 
 // Compute units of the current device (queried once per device).
-static int device_cu_count() {
+int device_cu_count() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

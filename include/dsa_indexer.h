@@ -168,6 +168,54 @@ int dsa_indexer_forward(const void* q_bf16, const float* weights,
 size_t dsa_forward_workspace_size(int64_t T, int H, int64_t ld, int k);
 
 /*
+ * dsa_logits_budget_bytes -- the logits memory budget ([KVB] section on
+ * SGLang's logits budget): 30 % of the device's total_mem bytes; when a
+ * static memory fraction is set (mem_fraction_static >= 0; pass a negative
+ * value for none), the smaller of that and free_mem_fraction of the memory
+ * outside the static part.  At least 1.  Host only.
+ */
+size_t dsa_logits_budget_bytes(size_t total_mem, double mem_fraction_static,
+                               double free_mem_fraction);
+
+/*
+ * dsa_logits_chunk_rows -- query rows per scoring pass under a logits
+ * budget ([KVB], same section): all T rows when T * ld fp32 elements are
+ * under 8,000,000 or fit budget_bytes; otherwise budget_bytes / (ld * 4)
+ * rows, at least 1.  0 for T <= 0.  Host only.
+ */
+int64_t dsa_logits_chunk_rows(int64_t T, int64_t ld, size_t budget_bytes);
+
+/*
+ * dsa_indexer_forward_chunked -- the forward pass with its logits bounded
+ * by a budget ([KVB], SGLang logits budget: over the budget the query rows
+ * are cut into pieces, each scored and ranked on its own, and the results
+ * put together).  Arguments as for dsa_indexer_forward, except:
+ *   (no logits argument) the logits of one chunk live in the workspace;
+ *   rows_per_chunk  >= 1 (dsa_logits_chunk_rows gives the budget's);
+ *   workspace       device, dsa_forward_chunked_workspace_size(T, R, H, ld,
+ *                   k, rows_per_chunk) bytes: q codes and scales of all rows,
+ *                   logits of rows_per_chunk rows, the chunk's rebased
+ *                   query_start_loc, top-k scratch.
+ * q is quantised once; then for each chunk [a, a + n) one small kernel
+ * rebases query_start_loc to the chunk's rows, the logits of the chunk's
+ * rows are scored into the workspace with the kernel class the whole batch
+ * would use, and their top-k is written to out rows a .. a + n - 1.  out
+ * equals dsa_indexer_forward's bit for bit, whatever rows_per_chunk.
+ */
+int dsa_indexer_forward_chunked(const void* q_bf16, const float* weights,
+                                const uint8_t* k_cache, int64_t num_pages,
+                                const int32_t* block_table, int64_t bt_stride,
+                                const int32_t* query_start_loc,
+                                const int32_t* positions, int64_t T, int R,
+                                int H, int head_dim, int page_size, int64_t ld,
+                                int k, int32_t* out, int64_t out_ld,
+                                int64_t rows_per_chunk, void* workspace,
+                                size_t ws_bytes, void* stream);
+
+size_t dsa_forward_chunked_workspace_size(int64_t T, int R, int H, int64_t ld,
+                                          int k, int64_t rows_per_chunk);
+
+/*
  * dsa_index_cache_mask -- IndexCache layer rule ([IC] 3, 4, 5.3), host only.
  *   pattern            host, nullable: one 'F'/'S' per DSA layer; overrides
  *                      freq when non-NULL; layers past its end are F.

@@ -273,3 +273,44 @@ def test_set_option_roundtrip():
     assert binding.dsa_set_option("logits_kernel", prev) == 2
     with pytest.raises(binding.DsaError):
         binding.dsa_set_option("no_such_knob", 1)
+
+
+def test_logits_budget_and_chunk_rows_match_oracle():
+    from oracle import chunking
+    import numpy as np
+    rng = np.random.default_rng(12)
+    for total in (0, 1, 10**9, 288 * 10**9, 2**40 + 7):
+        for mfs in (None, 0.0, 0.5, 0.85, 1.0, 1.5):
+            for free in (1.0, 0.25):
+                assert binding.dsa_logits_budget_bytes(total, mfs, free) == \
+                    chunking.budget_bytes(total, mfs, free), (total, mfs, free)
+    for _ in range(2000):
+        T = int(rng.integers(0, 70000))
+        ld = 256 * int(rng.integers(1, 5000))
+        budget = int(rng.integers(1, 1 << 36))
+        assert binding.dsa_logits_chunk_rows(T, ld, budget) == \
+            chunking.chunk_rows(T, ld, budget), (T, ld, budget)
+
+
+def test_forward_chunked_rejects_bad_arguments():
+    L = binding.lib()
+    P = ctypes.c_void_p(0x1000)
+    base = dict(q=P, w=P, kc=P, npg=4, bt=P, bts=4, qsl=P, pos=P, T=4, R=1,
+                H=16, D=128, ps=64, ld=256, k=8, out=P, out_ld=8, rows=2,
+                ws=P, ws_bytes=1 << 30, stream=None)
+
+    def call(**over):
+        a = dict(base)
+        a.update(over)
+        return L.dsa_indexer_forward_chunked(*a.values())
+    assert call(rows=0) == binding.DSA_ERR_INVALID_ARG
+    assert call(k=0) == binding.DSA_ERR_INVALID_ARG
+    assert call(out_ld=4) == binding.DSA_ERR_INVALID_ARG
+    assert call(ld=300) == binding.DSA_ERR_INVALID_ARG
+    assert call(D=64) == binding.DSA_ERR_UNSUPPORTED
+    assert call(ws_bytes=16) == binding.DSA_ERR_WORKSPACE
+    assert call(out=None) == binding.DSA_ERR_INVALID_ARG
+    assert call(T=0, ws=None, ws_bytes=0) == binding.DSA_OK
+    need = binding.dsa_forward_chunked_workspace_size(4, 1, 16, 256, 8, 2)
+    assert need >= 4 * 16 * 132 + 2 * 256 * 4 + 8
+    assert binding.dsa_forward_chunked_workspace_size(4, 1, 16, 256, 8, 0) == 0
