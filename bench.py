@@ -214,13 +214,17 @@ def _csv_rows(directory, suffix):
 
 
 def _per_dispatch(rows):
-    """{dispatch id: (kernel name, summed counter value in KiB)}"""
-    out = {}
+    """{dispatch id: (kernel name, summed counter value in KiB)}; only the
+    dispatches at the largest grid of their kernel name are kept (the
+    workload's own launch: the chunked leg launches the same kernels on
+    smaller grids)."""
+    out, grid = {}, {}
     for r in rows:
         key = r["Dispatch_Id"]
-        name, v = out.get(key, (r["Kernel_Name"], 0.0))
-        out[key] = (name, v + float(r["Counter_Value"]))
-    return out
+        name, v, g = out.get(key, (r["Kernel_Name"], 0.0, int(r["Grid_Size"])))
+        out[key] = (name, v + float(r["Counter_Value"]), g)
+        grid[name] = max(grid.get(name, 0), g)
+    return {k: (n, v) for k, (n, v, g) in out.items() if g == grid[n]}
 
 
 def _matcher(config):
@@ -286,10 +290,15 @@ def pmc_summary(args):
 def trace_summary(args):
     stats = _csv_rows(args.trace_summary, "kernel_stats.csv")
     trace = _csv_rows(args.trace_summary, "kernel_trace.csv")
-    durs = {}
+    durs, by_grid = {}, {}
     for r in trace:
-        durs.setdefault(r["Kernel_Name"], []).append(
-            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        g = (int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) *
+             int(r["Grid_Size_Z"]))
+        durs.setdefault(r["Kernel_Name"], []).append(d)
+        by_grid.setdefault(r["Kernel_Name"], {}).setdefault(g, []).append(d)
+    is_dom = _matcher(args.config)
+    dom = [n for n in by_grid if is_dom(n)]
     lines = [f"# Kernel trace: {WORKLOADS.get(args.config, args.config)}", "",
              "Commands (GPU box, from the repository root):", "", "```"]
     lines += args.command + ["```", "",
@@ -307,6 +316,15 @@ def trace_summary(args):
                      f"{float(r['AverageNs']) / 1e3:.3f} | "
                      f"{d[len(d) // 2]:.3f} | {d[0]:.3f} | {d[-1]:.3f} | "
                      f"{float(r['Percentage']):.2f} |")
+    for n in dom:
+        g = max(by_grid[n])
+        d = sorted(by_grid[n][g])
+        lines += ["", f"Dominant kernel at the workload's own launch (its "
+                  f"largest grid, {g} threads; dispatches of the same "
+                  f"kernel on smaller grids, if any, are the chunked-forward "
+                  f"leg): `{n}`, "
+                  f"{len(d)} dispatches, average {sum(d) / len(d):.3f} us, "
+                  f"median {d[len(d) // 2]:.3f} us."]
     if args.bench_log:
         with open(args.bench_log) as f:
             for line in f:
