@@ -1194,11 +1194,15 @@ __global__ __launch_bounds__(kMwThreads) void mw_write_kernel(
 // A key below the k-th largest can never be selected, so any lower bound
 // T_lo of the k-th largest key turns the row into a short candidate list
 // {key >= T_lo} that still holds the whole answer:
-//   sample   one 1024-thread workgroup per row reads 16384 keys at jittered
-//            stride n / 16384 and takes the m-th largest sample key as T_lo,
-//            m = k * 16384 / n + 4 sqrt(k * 16384 / n) + 16: about m n /
-//            16384 keys of the row (k plus a few standard deviations) are
-//            then at or above T_lo;
+//   sample   16 workgroups per row read the row's 16384 keys at jittered
+//            stride n / 16384 (scattered 4-byte reads: spread over many
+//            compute units, since one unit alone is limited by its own L2
+//            bandwidth for 16384 separate lines) into a contiguous buffer;
+//            then one 1024-thread workgroup per row reads them back
+//            coalesced and takes the m-th largest as T_lo, m = k * 16384 /
+//            n + 4 sqrt(k * 16384 / n) + 16: about m n / 16384 keys of the
+//            row (k plus a few standard deviations) are then at or above
+//            T_lo;
 //   collect  one 256-thread workgroup per 16384-key chunk writes its keys
 //            >= T_lo, in column order, to the chunk's slot of 512 (one
 //            fully coalesced pass over the row, the HBM-bound part);
@@ -1219,6 +1223,7 @@ constexpr int kSsCandMax = 4 * 4 * kTopkThreads;   // 16384 (RegKeys<4>)
 constexpr int64_t kSsMaxChunks = 1024;             // rows up to 16M columns
 
 struct SsWorkspace {
+  uint32_t* samp;     // [T][kSsSample] sampled keys (ordered)
   uint32_t* thr;      // [T] T_lo
   uint32_t* count;    // [T][C] candidates per chunk (> cap: overflow)
   uint2* cand;        // [T][C][cap] (key, column)
@@ -1241,6 +1246,7 @@ static SsWorkspace ss_carve(void* base, int64_t T, int64_t ld,
     off += align256(bytes);
     return q;
   };
+  w.samp = reinterpret_cast<uint32_t*>(take((size_t)T * kSsSample * 4));
   w.thr = reinterpret_cast<uint32_t*>(take((size_t)T * 4));
   w.count = reinterpret_cast<uint32_t*>(take((size_t)T * C * 4));
   w.cand = reinterpret_cast<uint2*>(take((size_t)T * C * kSsChunkCap * 8));
@@ -1254,6 +1260,35 @@ __device__ __forceinline__ uint32_t ss_hash(uint32_t x) {
   return x ^ (x >> 16);
 }
 
+constexpr int kSsGatherWgs = 16;                        // per row
+constexpr int kSsGatherPerThread = kSsSample / (kSsGatherWgs * kSsThreads);
+
+// Grid (16, T): sample q (0..16383) of row t is column q * stride +
+// hash(q) % stride (< n, stride = n / 16384 >= 1), stored as its ordered key
+// at samp[t][q]; workgroup g takes q in [1024 g, 1024 g + 1024).
+__global__ __launch_bounds__(kSsThreads) void ss_gather_kernel(
+    const float* __restrict__ logits, int64_t ld, const int32_t* positions,
+    int k, SsWorkspace ws) {
+  const int64_t t = blockIdx.y;
+  const int n = row_len(positions, t, ld);
+  if (n <= kSsCandMax || n <= k) return;
+  const float* row = logits + t * ld;
+  const uint32_t stride = (uint32_t)n / kSsSample;     // >= 1
+  uint32_t* out = ws.samp + t * kSsSample;
+  uint32_t key[kSsGatherPerThread];
+#pragma unroll
+  for (int j = 0; j < kSsGatherPerThread; ++j) {
+    const uint32_t q = (uint32_t)((blockIdx.x * kSsGatherPerThread + j) *
+                                  kSsThreads + threadIdx.x);
+    key[j] = float_to_ordered(row[q * stride + ss_hash(q) % stride]);
+  }
+#pragma unroll
+  for (int j = 0; j < kSsGatherPerThread; ++j)
+    out[(blockIdx.x * kSsGatherPerThread + j) * kSsThreads + threadIdx.x] =
+        key[j];
+}
+
+// One workgroup per row: the m-th largest of the row's 16384 samples.
 __global__ __launch_bounds__(kTopkThreads) void ss_sample_kernel(
     const float* __restrict__ logits, int64_t ld, const int32_t* positions,
     int k, SsWorkspace ws) {
@@ -1266,18 +1301,17 @@ __global__ __launch_bounds__(kTopkThreads) void ss_sample_kernel(
     sh.hist[b] = 0u;
     sh.hist2[b] = 0u;
   }
-  const float* row = logits + t * ld;
-  const uint32_t stride = (uint32_t)n / kSsSample;     // >= 1
+  const uint32_t* samp = ws.samp + t * kSsSample;
   RegKeys<4> r;
   r.n = kSsSample;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t q = (uint32_t)(s * 4 * kTopkThreads + 4 * tid + j);
-      const uint32_t col = q * stride + ss_hash(q) % stride;   // < n
-      r.key[s][j] = float_to_ordered(row[col]);
-    }
+    const uint4 v = *reinterpret_cast<const uint4*>(
+        samp + s * 4 * kTopkThreads + 4 * tid);
+    r.key[s][0] = v.x;
+    r.key[s][1] = v.y;
+    r.key[s][2] = v.z;
+    r.key[s][3] = v.w;
   }
   __syncthreads();
   const float e = (float)k * (float)kSsSample / (float)n;
@@ -1303,22 +1337,46 @@ __global__ __launch_bounds__(kSsThreads) void ss_collect_kernel(
   const uint32_t thr = ws.thr[t];
   const float* row = logits + t * ld;
   const int i0 = (int)c * kSsChunk;
-  uint32_t key[kSlices][4], cnt[kSlices], incl[kSlices];
+  if (thr == 0u) {
+    // every key qualifies: the candidate list would be the whole row, which
+    // the select kernel handles by its exact path (flagged as an overflow)
+    if (tid == 0) ws.count[t * ws.C + c] = kSsChunkCap + 1;
+    return;
+  }
+  uint32_t key[kSlices][4];
+  // all 16 loads in flight before any is used (interleaving them with the
+  // scans below makes every slice a separate round trip to HBM); buffer
+  // loads over the chunk's columns below n share one offset register, and
+  // reads past n return 0 (masked out below)
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(row + i0, min(n - i0, kSsChunk) * 4);
 #pragma unroll
   for (int s = 0; s < kSlices; ++s) {
-    const int c0 = i0 + s * 4 * kSsThreads + 4 * tid;
-    const float4 v =
-        *reinterpret_cast<const float4*>(row + min(c0, (int)ld - 4));
-    key[s][0] = float_to_ordered(v.x);
-    key[s][1] = float_to_ordered(v.y);
-    key[s][2] = float_to_ordered(v.z);
-    key[s][3] = float_to_ordered(v.w);
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(
+        rs, 16 * tid, s * 4 * kSsThreads * 4, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) key[s][j] = x[j];           // fp32 bits
+  }
+  // a slice's count and in-wave scan are recomputed after the barrier
+  // rather than kept, and a column at or past n gets key 0, below thr >= 1
+  // (only the 64 keys stay live: fewer registers, more workgroups resident
+  // per compute unit)
+  auto count = [&](int s) {
     uint32_t m = 0u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) m += (c0 + j < n && key[s][j] >= thr) ? 1u : 0u;
-    cnt[s] = m;
-    incl[s] = wave_inclusive_scan(m);
-    if (lane == 63) s_tot[s * kWaves + wave] = incl[s];
+    for (int j = 0; j < 4; ++j) m += key[s][j] >= thr ? 1u : 0u;
+    return m;
+  };
+  const int n_here = n - i0;                 // columns of this chunk below n
+#pragma unroll
+  for (int s = 0; s < kSlices; ++s) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t kk = float_to_ordered(__uint_as_float(key[s][j]));
+      key[s][j] = s * 4 * kSsThreads + 4 * tid + j < n_here ? kk : 0u;
+    }
+    const uint32_t incl = wave_inclusive_scan(count(s));
+    if (lane == 63) s_tot[s * kWaves + wave] = incl;
   }
   __syncthreads();
   if (wave == 0) {                           // 64 (slice, wave) totals
@@ -1332,11 +1390,12 @@ __global__ __launch_bounds__(kSsThreads) void ss_collect_kernel(
   uint2* slot = ws.cand + (t * ws.C + c) * kSsChunkCap;
 #pragma unroll
   for (int s = 0; s < kSlices; ++s) {
-    uint32_t o = s_tot[s * kWaves + wave] + incl[s] - cnt[s];
+    const uint32_t m = count(s);
+    uint32_t o = s_tot[s * kWaves + wave] + wave_inclusive_scan(m) - m;
     const int c0 = i0 + s * 4 * kSsThreads + 4 * tid;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (c0 + j < n && key[s][j] >= thr) {
+      if (key[s][j] >= thr) {
         if (o < (uint32_t)kSsChunkCap)
           slot[o] = make_uint2(key[s][j], (uint32_t)(c0 + j));
         ++o;
@@ -1523,6 +1582,9 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   const bool aligned = (reinterpret_cast<uintptr_t>(a.logits) & 15u) == 0;
   if (use_sample_select(a.ld) && aligned && options().topk_kernel != 3) {
     const SsWorkspace ss = ss_carve(a.workspace, a.T, a.ld, nullptr);
+    hipLaunchKernelGGL(ss_gather_kernel, dim3(kSsGatherWgs, (unsigned)a.T),
+                       dim3(kSsThreads), 0, stream, a.logits, a.ld,
+                       a.positions, a.k, ss);
     hipLaunchKernelGGL(ss_sample_kernel, dim3((unsigned)a.T),
                        dim3(kTopkThreads), 0, stream, a.logits, a.ld,
                        a.positions, a.k, ss);
