@@ -1,0 +1,119 @@
+"""Host logic of bench.py (CPU only): the one-GPU refusal, the counter and
+kernel-trace summaries built from rocprofv3 CSV files, and the rule that
+byte counters taken for other kernel sources are not reported."""
+
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+TILE = "void dsa::logits_tile16_kernel<1, false, true, 2, true>(dsa::LogitsArgs, int, int)"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def _write(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=list(rows[0]))
+        w.writeheader()
+        w.writerows(rows)
+
+
+def _run(*args):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"),
+                           *args], capture_output=True, text=True,
+                          timeout=300, cwd=ROOT)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = _run("--gpus", "2")
+    assert r.returncode == 2
+    assert "one GPU" in json.loads(r.stdout.strip())["error"]
+
+
+def _pmc_dir(tmp, name, cal_kib, big, small):
+    """Three calibration copies, then logits dispatches at a large grid
+    (values ``big``) and a smaller one (``small``); two rows per dispatch
+    (the summary adds them)."""
+    rows, d = [], 0
+    for _ in range(3):
+        d += 1
+        for half in (0.5, 0.5):
+            rows.append(dict(Dispatch_Id=d, Kernel_Name=COPY, Grid_Size=512,
+                             Counter_Name="X", Counter_Value=cal_kib * half))
+    for grid, vals in ((1 << 20, big), (1 << 16, small)):
+        for v in vals:
+            d += 1
+            for half in (0.25, 0.75):
+                rows.append(dict(Dispatch_Id=d, Kernel_Name=TILE,
+                                 Grid_Size=grid, Counter_Name="X",
+                                 Counter_Value=v * half))
+    p = tmp / name
+    p.mkdir()
+    _write(p / "x_counter_collection.csv", rows)
+    return str(p)
+
+
+def test_pmc_summary_takes_the_largest_grid_and_scales(tmp_path):
+    f = _pmc_dir(tmp_path, "f", 131072.0, [100.0, 300.0], [5.0, 5.0, 5.0])
+    w = _pmc_dir(tmp_path, "w", 262144.0, [40.0, 40.0], [1.0])
+    r = _run("--config", "tiny", "--pmc-summary", f, w)
+    assert r.returncode == 0, r.stderr
+    d = json.loads(r.stdout)
+    assert d["kernel"] == [TILE]
+    assert d["fetch_kib_per_dispatch"] == 200.0          # small grid excluded
+    assert d["write_kib_per_dispatch"] == 40.0
+    assert d["dispatches"] == [2, 2]
+    assert d["fetch_scale"] == 2.0 and d["write_scale"] == 1.0
+    assert d["traffic_bytes_per_launch"] == 200 * 1024 * 2 + 40 * 1024
+    assert d["sources_digest"] == bench.logits_sources_digest()
+
+
+def test_trace_summary_reports_the_workload_launch(tmp_path):
+    rows = []
+    for grid, durs in (((4096, 4, 1), [1000, 1200, 1100]),
+                       ((1024, 1, 1), [100, 100])):
+        for dur in durs:
+            rows.append(dict(Kernel_Name=TILE, Start_Timestamp=0,
+                             End_Timestamp=dur, Grid_Size_X=grid[0],
+                             Grid_Size_Y=grid[1], Grid_Size_Z=grid[2]))
+    _write(tmp_path / "t_kernel_trace.csv", rows)
+    _write(tmp_path / "t_kernel_stats.csv",
+           [dict(Name=TILE, Calls=5, AverageNs=700.0, Percentage=100.0)])
+    r = _run("--config", "tiny", "--trace-summary", str(tmp_path),
+             "--command", "rocprofv3 ... -- python3 bench.py --config tiny")
+    assert r.returncode == 0, r.stderr
+    out = r.stdout
+    assert "rocprofv3 ... -- python3 bench.py --config tiny" in out
+    line = [ln for ln in out.splitlines() if ln.startswith("Dominant kernel")]
+    assert len(line) == 1
+    assert "16384 threads" in line[0] and "3 dispatches" in line[0]
+    assert "average 1.100 us" in line[0]
+
+
+def test_traffic_is_null_once_the_sources_change(tmp_path, monkeypatch):
+    p = tmp_path / "c.json"
+    monkeypatch.setattr(bench, "counters_path", lambda config: str(p))
+    assert bench.traffic_from_counters("decode") is None          # no file
+    p.write_text(json.dumps({"sources_digest": "0" * 16,
+                             "traffic_bytes_per_launch": 123}))
+    assert bench.traffic_from_counters("decode") is None          # stale
+    p.write_text(json.dumps({"sources_digest": bench.logits_sources_digest(),
+                             "traffic_bytes_per_launch": 123}))
+    assert bench.traffic_from_counters("decode") == 123
+
+
+@pytest.mark.parametrize("config", ["decode", "prefill", "long"])
+def test_committed_counters_match_the_sources(config):
+    """The committed counter summaries were taken on the kernels as they
+    are: the bench reports their traffic."""
+    with open(bench.counters_path(config)) as f:
+        d = json.load(f)
+    assert d["sources_digest"] == bench.logits_sources_digest()
+    assert d["commands"], "summary without the commands that made it"
