@@ -585,7 +585,7 @@ def bench_index_cache(args):
     pos = torch.from_numpy(ref.positions).to(dev)
     T, k, ld = ref.T, ref.k, ref.ld
     buf = torch.empty((T, k), dtype=torch.int32, device=dev)
-    ws = torch.empty(binding.dsa_run_workspace_size(T, ref.H, ld, k),
+    ws = torch.empty(binding.dsa_run_workspace_size(T, ref.R, ref.H, ld, k),
                      dtype=torch.uint8, device=dev)
     pattern = synth.index_cache_pattern(L)
     runs = {"freq4": dict(freq=4, offset=2), "pattern": dict(pattern=pattern),

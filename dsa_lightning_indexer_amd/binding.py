@@ -69,10 +69,10 @@ _SIGNATURES = {
     "dsa_index_cache_mask": (_I, [ctypes.c_char_p, _I, _I, _I, _I, _I, _I,
                                   _I, _P]),
     "dsa_index_cache_run": (_I, [ctypes.c_char_p, _I, _I, _I, _I, _I, _I, _I,
-                                 _P, _P, _L,
-                                 _P, _P, _L, _I, _I, _L, _I, _P, _L, _P, _P,
-                                 LAYER_CALLBACK, _P, _P, _S, _P]),
-    "dsa_run_workspace_size": (_S, [_L, _I, _L, _I]),
+                                 _P, _P, _L, _P, _P, _L, _I, _I, _L, _I, _L,
+                                 _P, _L, _P, _P, LAYER_CALLBACK, _P, _P, _S,
+                                 _P]),
+    "dsa_run_workspace_size": (_S, [_L, _I, _I, _L, _I, _L]),
     "dsa_slot_mapping": (_I, [_P, _L, _P, _I, _P, _L, _P, _P]),
     "dsa_compressed_slot_mapping": (_I, [_P, _L, _P, _I, _P, _L, _I, _I, _P,
                                          _P, _P]),
@@ -306,15 +306,16 @@ def dsa_index_cache_mask(num_layers, pattern=None, freq=1, offset=2,
     return [bool(buf[i]) for i in range(num_layers)]
 
 
-def dsa_run_workspace_size(T, H, ld, k):
-    return lib().dsa_run_workspace_size(T, H, ld, k)
+def dsa_run_workspace_size(T, R, H, ld, k, rows_per_chunk=0):
+    return lib().dsa_run_workspace_size(T, R, H, ld, k, rows_per_chunk)
 
 
 def dsa_index_cache_run(layers, block_table, query_start_loc, positions, ld,
                         k, topk_buffer, pattern=None, freq=1, offset=2,
                         num_hidden_layers=-1, H=None, snapshots=False,
                         callback=None, workspace=None, stream=None,
-                        first_layer=0, mtp_draft_step=0, mtp_reuse=False):
+                        first_layer=0, mtp_draft_step=0, mtp_reuse=False,
+                        rows_per_chunk=0):
     """One forward pass over ``len(layers)`` DSA layers (ids first_layer ..).
 
     ``layers[l]`` is a dict with ``q_bf16`` (bf16 [T, H, 128]), ``weights``
@@ -342,7 +343,7 @@ def dsa_index_cache_run(layers, block_table, query_start_loc, positions, ld,
                 lay["k_cache"].shape[0])
     snaps = torch.empty((L, T, k), dtype=torch.int32, device=dev) \
         if snapshots else None
-    need = dsa_run_workspace_size(T, H, ld, k)
+    need = dsa_run_workspace_size(T, R, H, ld, k, rows_per_chunk)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     skip = (ctypes.c_uint8 * max(L, 1))()
@@ -357,7 +358,7 @@ def dsa_index_cache_run(layers, block_table, query_start_loc, positions, ld,
             block_table.shape[1],
             _dev_ptr(query_start_loc, torch.int32, "query_start_loc"),
             _dev_ptr(positions, torch.int32, "positions"), T, R, H, ld, k,
-            _dev_ptr(topk_buffer, torch.int32, "topk_buffer"),
+            rows_per_chunk, _dev_ptr(topk_buffer, torch.int32, "topk_buffer"),
             topk_buffer.shape[0],
             _dev_ptr(snaps, torch.int32, "snapshots") if snaps is not None
             else None, skip, cb, None,

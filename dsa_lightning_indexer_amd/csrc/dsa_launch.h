@@ -8,6 +8,10 @@
 
 namespace dsa {
 
+// Devices the per-device caches of the launchers cover (others query each
+// time).
+constexpr int kMaxDevices = 64;
+
 struct LogitsArgs {
   const uint8_t* q8;            // e4m3fn codes [T, H, 128]
   const float* q_scale;         // [T, H]

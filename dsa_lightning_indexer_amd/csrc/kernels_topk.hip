@@ -30,6 +30,7 @@
 // the row is longer than the bitmaps cover, the row falls back to a full
 // 12+12+8-bit radix select over the row.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "dsa_common.h"
@@ -1503,13 +1504,18 @@ static hipError_t launch_topk_single_t(const TopkArgs& a, hipStream_t stream,
                                        int max_cache, size_t elem) {
   const int cap = (int)std::min<int64_t>(a.ld, max_cache);
   const size_t dyn = (size_t)cap * elem;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(
+  // the dynamic-LDS limit is a per-device attribute of the kernel: set once
+  // on each device the library launches on (setting it twice is harmless)
+  static std::atomic<bool> attr_set[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices || !attr_set[dev].load()) {
+    e = hipFuncSetAttribute(
         reinterpret_cast<const void*>(topk_row_kernel<KEY32>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)(max_cache * elem));
     if (e != hipSuccess) return e;
-    attr_set = true;
+    if (dev >= 0 && dev < kMaxDevices) attr_set[dev].store(true);
   }
   hipLaunchKernelGGL(topk_row_kernel<KEY32>, dim3((unsigned)a.T),
                      dim3(kTopkThreads), dyn, stream, a.logits, a.ld,
@@ -1519,17 +1525,18 @@ static hipError_t launch_topk_single_t(const TopkArgs& a, hipStream_t stream,
 
 // Compute units of the current device (queried once per device).
 int device_cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[kMaxDevices];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return 256;
+  int n = cached[dev].load();
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
             hipSuccess || n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n);
   }
-  return cached[dev];
+  return n;
 }
 
 template <int S>

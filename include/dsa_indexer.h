@@ -268,7 +268,12 @@ typedef void (*dsa_layer_callback)(int layer, int is_full,
  *                rows [0, T) of the buffer are copied to snapshots[i].
  *   is_skip_out  host, nullable: uint8 [num_layers], the mask used.
  *   cb, cb_user  nullable per-layer callback.
- *   workspace    device, dsa_run_workspace_size(T, H, ld, k) bytes.
+ *   rows_per_chunk  0 (or >= T): F layers run as dsa_indexer_forward with
+ *                the logits of all T rows in the workspace; otherwise as
+ *                dsa_indexer_forward_chunked with chunks of this many rows
+ *                (the logits budget; same top-k rows bit for bit).
+ *   workspace    device, dsa_run_workspace_size(T, R, H, ld, k,
+ *                rows_per_chunk) bytes.
  * Rejects (DSA_ERR_INVALID_ARG) a mask whose first layer is S ([IC] 5.3:
  * it would read a buffer no layer has written in this pass), except in an
  * MTP draft pass that reuses (first_layer >= num_hidden_layers >= 0,
@@ -282,13 +287,14 @@ int dsa_index_cache_run(const char* pattern, int freq, int offset,
                         const int32_t* block_table, int64_t bt_stride,
                         const int32_t* query_start_loc,
                         const int32_t* positions, int64_t T, int R, int H,
-                        int64_t ld, int k, int32_t* topk_buffer,
-                        int64_t buffer_rows, int32_t* snapshots,
-                        uint8_t* is_skip_out, dsa_layer_callback cb,
-                        void* cb_user, void* workspace, size_t ws_bytes,
-                        void* stream);
+                        int64_t ld, int k, int64_t rows_per_chunk,
+                        int32_t* topk_buffer, int64_t buffer_rows,
+                        int32_t* snapshots, uint8_t* is_skip_out,
+                        dsa_layer_callback cb, void* cb_user, void* workspace,
+                        size_t ws_bytes, void* stream);
 
-size_t dsa_run_workspace_size(int64_t T, int H, int64_t ld, int k);
+size_t dsa_run_workspace_size(int64_t T, int R, int H, int64_t ld, int k,
+                              int64_t rows_per_chunk);
 
 /*
  * dsa_slot_mapping -- physical cache slot of every query row's token

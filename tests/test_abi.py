@@ -211,7 +211,8 @@ def _run_call(**over):
                 step=0, reuse=0, layers=_fake_layers(),
                 bt=ctypes.c_void_p(0x1000), bt_stride=4,
                 qsl=ctypes.c_void_p(0x1000), pos=ctypes.c_void_p(0x1000),
-                T=4, R=1, H=4, ld=256, k=8, buf=ctypes.c_void_p(0x1000),
+                T=4, R=1, H=4, ld=256, k=8, rows=0,
+                buf=ctypes.c_void_p(0x1000),
                 buf_rows=4, snaps=None, skip=None,
                 cb=binding.LAYER_CALLBACK(0), user=None,
                 ws=ctypes.c_void_p(0x1000), ws_bytes=1 << 30, stream=None)
@@ -242,6 +243,10 @@ def test_run_mtp_reuse_pass_may_start_with_s():
     assert _run_call(step=-1) == binding.DSA_ERR_INVALID_ARG
 
 
+def test_run_rejects_negative_chunk_rows():
+    assert _run_call(rows=-1) == binding.DSA_ERR_INVALID_ARG
+
+
 def test_run_rejects_bad_arguments():
     assert _run_call(pattern=b"FXF") == binding.DSA_ERR_INVALID_ARG
     assert _run_call(freq=0) == binding.DSA_ERR_INVALID_ARG
@@ -263,9 +268,17 @@ def test_run_with_no_rows_only_reports_mask():
 
 
 def test_workspace_sizes():
-    assert binding.dsa_run_workspace_size(64, 64, 8192, 2048) >= \
+    assert binding.dsa_run_workspace_size(64, 64, 64, 8192, 2048) >= \
         64 * 64 * 128 + 64 * 64 * 4 + 64 * 8192 * 4
-    assert binding.dsa_run_workspace_size(0, 64, 8192, 2048) == 0
+    assert binding.dsa_run_workspace_size(0, 64, 64, 8192, 2048) == 0
+    # chunked: the logits of rows_per_chunk rows instead of all T
+    full = binding.dsa_run_workspace_size(4096, 1, 64, 40960, 2048)
+    ch = binding.dsa_run_workspace_size(4096, 1, 64, 40960, 2048, 512)
+    assert ch == binding.dsa_forward_chunked_workspace_size(4096, 1, 64,
+                                                            40960, 2048, 512)
+    assert full - ch >= (4096 - 512) * 40960 * 4 - (1 << 20)
+    assert binding.dsa_run_workspace_size(4096, 1, 64, 40960, 2048, 4096) == \
+        full
 
 
 def test_set_option_roundtrip():

@@ -117,6 +117,32 @@ def test_index_cache_run_reduced(cfg):
     assert binding.dsa_device_error_flags(reset=True) == 0
 
 
+@pytest.mark.parametrize("rows", [1, 3, 5])
+def test_index_cache_run_chunked_equals_unchunked(rows):
+    """F layers under a logits budget (rows_per_chunk < T) give every
+    layer's buffer rows bit for bit as the unchunked run."""
+    _say(f"case: index cache run, {rows} rows per chunk")
+    L, R, context, H, k = 9, 6, 1800, 16, 128
+    mask = binding.dsa_index_cache_mask(L, freq=2, offset=1)
+    full = [l for l in range(L) if not mask[l]]
+    batches, ref = _stack(full, R, context, H, k, seed=12)
+    dev = _dev_layers(batches, L)
+    geo = (torch.from_numpy(ref.block_table).cuda(),
+           torch.from_numpy(ref.query_start_loc).cuda(),
+           torch.from_numpy(ref.positions).cuda(), ref.ld, k)
+    outs = []
+    for chunk in (0, rows):
+        buf = torch.full((R, k), 3, dtype=torch.int32, device="cuda")
+        skip, snaps = binding.dsa_index_cache_run(
+            dev, *geo, buf, freq=2, offset=1, snapshots=True,
+            rows_per_chunk=chunk)
+        torch.cuda.synchronize()
+        assert skip == mask
+        outs.append(snaps.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+    assert binding.dsa_device_error_flags(reset=True) == 0
+
+
 def test_mtp_draft_passes():
     """A trunk pass (4 layers, freq 2), then MTP draft passes over the one
     MTP layer (id 4) through the C ABI: step 0 computes (the oracle's
