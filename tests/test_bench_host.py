@@ -117,3 +117,17 @@ def test_committed_counters_match_the_sources(config):
         d = json.load(f)
     assert d["sources_digest"] == bench.logits_sources_digest()
     assert d["commands"], "summary without the commands that made it"
+
+
+def test_pmc_summary_refuses_a_foreign_largest_copy(tmp_path):
+    """A larger copy than the calibration copies (a timing copy in the
+    counter run) would scale every counter wrongly: refused."""
+    f = _pmc_dir(tmp_path, "f", 131072.0, [100.0], [])
+    rows = list(csv.DictReader(open(os.path.join(f, "x_counter_collection.csv"))))
+    rows.append(dict(Dispatch_Id=99, Kernel_Name=COPY, Grid_Size=512,
+                     Counter_Name="X", Counter_Value=524288.0))
+    _write(tmp_path / "f" / "x_counter_collection.csv", rows)
+    w = _pmc_dir(tmp_path, "w", 262144.0, [40.0], [])
+    r = _run("--config", "tiny", "--pmc-summary", f, w)
+    assert r.returncode != 0
+    assert "calibration" in r.stderr
