@@ -47,18 +47,19 @@ __global__ __launch_bounds__(256) void compressed_slot_mapping_kernel(
     int64_t* __restrict__ slots, int32_t* __restrict__ positions_c) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
-  const int p = positions[t];
+  const int64_t p = positions[t];              // p + 1 may pass INT32_MAX
   int64_t slot = -1;
   if (p >= 0 && (p + 1) % ratio == 0) {
-    const int c = p / ratio;
-    if ((int64_t)(c / bs) < bt_stride) {
+    const int64_t c = p / ratio;
+    if (c / bs < bt_stride) {
       const int r = request_of_row(qsl, R, t);
       const int blk = block_table[(int64_t)r * bt_stride + c / bs];
       if (blk >= 0) slot = (int64_t)blk * bs + c % bs;
     }
   }
   slots[t] = slot;
-  if (positions_c) positions_c[t] = p >= 0 ? (p + 1) / ratio - 1 : -1;
+  if (positions_c)
+    positions_c[t] = p >= 0 ? (int32_t)((p + 1) / ratio - 1) : -1;
 }
 
 // 16 lanes per token, 8 bf16 values per lane (one 16-byte load):

@@ -48,6 +48,24 @@ def test_compressed_slot_mapping_matches_oracle(ratio, bs):
                           ok.compressed_positions(pos, ratio))
 
 
+def test_compressed_slot_mapping_at_int32_extremes():
+    """Positions up to 2^31 - 1: (p + 1) is formed in 64 bits."""
+    _say("case: compressed slot mapping at int32 extremes")
+    bt = np.arange(8, dtype=np.int32).reshape(1, 8)
+    qsl = np.array([0, 6], dtype=np.int32)
+    big = 2 ** 31 - 1
+    pos = np.array([big, big - 1, big - 3, 3, 7, -1], dtype=np.int32)
+    for ratio, bs in ((4, 64), (128, 2), (1, 64), (big, 1)):
+        slots, pc = binding.dsa_compressed_slot_mapping(
+            _dev(bt), _dev(qsl), _dev(pos), ratio, bs)
+        torch.cuda.synchronize()
+        assert np.array_equal(slots.cpu().numpy(),
+                              ok.compressed_slot_mapping(bt, qsl, pos, ratio,
+                                                         bs)), ratio
+        assert np.array_equal(pc.cpu().numpy(),
+                              ok.compressed_positions(pos, ratio)), ratio
+
+
 def test_compressed_ratio_one_is_the_plain_kernel():
     _say("case: compressed slot mapping at ratio 1 vs dsa_slot_mapping")
     rng = np.random.default_rng(9)
