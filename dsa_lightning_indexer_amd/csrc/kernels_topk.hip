@@ -471,16 +471,16 @@ struct RegTopkShared {
 };
 
 // Keys held in registers: item s * 4 NT + 4 tid + j of a list in key[s][j]
-// (slice s, j = 0..3, NT = kTopkThreads), valid when that item index is
-// below n (no per-key mask registers).
-template <int S>
+// (slice s, j = 0..3, NT threads), valid when that item index is below n
+// (no per-key mask registers).
+template <int S, int NT = kTopkThreads>
 struct RegKeys {
   uint32_t key[S][4];
   int n;
   // written as (per-lane offset) < (uniform bound) so that only 4 *
   // threadIdx.x + j lives in vector registers
   __device__ __forceinline__ bool ok(int s, int j) const {
-    return 4 * (int)threadIdx.x + j < n - s * 4 * kTopkThreads;
+    return 4 * (int)threadIdx.x + j < n - s * 4 * NT;
   }
 };
 
@@ -492,7 +492,7 @@ struct RegKeys {
 // by the two-barrier bin search.  sh.hist and sh.hist2 must be zero and a
 // barrier passed before the call.  Call from all NT threads.
 template <int NT, int S>
-__device__ void reg_threshold(const RegKeys<S>& r, int k,
+__device__ void reg_threshold(const RegKeys<S, NT>& r, int k,
                               RegTopkShared<NT, S>& sh, uint32_t& mask,
                               uint32_t& thr, uint32_t& k_tie) {
   const int tid = threadIdx.x;
@@ -542,7 +542,7 @@ __device__ void reg_threshold(const RegKeys<S>& r, int k,
 // per thread and slice, a DPP scan within the wave and a scan of the
 // per-wave totals; orow[slot] = index_of(s, j, position in the list).
 template <int NT, int S, typename IndexOf>
-__device__ void reg_emit(const RegKeys<S>& r, int k, uint32_t mask,
+__device__ void reg_emit(const RegKeys<S, NT>& r, int k, uint32_t mask,
                          uint32_t thr, uint32_t k_tie, int32_t* orow,
                          RegTopkShared<NT, S>& sh, IndexOf index_of) {
   constexpr int NW = NT / 64;
@@ -630,7 +630,7 @@ __device__ void reg_emit(const RegKeys<S>& r, int k, uint32_t mask,
 // expands only the set bits of its two words.  Ties are taken lowest column
 // first up to k_tie.
 template <int NT, int S>
-__device__ void reg_emit_columns(const RegKeys<S>& r, int k, uint32_t mask,
+__device__ void reg_emit_columns(const RegKeys<S, NT>& r, int k, uint32_t mask,
                                  uint32_t thr, uint32_t k_tie, int32_t* orow,
                                  RegTopkShared<NT, S>& sh) {
   constexpr int NW = NT / 64;
@@ -662,14 +662,23 @@ __device__ void reg_emit_columns(const RegKeys<S>& r, int k, uint32_t mask,
     }
   }
   __syncthreads();
-  // thread tid owns words 2 tid, 2 tid + 1 of the row's ceil(n / 32)
+  // thread tid owns words WPT tid .. WPT tid + WPT - 1 of the row's
+  // ceil(n / 32) (S NT / 8 words in all; at least 2 per thread)
+  constexpr int WPT = (S * NT / 8 + NT - 1) / NT > 2
+                          ? (S * NT / 8 + NT - 1) / NT : 2;
   const int nw = (r.n + 31) >> 5;
-  const int w0 = 2 * tid;
-  uint32_t s0 = 0u, s1 = 0u, t0 = 0u, t1 = 0u;
-  if (w0 < nw) { s0 = sh.selw[w0]; t0 = sh.tiew[w0]; }
-  if (w0 + 1 < nw) { s1 = sh.selw[w0 + 1]; t1 = sh.tiew[w0 + 1]; }
-  const uint32_t c = (uint32_t)(__builtin_popcount(s0) + __builtin_popcount(s1)) |
-                     ((uint32_t)(__builtin_popcount(t0) + __builtin_popcount(t1)) << 16);
+  const int w0 = WPT * tid;
+  uint32_t sw_[WPT], tw_[WPT];
+  uint32_t n_sel = 0u, n_tie = 0u;
+#pragma unroll
+  for (int h = 0; h < WPT; ++h) {
+    sw_[h] = 0u;
+    tw_[h] = 0u;
+    if (w0 + h < nw) { sw_[h] = sh.selw[w0 + h]; tw_[h] = sh.tiew[w0 + h]; }
+    n_sel += (uint32_t)__builtin_popcount(sw_[h]);
+    n_tie += (uint32_t)__builtin_popcount(tw_[h]);
+  }
+  const uint32_t c = n_sel | (n_tie << 16);
   const uint32_t incl = wave_inclusive_scan(c);
   if (lane == 63) sh.wave_sum[wave] = incl;
   __syncthreads();
@@ -678,8 +687,8 @@ __device__ void reg_emit_columns(const RegKeys<S>& r, int k, uint32_t mask,
   uint32_t gt_b = before & 0xffffu, eq_b = before >> 16;
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(orow, k * 4);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    uint32_t sw = h ? s1 : s0, tw = h ? t1 : t0;
+  for (int h = 0; h < WPT; ++h) {
+    const uint32_t sw = sw_[h], tw = tw_[h];
     uint32_t any = sw | tw;
     while (any) {
       const int b = __builtin_ctz(any);
@@ -710,7 +719,7 @@ __device__ void topk_row_registers(const float* row, int64_t ld, int n, int k,
     sh.hist[b] = 0u;
     sh.hist2[b] = 0u;
   }
-  RegKeys<S> r;
+  RegKeys<S, NT> r;
   r.n = n;
 #pragma unroll
   for (int s = 0; s < S; ++s) {
@@ -750,14 +759,18 @@ constexpr int kRegMaxRow = kRegSlice * kRegMaxSlices;   // 49152
 // column-bitmap emit (sparse selections: prefill-length rows) instead of
 // the per-slice scans, whose cost does not grow with the number of keys
 // taken (dense selections: a quarter or more of a decode row).
-template <int S, bool BITMAP>
-__global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(
+// NT threads; PF: the next row's keys are loaded into registers while the
+// current row is selected (one resident workgroup per compute unit).
+// Without PF the workgroup is smaller and two share a compute unit, each
+// one's loads and barrier waits overlapping the other's work.
+template <int S, bool BITMAP, int NT, bool PF>
+__global__ __launch_bounds__(NT, 4) void topk_reg_kernel(
     const float* __restrict__ logits, int64_t ld,
     const int32_t* __restrict__ positions, int k, int32_t* __restrict__ out,
     int64_t out_ld, int64_t T) {
-  static_assert(S >= 1 && S <= kRegMaxSlices, "slices");
-  constexpr int kSlice = 4 * kTopkThreads;
-  __shared__ RegTopkShared<kTopkThreads, S> sh;
+  static_assert(S >= 1 && S * 4 * NT <= kRegMaxRow, "slices");
+  constexpr int kSlice = 4 * NT;
+  __shared__ RegTopkShared<NT, S> sh;
   const int tid = threadIdx.x;
   // n = p + 1 columns (p < 0: empty row; logits past ld do not exist)
   auto row_len = [&](int64_t t) {
@@ -776,6 +789,34 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(
                          __uint_as_float(x[2]), __uint_as_float(x[3]));
     }
   };
+  auto select = [&](int64_t t, int n, const float4 (&v)[S]) {
+    int32_t* orow = out + t * out_ld;
+    if (n <= k) {
+      topk_row_short<NT>(n, k, orow);
+      return;
+    }
+    for (int b = tid; b < kHistBins; b += NT) {
+      sh.hist[b] = 0u;
+      sh.hist2[b] = 0u;
+    }
+    RegKeys<S, NT> r;
+    r.n = n;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      r.key[s][0] = float_to_ordered(v[s].x);
+      r.key[s][1] = float_to_ordered(v[s].y);
+      r.key[s][2] = float_to_ordered(v[s].z);
+      r.key[s][3] = float_to_ordered(v[s].w);
+    }
+    __syncthreads();
+    uint32_t mask, thr, k_tie;
+    reg_threshold<NT, S>(r, k, sh, mask, thr, k_tie);
+    if (BITMAP)
+      reg_emit_columns<NT, S>(r, k, mask, thr, k_tie, orow, sh);
+    else
+      reg_emit<NT, S>(r, k, mask, thr, k_tie, orow, sh,
+                      [](int, int, int pos) { return pos; });
+  };
   int64_t t = blockIdx.x;
   if (t >= T) return;
   int n = row_len(t);
@@ -784,39 +825,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(
   for (;;) {
     const int64_t tn = t + gridDim.x;
     const int nn = tn < T ? row_len(tn) : 0;
-    float4 nxt[S];
-    issue(tn < T ? tn : t, tn < T ? nn : 0, nxt);
-    int32_t* orow = out + t * out_ld;
-    if (n <= k) {
-      topk_row_short<kTopkThreads>(n, k, orow);
-    } else {
-      for (int b = tid; b < kHistBins; b += kTopkThreads) {
-        sh.hist[b] = 0u;
-        sh.hist2[b] = 0u;
-      }
-      RegKeys<S> r;
-      r.n = n;
+    if (PF) {
+      float4 nxt[S];
+      issue(tn < T ? tn : t, tn < T ? nn : 0, nxt);
+      select(t, n, cur);
 #pragma unroll
-      for (int s = 0; s < S; ++s) {
-        r.key[s][0] = float_to_ordered(cur[s].x);
-        r.key[s][1] = float_to_ordered(cur[s].y);
-        r.key[s][2] = float_to_ordered(cur[s].z);
-        r.key[s][3] = float_to_ordered(cur[s].w);
-      }
-      __syncthreads();
-      uint32_t mask, thr, k_tie;
-      reg_threshold<kTopkThreads, S>(r, k, sh, mask, thr, k_tie);
-      if (BITMAP)
-        reg_emit_columns<kTopkThreads, S>(r, k, mask, thr, k_tie, orow, sh);
-      else
-        reg_emit<kTopkThreads, S>(r, k, mask, thr, k_tie, orow, sh,
-                                  [](int, int, int pos) { return pos; });
+      for (int s = 0; s < S; ++s) cur[s] = nxt[s];
+    } else {
+      select(t, n, cur);
+      if (tn < T) issue(tn, nn, cur);
     }
     if (tn >= T) break;
     t = tn;
     n = nn;
-#pragma unroll
-    for (int s = 0; s < S; ++s) cur[s] = nxt[s];
   }
 }
 
@@ -1545,17 +1566,50 @@ static hipError_t launch_topk_reg_t(const TopkArgs& a, hipStream_t stream) {
   const int64_t grid = std::min<int64_t>(a.T, device_cu_count());
   // the bitmap emit when the longest rows take fewer than 1/8 of their keys
   if ((int64_t)a.k * 8 < a.ld)
-    hipLaunchKernelGGL((topk_reg_kernel<S, true>), dim3((unsigned)grid),
-                       dim3(kTopkThreads), 0, stream, a.logits, a.ld,
-                       a.positions, a.k, a.out, a.out_ld, a.T);
+    hipLaunchKernelGGL((topk_reg_kernel<S, true, kTopkThreads, true>),
+                       dim3((unsigned)grid), dim3(kTopkThreads), 0, stream,
+                       a.logits, a.ld, a.positions, a.k, a.out, a.out_ld, a.T);
   else
-    hipLaunchKernelGGL((topk_reg_kernel<S, false>), dim3((unsigned)grid),
-                       dim3(kTopkThreads), 0, stream, a.logits, a.ld,
-                       a.positions, a.k, a.out, a.out_ld, a.T);
+    hipLaunchKernelGGL((topk_reg_kernel<S, false, kTopkThreads, true>),
+                       dim3((unsigned)grid), dim3(kTopkThreads), 0, stream,
+                       a.logits, a.ld, a.positions, a.k, a.out, a.out_ld, a.T);
   return hipGetLastError();
 }
 
+// 512-thread workgroups without the register prefetch, two per compute
+// unit (sparse selections: the bitmap emit).  A row's selection is a
+// chain of histogram passes and barriers that leaves one 1024-thread
+// workgroup waiting about half its cycles; with two workgroups each one's
+// loads and waits overlap the other's work (prefill top-k 0.46 -> 0.39 ms).
+constexpr int kReg2Threads = 512;
+template <int S>
+static hipError_t launch_topk_reg2_t(const TopkArgs& a, hipStream_t stream) {
+  const int64_t grid = std::min<int64_t>(a.T, 2 * (int64_t)device_cu_count());
+  hipLaunchKernelGGL((topk_reg_kernel<S, true, kReg2Threads, false>),
+                     dim3((unsigned)grid), dim3(kReg2Threads), 0, stream,
+                     a.logits, a.ld, a.positions, a.k, a.out, a.out_ld, a.T);
+  return hipGetLastError();
+}
+
+static hipError_t launch_topk_reg2(const TopkArgs& a, hipStream_t stream) {
+  constexpr int kSl = 4 * kReg2Threads;
+  switch ((a.ld + kSl - 1) / kSl) {
+#define DSA_REG2(N) case N: return launch_topk_reg2_t<N>(a, stream);
+    DSA_REG2(1) DSA_REG2(2) DSA_REG2(3) DSA_REG2(4) DSA_REG2(5) DSA_REG2(6)
+    DSA_REG2(7) DSA_REG2(8) DSA_REG2(9) DSA_REG2(10) DSA_REG2(11)
+    DSA_REG2(12) DSA_REG2(13) DSA_REG2(14) DSA_REG2(15) DSA_REG2(16)
+    DSA_REG2(17) DSA_REG2(18) DSA_REG2(19) DSA_REG2(20) DSA_REG2(21)
+    DSA_REG2(22) DSA_REG2(23)
+#undef DSA_REG2
+    default: return launch_topk_reg2_t<24>(a, stream);
+  }
+}
+
 static hipError_t launch_topk_reg(const TopkArgs& a, hipStream_t stream) {
+  // sparse selections (the bitmap emit): two 512-thread workgroups per
+  // compute unit unless option 1 asks for the 1024-thread kernel
+  if (options().topk_kernel != 1 && (int64_t)a.k * 8 < a.ld)
+    return launch_topk_reg2(a, stream);
   switch ((a.ld + kRegSlice - 1) / kRegSlice) {
     case 1: return launch_topk_reg_t<1>(a, stream);
     case 2: return launch_topk_reg_t<2>(a, stream);

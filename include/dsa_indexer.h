@@ -403,7 +403,9 @@ int dsa_device_error_flags(int reset);
  * with 16 waves x 1 row but ReLU as an add and an FMA per MFMA output
  * instead of the default's shared linear term), "row_pages_per_wave",
  * "tile_pages_per_split", "topk_kernel" (rows of up to 49152 columns: 1
- * register-resident keys, 2 keys cached in LDS; rows longer than 65536
+ * register-resident keys in one 1024-thread workgroup per compute unit
+ * also for sparse selections, which by default (0 or 4) take two 512-thread
+ * workgroups per compute unit, 2 keys cached in LDS; rows longer than 65536
  * columns: 3 multi-workgroup radix select instead of sample select).
  */
 int dsa_set_option(const char* key, int value);

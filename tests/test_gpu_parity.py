@@ -270,7 +270,7 @@ def test_page_permutation_gives_identical_logits():
     assert torch.equal(tk1, tk2)
 
 
-@pytest.mark.parametrize("kernel", [1, 2])
+@pytest.mark.parametrize("kernel", [1, 2, 4])
 def test_topk_ties_and_constant_rows(kernel):
     _say(f"case: top-k ties, top-k kernel {kernel}")
     binding.dsa_set_option("topk_kernel", kernel)
@@ -290,7 +290,7 @@ def test_topk_ties_and_constant_rows(kernel):
                                               f"ties row {t}")
 
 
-@pytest.mark.parametrize("kernel", [1, 2])
+@pytest.mark.parametrize("kernel", [1, 2, 4])
 @pytest.mark.parametrize("ld", [256, 4096, 8192, 20480, 40960, 49152, 53248])
 def test_topk_row_lengths(ld, kernel):
     """Single-workgroup top-k over row lengths that span one to twelve
@@ -315,14 +315,17 @@ def test_topk_row_lengths(ld, kernel):
                                               f"ld {ld} row {t}")
 
 
+@pytest.mark.parametrize("kernel", [0, 1])
 @pytest.mark.parametrize("k", [512, 2048])
-def test_topk_rows_looped_per_workgroup(k):
+def test_topk_rows_looped_per_workgroup(k, kernel):
     """More rows than compute units: each resident workgroup takes several
     rows in turn with the next row's keys prefetched, so consecutive rows of
     one workgroup mix random, tied, constant, short (<= k) and empty rows.
     k = 512 of 8192 columns takes the column-bitmap emit, k = 2048 the
     per-slice one."""
-    _say(f"case: top-k, 700 rows looped over resident workgroups, k={k}")
+    _say(f"case: top-k, 700 rows looped over resident workgroups, k={k}, "
+         f"top-k kernel {kernel}")
+    binding.dsa_set_option("topk_kernel", kernel)
     T, ld = 700, 8192
     rng = np.random.default_rng(k)
     lg = (rng.standard_normal((T, ld)) * 3).astype(np.float32)
