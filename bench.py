@@ -303,7 +303,7 @@ def trace_summary(args):
     is_dom = _matcher(args.config)
     dom = [n for n in by_grid if is_dom(n)]
     lines = [f"# Kernel trace: {WORKLOADS.get(args.config, args.config)}", "",
-             "Commands (GPU box, from the repository root):", "", "```"]
+             "Commands (from the repository root):", "", "```"]
     lines += args.command + ["```", "",
                              "Durations are per dispatch over every dispatch "
                              "of the run (warm-up, graph replays and the "
@@ -349,7 +349,7 @@ def main():
     if args.pmc_summary:
         return pmc_summary(args)
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; "
+        print(json.dumps({"error": "this benchmark runs on one GPU only; "
                                    "--gpus N > 1 is not supported"}))
         sys.exit(2)
     if args.config == "index_cache":
