@@ -1577,18 +1577,31 @@ static hipError_t launch_topk_reg_t(const TopkArgs& a, hipStream_t stream) {
 }
 
 // 512-thread workgroups without the register prefetch, two per compute
-// unit (sparse selections: the bitmap emit).  A row's selection is a
-// chain of histogram passes and barriers that leaves one 1024-thread
-// workgroup waiting about half its cycles; with two workgroups each one's
-// loads and waits overlap the other's work (prefill top-k 0.46 -> 0.39 ms).
+// unit.  A row's selection is a chain of histogram passes and barriers that
+// leaves one 1024-thread workgroup waiting about half its cycles; with two
+// workgroups each one's loads and waits overlap the other's work.
 constexpr int kReg2Threads = 512;
-template <int S>
+template <int S, bool BITMAP = true>
 static hipError_t launch_topk_reg2_t(const TopkArgs& a, hipStream_t stream) {
   const int64_t grid = std::min<int64_t>(a.T, 2 * (int64_t)device_cu_count());
-  hipLaunchKernelGGL((topk_reg_kernel<S, true, kReg2Threads, false>),
+  hipLaunchKernelGGL((topk_reg_kernel<S, BITMAP, kReg2Threads, false>),
                      dim3((unsigned)grid), dim3(kReg2Threads), 0, stream,
                      a.logits, a.ld, a.positions, a.k, a.out, a.out_ld, a.T);
   return hipGetLastError();
+}
+
+// dense selections (rows of up to 8 slices of 2048 columns)
+constexpr int kReg2DenseMaxRow = 8 * 4 * kReg2Threads;    // 16384
+static hipError_t launch_topk_reg2_dense(const TopkArgs& a,
+                                         hipStream_t stream) {
+  constexpr int kSl = 4 * kReg2Threads;
+  switch ((a.ld + kSl - 1) / kSl) {
+#define DSA_REG2D(N) case N: return launch_topk_reg2_t<N, false>(a, stream);
+    DSA_REG2D(1) DSA_REG2D(2) DSA_REG2D(3) DSA_REG2D(4) DSA_REG2D(5)
+    DSA_REG2D(6) DSA_REG2D(7)
+#undef DSA_REG2D
+    default: return launch_topk_reg2_t<8, false>(a, stream);
+  }
 }
 
 static hipError_t launch_topk_reg2(const TopkArgs& a, hipStream_t stream) {
@@ -1606,10 +1619,16 @@ static hipError_t launch_topk_reg2(const TopkArgs& a, hipStream_t stream) {
 }
 
 static hipError_t launch_topk_reg(const TopkArgs& a, hipStream_t stream) {
-  // sparse selections (the bitmap emit): two 512-thread workgroups per
-  // compute unit unless option 1 asks for the 1024-thread kernel
-  if (options().topk_kernel != 1 && (int64_t)a.k * 8 < a.ld)
-    return launch_topk_reg2(a, stream);
+  // more rows than compute units: two 512-thread workgroups per compute
+  // unit (measured: prefill rows 0.46 -> 0.39 ms; 384 / 1024 dense decode
+  // rows of 8192 columns 11.6 -> 9.5 / 22.6 -> 17.6 us); otherwise one
+  // 1024-thread workgroup per row, faster when every row has a compute unit
+  // to itself (64 rows: 6.5 against 6.9 us).  Option 1 / 4 force either.
+  const int opt = options().topk_kernel;
+  const bool two =
+      opt == 4 || (opt != 1 && a.T > (int64_t)device_cu_count());
+  if (two && (int64_t)a.k * 8 < a.ld) return launch_topk_reg2(a, stream);
+  if (two && a.ld <= kReg2DenseMaxRow) return launch_topk_reg2_dense(a, stream);
   switch ((a.ld + kRegSlice - 1) / kRegSlice) {
     case 1: return launch_topk_reg_t<1>(a, stream);
     case 2: return launch_topk_reg_t<2>(a, stream);

@@ -402,11 +402,12 @@ int dsa_device_error_flags(int reset);
  * 3 tiled with direct loads, 4 row-wise on a (row, page group) grid, 5 tiled
  * with 16 waves x 1 row but ReLU as an add and an FMA per MFMA output
  * instead of the default's shared linear term), "row_pages_per_wave",
- * "tile_pages_per_split", "topk_kernel" (rows of up to 49152 columns: 1
- * register-resident keys in one 1024-thread workgroup per compute unit
- * also for sparse selections, which by default (0 or 4) take two 512-thread
- * workgroups per compute unit, 2 keys cached in LDS; rows longer than 65536
- * columns: 3 multi-workgroup radix select instead of sample select).
+ * "tile_pages_per_split", "topk_kernel" (rows of up to 49152 columns, keys
+ * in registers: by default one 1024-thread workgroup per row, two 512-thread
+ * workgroups per compute unit when the rows outnumber the compute units; 1
+ * always the former, 4 always the latter; 2 keys cached in LDS; rows longer
+ * than 65536 columns: 3 multi-workgroup radix select instead of sample
+ * select).
  */
 int dsa_set_option(const char* key, int value);
 
