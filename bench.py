@@ -437,6 +437,20 @@ def main():
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / K
 
+    # Spread: the same replays again with an event between each (per-step
+    # time of each replay of R steps); reported beside the mean above.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda._sleep(int(20e6))
+    evs[0].record()
+    for i in range(reps):
+        graph.replay()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) / R for i in range(reps))
+    pct = {f"p{q}": round(per_step[min(len(per_step) - 1,
+                                       int(q / 100 * len(per_step)))], 5)
+           for q in (10, 50, 90)}
+
     # Per-kernel durations: for each kernel, NK back-to-back launches on the
     # launch stream (rotating over the K-cache copies) between two HIP
     # events, queued behind a GPU sleep so that the host has enqueued them
@@ -542,6 +556,7 @@ def main():
         "metric": METRIC, "value": round(T / (ms_step * 1e-3), 1),
         "unit": "query-rows/s", "n_gpus": 1, "steps": K,
         "warmup": max(args.warmup, R), "ms_per_step": round(ms_step, 5),
+        "ms_per_step_spread": pct,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8_e4m3 (fp32 accumulate)", "data": "synthetic",
         "config": {"workload": WORKLOADS[args.config], "rows": T,
