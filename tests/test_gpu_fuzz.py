@@ -68,3 +68,102 @@ def test_random_configuration(seed):
         parity.check_topk_exact_on_gpu_logits(tk[t], lg[t], p, b.k,
                                               f"seed {seed} row {t}")
     assert binding.dsa_device_error_flags(reset=True) == 0
+
+
+# ------------------------------------------- the paths around the hot path --
+from oracle import chunking, handoff  # noqa: E402
+from oracle import k_write as ok  # noqa: E402
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_random_k_write_and_slots(seed):
+    """Random block tables (some entries -1), query layouts and positions
+    (some -1 or past the table): plain and compressed slot mappings, then
+    the K write of random keys into a pre-filled pool, byte for byte."""
+    rng = np.random.Generator(np.random.PCG64(5000 + seed))
+    R = int(rng.integers(1, 6))
+    width = int(rng.integers(1, 12))
+    pool = R * width + int(rng.integers(0, 8))
+    bt = rng.permutation(pool).astype(np.int32)[: R * width].reshape(R, width)
+    bt[rng.random(bt.shape) < 0.1] = -1
+    T = int(rng.integers(1, 400))
+    cuts = np.sort(rng.integers(0, T + 1, R - 1))
+    qsl = np.r_[0, cuts, T].astype(np.int32)
+    pos = rng.integers(-1, width * 64 + 40, T).astype(np.int32)
+    print(f"case: seed {seed}: R={R} width={width} T={T}", flush=True)
+    slots = binding.dsa_slot_mapping(_dev(bt), _dev(qsl), _dev(pos))
+    ref = ok.slot_mapping(bt, qsl, pos)
+    assert np.array_equal(slots.cpu().numpy(), ref)
+    ratio = int(rng.choice([1, 2, 4, 128]))
+    bs = int(rng.choice([1, 2, 64]))
+    cs, pc = binding.dsa_compressed_slot_mapping(_dev(bt), _dev(qsl),
+                                                 _dev(pos), ratio, bs)
+    assert np.array_equal(cs.cpu().numpy(),
+                          ok.compressed_slot_mapping(bt, qsl, pos, ratio, bs))
+    assert np.array_equal(pc.cpu().numpy(), ok.compressed_positions(pos, ratio))
+    # distinct slots only: the write path never stores two tokens at one slot
+    keep = ref.copy()
+    seen = set()
+    for i, sl in enumerate(keep):
+        if sl >= 0 and sl in seen:
+            keep[i] = -1
+        seen.add(int(sl))
+    k = torch.from_numpy((rng.standard_normal((T, 128)) *
+                          rng.choice([1e-3, 1.0, 50.0])).astype(np.float32)
+                         ).bfloat16()
+    cache0 = rng.integers(0, 256, (pool, 8448), dtype=np.uint8)
+    want = ok.write_k_cache(cache0.copy(), k.float().numpy(), keep)
+    cache = _dev(cache0)
+    binding.dsa_indexer_k_write(k.cuda(), _dev(keep), cache)
+    torch.cuda.synchronize()
+    assert np.array_equal(cache.cpu().numpy(), want)
+    assert binding.dsa_device_error_flags(reset=True) == 0
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_random_handoff_rows(seed):
+    """Random top-k rows (ascending positions, -1 tails, indices beyond the
+    block table) as slots and as the mask, exactly."""
+    rng = np.random.Generator(np.random.PCG64(6000 + seed))
+    R = int(rng.integers(1, 5))
+    width = int(rng.integers(1, 600))
+    bt = rng.integers(-1, 100000, (R, width)).astype(np.int32)
+    T = int(rng.integers(1, 40))
+    qsl = np.r_[0, np.sort(rng.integers(0, T + 1, R - 1)), T].astype(np.int32)
+    k = int(rng.integers(1, 3000))
+    ld = 256 * int(rng.integers(1, 200))
+    tk = np.full((T, k), -1, np.int32)
+    for t in range(T):
+        n = int(rng.integers(0, k + 1))
+        cols = np.sort(rng.choice(ld + 64, min(n, ld + 64), replace=False))
+        tk[t, : cols.size] = cols
+    print(f"case: seed {seed}: T={T} k={k} ld={ld} width={width}", flush=True)
+    slots = binding.dsa_topk_to_slots(_dev(tk), _dev(bt), _dev(qsl))
+    mask = binding.dsa_topk_mask(_dev(tk), ld)
+    torch.cuda.synchronize()
+    assert np.array_equal(slots.cpu().numpy(),
+                          handoff.topk_to_slots(tk, bt, qsl))
+    assert np.array_equal(mask.cpu().numpy(), handoff.topk_mask(tk, ld))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_chunked_forward(seed):
+    """The chunked forward at a random chunk size equals the forward, bit
+    for bit, on the random configurations above."""
+    b = _case(seed * 7 + 1)
+    rows = int(np.random.default_rng(seed).integers(1, b.T + 1))
+    print(f"case: seed {seed}: T={b.T} H={b.H} rows/chunk={rows}", flush=True)
+    d = parity.upload(b)
+    _, ref = binding.dsa_indexer_forward(
+        d["q_bf16"], d["weights"], d["k_cache"], d["block_table"], d["qsl"],
+        d["positions"], b.ld, b.k)
+    out = binding.dsa_indexer_forward_chunked(
+        d["q_bf16"], d["weights"], d["k_cache"], d["block_table"], d["qsl"],
+        d["positions"], b.ld, b.k, rows_per_chunk=rows)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert chunking.pieces(b.T, rows)[-1][1] == b.T
