@@ -3,6 +3,7 @@ call) through the C ABI: against the separate entry points bit for bit."""
 
 import sys
 
+import numpy as np
 import pytest
 import torch
 
@@ -150,3 +151,84 @@ def test_forward_rejects_small_workspace():
     with pytest.raises(binding.DsaError) as e:
         _forward(b, d, workspace=ws)
     assert e.value.status == binding.DSA_ERR_WORKSPACE
+
+
+def _graph_check(run, out, replays=4):
+    """Capture run() in a HIP graph on a side stream; every replay (with a
+    fill of the output and eager work between replays) equals the eager
+    result bit for bit."""
+    run()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        run()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            run()
+    torch.cuda.synchronize()
+    for i in range(replays):
+        out.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {i}"
+        run()                                  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"eager after replay {i}"
+
+
+def test_chunked_forward_graph_replays():
+    """The chunked forward (its per-chunk query_start_loc kernel included)
+    captured in a HIP graph."""
+    _say("case: chunked forward in a HIP graph")
+    b = synth.build_batch(np.random.Generator(np.random.PCG64(41)),
+                          [3000, 1200], [list(range(2900, 3000)),
+                                         list(range(1100, 1200))],
+                          H=64, k=256)
+    d = parity.upload(b)
+    rows = 37
+    need = binding.dsa_forward_chunked_workspace_size(b.T, b.R, b.H, b.ld,
+                                                      b.k, rows)
+    ws = torch.empty((need,), dtype=torch.uint8, device="cuda")
+    tk = torch.empty((b.T, b.k), dtype=torch.int32, device="cuda")
+
+    def run():
+        binding.dsa_indexer_forward_chunked(
+            d["q_bf16"], d["weights"], d["k_cache"], d["block_table"],
+            d["qsl"], d["positions"], b.ld, b.k, rows_per_chunk=rows, out=tk,
+            workspace=ws)
+    _graph_check(run, tk)
+    assert binding.dsa_device_error_flags(reset=True) == 0
+
+
+def test_index_cache_run_graph_replays():
+    """A five-layer IndexCache run (freq 2, chunked F layers) captured in a
+    HIP graph."""
+    _say("case: index cache run in a HIP graph")
+    L = 5
+    mask = binding.dsa_index_cache_mask(L, freq=2, offset=1)
+    full = [l for l in range(L) if not mask[l]]
+    batches = synth.index_cache_layers(full, seed=17, R=8, context=2000,
+                                       H=16, k=128)
+    ref = batches[full[0]]
+    layers = [None if batches.get(l) is None else {
+        "q_bf16": batches[l].q_bf16.cuda(),
+        "weights": torch.from_numpy(batches[l].weights).cuda(),
+        "k_cache": torch.from_numpy(batches[l].k_cache).cuda()}
+        for l in range(L)]
+    bt = torch.from_numpy(ref.block_table).cuda()
+    qsl = torch.from_numpy(ref.query_start_loc).cuda()
+    pos = torch.from_numpy(ref.positions).cuda()
+    buf = torch.empty((ref.T, 128), dtype=torch.int32, device="cuda")
+    need = binding.dsa_run_workspace_size(ref.T, ref.R, 16, ref.ld, 128, 3)
+    ws = torch.empty((need,), dtype=torch.uint8, device="cuda")
+
+    def run():
+        binding.dsa_index_cache_run(layers, bt, qsl, pos, ref.ld, 128, buf,
+                                    freq=2, offset=1, rows_per_chunk=3,
+                                    workspace=ws)
+    _graph_check(run, buf)
+    assert binding.dsa_device_error_flags(reset=True) == 0
