@@ -1,7 +1,7 @@
 """Seeded random small configurations through the C ABI against the oracle:
 request counts, context lengths, query rows per request (one per request,
-a few, many, or over a hundred single-row requests -- the balanced, tiled
-and row-wise logits kernels), head
+a few, many in any order with repeated positions, or over a hundred
+single-row requests -- the balanced, tiled and row-wise logits kernels), head
 counts 1..64, index_topk from 1 to beyond the context, and row strides with
 unused columns.  Every case: logits under the stated tolerance, top-k
 within the tie window and exactly the top-k of the GPU's own logits."""
@@ -38,7 +38,10 @@ def _case(seed):
         else:
             m = int(rng.integers(1, 4 if mode == 1 else 41))
             m = min(m, L)
-            pos.append(sorted(rng.choice(L, m, replace=False).tolist()))
+            if mode == 2:                 # any order, positions may repeat
+                pos.append(rng.integers(0, L, m).tolist())
+            else:
+                pos.append(sorted(rng.choice(L, m, replace=False).tolist()))
     H = HEADS[seed % len(HEADS)]
     k = int(rng.choice([1, 7, 64, 300, 2048]))
     b = synth.build_batch(rng, ctx, pos, H=H, k=k,
