@@ -31,6 +31,7 @@ __global__ __launch_bounds__(256) void topk_to_slots_kernel(
 }
 
 constexpr int kMaskChunk = 16384;            // columns per workgroup
+typedef float f4v __attribute__((ext_vector_type(4)));
 constexpr int kMaskThreads = 256;
 
 // Grid (T, ceil(ld / 16384)): the workgroup marks the row's selected
@@ -63,7 +64,11 @@ __global__ __launch_bounds__(kMaskThreads) void topk_mask_kernel(
                                    (b & 2u) ? 0.f : -INFINITY,
                                    (b & 4u) ? 0.f : -INFINITY,
                                    (b & 8u) ? 0.f : -INFINITY);
-    *reinterpret_cast<float4*>(out + c) = val;
+    // non-temporal: the mask is read by the attention later, not here, and
+    // caching a stream of this size only displaces other lines (prefill
+    // 1.34 GB: 0.295 -> 0.261 ms)
+    const f4v nv = {val.x, val.y, val.z, val.w};
+    __builtin_nontemporal_store(nv, reinterpret_cast<f4v*>(out + c));
   }
 }
 
