@@ -201,6 +201,8 @@ int64_t dsa_logits_chunk_rows(int64_t T, int64_t ld, size_t budget_bytes);
  * rows are scored into the workspace with the kernel class the whole batch
  * would use, and their top-k is written to out rows a .. a + n - 1.  out
  * equals dsa_indexer_forward's bit for bit, whatever rows_per_chunk.
+ * Errors as for dsa_indexer_forward; also DSA_ERR_INVALID_ARG for
+ * rows_per_chunk < 1 and DSA_ERR_WORKSPACE for a smaller workspace.
  */
 int dsa_indexer_forward_chunked(const void* q_bf16, const float* weights,
                                 const uint8_t* k_cache, int64_t num_pages,
@@ -371,6 +373,8 @@ int dsa_indexer_k_write(const void* k_bf16, int64_t N, int head_dim,
  *   block_table  device, int32 [R, bt_stride]; query_start_loc int32 [R+1].
  *   slots        device, out: int64 [T, k] (row stride k); -1 for a -1
  *                entry or an index without a block-table page.
+ * DSA_ERR_INVALID_ARG unless T >= 0, k >= 1, topk_ld >= k, R >= 1 and
+ * bt_stride >= 1, or for a null pointer when T > 0; T == 0 is a no-op.
  */
 int dsa_topk_to_slots(const int32_t* topk, int64_t T, int k, int64_t topk_ld,
                       const int32_t* block_table, int64_t bt_stride,
@@ -383,7 +387,10 @@ int dsa_topk_to_slots(const int32_t* topk, int64_t T, int k, int64_t topk_ld,
  * and -inf elsewhere, added to q k^T).
  *   topk  device, int32 [T, topk_ld], k entries used per row (-1 ignored).
  *   mask  device, out: fp32 [T, ld], ld % 256 == 0; every column written:
- *         0 if the row selects it, -inf otherwise.
+ *         0 if the row selects it, -inf otherwise (indices >= ld ignored).
+ * The mask is written with non-temporal stores.  DSA_ERR_INVALID_ARG
+ * unless T >= 0, k >= 1, topk_ld >= k and ld is a positive multiple of
+ * 256, or for a null pointer when T > 0; T == 0 is a no-op.
  */
 int dsa_topk_mask(const int32_t* topk, int64_t T, int k, int64_t topk_ld,
                   float* mask, int64_t ld, void* stream);
