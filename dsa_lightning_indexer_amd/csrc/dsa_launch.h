@@ -55,6 +55,7 @@ struct Options {
   int logits_kernel = 0;        // 1 row-wise, 2 tiled 8x2, 3 tiled direct, 4 row grid, 5 tiled 16x1 with the two-op epilogue
   int row_pages_per_wave = 0;
   int tile_pages_per_split = 0;
+  int row_head_waves = 0;       // decode: 1 + head waves per row (0: one)
   int topk_kernel = 0;          // 0/1 register rows, 2 LDS-cached rows, 3 long rows by multi-WG radix, register rows: 0 two 512-thread workgroups per CU when rows outnumber CUs, else one 1024-thread, 1 always 1024, 4 always 512
 };
 Options& options();

@@ -378,7 +378,8 @@ struct RowSpan {
 // (the row is left untouched and wave 0 raises the flag).
 template <int NCH>
 __device__ __forceinline__ RowSpan balanced_span(const LogitsArgs& a, int D,
-                                                 int per_xcd, int wv) {
+                                                 int per_xcd, int wv,
+                                                 int head_pages) {
   const int lane = lane_id();
   int pl[NCH], n[NCH];
   uint32_t incl[NCH];                         // page prefix over the batch
@@ -391,7 +392,7 @@ __device__ __forceinline__ RowSpan balanced_span(const LogitsArgs& a, int D,
     const bool ok = pl[c] >= 0 && pl[c] < a.ld &&
                     (int64_t)(pl[c] >> 6) < a.bt_stride;
     bad |= in && !ok;
-    n[c] = (in && ok) ? (pl[c] >> 6) + 1 : 0;
+    n[c] = (in && ok) ? max(0, (pl[c] >> 6) + 1 - head_pages) : 0;
     incl[c] = total + wave_inclusive_scan((uint32_t)n[c]);
     total = __builtin_amdgcn_readlane(incl[c], 63);
   }
@@ -430,21 +431,40 @@ __device__ __forceinline__ RowSpan balanced_span(const LogitsArgs& a, int D,
     base += __builtin_amdgcn_readlane(wincl, 63);
   }
   sp.row = wave_uniform(sp.row);
-  sp.jb = wave_uniform(sp.jb);
-  sp.je = wave_uniform(sp.je);
+  sp.jb = wave_uniform(sp.jb) + head_pages;
+  sp.je = wave_uniform(sp.je) + head_pages;
   sp.p = wave_uniform(sp.p);
   return sp;
 }
 
+// head_waves > 0: the first head_waves workgroups are head waves: wave
+// (t, i) = (b / HW, b % HW) takes pages [i D, i D + D) of row t, known
+// without the positions, so its block-table, q and position loads go out
+// together and its K loads one round trip before the balanced waves'
+// (which first need every row's position); the balanced waves share the
+// pages from HW D on.  head_waves is a multiple of 8 (XCD parity).
 template <int MT, bool FULL, int D, int NCH>
 __global__ __launch_bounds__(64) void logits_balanced_kernel(LogitsArgs a,
-                                                             int per_xcd) {
+                                                             int per_xcd,
+                                                             int hw,
+                                                             int head_waves) {
   const int lane = lane_id();
   const int i16 = lane & 15, g = lane >> 4;
-  const RowSpan sp = balanced_span<NCH>(a, D, per_xcd, (int)blockIdx.x);
-  if (sp.row < 0) return;
+  const bool head = (int)blockIdx.x < head_waves;
+  RowSpan sp;
+  if (head) {
+    const int hb = (int)blockIdx.x;
+    sp = RowSpan{hb / hw, (hb % hw) * D, (hb % hw) * D + D, 0};
+    if (sp.row >= a.T) return;
+  } else {
+    sp = balanced_span<NCH>(a, D, per_xcd, (int)blockIdx.x - head_waves,
+                            hw * D);
+    if (sp.row < 0) return;
+  }
   const int64_t t = sp.row;
-  const int p = sp.p, jb = sp.jb, je = sp.je;
+  int p = sp.p, je = sp.je;
+  const int jb = sp.jb;
+  if (head) p = load_uniform(a.positions, t);
 
   // request guess r = t (one query row per request), checked below; the
   // page ids of the first chunk are fetched with it
@@ -460,6 +480,13 @@ __global__ __launch_bounds__(64) void logits_balanced_kernel(LogitsArgs a,
   float w[MT][4];
   load_head_weights<MT, FULL>(a.weights + t * a.H, a.q_scale + t * a.H, a.H,
                               w);
+  if (head) {
+    // the position arrived with the other loads: clip the range, or leave
+    // (a bad position is flagged by the balanced wave that reads them all)
+    if (p < 0 || p >= a.ld || (int64_t)(p >> 6) >= a.bt_stride) return;
+    je = min(je, (p >> 6) + 1);
+    if (jb >= je) return;
+  }
   if (!(q0 <= t && t < q1)) {                 // rows are not one per request
     r = wave_uniform(request_of_row_wave(a.qsl, a.R, t));
     btr = a.block_table + (int64_t)r * a.bt_stride;
@@ -1339,13 +1366,20 @@ static hipError_t launch_logits_mt(const LogitsArgs& a, hipStream_t stream,
     const int64_t part = (pmax + 7) / 8;
     const int64_t per_xcd =
         std::max<int64_t>(1, std::min<int64_t>((part + D - 1) / D, 1 << 13));
-    const dim3 grid((unsigned)(8 * (per_xcd + a.T)));
+    // one head wave per row (measured: 10.54 -> 10.39 us on the decode
+    // batch; more head waves gain nothing, the balanced waves' chain of
+    // three round trips still ends the kernel); option value 1 + n sets n
+    const int hw = o.row_head_waves > 0 ? o.row_head_waves - 1 : 1;
+    const int64_t head_waves = hw ? (a.T * hw + 7) / 8 * 8 : 0;
+    const dim3 grid((unsigned)(head_waves + 8 * (per_xcd + a.T)));
     const bool two = a.T > 64;
 #define DSA_BAL(DD)                                                          \
     if (two) hipLaunchKernelGGL((logits_balanced_kernel<MT, FULL, DD, 2>),    \
-                                grid, dim3(64), 0, stream, a, (int)per_xcd);  \
+                                grid, dim3(64), 0, stream, a, (int)per_xcd,   \
+                                hw, (int)head_waves);                         \
     else hipLaunchKernelGGL((logits_balanced_kernel<MT, FULL, DD, 1>),        \
-                            grid, dim3(64), 0, stream, a, (int)per_xcd);
+                            grid, dim3(64), 0, stream, a, (int)per_xcd, hw,   \
+                            (int)head_waves);
     if (D == 2) { DSA_BAL(2) } else if (D == 3) { DSA_BAL(3) } else { DSA_BAL(4) }
 #undef DSA_BAL
   } else if (!tiled) {

@@ -409,6 +409,8 @@ int dsa_device_error_flags(int reset);
  * 3 tiled with direct loads, 4 row-wise on a (row, page group) grid, 5 tiled
  * with 16 waves x 1 row but ReLU as an add and an FMA per MFMA output
  * instead of the default's shared linear term), "row_pages_per_wave",
+ * "row_head_waves" (decode rows: 1 + the waves per row that take its first
+ * pages before the positions are read; default one such wave, 1 = none),
  * "tile_pages_per_split", "topk_kernel" (rows of up to 49152 columns, keys
  * in registers: by default one 1024-thread workgroup per row, two 512-thread
  * workgroups per compute unit when the rows outnumber the compute units; 1

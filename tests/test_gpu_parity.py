@@ -27,7 +27,7 @@ def _clear_flags():
     binding.dsa_device_error_flags(reset=True)
     yield
     for key in ("logits_kernel", "row_pages_per_wave", "tile_pages_per_split",
-                "topk_kernel"):
+                "topk_kernel", "row_head_waves"):
         binding.dsa_set_option(key, 0)
 
 
@@ -122,6 +122,35 @@ def test_decode_batch_all_rows(kernel):
          f"max |err| / M = {err_m:.3e} (2^{np.log2(err_m):.1f}), "
          f"padded rows {padded}")
     assert padded > 0                 # the batch exercises -1 padding
+    _assert_no_device_errors()
+
+
+@pytest.mark.parametrize("hw", [0, 2, 4, 8])
+def test_decode_head_waves(hw):
+    """Head waves on each row's first pages (option value 1 + their number;
+    0 = the default one): logits bit-identical to the balanced kernel
+    without them (value 1; same per-page arithmetic), top-k too; also with
+    several rows per request (the request guess fails)."""
+    _say(f"case: decode with head-wave option {hw}")
+    for b in (synth.decode(R=64, lo=100, hi=3000, seed=31),
+              synth.build_batch(np.random.Generator(np.random.PCG64(8)),
+                                [900, 2000, 40],
+                                [[899, 500, 3], [1999, 1000, 77, 64], [39]],
+                                H=64, k=256)):
+        binding.dsa_set_option("row_head_waves", 1)            # none
+        _, _, lg0, tk0 = parity.run_gpu(b)
+        binding.dsa_set_option("row_head_waves", hw)
+        _, _, lg1, tk1 = parity.run_gpu(b)
+        for t in range(b.T):
+            p = int(b.positions[t])
+            assert torch.equal(lg0[t, : p + 1], lg1[t, : p + 1]), f"row {t}"
+        assert torch.equal(tk0, tk1)
+        ora = parity.oracle_logits(b, rows=[0, b.T - 1])
+        mag = parity.magnitude(b, rows=[0, b.T - 1])
+        lg1h = lg1.cpu().numpy()
+        for i, t in enumerate([0, b.T - 1]):
+            parity.check_logits_row(lg1h[t], ora[i], int(b.positions[t]),
+                                    f"row {t}", mag[i])
     _assert_no_device_errors()
 
 
