@@ -327,3 +327,36 @@ def test_forward_chunked_rejects_bad_arguments():
     need = binding.dsa_forward_chunked_workspace_size(4, 1, 16, 256, 8, 2)
     assert need >= 4 * 16 * 132 + 2 * 256 * 4 + 8
     assert binding.dsa_forward_chunked_workspace_size(4, 1, 16, 256, 8, 0) == 0
+
+
+def test_missing_library_raises(monkeypatch):
+    """No CPU fallback: without the built library every entry point raises
+    before doing anything."""
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", "/nonexistent/libdsa_indexer.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.dsa_index_cache_mask(4)
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.dsa_logits_chunk_rows(8, 256, 1 << 20)
+
+
+def test_product_package_never_imports_the_oracle():
+    """The product path (binding, build, synthetic inputs) shares no code
+    with the oracle: no module of the package imports it."""
+    import ast
+    import os
+    pkg = os.path.dirname(binding.__file__)
+    for name in os.listdir(pkg):
+        if not name.endswith(".py"):
+            continue
+        tree = ast.parse(open(os.path.join(pkg, name)).read())
+        for node in ast.walk(tree):
+            mods = []
+            if isinstance(node, ast.Import):
+                mods = [a.name for a in node.names]
+            elif isinstance(node, ast.ImportFrom):
+                mods = [node.module or ""]
+            for m in mods:
+                assert not m.split(".")[0] == "oracle", (name, m)
