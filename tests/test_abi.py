@@ -342,21 +342,27 @@ def test_missing_library_raises(monkeypatch):
         binding.dsa_logits_chunk_rows(8, 256, 1 << 20)
 
 
-def test_product_package_never_imports_the_oracle():
-    """The product path (binding, build, synthetic inputs) shares no code
-    with the oracle: no module of the package imports it."""
+def _imports(path):
     import ast
+    tree = ast.parse(open(path).read())
+    for node in ast.walk(tree):
+        if isinstance(node, ast.Import):
+            yield from (a.name for a in node.names)
+        elif isinstance(node, ast.ImportFrom) and node.level == 0:
+            yield node.module or ""
+
+
+def test_product_and_oracle_share_no_code():
+    """The product path (binding, build, synthetic inputs) and the oracle
+    import nothing of each other."""
     import os
     pkg = os.path.dirname(binding.__file__)
+    root = os.path.dirname(pkg)
     for name in os.listdir(pkg):
-        if not name.endswith(".py"):
-            continue
-        tree = ast.parse(open(os.path.join(pkg, name)).read())
-        for node in ast.walk(tree):
-            mods = []
-            if isinstance(node, ast.Import):
-                mods = [a.name for a in node.names]
-            elif isinstance(node, ast.ImportFrom):
-                mods = [node.module or ""]
-            for m in mods:
-                assert not m.split(".")[0] == "oracle", (name, m)
+        if name.endswith(".py"):
+            for m in _imports(os.path.join(pkg, name)):
+                assert m.split(".")[0] != "oracle", (name, m)
+    for name in os.listdir(os.path.join(root, "oracle")):
+        if name.endswith(".py"):
+            for m in _imports(os.path.join(root, "oracle", name)):
+                assert m.split(".")[0] != "dsa_lightning_indexer_amd", (name, m)
