@@ -919,12 +919,19 @@ __device__ __forceinline__ void lds_copy(const void* base, int bytes,
   d[3] = 0x00020000u;
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(const lds_u8*)lds);
+  // m0 is a reserved register, so the compiler warns that the clobber below
+  // may be ignored: it would then assume m0 unchanged.  The kernels that use
+  // this copy contain no compiler-generated read of m0 (their only m0
+  // writes are these, each read by the copy in the same statement).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
   if (SIZE == 16)
     asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :: "v"(voff), "s"(d), "s"(m0) : "memory", "m0");
   else
     asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
                  :: "v"(voff), "s"(d), "s"(m0) : "memory", "m0");
+#pragma clang diagnostic pop
 }
 
 template <int MT, bool FULL, bool LIN, int PP, bool PF>

@@ -627,13 +627,12 @@ __device__ void reg_emit(const RegKeys<S, NT>& r, int k, uint32_t mask,
 // nibbles with DPP and one writes the word, so every word of the row is
 // written once, no atomics), one workgroup scan over the words' packed
 // (selected, tie) counts gives every word its first slot, and each lane
-// expands only the set bits of its two words.  Ties are taken lowest column
+// expands only the set bits of its words.  Ties are taken lowest column
 // first up to k_tie.
 template <int NT, int S>
 __device__ void reg_emit_columns(const RegKeys<S, NT>& r, int k, uint32_t mask,
                                  uint32_t thr, uint32_t k_tie, int32_t* orow,
                                  RegTopkShared<NT, S>& sh) {
-  constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
