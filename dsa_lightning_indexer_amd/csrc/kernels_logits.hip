@@ -719,7 +719,7 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a,
       const int rr = g >> 1;
       const int tok = 16 * (2 * ntp + (g & 1)) + i16;
       const int pr = rr ? prow[1] : prow[0];
-      if (pr >= 0) {
+      if (pr >= 0 && jp <= (pr >> 6)) {        // the row's own pages only
         const int s = jp * kPageTokens + tok;
         const float val = (s <= pr && page_ok) ? tot * s_scale[buf][tok]
                                                : -INFINITY;
@@ -1092,11 +1092,12 @@ __global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
       const float lv = s_lin[pbuf][wave][kPageTokens * h + tok];
       const float ks = s_scale[psbuf][h][tok];
       const float val = (s <= prow && pok[h]) ? (pt[h] + lv) * ks : -INFINITY;
-      // the page's 64 logits as a buffer, empty for a padding row or a page
-      // past the range: an unconditional store, no 64-bit address math
+      // the page's 64 logits as a buffer, empty for a padding row, a page
+      // past the range or past the row's own last page (a shorter row of
+      // the tile): an unconditional store, no 64-bit address math
       const __amdgpu_buffer_rsrc_t ro = make_rsrc(
           orow + (int64_t)min(pj, npages - 1) * kPageTokens,
-          prow >= 0 && pj < je ? kPageTokens * 4 : 0);
+          prow >= 0 && pj < je && pj <= (prow >> 6) ? kPageTokens * 4 : 0);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, 4 * tok,
                                             0, 0);
     }
@@ -1178,7 +1179,7 @@ __global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
       } else {
         const float val = (s <= prow && page_ok) ? tot * s_scale[sbuf][h][tok]
                                                  : -INFINITY;
-        if (prow >= 0 && pj < je) orow[s] = val;
+        if (prow >= 0 && pj < je && pj <= (prow >> 6)) orow[s] = val;
       }
     }
     if (LIN) { pjp = jp; pbuf = buf; psbuf = sbuf; }
@@ -1321,7 +1322,7 @@ __global__ __launch_bounds__(512) void logits_tile_direct_kernel(
       }
       // lane group g ends with (row g >> 1, N-tile 2*ntp + (g & 1))
       const float tot = reduce_scatter4(v[0][0], v[0][1], v[1][0], v[1][1]);
-      if (pr_out >= 0) {
+      if (pr_out >= 0 && jp <= (pr_out >> 6)) {  // the row's own pages only
         const int s = jp * kPageTokens + 16 * (2 * ntp + (g & 1)) + i16;
         orow[s] = (s <= pr_out && ok) ? tot * ks[ntp] : -INFINITY;
       }

@@ -1,0 +1,94 @@
+"""What each entry point writes and what it leaves alone, as the header
+states it: a logits row t (position p) gets values on columns 0..p, -inf on
+p < s < 64 ceil((p + 1) / 64) and nothing after that, whatever the other
+rows of its tile reach; a top-k row gets slots 0..k-1 only.  Every logits
+kernel class is forced in turn, on one row per request (decode) and on many
+rows per request at scattered positions (tiles whose rows end on different
+pages), with spare columns and spare output slots pre-filled."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from dsa_lightning_indexer_amd import binding, synth
+from tests import parity
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(),
+                                 reason="needs a GPU")]
+
+SENTINEL = 7.25
+SLOT_SENTINEL = -77
+
+
+@pytest.fixture(autouse=True)
+def _reset():
+    binding.dsa_device_error_flags(reset=True)
+    yield
+    binding.dsa_set_option("logits_kernel", 0)
+    binding.dsa_set_option("topk_kernel", 0)
+
+
+def _batch(layout):
+    rng = np.random.Generator(np.random.PCG64(4242 if layout == "decode"
+                                              else 4343))
+    if layout == "decode":
+        ctx = rng.integers(1, 1500, 20).tolist()
+        pos = [[L - 1] for L in ctx]
+    else:
+        # rows of one request in any order, spanning many pages: a 16-row
+        # tile holds rows that end on different pages
+        ctx = [1900, 700, 64]
+        pos = [rng.integers(0, 1900, 37).tolist(),
+               rng.integers(0, 700, 21).tolist(),
+               [63, 0, 31]]
+    b = synth.build_batch(rng, ctx, pos, H=16, k=100)
+    b.ld += 512                                   # spare columns
+    return b
+
+
+@pytest.mark.parametrize("layout", ["decode", "scattered"])
+@pytest.mark.parametrize("kernel", [0, 1, 2, 3, 4, 5])
+def test_logits_written_region(layout, kernel):
+    b = _batch(layout)
+    print(f"case: layout {layout} logits_kernel {kernel} T={b.T} ld={b.ld}",
+          flush=True)
+    sys.stdout.flush()
+    binding.dsa_set_option("logits_kernel", kernel)
+    d = parity.upload(b)
+    q8, qs = binding.dsa_quantize_q(d["q_bf16"])
+    lg = torch.full((b.T, b.ld), SENTINEL, dtype=torch.float32, device="cuda")
+    binding.dsa_indexer_logits(q8, qs, d["weights"], d["k_cache"],
+                               d["block_table"], d["qsl"], d["positions"],
+                               b.ld, logits=lg)
+    torch.cuda.synchronize()
+    g = lg.cpu().numpy()
+    ora = parity.oracle_logits(b)
+    mag = parity.magnitude(b)
+    for t in range(b.T):
+        p = int(b.positions[t])
+        end = 64 * ((p + 1 + 63) // 64)
+        parity.check_logits_row(g[t], ora[t], p, f"row {t}", mag[t])
+        assert np.all(np.isneginf(g[t, p + 1:end])), f"row {t}: tail of page"
+        assert np.all(g[t, end:] == SENTINEL), f"row {t}: column past its pages"
+    assert binding.dsa_device_error_flags(reset=True) == 0
+
+
+@pytest.mark.parametrize("topk_kernel", [0, 1, 2, 4])
+def test_topk_writes_only_k_slots(topk_kernel):
+    b = _batch("scattered")
+    print(f"case: topk_kernel {topk_kernel} T={b.T}", flush=True)
+    binding.dsa_set_option("topk_kernel", topk_kernel)
+    d = parity.upload(b)
+    _, _, lg, ref = parity.run_gpu(b, d)
+    spare = 40
+    out = torch.full((b.T, b.k + spare), SLOT_SENTINEL, dtype=torch.int32,
+                     device="cuda")
+    binding.dsa_indexer_topk(lg, d["positions"], b.k, out=out)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.array_equal(o[:, : b.k], ref.cpu().numpy())
+    assert np.all(o[:, b.k:] == SLOT_SENTINEL)
+    assert binding.dsa_device_error_flags(reset=True) == 0
