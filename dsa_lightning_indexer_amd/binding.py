@@ -434,9 +434,11 @@ def dsa_indexer_k_write(k_bf16, slot_mapping, k_cache, stream=None):
 
 
 def dsa_topk_to_slots(topk, block_table, query_start_loc, slots=None,
-                      stream=None):
-    """int64 [T, k] physical slot of every top-k entry (-1 stays -1)."""
-    T, k = topk.shape
+                      stream=None, k=None):
+    """int64 [T, k] physical slot of every top-k entry (-1 stays -1); the
+    first k (default: all) entries of each topk row are used."""
+    T, width = topk.shape
+    k = width if k is None else int(k)
     R = block_table.shape[0]
     dev = topk.device
     if query_start_loc.numel() != R + 1:
@@ -445,7 +447,7 @@ def dsa_topk_to_slots(topk, block_table, query_start_loc, slots=None,
         slots = torch.empty((T, k), dtype=torch.int64, device=dev)
     with torch.cuda.device(dev):
         _check(lib().dsa_topk_to_slots(
-            _dev_ptr(topk, torch.int32, "topk"), T, k, k,
+            _dev_ptr(topk, torch.int32, "topk"), T, k, width,
             _dev_ptr(block_table, torch.int32, "block_table"),
             block_table.shape[1],
             _dev_ptr(query_start_loc, torch.int32, "query_start_loc"), R,
@@ -453,15 +455,17 @@ def dsa_topk_to_slots(topk, block_table, query_start_loc, slots=None,
     return slots
 
 
-def dsa_topk_mask(topk, ld, mask=None, stream=None):
-    """fp32 [T, ld]: 0 at the selected columns, -inf elsewhere."""
-    T, k = topk.shape
+def dsa_topk_mask(topk, ld, mask=None, stream=None, k=None):
+    """fp32 [T, ld]: 0 at the selected columns, -inf elsewhere; the first k
+    (default: all) entries of each topk row are used."""
+    T, width = topk.shape
+    k = width if k is None else int(k)
     dev = topk.device
     if mask is None:
         mask = torch.empty((T, ld), dtype=torch.float32, device=dev)
     with torch.cuda.device(dev):
         _check(lib().dsa_topk_mask(
-            _dev_ptr(topk, torch.int32, "topk"), T, k, k,
+            _dev_ptr(topk, torch.int32, "topk"), T, k, width,
             _dev_ptr(mask, torch.float32, "mask"), ld, _stream(stream, dev)))
     return mask
 

@@ -65,3 +65,30 @@ def test_handoff_random_rows_and_chunk_edges(ld):
     assert np.array_equal(slots.cpu().numpy(),
                           handoff.topk_to_slots(topk, bt, qsl))
     assert np.array_equal(mask.cpu().numpy(), handoff.topk_mask(topk, ld))
+
+
+def test_handoff_uses_only_k_entries_of_a_wider_buffer():
+    """topk_ld > k (the shared buffer wider than the rows' k): the entries
+    past k hold decoy indices and must be ignored; slots keep row stride k."""
+    _say("case: hand-off, k entries of a wider top-k buffer")
+    rng = np.random.default_rng(77)
+    T, k, extra, R, ld = 24, 100, 28, 2, 4096
+    pages = ld // 64
+    bt = rng.permutation(R * pages).astype(np.int32).reshape(R, pages)
+    qsl = np.array([0, 9, T], dtype=np.int32)
+    topk = np.full((T, k), -1, dtype=np.int32)
+    for t in range(T):
+        n = int(rng.integers(0, k + 1))
+        topk[t, :n] = np.sort(rng.choice(ld, n, replace=False))
+    wide = np.concatenate(
+        [topk, rng.integers(0, ld, (T, extra)).astype(np.int32)], axis=1)
+    tk = torch.from_numpy(wide).cuda()
+    slots = binding.dsa_topk_to_slots(tk, torch.from_numpy(bt).cuda(),
+                                      torch.from_numpy(qsl).cuda(), k=k)
+    mask = binding.dsa_topk_mask(tk, ld, k=k)
+    torch.cuda.synchronize()
+    assert slots.shape == (T, k)
+    assert np.array_equal(slots.cpu().numpy(),
+                          handoff.topk_to_slots(topk, bt, qsl))
+    assert np.array_equal(mask.cpu().numpy(), handoff.topk_mask(topk, ld))
+    assert binding.dsa_device_error_flags(reset=True) == 0
