@@ -13,6 +13,7 @@ import pytest
 import torch
 
 from dsa_lightning_indexer_amd import binding, synth
+from oracle import indexer as oi
 from tests import parity
 
 pytestmark = [pytest.mark.gpu,
@@ -91,4 +92,30 @@ def test_topk_writes_only_k_slots(topk_kernel):
     o = out.cpu().numpy()
     assert np.array_equal(o[:, : b.k], ref.cpu().numpy())
     assert np.all(o[:, b.k:] == SLOT_SENTINEL)
+    assert binding.dsa_device_error_flags(reset=True) == 0
+
+
+@pytest.mark.parametrize("topk_kernel", [0, 3])
+def test_long_row_topk_writes_only_k_slots(topk_kernel):
+    """Rows longer than 65536 columns (sample select, 0; multi-workgroup
+    radix, 3) into a wider buffer: the exact top-k in slots 0..k-1, nothing
+    after; a short row of the same batch is padded."""
+    rng = np.random.default_rng(99)
+    ld, k, spare = 70144, 2048, 40
+    pos = np.array([70000, 65600, 1000, ld - 1], dtype=np.int32)
+    T = pos.size
+    lg = rng.standard_normal((T, ld)).astype(np.float32)
+    print(f"case: long rows, topk_kernel {topk_kernel}", flush=True)
+    binding.dsa_set_option("topk_kernel", topk_kernel)
+    out = torch.full((T, k + spare), SLOT_SENTINEL, dtype=torch.int32,
+                     device="cuda")
+    binding.dsa_indexer_topk(torch.from_numpy(lg).cuda(),
+                             torch.from_numpy(pos).cuda(), k, out=out)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    for t in range(T):
+        want = oi.topk_row(lg[t, : pos[t] + 1], k)
+        want = np.concatenate([np.sort(want[want >= 0]), want[want < 0]])
+        assert np.array_equal(o[t, :k], want), f"row {t}"
+    assert np.all(o[:, k:] == SLOT_SENTINEL)
     assert binding.dsa_device_error_flags(reset=True) == 0
