@@ -232,3 +232,61 @@ def test_index_cache_run_graph_replays():
                                     workspace=ws)
     _graph_check(run, buf)
     assert binding.dsa_device_error_flags(reset=True) == 0
+
+
+def test_write_path_and_handoff_graph_replays():
+    """Slot mapping, K write, compressed slot mapping and both hand-off
+    forms captured in one HIP graph on a side stream (each entry point
+    launches on the stream it is given, allocates nothing and records no
+    memset): every replay, after the outputs are overwritten and the cache
+    restored, equals the eager results."""
+    _say("case: write path and hand-off in a HIP graph")
+    b = synth.decode(R=8, lo=500, hi=2000, seed=9)
+    d = parity.upload(b)
+    _, _, _, tk = parity.run_gpu(b, d)
+    rng = np.random.default_rng(9)
+    kb = torch.from_numpy(rng.standard_normal((b.T, 128)).astype(np.float32)) \
+        .bfloat16().cuda()
+    cache0 = d["k_cache"].clone()
+    slots = torch.empty(b.T, dtype=torch.int64, device="cuda")
+    cslots = torch.empty(b.T, dtype=torch.int64, device="cuda")
+    cpos = torch.empty(b.T, dtype=torch.int32, device="cuda")
+    tslots = torch.empty((b.T, b.k), dtype=torch.int64, device="cuda")
+    mask = torch.empty((b.T, b.ld), dtype=torch.float32, device="cuda")
+
+    def calls():
+        binding.dsa_slot_mapping(d["block_table"], d["qsl"], d["positions"],
+                                 slots=slots)
+        binding.dsa_indexer_k_write(kb, slots, d["k_cache"])
+        binding.dsa_compressed_slot_mapping(d["block_table"], d["qsl"],
+                                            d["positions"], 4, 16,
+                                            slots=cslots, positions_c=cpos)
+        binding.dsa_topk_to_slots(tk, d["block_table"], d["qsl"], slots=tslots)
+        binding.dsa_topk_mask(tk, b.ld, mask=mask)
+
+    outs = (slots, d["k_cache"], cslots, cpos, tslots, mask)
+    calls()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        d["k_cache"].copy_(cache0)
+        calls()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            calls()
+    torch.cuda.synchronize()
+    for i in range(3):
+        for x in (slots, cslots, tslots):
+            x.fill_(-5)
+        cpos.fill_(-5)
+        mask.fill_(1.0)
+        d["k_cache"].copy_(cache0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for j, (x, r) in enumerate(zip(outs, ref)):
+            assert torch.equal(x, r), f"replay {i}, output {j}"
+    assert binding.dsa_device_error_flags(reset=True) == 0
