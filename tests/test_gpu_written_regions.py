@@ -119,3 +119,31 @@ def test_long_row_topk_writes_only_k_slots(topk_kernel):
         assert np.array_equal(o[t, :k], want), f"row {t}"
     assert np.all(o[:, k:] == SLOT_SENTINEL)
     assert binding.dsa_device_error_flags(reset=True) == 0
+
+
+@pytest.mark.parametrize("topk_kernel,ld", [(0, 8192), (1, 8192), (2, 8192),
+                                            (4, 8192), (0, 70144),
+                                            (3, 70144)])
+def test_topk_reads_only_columns_up_to_p(topk_kernel, ld):
+    """Columns past a row's position hold values that would win the
+    selection (1e30, +inf): every top-k kernel class ignores them."""
+    rng = np.random.default_rng(ld + topk_kernel)
+    k = 300
+    pos = np.array([ld - 1, ld // 2 + 7, 5000, 299, 300, 0], dtype=np.int32)
+    T = pos.size
+    lg = rng.standard_normal((T, ld)).astype(np.float32)
+    for t in range(T):
+        lg[t, pos[t] + 1:] = np.float32(1e30)
+        lg[t, pos[t] + 1::7] = np.inf
+    print(f"case: columns past p, topk_kernel {topk_kernel}, ld {ld}",
+          flush=True)
+    binding.dsa_set_option("topk_kernel", topk_kernel)
+    out = binding.dsa_indexer_topk(torch.from_numpy(lg).cuda(),
+                                   torch.from_numpy(pos).cuda(), k)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    for t in range(T):
+        want = oi.topk_row(lg[t, : pos[t] + 1], k)
+        want = np.concatenate([np.sort(want[want >= 0]), want[want < 0]])
+        assert np.array_equal(o[t], want), f"row {t}"
+    assert binding.dsa_device_error_flags(reset=True) == 0
