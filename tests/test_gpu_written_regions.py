@@ -147,3 +147,30 @@ def test_topk_reads_only_columns_up_to_p(topk_kernel, ld):
         want = np.concatenate([np.sort(want[want >= 0]), want[want < 0]])
         assert np.array_equal(o[t], want), f"row {t}"
     assert binding.dsa_device_error_flags(reset=True) == 0
+
+
+@pytest.mark.parametrize("layout", ["decode", "scattered"])
+@pytest.mark.parametrize("kernel", [0, 1, 2, 3, 4, 5])
+def test_logits_ignore_block_table_entries_past_the_rows(layout, kernel):
+    """Block-table entries past the last page a request's rows reach hold
+    an out-of-pool page id: no kernel uses them (no range flag, logits as
+    with a clean table)."""
+    b = _batch(layout)
+    b.block_table = np.concatenate(
+        [b.block_table, np.full((b.R, 3), -1, np.int32)], axis=1)
+    qsl = b.query_start_loc
+    for r in range(b.R):
+        rows = b.positions[qsl[r]:qsl[r + 1]]
+        need = (int(rows.max()) + 64) // 64 if rows.size else 0
+        b.block_table[r, need:] = 1 << 30
+    print(f"case: junk past the pages, layout {layout}, kernel {kernel}",
+          flush=True)
+    binding.dsa_set_option("logits_kernel", kernel)
+    _, _, lg, _ = parity.run_gpu(b)
+    assert binding.dsa_device_error_flags(reset=True) == 0
+    g = lg.cpu().numpy()
+    ora = parity.oracle_logits(b)
+    mag = parity.magnitude(b)
+    for t in range(b.T):
+        parity.check_logits_row(g[t], ora[t], int(b.positions[t]), f"row {t}",
+                                mag[t])
