@@ -43,6 +43,10 @@
  *    affected logits become -inf and a sticky flag is raised, readable with
  *    dsa_device_error_flags().
  *  - Supported shapes: head_dim == 128, page_size == 64, 1 <= H <= 64.
+ *  - The *_workspace_size queries return 0 for arguments the matching entry
+ *    point rejects or treats as a no-op (T <= 0, T > 2^31, ld <= 0,
+ *    ld > 2^30, H outside [1, 64]); within those limits their sums cannot
+ *    wrap.
  */
 #ifndef DSA_INDEXER_H
 #define DSA_INDEXER_H
@@ -172,7 +176,8 @@ size_t dsa_forward_workspace_size(int64_t T, int H, int64_t ld, int k);
  * SGLang's logits budget): 30 % of the device's total_mem bytes; when a
  * static memory fraction is set (mem_fraction_static >= 0; pass a negative
  * value for none), the smaller of that and free_mem_fraction of the memory
- * outside the static part.  At least 1.  Host only.
+ * outside the static part; free_mem_fraction is clamped to [0, 1].  At
+ * least 1.  Host only.
  */
 size_t dsa_logits_budget_bytes(size_t total_mem, double mem_fraction_static,
                                double free_mem_fraction);
@@ -181,7 +186,7 @@ size_t dsa_logits_budget_bytes(size_t total_mem, double mem_fraction_static,
  * dsa_logits_chunk_rows -- query rows per scoring pass under a logits
  * budget ([KVB], same section): all T rows when T * ld fp32 elements are
  * under 8,000,000 or fit budget_bytes; otherwise budget_bytes / (ld * 4)
- * rows, at least 1.  0 for T <= 0.  Host only.
+ * rows, at least 1.  0 for T <= 0 or ld <= 0.  Host only.
  */
 int64_t dsa_logits_chunk_rows(int64_t T, int64_t ld, size_t budget_bytes);
 
