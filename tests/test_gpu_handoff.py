@@ -92,3 +92,33 @@ def test_handoff_uses_only_k_entries_of_a_wider_buffer():
                           handoff.topk_to_slots(topk, bt, qsl))
     assert np.array_equal(mask.cpu().numpy(), handoff.topk_mask(topk, ld))
     assert binding.dsa_device_error_flags(reset=True) == 0
+
+
+def test_handoff_junk_indices():
+    """Entries that name no cached token -- negative values other than -1,
+    indices at or past ld and past the block table, INT32_MAX/MIN -- give
+    slot -1 and no mask column, as in the oracle; valid entries beside them
+    are unaffected."""
+    _say("case: hand-off, junk indices")
+    rng = np.random.default_rng(5)
+    T, k, R, ld = 12, 64, 2, 16640
+    pages = ld // 64
+    bt = rng.permutation(R * pages).astype(np.int32).reshape(R, pages)
+    qsl = np.array([0, 5, T], dtype=np.int32)
+    junk = np.array([-7, -(2 ** 31), ld, ld + 100, 20000, 2 ** 31 - 1,
+                     pages * 64, -2], dtype=np.int32)
+    topk = np.full((T, k), -1, dtype=np.int32)
+    for t in range(T):
+        good = np.sort(rng.choice(ld, 40, replace=False))
+        row = np.concatenate([good, junk])
+        rng.shuffle(row)
+        topk[t, :row.size] = row
+    tk = torch.from_numpy(topk).cuda()
+    slots = binding.dsa_topk_to_slots(tk, torch.from_numpy(bt).cuda(),
+                                      torch.from_numpy(qsl).cuda())
+    mask = binding.dsa_topk_mask(tk, ld)
+    torch.cuda.synchronize()
+    assert np.array_equal(slots.cpu().numpy(),
+                          handoff.topk_to_slots(topk, bt, qsl))
+    assert np.array_equal(mask.cpu().numpy(), handoff.topk_mask(topk, ld))
+    assert binding.dsa_device_error_flags(reset=True) == 0
