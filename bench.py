@@ -213,18 +213,26 @@ def _csv_rows(directory, suffix):
     return rows
 
 
+def _base_name(name):
+    """Kernel name without its template arguments (the instances of one
+    kernel chosen per launch shape count as one kernel)."""
+    return name.split("<")[0]
+
+
 def _per_dispatch(rows):
     """{dispatch id: (kernel name, summed counter value in KiB)}; only the
-    dispatches at the largest grid of their kernel name are kept (the
-    workload's own launch: the chunked leg launches the same kernels on
-    smaller grids)."""
+    dispatches at the largest grid of their kernel (any instance) are kept
+    (the workload's own launch: the chunked leg launches the same kernels
+    on smaller grids)."""
     out, grid = {}, {}
     for r in rows:
         key = r["Dispatch_Id"]
         name, v, g = out.get(key, (r["Kernel_Name"], 0.0, int(r["Grid_Size"])))
         out[key] = (name, v + float(r["Counter_Value"]), g)
-        grid[name] = max(grid.get(name, 0), g)
-    return {k: (n, v) for k, (n, v, g) in out.items() if g == grid[n]}
+        b = _base_name(name)
+        grid[b] = max(grid.get(b, 0), g)
+    return {k: (n, v) for k, (n, v, g) in out.items()
+            if g == grid[_base_name(n)]}
 
 
 def _matcher(config):
@@ -319,8 +327,14 @@ def trace_summary(args):
                      f"{float(r['AverageNs']) / 1e3:.3f} | "
                      f"{d[len(d) // 2]:.3f} | {d[0]:.3f} | {d[-1]:.3f} | "
                      f"{float(r['Percentage']):.2f} |")
+    top = {}
+    for n in dom:
+        b = _base_name(n)
+        top[b] = max(top.get(b, 0), max(by_grid[n]))
     for n in dom:
         g = max(by_grid[n])
+        if g != top[_base_name(n)]:
+            continue                  # a smaller instance: the chunked leg
         d = sorted(by_grid[n][g])
         lines += ["", f"Dominant kernel at the workload's own launch (its "
                   f"largest grid, {g} threads; dispatches of the same "

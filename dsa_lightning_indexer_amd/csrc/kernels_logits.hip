@@ -1440,8 +1440,16 @@ static hipError_t launch_logits_mt(const LogitsArgs& a, hipStream_t stream,
     // unless the split size is forced
     const int pps16 = o.tile_pages_per_split > 0 ? pps : 0;
     const dim3 g3((unsigned)gx, (unsigned)tiles);
+    // four pages per copy step (twice the lookahead) when the workgroups
+    // take more than two rounds of the compute units: measured faster on
+    // the prefill chunk (8 rounds); on the 1M tail (2 rounds) the step was
+    // slower
+    const bool deep = gx * tiles > 2 * (int64_t)device_cu_count();
     if (o.logits_kernel == 5)
       hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL, false, 2, false>), g3,
+                         dim3(kT16Threads), 0, stream, a, pps16, 64);
+    else if (o.logits_kernel != 2 && o.logits_kernel != 3 && deep)
+      hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL, true, 4, true>), g3,
                          dim3(kT16Threads), 0, stream, a, pps16, 64);
     else if (o.logits_kernel != 2 && o.logits_kernel != 3)
       hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL, true, 2, true>), g3,
