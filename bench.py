@@ -3,23 +3,29 @@
 
     python bench.py [--steps K] [--warmup W] [--config decode|prefill|long|
                      tiny|index_cache] [--rotate R] [--no-cpu-baseline]
+                     [--only]
 
 One step = one pass of the whole hot path over one batch: IndexCache mask
 (host), q quantisation, paged FP8 logits, per-row top-k into the shared index
-buffer, each through the C ABI of libdsa_indexer.so.  The default workload is
-the decode batch: 64 requests with contexts uniform in [1024, 8192], one
-query each at the last position, 64 heads, head_dim 128, index_topk 2048,
-FP8 e4m3 K with one fp32 scale per token, 64-token pages drawn from a
-shuffled 16384-page pool (synthetic, seeded).
+buffer, each through the C ABI of libdsa_indexer.so.  The headline workload
+(``value``) is the decode batch: 64 requests with contexts uniform in
+[1024, 8192], one query each at the last position, 64 heads, head_dim 128,
+index_topk 2048, FP8 e4m3 K with one fp32 scale per token, 64-token pages
+drawn from a shuffled 16384-page pool (synthetic, seeded).  The default run
+adds one record per other workload of the metric: ``prefill`` (8192 queries
+against a 40960-token cache: the FP8-MFMA-bound chunk), ``long`` (16 rows
+at the end of a 1M-token cache) and ``index_cache`` (61-layer stacks at
+freq 4, a seeded pattern and freq 1); ``--only`` measures the chosen
+``--config`` alone.
 
 Timing: inputs are resident in HBM before the timed region.  R copies of the
 K cache (and of q / weights) rotate across steps so that consecutive steps do
-not hit the 256 MB Infinity Cache.  The timed region replays one HIP graph
-that holds R steps (one per copy), so it measures GPU execution, not Python
-launch overhead; every replay is first checked bit-exactly against the eager
-result.  Per-kernel durations come from HIP events on the launch stream
-around 64 back-to-back launches of each kernel, queued behind a GPU sleep so
-that no host gap falls inside a bracket.
+not hit the 256 MB Infinity Cache.  W eager warm-up steps, then one HIP graph
+holding exactly K steps (step i uses copy i mod R) is captured, checked
+bit-exactly against the eager result, and its replay is the timed region
+(bracketed by device synchronisation).  Per-kernel durations come from HIP
+events on the launch stream around 64 back-to-back launches of each kernel,
+queued behind a GPU sleep so that no host gap falls inside a bracket.
 
 Prints ONE JSON line.  ``roofline`` is for the dominant kernel (the logits
 kernel): achieved = algorithmic bytes (or FLOPs) per launch / its average
@@ -65,14 +71,16 @@ WORKLOADS = {
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="decode",
                     choices=sorted(WORKLOADS) + ["index_cache"])
+    ap.add_argument("--only", action="store_true",
+                    help="measure --config alone (no other workload records)")
     ap.add_argument("--rotate", type=int, default=8,
                     help="K-cache copies rotated across steps (cold cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for scaling "
                          "hardware byte counters)")
@@ -98,23 +106,27 @@ def make_batch(name):
 
 
 def logits_work(b):
-    """Algorithmic bytes and FLOPs of one logits launch.
+    """Algorithmic bytes and FLOPs of one step, charged to its logits launch
+    (the dominant kernel).
 
-    Per visible (row, token) pair: 132 B of K (128 FP8 key bytes + 4 B fp32
-    scale) read and 4 B of logit written, and 2 * H * 128 FLOPs.  Per row:
-    H * 128 B of FP8 q, H * 4 B of q scales and H * 4 B of weights.  A decode
-    row reads every visible key once; a prefill or long-context tile reads a
-    key once for all of its rows, so its bytes count the distinct keys.
+    Bytes: 132 B of K (128 FP8 key bytes + 4 B fp32 scale) per key read --
+    every visible (row, key) pair for rows that are one per request (each
+    key is used by one row), every cached key once for a request whose rows
+    share the keys (prefill, long context: a tile reads a key once for all
+    of its rows) -- plus H * (128 + 4 + 4) B of FP8 q, q scales and weights
+    per row, plus the k int32 indices written per row.  The logits written
+    by the logits kernel and read back by the top-k are a round trip inside
+    the step, not counted.  FLOPs: 2 * H * 128 per visible (row, key) pair.
     """
     H = b.H
     pairs = b.visible_pairs
     flops = 2.0 * H * 128 * pairs
-    per_row = b.T * H * (128 + 4 + 4)
+    per_row = b.T * H * (128 + 4 + 4) + 4 * b.k * b.T
     if b.T == b.R:                                 # one row per request
         kbytes = 132 * pairs
     else:                                          # keys shared by a request
         kbytes = 132 * sum(int(c) for c in b.contexts)
-    return kbytes + 4 * pairs + per_row, flops
+    return kbytes + per_row, flops
 
 
 def dominant_kernel(b):
@@ -126,41 +138,60 @@ def dominant_kernel(b):
     return "logits_tile16_kernel<", ""
 
 
-def cpu_baseline(b, seconds):
-    """Time the CPU oracle on the same workload (whole batches, repeated
-    until ``seconds`` of work; a bounded row sample for large batches)."""
+def host_cpu():
+    """(CPU model name, usable cores) of this host."""
+    model = "unknown"
     try:
-        from threadpoolctl import threadpool_info
-        info = threadpool_info()
-        cores = max([i.get("num_threads", 1) for i in info] or [1])
-    except Exception:                                   # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(b, seconds, max_rows=None):
+    """Time the CPU oracle on the same workload: quantise q, logits and the
+    sort-based top-k of a declared sample of rows (the whole batch, or
+    ``max_rows`` evenly spaced rows), passes repeated until ``seconds`` of
+    work; BLAS threads = the usable cores."""
     from oracle import indexer as oi
+    model, cores = host_cpu()
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores)
+    except Exception:                                   # pragma: no cover
+        limiter = None
     rows = np.arange(b.T)
     sample = "whole batch"
-    if b.visible_pairs > 2_000_000:                     # bound the sample
-        per_row = b.visible_pairs / b.T
-        nrows = max(1, int(2_000_000 / per_row))
-        rows = np.linspace(0, b.T - 1, nrows).round().astype(np.int64)
+    if max_rows is not None and b.T > max_rows:
+        rows = np.linspace(0, b.T - 1, max_rows).round().astype(np.int64)
         sample = f"{len(rows)} evenly spaced rows of {b.T}"
-    t0 = time.perf_counter()
-    done = 0
-    reps = 0
-    while True:
-        q = b.q_bf16[rows].float().numpy()
-        codes = np.zeros((b.T, b.H, 128), np.uint8)
-        sc = np.ones((b.T, b.H), np.float32)
-        codes[rows], sc[rows] = oi.quantize_q(q)
-        lg = oi.indexer_logits(codes, sc, b.weights, b.k_cache, b.block_table,
-                               b.query_start_loc, b.positions, b.ld, rows=rows)
-        oi.indexer_topk(lg, b.positions, b.k, rows=rows)
-        done += len(rows)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+    try:
+        t0 = time.perf_counter()
+        done = 0
+        reps = 0
+        while True:
+            q = b.q_bf16[rows].float().numpy()
+            codes = np.zeros((b.T, b.H, 128), np.uint8)
+            sc = np.ones((b.T, b.H), np.float32)
+            codes[rows], sc[rows] = oi.quantize_q(q)
+            lg = oi.indexer_logits(codes, sc, b.weights, b.k_cache,
+                                   b.block_table, b.query_start_loc,
+                                   b.positions, b.ld, rows=rows)
+            oi.indexer_topk(lg, b.positions, b.k, rows=rows)
+            done += len(rows)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    finally:
+        if limiter is not None:
+            limiter.unregister()
     return {"value": done / el, "unit": "query-rows/s", "cores": int(cores),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model,
             "sample": f"{sample}, {reps} pass(es), {done} rows in {el:.1f} s "
                       "(numpy fp64 oracle: quantise q, logits, sort-based "
                       "top-k)"}
@@ -356,29 +387,81 @@ def trace_summary(args):
     print("\n".join(lines))
 
 
-def main():
-    args = parse()
-    if args.trace_summary:
-        return trace_summary(args)
-    if args.pmc_summary:
-        return pmc_summary(args)
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; "
-                                   "--gpus N > 1 is not supported"}))
-        sys.exit(2)
-    if args.config == "index_cache":
-        return bench_index_cache(args)
+def _events(torch):
+    return (torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True))
 
+
+def _timed(torch, fn, launches, rotate):
+    """Average duration (ms) of ``launches`` back-to-back calls fn(i %
+    rotate) between two HIP events on the launch stream, queued behind a
+    GPU sleep so that the host has enqueued them all first."""
+    a, z = _events(torch)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(20e6))
+    a.record()
+    for i in range(launches):
+        fn(i % rotate)
+    z.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(z) / launches
+
+
+def _graph_steps(torch, step, K, R, warmup, check_buf, ref_step):
+    """W eager warm-up steps, then a HIP graph of exactly K steps (step i on
+    copy i mod R), checked bit-exactly against the eager result of its last
+    step, replayed once for the timed region.  Returns (ms per step, [ms per
+    step of 4 more replays])."""
+    for i in range(warmup):
+        step(i % R)
+    last = (K - 1) % R
+    step(last)
+    torch.cuda.synchronize()
+    ref = check_buf.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(K):
+            step(i % R)
+    torch.cuda.synchronize()
+    check_buf.fill_(-7)
+    graph.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(check_buf, ref):
+        raise SystemExit("graph replay differs from the eager result")
+    ref_step(last)                              # eager work between replays
+    torch.cuda.synchronize()
+    a, z = _events(torch)
+    torch.cuda.synchronize()
+    a.record()
+    graph.replay()
+    z.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(z) / K
+    again = []
+    for _ in range(4):
+        a, z = _events(torch)
+        a.record()
+        graph.replay()
+        z.record()
+        torch.cuda.synchronize()
+        again.append(round(a.elapsed_time(z) / K, 5))
+    if not torch.equal(check_buf, ref):
+        raise SystemExit("graph replay differs from the eager result")
+    del graph
+    return ms, again
+
+
+def measure_workload(args, name, K, W, extras=False, cpu=True,
+                     cpu_rows=None):
+    """One workload: step time over a graph of K steps, per-kernel times and
+    the logits kernel's roofline (and, with ``extras``, the kernels around
+    the hot path).  Returns the record (a dict)."""
     import torch
     from dsa_lightning_indexer_amd import binding
 
     dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    for kv in args.opt:
-        key, val = kv.split("=")
-        binding.dsa_set_option(key, int(val))
-    b = make_batch(args.config)
-    R = max(1, args.rotate if args.config in ("decode", "long") else 1)
+    b = make_batch(name)
+    R = max(1, args.rotate if name in ("decode", "long") else 1)
     bt = torch.from_numpy(b.block_table).to(dev)
     qsl = torch.from_numpy(b.query_start_loc).to(dev)
     pos = torch.from_numpy(b.positions).to(dev)
@@ -400,9 +483,138 @@ def main():
                                     ld, k, logits=logits, out=buf,
                                     workspace=fws)
 
-    def step(i):
+    def step(r):
         binding.dsa_index_cache_mask(1)                       # one F layer
-        forward(i % R)
+        forward(r)
+
+    torch.cuda.synchronize()
+    binding.dsa_device_error_flags(reset=True)
+    ms_step, again = _graph_steps(torch, step, K, R, W, buf, step)
+    NK = 64
+    kq = _timed(torch, lambda r: binding.dsa_quantize_q(qs_in[r], q8, qsc),
+                NK, R)
+    kl = _timed(torch, lambda r: binding.dsa_indexer_logits(
+        q8, qsc, ws_in[r], kcs[r], bt, qsl, pos, ld, logits), NK, R)
+    kt = _timed(torch, lambda r: binding.dsa_indexer_topk(
+        logits, pos, k, buf, tws), NK, R)
+    kf = _timed(torch, forward, NK, R)
+    kernels = {"quantize_q": round(kq, 5), "logits": round(kl, 5),
+               "topk": round(kt, 5), "forward": round(kf, 5)}
+    rec = {}
+    if extras:
+        # Row-chunked forward under a 256 MiB logits budget.
+        ch_rows = binding.dsa_logits_chunk_rows(T, ld, 256 << 20)
+        ch_ws = torch.empty(max(1, binding.dsa_forward_chunked_workspace_size(
+            T, b.R, H, ld, k, ch_rows)), dtype=torch.uint8, device=dev)
+        ch_out = torch.empty((T, k), dtype=torch.int32, device=dev)
+        kernels["forward_chunked_256MiB"] = round(_timed(
+            torch, lambda r: binding.dsa_indexer_forward_chunked(
+                qs_in[r], ws_in[r], kcs[r], bt, qsl, pos, ld, k,
+                rows_per_chunk=ch_rows, out=ch_out, workspace=ch_ws),
+            NK, R), 5)
+        del ch_ws
+        rec["chunked_rows_per_chunk"] = int(ch_rows)
+        # The indexer-K write path (the rows' own tokens as new keys, into
+        # a copy of the cache), the compressed slots, the hand-off.
+        new_k = torch.randn((T, 128), dtype=torch.bfloat16, device=dev)
+        slots = binding.dsa_slot_mapping(bt, qsl, pos)
+        c_slots = torch.empty((T,), dtype=torch.int64, device=dev)
+        c_pos = torch.empty((T,), dtype=torch.int32, device=dev)
+        kernels["compressed_slot_mapping"] = round(_timed(
+            torch, lambda r: binding.dsa_compressed_slot_mapping(
+                bt, qsl, pos, 4, 64, slots=c_slots, positions_c=c_pos),
+            NK, R), 5)
+        kw_cache = kcs[0].clone()
+        kkw = _timed(torch, lambda r: binding.dsa_indexer_k_write(
+            new_k, slots, kw_cache), NK, R)
+        kernels["k_write"] = round(kkw, 5)
+        del kw_cache
+        ho_slots = torch.empty((T, k), dtype=torch.int64, device=dev)
+        kernels["topk_to_slots"] = round(_timed(
+            torch, lambda r: binding.dsa_topk_to_slots(buf, bt, qsl,
+                                                       slots=ho_slots),
+            NK, R), 5)
+        ho_mask = torch.empty((T, ld), dtype=torch.float32, device=dev)
+        kmask = _timed(torch, lambda r: binding.dsa_topk_mask(
+            buf, ld, mask=ho_mask), NK, R)
+        kernels["topk_mask"] = round(kmask, 5)
+        del ho_mask
+        rec["topk_mask_gbs"] = round(T * ld * 4 / (kmask * 1e-3) / 1e9, 1)
+        rec["k_write_gbs"] = round(T * (2 * 128 + 8 + 132) /
+                                   (kkw * 1e-3) / 1e9, 1)
+    assert binding.dsa_device_error_flags(reset=True) == 0
+
+    alg_bytes, flops = logits_work(b)
+    gbs = alg_bytes / (kl * 1e-3) / 1e9
+    tfl = flops / (kl * 1e-3) / 1e12
+    if T > 2 * b.R:                       # rows share the keys: MFMA-bound
+        roof = {"bound": "mfma", "achieved": round(tfl, 2),
+                "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tfl / FP8_PEAK_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = traffic_from_counters(name)
+    roof["kernel"] = dominant_kernel(b)[0].rstrip("<")
+    roof["algorithmic_bytes"] = int(alg_bytes)
+    roof["algorithmic_flops"] = flops
+    roof["kernel_ms"] = round(kl, 5)
+    roof["hbm_gbs"] = round(gbs, 1)
+    roof["fp8_tflops"] = round(tfl, 2)
+    rec.update({
+        "workload": WORKLOADS[name],
+        "value": round(T / (ms_step * 1e-3), 1), "unit": "query-rows/s",
+        "ms_per_step": round(ms_step, 5), "ms_per_step_more_replays": again,
+        "rows": T, "heads": H, "index_topk": k,
+        "visible_pairs": b.visible_pairs, "kcache_copies_rotated": R,
+        "kernels_ms": kernels, "roofline": roof})
+    del kcs, qs_in, ws_in, logits, fws, tws
+    if cpu and not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds, cpu_rows)
+    torch.cuda.empty_cache()
+    return rec
+
+
+def copy_rate(torch):
+    """Attainable HBM rate on this machine: a 1 GiB device-to-device copy (read
+    and write counted), GB/s."""
+    dev = torch.device("cuda", 0)
+    c_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    c_dst = torch.empty_like(c_src)
+    c_dst.copy_(c_src)
+    a, z = _events(torch)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(5):
+        c_dst.copy_(c_src)
+    z.record()
+    torch.cuda.synchronize()
+    del c_src, c_dst
+    torch.cuda.empty_cache()
+    return 2 * (1 << 30) * 5 / (a.elapsed_time(z) * 1e-3) / 1e9
+
+
+def main():
+    args = parse()
+    if args.trace_summary:
+        return trace_summary(args)
+    if args.pmc_summary:
+        return pmc_summary(args)
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; "
+                                   "--gpus N > 1 is not supported"}))
+        sys.exit(2)
+    K, W = max(1, args.steps), max(0, args.warmup)
+
+    import torch
+    from dsa_lightning_indexer_amd import binding
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    for kv in args.opt:
+        key, val = kv.split("=")
+        binding.dsa_set_option(key, int(val))
 
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.uint8, device=dev).fill_(1)
@@ -412,202 +624,75 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # Eager warm-up; the last slot's output is the reference for the graph.
-    for i in range(max(args.warmup, R)):
-        step(i)
-    torch.cuda.synchronize()
-    assert binding.dsa_device_error_flags(reset=True) == 0
-    last = (max(args.warmup, R) - 1) % R
-    step(last)
-    torch.cuda.synchronize()
-    ref_buf = buf.clone()
+    if args.config == "index_cache":
+        out = bench_index_cache(args, K, W)
+        print(json.dumps(out), flush=True)
+        return
 
-    # One HIP graph holds R steps (one per K-cache copy); the timed region
-    # replays it.  Every replay is checked against the eager result first.
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for r in range(R):
-            step(r)
-    torch.cuda.synchronize()
-    for _ in range(3):
-        buf.fill_(-7)
-        graph.replay()
-        torch.cuda.synchronize()
-        if (R - 1) != last:
-            step(last)                       # eager work between replays
-            torch.cuda.synchronize()
-        if not torch.equal(buf, ref_buf):
-            raise SystemExit("graph replay differs from the eager result")
-
-    reps = max(1, math.ceil(args.steps / R))
-    K = reps * R
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(int(20e6))
-    start.record()
-    for _ in range(reps):
-        graph.replay()
-    end.record()
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / K
-
-    # Spread: the same replays again with an event between each (per-step
-    # time of each replay of R steps); reported beside the mean above.
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-    torch.cuda._sleep(int(20e6))
-    evs[0].record()
-    for i in range(reps):
-        graph.replay()
-        evs[i + 1].record()
-    torch.cuda.synchronize()
-    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) / R for i in range(reps))
-    pct = {f"p{q}": round(per_step[min(len(per_step) - 1,
-                                       int(q / 100 * len(per_step)))], 5)
-           for q in (10, 50, 90)}
-
-    # Per-kernel durations: for each kernel, NK back-to-back launches on the
-    # launch stream (rotating over the K-cache copies) between two HIP
-    # events, queued behind a GPU sleep so that the host has enqueued them
-    # all before the GPU reaches the first event.
-    NK = 64
-
-    def timed(fn):
-        a = torch.cuda.Event(enable_timing=True)
-        z = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        torch.cuda._sleep(int(20e6))
-        a.record()
-        for i in range(NK):
-            fn(i % R)
-        z.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(z) / NK
-
-    kq = timed(lambda r: binding.dsa_quantize_q(qs_in[r], q8, qsc))
-    kl = timed(lambda r: binding.dsa_indexer_logits(
-        q8, qsc, ws_in[r], kcs[r], bt, qsl, pos, ld, logits))
-    kt = timed(lambda r: binding.dsa_indexer_topk(logits, pos, k, buf, tws))
-    kf = timed(forward)
-    # Row-chunked forward under a 256 MiB logits budget (the prefill chunk's
-    # 1.34 GB of logits become 6 chunks of 1638 rows; decode and the 1M
-    # tail fit in one chunk).
-    ch_budget = 256 << 20
-    ch_rows = binding.dsa_logits_chunk_rows(T, ld, ch_budget)
-    ch_ws = torch.empty(max(1, binding.dsa_forward_chunked_workspace_size(
-        T, b.R, H, ld, k, ch_rows)), dtype=torch.uint8, device=dev)
-    ch_out = torch.empty((T, k), dtype=torch.int32, device=dev)
-    kch = timed(lambda r: binding.dsa_indexer_forward_chunked(
-        qs_in[r], ws_in[r], kcs[r], bt, qsl, pos, ld, k,
-        rows_per_chunk=ch_rows, out=ch_out, workspace=ch_ws))
-    del ch_ws
-    # The indexer-K write path (the step before the hot path): the rows'
-    # own tokens as new keys, quantised and stored at their slots of a copy
-    # of the cache.
-    new_k = torch.randn((T, 128), dtype=torch.bfloat16, device=dev)
-    slots = binding.dsa_slot_mapping(bt, qsl, pos)
-    # DeepSeek-V4 compressed variant (ratio 4, 64-entry storage blocks): the
-    # same rows' slots and compressed positions.
-    c_slots = torch.empty((T,), dtype=torch.int64, device=dev)
-    c_pos = torch.empty((T,), dtype=torch.int32, device=dev)
-    kcs_map = timed(lambda r: binding.dsa_compressed_slot_mapping(
-        bt, qsl, pos, 4, 64, slots=c_slots, positions_c=c_pos))
-    kw_cache = kcs[0].clone()
-    kkw = timed(lambda r: binding.dsa_indexer_k_write(new_k, slots, kw_cache))
-    del kw_cache
-    # The sparse-attention hand-off (the step after the hot path): the top-k
-    # rows as physical slots and as the fp32 0 / -inf score mask.
-    ho_slots = torch.empty((T, k), dtype=torch.int64, device=dev)
-    kho = timed(lambda r: binding.dsa_topk_to_slots(buf, bt, qsl,
-                                                    slots=ho_slots))
-    ho_mask = torch.empty((T, ld), dtype=torch.float32, device=dev)
-    kmask = timed(lambda r: binding.dsa_topk_mask(buf, ld, mask=ho_mask))
-    del ho_mask
-    assert binding.dsa_device_error_flags(reset=True) == 0
-
-    # Attainable HBM rate on this machine: a 1 GiB device-to-device copy (read
-    # and write counted), reported beside the published peak.  Not in the
-    # counter runs: their scale comes from the largest copies, which must be
-    # the 256 MiB calibration copies.
-    copy_gbs = None
+    head = args.config
+    cpu_rows = 256 if head == "prefill" else None
+    main_rec = measure_workload(args, head, K, W, extras=True,
+                                cpu=head != "long", cpu_rows=cpu_rows)
+    roof = main_rec.pop("roofline")
+    # Not in counter runs: their scale comes from the largest copies, which
+    # must be the 256 MiB calibration copies.
     if not args.copy_calibration:
-        c_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-        c_dst = torch.empty_like(c_src)
-        c_dst.copy_(c_src)
-        ca = torch.cuda.Event(enable_timing=True)
-        cz = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        ca.record()
-        for _ in range(5):
-            c_dst.copy_(c_src)
-        cz.record()
-        torch.cuda.synchronize()
-        copy_gbs = 2 * (1 << 30) * 5 / (ca.elapsed_time(cz) * 1e-3) / 1e9
-        del c_src, c_dst
-
-    alg_bytes, flops = logits_work(b)
-    kdom = kl
-    gbs = alg_bytes / (kdom * 1e-3) / 1e9
-    tfl = flops / (kdom * 1e-3) / 1e12
-    if args.config in ("prefill", "long"):
-        roof = {"bound": "mfma", "achieved": round(tfl, 2),
-                "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tfl / FP8_PEAK_TFLOPS, 4), "traffic": None}
-    else:
-        roof = {"bound": "hbm", "achieved": round(gbs, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
-    roof["traffic"] = traffic_from_counters(args.config)
-    if copy_gbs is not None:
-        roof["copy_gbs_measured"] = round(copy_gbs, 1)
+        cg = copy_rate(torch)
+        roof["copy_gbs_measured"] = round(cg, 1)
         if roof["bound"] == "hbm":
-            roof["frac_of_measured_copy"] = round(gbs / copy_gbs, 4)
-    roof["kernel"] = dominant_kernel(b)[0].rstrip("<")
-    roof["algorithmic_bytes"] = int(alg_bytes)
-    roof["algorithmic_flops"] = flops
-    roof["kernel_ms"] = round(kdom, 5)
-
+            roof["frac_of_measured_copy"] = round(roof["achieved"] / cg, 4)
     out = {
-        "metric": METRIC, "value": round(T / (ms_step * 1e-3), 1),
-        "unit": "query-rows/s", "n_gpus": 1, "steps": K,
-        "warmup": max(args.warmup, R), "ms_per_step": round(ms_step, 5),
-        "ms_per_step_spread": pct,
+        "metric": METRIC, "value": main_rec.pop("value"),
+        "unit": main_rec.pop("unit"), "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": main_rec.pop("ms_per_step"),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8_e4m3 (fp32 accumulate)", "data": "synthetic",
-        "config": {"workload": WORKLOADS[args.config], "rows": T,
-                   "heads": H, "index_topk": k,
-                   "visible_pairs": b.visible_pairs,
-                   "kcache_copies_rotated": R},
-        "kernels_ms": {"quantize_q": round(kq, 5), "logits": round(kl, 5),
-                       "topk": round(kt, 5), "forward": round(kf, 5),
-                       "k_write": round(kkw, 5), "topk_to_slots": round(kho, 5),
-                       "topk_mask": round(kmask, 5),
-                       "compressed_slot_mapping": round(kcs_map, 5),
-                       "forward_chunked_256MiB": round(kch, 5)},
-        "chunked_rows_per_chunk": int(ch_rows),
-        "topk_mask_gbs": round(T * ld * 4 / (kmask * 1e-3) / 1e9, 1),
-        "k_write_gbs": round(T * (2 * 128 + 8 + 132) / (kkw * 1e-3) / 1e9, 1),
-        "logits_gbs": round(gbs, 1), "logits_tflops": round(tfl, 2),
+        "config": {"workload": main_rec.pop("workload"),
+                   "rows": main_rec.pop("rows"),
+                   "heads": main_rec.pop("heads"),
+                   "index_topk": main_rec.pop("index_topk"),
+                   "visible_pairs": main_rec.pop("visible_pairs"),
+                   "kcache_copies_rotated":
+                       main_rec.pop("kcache_copies_rotated")},
         "roofline": roof,
     }
+    cpu_rec = main_rec.pop("cpu_baseline", None)
+    out.update(main_rec)
+    if cpu_rec is not None:
+        out["cpu_baseline"] = cpu_rec
+    if not args.only:
+        # the metric's other workloads: the FP8-MFMA-bound prefill chunk,
+        # the 1M-token tail and the IndexCache stacks
+        for name in ("prefill", "long"):
+            if name == head:
+                continue
+            try:
+                out[name] = measure_workload(
+                    args, name, K, W, cpu=name == "prefill",
+                    cpu_rows=256 if name == "prefill" else None)
+            except Exception as e:                    # pragma: no cover
+                out[name] = {"error": repr(e)}
+        try:
+            out["index_cache"] = bench_index_cache(args, K, W)
+        except Exception as e:                        # pragma: no cover
+            out["index_cache"] = {"error": repr(e)}
     if args.opt:
         out["options"] = args.opt
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
-def bench_index_cache(args):
+def bench_index_cache(args, K, W):
     """IndexCache stack: 61 layers, 32 decode requests x 16384 context,
-    freq=4 / offset=2 (16 F layers) against freq=1 (61 F layers); one step =
-    one dsa_index_cache_run over the whole stack."""
+    freq 4 / offset 2 (16 F layers), the seeded 61-character pattern and
+    freq 1 (61 F layers), every layer with its own K cache, q and weights.
+    Each run is captured once as a HIP graph (one dsa_index_cache_run over
+    the whole stack), checked against the eager run, and replayed K times
+    back to back for the timed region."""
     import torch
     from dsa_lightning_indexer_amd import binding, synth
 
     dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
     L = 61
-    full4 = [l for l, s in enumerate(binding.dsa_index_cache_mask(
-        L, freq=4, offset=2)) if not s]
     layers_np = synth.index_cache_layers(list(range(L)))
     ref = layers_np[0]
     layers = []
@@ -620,9 +705,9 @@ def bench_index_cache(args):
     bt = torch.from_numpy(ref.block_table).to(dev)
     qsl = torch.from_numpy(ref.query_start_loc).to(dev)
     pos = torch.from_numpy(ref.positions).to(dev)
-    T, k, ld = ref.T, ref.k, ref.ld
+    T, k, ld, H = ref.T, ref.k, ref.ld, ref.H
     buf = torch.empty((T, k), dtype=torch.int32, device=dev)
-    ws = torch.empty(binding.dsa_run_workspace_size(T, ref.R, ref.H, ld, k),
+    ws = torch.empty(binding.dsa_run_workspace_size(T, ref.R, H, ld, k),
                      dtype=torch.uint8, device=dev)
     pattern = synth.index_cache_pattern(L)
     runs = {"freq4": dict(freq=4, offset=2), "pattern": dict(pattern=pattern),
@@ -634,45 +719,71 @@ def bench_index_cache(args):
         def run():
             binding.dsa_index_cache_run(layers, bt, qsl, pos, ld, k, buf,
                                         workspace=ws, **kw)
-        for _ in range(max(2, args.warmup // 10)):
+        for _ in range(max(1, W)):
             run()
         torch.cuda.synchronize()
-        n = max(3, args.steps // 20)
-        s, e = torch.cuda.Event(True), torch.cuda.Event(True)
-        torch.cuda._sleep(int(60e6))
-        s.record()
-        for _ in range(n):
+        ref_buf = buf.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
             run()
-        e.record()
         torch.cuda.synchronize()
-        res[name] = s.elapsed_time(e) / n
-    F = len(full4)
-    assert F == n_full["freq4"]
-    # algorithmic bytes of one F layer: K pages, logits written, q fp8 +
-    # scales + weights (the logits kernel's own traffic, as for decode)
-    per_layer_bytes = 132 * 32 * 16384 + 4 * 32 * 16384 + 32 * 64 * 136
-    out = {
+        buf.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(buf, ref_buf):
+            raise SystemExit(f"IndexCache {name}: graph replay differs")
+        a, z = _events(torch)
+        torch.cuda._sleep(int(20e6))
+        a.record()
+        for _ in range(K):
+            g.replay()
+        z.record()
+        torch.cuda.synchronize()
+        res[name] = a.elapsed_time(z) / K
+        del g
+    # one F layer's logits kernel alone, rotating over the 16 freq-4 F
+    # layers' inputs (each launch reads a cache the previous ones did not)
+    full4 = [l for l, sk in enumerate(binding.dsa_index_cache_mask(
+        L, freq=4, offset=2)) if not sk]
+    q8s = [binding.dsa_quantize_q(layers[l]["q_bf16"]) for l in full4]
+    lg = torch.empty((T, ld), dtype=torch.float32, device=dev)
+    kl = _timed(torch, lambda i: binding.dsa_indexer_logits(
+        q8s[i][0], q8s[i][1], layers[full4[i]]["weights"],
+        layers[full4[i]]["k_cache"], bt, qsl, pos, ld, lg), 64, len(full4))
+    assert binding.dsa_device_error_flags(reset=True) == 0
+    # algorithmic bytes of one F layer (as for decode): K pages, q fp8 +
+    # scales + weights, top-k indices written; no logits round trip
+    per_layer_bytes = 132 * T * 16384 + T * H * 136 + 4 * T * k
+    del layers, ws, q8s
+    torch.cuda.empty_cache()
+    return {
         "metric": "IndexCache stack forward (61 DSA layers)",
         "value": round(T / (res["freq4"] * 1e-3), 1), "unit": "query-rows/s",
-        "n_gpus": 1, "steps": max(3, args.steps // 20),
-        "ms_per_step": round(res["freq4"], 4), "higher_is_better": True,
-        "data": "synthetic", "dtype": "fp8_e4m3 (fp32 accumulate)",
-        "config": {"workload": "IndexCache stack: 61 layers, freq 4 offset 2 "
-                               f"({F} F), a seeded 61-character pattern "
-                               f"({n_full['pattern']} F) and freq 1 (61 F); "
-                               "32 decode requests x 16384 context, H=64, "
-                               "index_topk 2048", "pattern": pattern},
+        "steps": K, "warmup": W, "ms_per_step": round(res["freq4"], 4),
+        "workload": "IndexCache stack: 61 layers, freq 4 offset 2 "
+                    f"({n_full['freq4']} F), a seeded 61-character pattern "
+                    f"({n_full['pattern']} F) and freq 1 (61 F); 32 decode "
+                    "requests x 16384 context, H=64, index_topk 2048, every "
+                    "layer its own K cache, q and weights",
+        "pattern": pattern,
         "ms": {name: round(v, 4) for name, v in res.items()},
         "full_layers": n_full,
         "speedup_vs_freq1": {name: round(res["freq1"] / v, 3)
                              for name, v in res.items()},
         "full_layer_ratio": {name: round(61 / f, 3)
                              for name, f in n_full.items()},
-        "hbm_gbs": {name: round(n_full[name] * per_layer_bytes /
-                                (v * 1e-3) / 1e9, 1)
-                    for name, v in res.items()},
+        "stack_hbm_gbs": {name: round(n_full[name] * per_layer_bytes /
+                                      (v * 1e-3) / 1e9, 1)
+                          for name, v in res.items()},
+        "f_layer_logits_ms": round(kl, 5),
+        "f_layer_logits_roofline": {
+            "bound": "hbm", "achieved": round(per_layer_bytes /
+                                              (kl * 1e-3) / 1e9, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(per_layer_bytes / (kl * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          4),
+            "algorithmic_bytes": per_layer_bytes},
     }
-    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

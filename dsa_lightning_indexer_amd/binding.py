@@ -120,6 +120,27 @@ def _dev_ptr(t, dtype, name):
     return t.data_ptr()
 
 
+def _shape(t, shape, name):
+    """Raise ValueError unless tensor ``t`` has ``shape`` (None = any
+    extent on that axis)."""
+    if t is None:
+        return
+    got = tuple(t.shape)
+    if len(got) != len(shape) or any(
+            w is not None and g != w for g, w in zip(got, shape)):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {got}")
+
+
+def _rows_at_least(t, rows, name, cols=None):
+    """Raise ValueError unless 2-D ``t`` has >= ``rows`` rows (and, when
+    given, >= ``cols`` columns)."""
+    if t.dim() != 2 or t.shape[0] < rows or (cols is not None and
+                                             t.shape[1] < cols):
+        raise ValueError(f"{name} must be 2-D with at least {rows} rows"
+                         + (f" and {cols} columns" if cols is not None else "")
+                         + f", got {tuple(t.shape)}")
+
+
 def _stream(stream, device):
     if stream is None:
         stream = torch.cuda.current_stream(device)
@@ -155,6 +176,10 @@ def dsa_indexer_logits(q_fp8, q_scale, weights, k_cache, block_table,
         raise ValueError("k_cache must be uint8 [num_pages, 8448]")
     if query_start_loc.numel() != R + 1:
         raise ValueError("query_start_loc must have R + 1 entries")
+    _shape(q_scale, (T, H), "q_scale")
+    _shape(weights, (T, H), "weights")
+    _shape(positions, (T,), "positions")
+    _rows_at_least(logits, T, "logits")
     with torch.cuda.device(dev):
         _check(lib().dsa_indexer_logits(
             _dev_ptr(q_fp8, torch.uint8, "q_fp8"),
@@ -181,6 +206,8 @@ def dsa_indexer_topk(logits, positions, k, out=None, workspace=None,
     dev = logits.device
     if out is None:
         out = torch.empty((T, k), dtype=torch.int32, device=dev)
+    _shape(positions, (T,), "positions")
+    _rows_at_least(out, T, "out", k)
     need = dsa_topk_workspace_size(T, ld, k)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -215,6 +242,10 @@ def dsa_indexer_forward(q_bf16, weights, k_cache, block_table,
         raise ValueError("k_cache must be uint8 [num_pages, 8448]")
     if query_start_loc.numel() != R + 1:
         raise ValueError("query_start_loc must have R + 1 entries")
+    _shape(weights, (T, H), "weights")
+    _shape(positions, (T,), "positions")
+    _rows_at_least(logits, T, "logits")
+    _rows_at_least(out, T, "out", k)
     need = dsa_forward_workspace_size(T, H, logits.shape[1], k)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -268,6 +299,9 @@ def dsa_indexer_forward_chunked(q_bf16, weights, k_cache, block_table,
         raise ValueError("k_cache must be uint8 [num_pages, 8448]")
     if query_start_loc.numel() != R + 1:
         raise ValueError("query_start_loc must have R + 1 entries")
+    _shape(weights, (T, H), "weights")
+    _shape(positions, (T,), "positions")
+    _rows_at_least(out, T, "out", k)
     if rows_per_chunk is None:
         if budget_bytes is None:
             total = torch.cuda.get_device_properties(dev).total_memory
@@ -333,6 +367,13 @@ def dsa_index_cache_run(layers, block_table, query_start_loc, positions, ld,
         H = next((l["q_bf16"].shape[1] for l in layers if l is not None), 1)
     arr = (LayerInputs * max(L, 1))()
     for i, lay in enumerate(layers):
+        if lay is not None:
+            _shape(lay["q_bf16"], (T, H, HEAD_DIM), f"layers[{i}].q_bf16")
+            _shape(lay["weights"], (T, H), f"layers[{i}].weights")
+            if lay["k_cache"].dim() != 2 or \
+                    lay["k_cache"].shape[1] != PAGE_BYTES:
+                raise ValueError(f"layers[{i}].k_cache must be uint8 "
+                                 "[num_pages, 8448]")
         if lay is None:
             arr[i] = LayerInputs(None, None, None, 0)
         else:
@@ -377,6 +418,7 @@ def dsa_slot_mapping(block_table, query_start_loc, positions, slots=None,
         raise ValueError("query_start_loc must have R + 1 entries")
     if slots is None:
         slots = torch.empty((T,), dtype=torch.int64, device=dev)
+    _shape(slots, (T,), "slots")
     with torch.cuda.device(dev):
         _check(lib().dsa_slot_mapping(
             _dev_ptr(block_table, torch.int32, "block_table"),
@@ -402,6 +444,8 @@ def dsa_compressed_slot_mapping(block_table, query_start_loc, positions,
         slots = torch.empty((T,), dtype=torch.int64, device=dev)
     if positions_c is None and want_positions_c:
         positions_c = torch.empty((T,), dtype=torch.int32, device=dev)
+    _shape(slots, (T,), "slots")
+    _shape(positions_c, (T,), "positions_c")
     with torch.cuda.device(dev):
         _check(lib().dsa_compressed_slot_mapping(
             _dev_ptr(block_table, torch.int32, "block_table"),
@@ -445,6 +489,7 @@ def dsa_topk_to_slots(topk, block_table, query_start_loc, slots=None,
         raise ValueError("query_start_loc must have R + 1 entries")
     if slots is None:
         slots = torch.empty((T, k), dtype=torch.int64, device=dev)
+    _shape(slots, (T, k), "slots")
     with torch.cuda.device(dev):
         _check(lib().dsa_topk_to_slots(
             _dev_ptr(topk, torch.int32, "topk"), T, k, width,
@@ -463,6 +508,7 @@ def dsa_topk_mask(topk, ld, mask=None, stream=None, k=None):
     dev = topk.device
     if mask is None:
         mask = torch.empty((T, ld), dtype=torch.float32, device=dev)
+    _shape(mask, (T, ld), "mask")
     with torch.cuda.device(dev):
         _check(lib().dsa_topk_mask(
             _dev_ptr(topk, torch.int32, "topk"), T, k, width,

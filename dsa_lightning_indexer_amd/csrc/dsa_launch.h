@@ -39,6 +39,10 @@ struct TopkArgs {
   int64_t out_ld;
   void* workspace;
   size_t ws_bytes;
+  // Rows with a position >= pos_limit get a row of -1 (0: ld).  The forward
+  // pass sets min(ld, 64 * bt_stride): the logits kernels leave such a row
+  // unscored.
+  int64_t pos_limit = 0;
 };
 
 // One layer's hot path: q quantisation into q8 / q_scale, logits, top-k.
@@ -50,15 +54,17 @@ struct ForwardArgs {
   TopkArgs tk;                  // tk.logits == lg.logits
 };
 
-// Kernel-choice knobs (dsa_set_option); 0 = automatic.
+// Kernel-choice knobs (dsa_set_option); 0 = automatic.  Kept per device as
+// atomics; options() is a snapshot of the calling thread's current device.
 struct Options {
-  int logits_kernel = 0;        // 1 row-wise, 2 tiled 8x2, 3 tiled direct, 4 row grid, 5 tiled 16x1 with the two-op epilogue
+  int logits_kernel = 0;        // 1 row-wise, 2 tiled 8x2, 3 tiled direct, 4 row grid, 5 tiled 16x1 with the two-op epilogue, 6 tiled 16x1 (the default tiled kernel, forced)
   int row_pages_per_wave = 0;
   int tile_pages_per_split = 0;
   int row_head_waves = 0;       // decode: 1 + head waves per row (0: one)
   int topk_kernel = 0;          // 0/1 register rows, 2 LDS-cached rows, 3 long rows by multi-WG radix, register rows: 0 two 512-thread workgroups per CU when rows outnumber CUs, else one 1024-thread, 1 always 1024, 4 always 512
+  int tile_pages_per_step = 0;  // 16-row tile kernel: pages per copy step (0 auto, 2 or 4)
 };
-Options& options();
+Options options();
 
 hipError_t launch_quantize_q(const uint16_t* q_bf16, int64_t blocks,
                              uint8_t* q8, float* q_scale, hipStream_t stream);

@@ -1352,7 +1352,8 @@ LogitsPlan logits_plan(int64_t T, int R) {
   const Options& o = options();
   bool tiled = T > 2 * (int64_t)R;
   if (o.logits_kernel == 1 || o.logits_kernel == 4) tiled = false;
-  if (o.logits_kernel == 2 || o.logits_kernel == 3 || o.logits_kernel == 5)
+  if (o.logits_kernel == 2 || o.logits_kernel == 3 || o.logits_kernel == 5 ||
+      o.logits_kernel == 6)
     tiled = true;
   if (tiled) return LogitsPlan::Tiled;
   return T <= kBalancedMaxRows && o.logits_kernel != 4 ? LogitsPlan::Balanced
@@ -1444,7 +1445,9 @@ static hipError_t launch_logits_mt(const LogitsArgs& a, hipStream_t stream,
     // take more than two rounds of the compute units: measured faster on
     // the prefill chunk (8 rounds); on the 1M tail (2 rounds) the step was
     // slower
-    const bool deep = gx * tiles > 2 * (int64_t)device_cu_count();
+    const bool deep = o.tile_pages_per_step == 4 ||
+                      (o.tile_pages_per_step == 0 &&
+                       gx * tiles > 2 * (int64_t)device_cu_count());
     if (o.logits_kernel == 5)
       hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL, false, 2, false>), g3,
                          dim3(kT16Threads), 0, stream, a, pps16, 64);

@@ -47,6 +47,19 @@ constexpr int kBitmapWords = kMaxRowForBitmap / 32;
 constexpr int kMaxCachedHi = 48128;            // 94 KiB: top 16 key bits
 constexpr int kMaxCachedFull = 23552;          // 92 KiB: whole 32-bit keys
 
+// Columns a row ranks: n = p + 1, or 0 (a row of -1) for a position the
+// logits call leaves unscored -- p < 0, or p >= plim (past the logits row,
+// or past the rows' block-table entries in the forward pass).
+__device__ __forceinline__ int row_len_of(int p, int plim) {
+  return (p < 0 || p >= plim) ? 0 : p + 1;
+}
+
+// plim of a launch: ld, or the tighter bound the caller gives.
+static int pos_limit(const TopkArgs& a) {
+  const int64_t lim = a.pos_limit > 0 ? std::min(a.pos_limit, a.ld) : a.ld;
+  return (int)std::min<int64_t>(lim, INT32_MAX);
+}
+
 struct TopkShared {
   uint32_t hist[kHistBins];                    // pass 1 and fallback passes
   uint32_t hist1[kHistBins];                   // candidate pass on bits 19..8
@@ -302,7 +315,7 @@ template <bool KEY32>
 __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(
     const float* __restrict__ logits, int64_t ld,
     const int32_t* __restrict__ positions, int k, int32_t* __restrict__ out,
-    int64_t out_ld, int cache_cap) {
+    int64_t out_ld, int cache_cap, int plim) {
   using CacheT = typename std::conditional<KEY32, uint32_t, uint16_t>::type;
   extern __shared__ __align__(16) unsigned char s_raw[];
   CacheT* s_hi = reinterpret_cast<CacheT*>(s_raw);
@@ -313,9 +326,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(
   const int lane = lane_id();
   const int wave = tid >> 6;
   int32_t* orow = out + t * out_ld;
-  int p = positions[t];
-  if (p >= ld) p = (int)ld - 1;              // logits past ld do not exist
-  const int n = p + 1;                       // p < 0 -> empty row
+  // p < 0 or p >= plim (a position the logits call does not score):
+  // empty row, all -1
+  const int n = row_len_of(positions[t], plim);
   if (n <= k) {
     for (int i = tid; i < k; i += kTopkThreads) orow[i] = i < n ? i : -1;
     return;
@@ -766,14 +779,14 @@ template <int S, bool BITMAP, int NT, bool PF>
 __global__ __launch_bounds__(NT, 4) void topk_reg_kernel(
     const float* __restrict__ logits, int64_t ld,
     const int32_t* __restrict__ positions, int k, int32_t* __restrict__ out,
-    int64_t out_ld, int64_t T) {
+    int64_t out_ld, int64_t T, int plim) {
   static_assert(S >= 1 && S * 4 * NT <= kRegMaxRow, "slices");
   constexpr int kSlice = 4 * NT;
   __shared__ RegTopkShared<NT, S> sh;
   const int tid = threadIdx.x;
-  // n = p + 1 columns (p < 0: empty row; logits past ld do not exist)
+  // n = p + 1 columns (p < 0 or p >= plim: empty row)
   auto row_len = [&](int64_t t) {
-    return min(load_uniform(positions, t), (int)ld - 1) + 1;
+    return row_len_of(load_uniform(positions, t), plim);
   };
   // buffer loads over the row (one offset register for all slices; reads
   // past the row's n columns return 0 and are masked out anyway)
@@ -879,6 +892,7 @@ struct MwWorkspace {
   uint32_t* cand_key; // [T][cap]
   uint32_t* cand_idx; // [T][cap]
   int64_t C;          // chunks per row
+  int plim;           // positions >= plim: empty row
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -971,10 +985,8 @@ struct MwShared {
 };
 
 __device__ __forceinline__ int row_len(const int32_t* positions, int64_t t,
-                                       int64_t ld) {
-  int p = positions[t];
-  if (p >= ld) p = (int)ld - 1;
-  return p + 1;
+                                       int plim) {
+  return row_len_of(positions[t], plim);
 }
 
 // Becomes true in exactly one workgroup per row: the last of `parts`
@@ -998,7 +1010,7 @@ __global__ __launch_bounds__(kMwThreads) void mw_pass1_kernel(
   __shared__ MwShared sh;
   const int64_t t = blockIdx.y;
   const int64_t c = blockIdx.x;
-  const int n = row_len(positions, t, ld);
+  const int n = row_len(positions, t, ws.plim);
   if (n <= k) return;
   const uint32_t parts = (uint32_t)((n + kMwChunk - 1) / kMwChunk);
   if (c >= parts) return;
@@ -1104,7 +1116,7 @@ __global__ __launch_bounds__(kMwThreads) void mw_pass2_kernel(
   __shared__ MwShared sh;
   const int64_t t = blockIdx.y;
   const int64_t c = blockIdx.x;
-  const int n = row_len(positions, t, ld);
+  const int n = row_len(positions, t, ws.plim);
   if (n <= k) return;
   const uint32_t parts = (uint32_t)((n + kMwChunk - 1) / kMwChunk);
   if (c >= parts) return;
@@ -1163,7 +1175,7 @@ __global__ __launch_bounds__(kMwThreads) void mw_write_kernel(
   __shared__ MwShared sh;
   const int64_t t = blockIdx.y;
   const int64_t c = blockIdx.x;
-  const int n = row_len(positions, t, ld);
+  const int n = row_len(positions, t, ws.plim);
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   int32_t* orow = out + t * out_ld;
   if (n <= k) {
@@ -1249,6 +1261,7 @@ struct SsWorkspace {
   uint32_t* count;    // [T][C] candidates per chunk (> cap: overflow)
   uint2* cand;        // [T][C][cap] (key, column)
   int64_t C;
+  int plim;           // positions >= plim: empty row
 };
 
 static bool use_sample_select(int64_t ld) {
@@ -1291,7 +1304,7 @@ __global__ __launch_bounds__(kSsThreads) void ss_gather_kernel(
     const float* __restrict__ logits, int64_t ld, const int32_t* positions,
     int k, SsWorkspace ws) {
   const int64_t t = blockIdx.y;
-  const int n = row_len(positions, t, ld);
+  const int n = row_len(positions, t, ws.plim);
   if (n <= kSsCandMax || n <= k) return;
   const float* row = logits + t * ld;
   const uint32_t stride = (uint32_t)n / kSsSample;     // >= 1
@@ -1315,7 +1328,7 @@ __global__ __launch_bounds__(kTopkThreads) void ss_sample_kernel(
     int k, SsWorkspace ws) {
   __shared__ RegTopkShared<kTopkThreads, 4> sh;
   const int64_t t = blockIdx.x;
-  const int n = row_len(positions, t, ld);
+  const int n = row_len(positions, t, ws.plim);
   if (n <= kSsCandMax || n <= k) return;
   const int tid = threadIdx.x;
   for (int b = tid; b < kHistBins; b += kTopkThreads) {
@@ -1350,7 +1363,7 @@ __global__ __launch_bounds__(kSsThreads) void ss_collect_kernel(
   __shared__ uint32_t s_tot[kSlices * kWaves];
   const int64_t t = blockIdx.y;
   const int64_t c = blockIdx.x;
-  const int n = row_len(positions, t, ld);
+  const int n = row_len(positions, t, ws.plim);
   if (n <= kSsCandMax || n <= k) return;
   const int parts = (n + kSsChunk - 1) / kSsChunk;
   if (c >= parts) return;
@@ -1437,7 +1450,7 @@ __global__ __launch_bounds__(kTopkThreads) void ss_select_kernel(
   __shared__ uint32_t s_pre[kSsMaxChunks + 1];
   __shared__ uint32_t s_flag[2];
   const int64_t t = blockIdx.x;
-  const int n = row_len(positions, t, ld);
+  const int n = row_len(positions, t, ws.plim);
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   int32_t* orow = out + t * out_ld;
   if (n <= k) {
@@ -1539,7 +1552,7 @@ static hipError_t launch_topk_single_t(const TopkArgs& a, hipStream_t stream,
   }
   hipLaunchKernelGGL(topk_row_kernel<KEY32>, dim3((unsigned)a.T),
                      dim3(kTopkThreads), dyn, stream, a.logits, a.ld,
-                     a.positions, a.k, a.out, a.out_ld, cap);
+                     a.positions, a.k, a.out, a.out_ld, cap, pos_limit(a));
   return hipGetLastError();
 }
 
@@ -1567,11 +1580,13 @@ static hipError_t launch_topk_reg_t(const TopkArgs& a, hipStream_t stream) {
   if ((int64_t)a.k * 8 < a.ld)
     hipLaunchKernelGGL((topk_reg_kernel<S, true, kTopkThreads, true>),
                        dim3((unsigned)grid), dim3(kTopkThreads), 0, stream,
-                       a.logits, a.ld, a.positions, a.k, a.out, a.out_ld, a.T);
+                       a.logits, a.ld, a.positions, a.k, a.out, a.out_ld, a.T,
+                       pos_limit(a));
   else
     hipLaunchKernelGGL((topk_reg_kernel<S, false, kTopkThreads, true>),
                        dim3((unsigned)grid), dim3(kTopkThreads), 0, stream,
-                       a.logits, a.ld, a.positions, a.k, a.out, a.out_ld, a.T);
+                       a.logits, a.ld, a.positions, a.k, a.out, a.out_ld, a.T,
+                       pos_limit(a));
   return hipGetLastError();
 }
 
@@ -1585,7 +1600,8 @@ static hipError_t launch_topk_reg2_t(const TopkArgs& a, hipStream_t stream) {
   const int64_t grid = std::min<int64_t>(a.T, 2 * (int64_t)device_cu_count());
   hipLaunchKernelGGL((topk_reg_kernel<S, BITMAP, kReg2Threads, false>),
                      dim3((unsigned)grid), dim3(kReg2Threads), 0, stream,
-                     a.logits, a.ld, a.positions, a.k, a.out, a.out_ld, a.T);
+                     a.logits, a.ld, a.positions, a.k, a.out, a.out_ld, a.T,
+                       pos_limit(a));
   return hipGetLastError();
 }
 
@@ -1660,7 +1676,8 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   if (!use_multi_wg(a.ld)) return launch_topk_single(a, stream);
   const bool aligned = (reinterpret_cast<uintptr_t>(a.logits) & 15u) == 0;
   if (use_sample_select(a.ld) && aligned && options().topk_kernel != 3) {
-    const SsWorkspace ss = ss_carve(a.workspace, a.T, a.ld, nullptr);
+    SsWorkspace ss = ss_carve(a.workspace, a.T, a.ld, nullptr);
+    ss.plim = pos_limit(a);
     hipLaunchKernelGGL(ss_gather_kernel, dim3(kSsGatherWgs, (unsigned)a.T),
                        dim3(kSsThreads), 0, stream, a.logits, a.ld,
                        a.positions, a.k, ss);
@@ -1676,6 +1693,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   MwWorkspace ws = carve(a.workspace, a.T, a.ld, nullptr);
+  ws.plim = pos_limit(a);
   const size_t zb = mw_zero_bytes(a.T, a.ld);
   const size_t n16 = zb / 16;
   hipLaunchKernelGGL(mw_clear_kernel,

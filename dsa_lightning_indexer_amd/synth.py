@@ -26,8 +26,10 @@ which starts from the cache bytes.  Tokens past a request's length inside its
 last page are zero bytes.
 """
 
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 import math
+import os
 
 import numpy as np
 import torch
@@ -210,13 +212,16 @@ def index_cache_pattern(num_layers=61, seed=SEEDS["index_cache_pattern"]):
 
 
 def index_cache_layers(full_layers, seed=SEEDS["index_cache"], R=32,
-                       context=16384, H=64, k=2048):
+                       context=16384, H=64, k=2048, workers=None):
     """Independent per-layer inputs for the IndexCache stack.
 
     All layers share one batch of R decode requests (context tokens each, one
     query at the last position) and so one block table, drawn from ``seed``;
     every listed layer gets its own K cache, q and weights from its own PCG64
-    stream spawned from ``seed``.  Returns {layer: IndexerBatch}.
+    stream spawned from ``seed``.  Layers are drawn on up to ``workers``
+    threads (default: the usable cores, at most 16); each layer's bytes
+    depend only on its own stream, so the result does not depend on the
+    thread count.  Returns {layer: IndexerBatch}.
     """
     ss = np.random.SeedSequence(seed)
     n_streams = (max(full_layers) + 1) if full_layers else 0
@@ -224,9 +229,16 @@ def index_cache_layers(full_layers, seed=SEEDS["index_cache"], R=32,
     contexts = [context] * R
     layout = page_layout(np.random.Generator(np.random.PCG64(kids[0])),
                          contexts)
-    out = {}
-    for l in full_layers:
+
+    def one(l):
         rng = np.random.Generator(np.random.PCG64(kids[l + 1]))
-        out[l] = build_batch(rng, contexts, [[context - 1]] * R, H=H, k=k,
-                             name=f"index_cache_layer{l}", layout=layout)
-    return out
+        return build_batch(rng, contexts, [[context - 1]] * R, H=H, k=k,
+                           name=f"index_cache_layer{l}", layout=layout)
+
+    if workers is None:
+        workers = min(16, len(os.sched_getaffinity(0)))
+    layers = list(full_layers)
+    if workers <= 1 or len(layers) <= 1:
+        return {l: one(l) for l in layers}
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        return dict(zip(layers, ex.map(one, layers)))

@@ -38,10 +38,13 @@
  *  - Return value: DSA_OK (0) or a negative dsa_status.  Argument errors are
  *    detected on the host before anything is enqueued; the message is
  *    available from dsa_last_error() on the calling thread.
- *  - Device-side range errors (a block_table entry outside the page pool, a
- *    position outside the logits row or block-table row) never fault: the
- *    affected logits become -inf and a sticky flag is raised, readable with
- *    dsa_device_error_flags().
+ *  - Device-side range errors never fault; each raises a sticky flag,
+ *    readable with dsa_device_error_flags().  A block_table entry outside
+ *    the page pool: the logits of that page's tokens are -inf.  A position
+ *    outside the logits row (p < 0 or p >= ld) or past the request's
+ *    block-table row (p / 64 >= bt_stride): the row's logits are not
+ *    written, and its top-k row (forward, run, or dsa_indexer_topk for p <
+ *    0 or p >= ld) is all -1.
  *  - Supported shapes: head_dim == 128, page_size == 64, 1 <= H <= 64.
  *  - The *_workspace_size queries return 0 for arguments the matching entry
  *    point rejects or treats as a no-op (T <= 0, T > 2^31, ld <= 0,
@@ -135,7 +138,9 @@ int dsa_indexer_logits(const uint8_t* q_fp8, const float* q_scale,
  *   positions  device, int32 [T].
  *   out        device, out: int32 [T, out_ld], out_ld >= k; slots [0, k) of
  *              every row are written.
- * n = p_t + 1.  If n <= k the row is 0, 1, ..., n-1 followed by -1.
+ * n = p_t + 1 (n = 0, a row of -1, when p_t < 0 or p_t >= ld: a position
+ * the logits call does not score).  If n <= k the row is 0, 1, ..., n-1
+ * followed by -1.
  * Otherwise it holds the k token positions with the largest logits, ties at
  * the k-th value broken toward the lower position, listed in ascending
  * position order.  workspace/ws_bytes: dsa_topk_workspace_size() bytes of
@@ -158,7 +163,9 @@ size_t dsa_topk_workspace_size(int64_t T, int64_t ld, int k);
  *              codes and scales, top-k scratch); contents on entry do not
  *              matter.
  * The three kernels run in turn on `stream`; the result equals the three
- * separate calls bit for bit.
+ * separate calls bit for bit, except that a row whose position is past its
+ * block-table row (p / 64 >= bt_stride; flagged, logits not written) gets a
+ * top-k row of -1.
  */
 int dsa_indexer_forward(const void* q_bf16, const float* weights,
                         const uint8_t* k_cache, int64_t num_pages,
@@ -409,15 +416,21 @@ int dsa_device_error_flags(int reset);
 
 /*
  * dsa_set_option -- tuning/testing knobs; returns the previous value or
- * DSA_ERR_INVALID_ARG for an unknown key.  Value 0 restores the automatic
- * choice.  Keys: "logits_kernel" (1 row-wise, 2 tiled with 8 waves x 2 rows,
- * 3 tiled with direct loads, 4 row-wise on a (row, page group) grid, 5 tiled
- * with 16 waves x 1 row but ReLU as an add and an FMA per MFMA output
- * instead of the default's shared linear term), "row_pages_per_wave",
- * "row_head_waves" (decode rows: 1 + the waves per row that take its first
- * pages before the positions are read; default one such wave, 1 = none),
- * "tile_pages_per_split", "topk_kernel" (rows of up to 49152 columns, keys
- * in registers: by default one 1024-thread workgroup per row, two 512-thread
+ * DSA_ERR_INVALID_ARG for an unknown key or value.  Knobs are kept per
+ * device (the calling thread's current HIP device) in atomics: concurrent
+ * calls are safe, and each launch reads one snapshot of its device's knobs.
+ * Value 0 restores the automatic choice.  Keys: "logits_kernel" (1
+ * row-wise, 2 tiled with 8 waves x 2 rows, 3 tiled with direct loads, 4
+ * row-wise on a (row, page group) grid, 5 tiled with 16 waves x 1 row but
+ * ReLU as an add and an FMA per MFMA output instead of the default's shared
+ * linear term, 6 the default tiled kernel whatever the batch's shape),
+ * "row_pages_per_wave", "row_head_waves" (decode rows: 1 + the
+ * waves per row that take its first pages before the positions are read;
+ * default one such wave, 1 = none), "tile_pages_per_split",
+ * "tile_pages_per_step" (16-row tile kernel: pages staged per copy step, 2
+ * or 4; automatic: 4 when its grid takes more than two rounds of the
+ * compute units), "topk_kernel" (rows of up to 49152 columns, keys in
+ * registers: by default one 1024-thread workgroup per row, two 512-thread
  * workgroups per compute unit when the rows outnumber the compute units; 1
  * always the former, 4 always the latter; 2 keys cached in LDS; rows longer
  * than 65536 columns: 3 multi-workgroup radix select instead of sample

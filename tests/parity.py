@@ -31,6 +31,18 @@ LOGIT_FLOOR = 1e-2
 TOPK_TIE = 1e-3
 
 
+# Logits kernel classes the tests force (dsa_set_option "logits_kernel"),
+# plus 7: the default tiled kernel with four pages per copy step (the
+# instance the launcher picks for grids of more than two rounds).
+LOGITS_KERNELS = (0, 1, 2, 3, 4, 5, 6, 7)
+
+
+def set_logits_kernel(kernel):
+    """Force logits kernel class ``kernel`` (0 = automatic)."""
+    binding.dsa_set_option("logits_kernel", 6 if kernel == 7 else kernel)
+    binding.dsa_set_option("tile_pages_per_step", 4 if kernel == 7 else 0)
+
+
 def upload(b, device="cuda"):
     d = dict(
         q_bf16=b.q_bf16.to(device),
@@ -81,18 +93,44 @@ def magnitude(b, rows=None):
     codes, s = _oracle_q(b, rows)
     req = oi.request_of_rows(b.query_start_loc, b.T)
     out = np.zeros((len(rows), b.ld))
+    kabs = {}                                  # |khat| of a request's tokens
     for i, t in enumerate(rows):
         p = int(b.positions[t])
+        r = int(req[t])
+        if r not in kabs or kabs[r].shape[0] < p + 1:
+            need = int(max(b.positions[rows][req[rows] == r])) + 1
+            kabs[r] = np.abs(oi.gather_k(b.k_cache, b.block_table[r], 0, need))
         qa = np.abs(oi.dequantize(codes[t], s[t]))
-        ka = np.abs(oi.gather_k(b.k_cache, b.block_table[req[t]], 0, p + 1))
-        out[i, : p + 1] = np.abs(b.weights[t]).astype(np.float64) @ (qa @ ka.T)
+        out[i, : p + 1] = np.abs(b.weights[t]).astype(np.float64) @ \
+            (qa @ kabs[r][: p + 1].T)
     return out
+
+
+# The survey's logits criterion (the north star's "max relative error 2e-3"
+# with a floor for logits near zero): |g - o| <= 2e-3 * max(|o|, 1e-2 S_t),
+# S_t = max |o| over the row's visible columns.  Every check_logits_row call
+# evaluates it on every visible column and appends one record here; the
+# session summary (tests/conftest.py) reports the totals.
+G11_LOG = []
+
+
+def g11_ratios(g, o):
+    """|g - o| / (2e-3 max(|o|, 1e-2 S_t)) per column (0 where both the
+    error and the bound are 0)."""
+    o = np.asarray(o, dtype=np.float64)
+    err = np.abs(np.asarray(g, dtype=np.float64) - o)
+    S = float(np.max(np.abs(o))) if o.size else 0.0
+    bound = LOGIT_RTOL * np.maximum(np.abs(o), LOGIT_FLOOR * S)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(bound > 0, err / bound, np.where(err > 0, np.inf, 0.0))
+    return r
 
 
 def check_logits_row(g, o, p, what="", m=None):
     """Logit tolerance on columns 0..p (``m`` = magnitude row; without it
-    only the relative term applies).  Returns the max relative error over
-    columns with |o| >= 1e-2 * max|o|."""
+    only the relative term applies).  Also evaluates the survey criterion
+    (G11_LOG).  Returns the max relative error over columns with |o| >=
+    1e-2 * max|o|."""
     o = np.asarray(o[: p + 1], dtype=np.float64)
     g = np.asarray(g[: p + 1], dtype=np.float64)
     tol = LOGIT_RTOL * np.abs(o)
@@ -105,6 +143,15 @@ def check_logits_row(g, o, p, what="", m=None):
         f"gpu={g[bad[0]]!r} oracle={o[bad[0]]!r} tol={tol[bad[0]]!r}")
     S = float(np.max(np.abs(o))) if o.size else 0.0
     big = np.abs(o) >= LOGIT_FLOOR * S
+    r = g11_ratios(g, o)
+    rec = {"what": what, "cols": int(o.size), "viol": int(np.sum(r > 1)),
+           "max_ratio": float(r.max()) if r.size else 0.0,
+           "viol_cols_max_abs_over_S": float(np.max(np.abs(o[r > 1])) / S)
+           if np.any(r > 1) else 0.0}
+    if m is not None and np.any(r > 1):
+        mm = np.asarray(m[: p + 1], dtype=np.float64)
+        rec["viol_max_err_over_M"] = float(np.max(err[r > 1] / mm[r > 1]))
+    G11_LOG.append(rec)
     return float(np.max(err[big] / np.abs(o[big]))) if big.any() else 0.0
 
 

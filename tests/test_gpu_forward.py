@@ -8,6 +8,7 @@ import pytest
 import torch
 
 from dsa_lightning_indexer_amd import binding, synth
+from oracle import indexer as oi
 from tests import parity
 
 pytestmark = [pytest.mark.gpu,
@@ -24,7 +25,8 @@ def _say(msg):
 def _reset():
     binding.dsa_device_error_flags(reset=True)
     yield
-    for key in ("logits_kernel", "topk_kernel", "row_pages_per_wave"):
+    for key in ("logits_kernel", "topk_kernel", "row_pages_per_wave",
+                "tile_pages_per_step"):
         binding.dsa_set_option(key, 0)
 
 
@@ -125,22 +127,57 @@ def test_forward_graph_replays():
 
 
 def test_forward_out_of_range_position_row():
-    """A position past the logits row: flagged, its logits row untouched,
-    every other row as from the separate calls."""
-    _say("case: forward with an out-of-range position (host-forced)")
+    """A position past the logits row, and one inside it but past the
+    request's block-table row: both flagged, their logits rows untouched,
+    their top-k rows all -1, every other row as from the separate calls."""
+    _say("case: forward with out-of-range positions (host-forced)")
     b = synth.decode(R=16, seed=77)
     d = parity.upload(b)
     _, _, lg_ref, tk_ref = parity.run_gpu(b, d)
+    bt_cols = 64 * b.block_table.shape[1]
+    ld = bt_cols + 512                       # room for a row past the table
     pos = d["positions"].clone()
-    pos[5] = b.ld + 100
+    pos[5] = ld + 100                        # past the logits row
+    pos[9] = bt_cols + 7                     # inside it, past the table row
     d2 = dict(d, positions=pos)
-    lg = torch.full((b.T, b.ld), 3.0, device="cuda")
-    _, tk = _forward(b, d2, logits=lg)
+    lg = torch.full((b.T, ld), 3.0, device="cuda")
+    tk = torch.full((b.T, b.k), 11, dtype=torch.int32, device="cuda")
+    need = binding.dsa_forward_workspace_size(b.T, b.H, ld, b.k)
+    ws = torch.empty((need,), dtype=torch.uint8, device="cuda")
+    binding.dsa_indexer_forward(d2["q_bf16"], d2["weights"], d2["k_cache"],
+                                d2["block_table"], d2["qsl"], pos, ld, b.k,
+                                logits=lg, out=tk, workspace=ws)
     torch.cuda.synchronize()
     assert binding.dsa_device_error_flags(reset=True) & 2
-    assert torch.all(lg[5] == 3.0)
-    keep = [t for t in range(b.T) if t != 5]
+    for t in (5, 9):
+        assert torch.all(lg[t] == 3.0)
+        assert torch.all(tk[t] == -1), f"row {t}"
+    keep = [t for t in range(b.T) if t not in (5, 9)]
     assert torch.equal(tk[keep], tk_ref[keep])
+
+
+@pytest.mark.parametrize("ld,opt", [(4096, 0), (4096, 2), (131072, 0),
+                                    (131072, 3)])
+def test_topk_position_outside_the_row_gives_minus_one(ld, opt):
+    """dsa_indexer_topk: a row at p >= ld (no logits for it) or p < 0 is all
+    -1 in every top-k kernel class; a row at ld - 1 is the exact top-k."""
+    _say(f"case: top-k rows past ld (ld {ld}, topk_kernel {opt})")
+    T, k = 4, 64
+    g = torch.Generator().manual_seed(ld + opt)
+    logits = torch.randn((T, ld), generator=g).cuda()
+    pos = torch.tensor([ld - 1, ld, ld + 1000, -3], dtype=torch.int32,
+                       device="cuda")
+    out = torch.full((T, k), 11, dtype=torch.int32, device="cuda")
+    binding.dsa_set_option("topk_kernel", opt)
+    try:
+        binding.dsa_indexer_topk(logits, pos, k, out=out)
+        torch.cuda.synchronize()
+    finally:
+        binding.dsa_set_option("topk_kernel", 0)
+    out = out.cpu().numpy()
+    ref = oi.topk_row(logits[0].cpu().numpy().astype(np.float64), k)
+    assert np.array_equal(out[0], np.sort(ref))
+    assert np.all(out[1:] == -1)
 
 
 def test_forward_rejects_small_workspace():

@@ -40,9 +40,10 @@ def _dev_layers(batches, L):
     return out
 
 
-def _check_run(batches, ref, mask, snaps, k, rows_per_layer=None):
+def _check_run(batches, ref, mask, snaps, k, rows_per_layer=None, dev=None):
     """S snapshots equal the previous F snapshot bit-exactly; F snapshots
-    match the oracle (sampled rows) and the standalone top-k exactly."""
+    match the oracle (sampled rows: top-k sets and logits) and the
+    standalone calls exactly.  ``dev``: device copies of the layers."""
     snaps = snaps.cpu().numpy()
     last_full = None
     bt = torch.from_numpy(ref.block_table).cuda()
@@ -55,20 +56,24 @@ def _check_run(batches, ref, mask, snaps, k, rows_per_layer=None):
             continue
         last_full = l
         b = batches[l]
-        d = {"q_bf16": b.q_bf16.cuda(),
-             "weights": torch.from_numpy(b.weights).cuda(),
-             "k_cache": torch.from_numpy(b.k_cache).cuda(),
-             "block_table": bt, "qsl": qsl, "positions": pos}
+        lay = dev[l] if dev is not None else {
+            "q_bf16": b.q_bf16.cuda(),
+            "weights": torch.from_numpy(b.weights).cuda(),
+            "k_cache": torch.from_numpy(b.k_cache).cuda()}
+        d = dict(lay, block_table=bt, qsl=qsl, positions=pos)
         _, _, lg, tk = parity.run_gpu(b, d, k)
         assert np.array_equal(tk.cpu().numpy(), snaps[l]), \
             f"layer {l}: run() differs from the standalone calls"
         rows = range(b.T) if rows_per_layer is None else rows_per_layer
         rows = list(rows)
         ora = parity.oracle_logits(b, rows=rows)
+        lg_rows = lg[rows].cpu().numpy()
         for i, t in enumerate(rows):
             p = int(b.positions[t])
             parity.check_topk_row(snaps[l][t], ora[i, : p + 1], k,
                                   f"layer {l} row {t}")
+            parity.check_logits_row(lg_rows[i], ora[i], p,
+                                    f"layer {l} row {t}")
 
 
 @pytest.mark.parametrize("cfg", [dict(freq=4, offset=2),
@@ -189,22 +194,48 @@ def test_mtp_draft_passes():
     assert binding.dsa_device_error_flags(reset=True) == 0
 
 
-def test_index_cache_run_full_size_freq4():
-    _say("case: index cache full size (61 layers, 32 x 16384, freq 4)")
+@pytest.fixture(scope="module")
+def full_stack():
+    """The IndexCache workload at full size: 61 layers, each with its own K
+    cache, q and weights; 32 decode requests x 16384 context, H = 64, k =
+    2048.  Generated once for the three runs below."""
+    _say("generating the 61-layer stack (32 x 16384, H=64)")
     L = 61
-    mask = binding.dsa_index_cache_mask(L, freq=4, offset=2)
-    full = [l for l in range(L) if not mask[l]]
-    assert len(full) == 16
-    batches, ref = _stack(full, 32, 16384, 64, 2048)
+    batches, ref = _stack(list(range(L)), 32, 16384, 64, 2048)
+    dev = _dev_layers(batches, L)
+    yield L, batches, ref, dev
+    del dev
+
+
+@pytest.mark.parametrize("run", ["freq4", "pattern", "freq1"])
+def test_index_cache_run_full_size(full_stack, run):
+    """dsa_index_cache_run at full size with freq 4 / offset 2 (16 F), the
+    seeded 61-character pattern and freq 1 (61 F): the mask, S snapshots
+    bit-exact, every F layer equal to the standalone calls and 5 oracle rows
+    per F layer (top-k sets and logits)."""
+    L, batches, ref, dev = full_stack
+    kw = {"freq4": dict(freq=4, offset=2),
+          "pattern": dict(pattern=synth.index_cache_pattern(L)),
+          "freq1": dict(freq=1, offset=2)}[run]
+    _say(f"case: index cache full size (61 layers, 32 x 16384), {run}")
+    mask = binding.dsa_index_cache_mask(L, **kw)
+    assert mask == oic.skip_mask(L, **kw).tolist()
+    if run == "freq4":
+        assert sum(1 for x in mask if not x) == 16
+    if run == "freq1":
+        assert not any(mask)
+    # layers a run does not compute are passed as None: nothing reads them
+    layers = [None if mask[l] else dev[l] for l in range(L)]
     buf = torch.empty((32, 2048), dtype=torch.int32, device="cuda")
     skip, snaps = binding.dsa_index_cache_run(
-        _dev_layers(batches, L), torch.from_numpy(ref.block_table).cuda(),
+        layers, torch.from_numpy(ref.block_table).cuda(),
         torch.from_numpy(ref.query_start_loc).cuda(),
         torch.from_numpy(ref.positions).cuda(), ref.ld, 2048, buf,
-        freq=4, offset=2, snapshots=True)
+        snapshots=True, H=64, **kw)
     torch.cuda.synchronize()
     assert skip == mask
-    _check_run(batches, ref, mask, snaps, 2048, rows_per_layer=[0, 13, 31])
+    _check_run(batches, ref, mask, snaps, 2048,
+               rows_per_layer=[0, 7, 13, 22, 31], dev=dev)
     assert binding.dsa_device_error_flags(reset=True) == 0
 
 

@@ -180,8 +180,10 @@ def test_prefill_chunk_sampled_rows(kernel):
     b = synth.prefill()
     _, _, lg, tk = parity.run_gpu(b)
     rng = np.random.default_rng(2)
-    rows = sorted(set([0, 1, 15, 16, 17, 63, 64, 4095, 8190, 8191] +
-                      rng.choice(b.T, 14, replace=False).tolist()))
+    # 256 evenly spaced rows (the sample the bench's CPU leg times) plus the
+    # tile and page edges
+    even = np.linspace(0, b.T - 1, 256).round().astype(np.int64).tolist()
+    rows = sorted(set([0, 1, 15, 16, 17, 63, 64, 4095, 8190, 8191] + even))
     ora = parity.oracle_logits(b, rows=rows)
     mag = parity.magnitude(b, rows=rows)
     lg_rows = lg[rows].cpu().numpy()
@@ -250,10 +252,10 @@ EDGE_CASES = {
 
 
 @pytest.mark.parametrize("name", sorted(EDGE_CASES))
-@pytest.mark.parametrize("kernel", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("kernel", [1, 2, 3, 4, 5, 6, 7])
 def test_edge_cases(name, kernel):
     _say(f"case: edge {name}, logits kernel {kernel}")
-    binding.dsa_set_option("logits_kernel", kernel)
+    parity.set_logits_kernel(kernel)
     contexts, positions, H, k = EDGE_CASES[name]
     b = _edge_batch(zlib.crc32(name.encode()) % 1000, contexts, positions, H, k,
                     pool_pages=sum((c + 63) // 64 for c in contexts) + 3)

@@ -28,7 +28,7 @@ SLOT_SENTINEL = -77
 def _reset():
     binding.dsa_device_error_flags(reset=True)
     yield
-    binding.dsa_set_option("logits_kernel", 0)
+    parity.set_logits_kernel(0)
     binding.dsa_set_option("topk_kernel", 0)
 
 
@@ -51,13 +51,13 @@ def _batch(layout):
 
 
 @pytest.mark.parametrize("layout", ["decode", "scattered"])
-@pytest.mark.parametrize("kernel", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("kernel", parity.LOGITS_KERNELS)
 def test_logits_written_region(layout, kernel):
     b = _batch(layout)
     print(f"case: layout {layout} logits_kernel {kernel} T={b.T} ld={b.ld}",
           flush=True)
     sys.stdout.flush()
-    binding.dsa_set_option("logits_kernel", kernel)
+    parity.set_logits_kernel(kernel)
     d = parity.upload(b)
     q8, qs = binding.dsa_quantize_q(d["q_bf16"])
     lg = torch.full((b.T, b.ld), SENTINEL, dtype=torch.float32, device="cuda")
@@ -150,7 +150,7 @@ def test_topk_reads_only_columns_up_to_p(topk_kernel, ld):
 
 
 @pytest.mark.parametrize("layout", ["decode", "scattered"])
-@pytest.mark.parametrize("kernel", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("kernel", parity.LOGITS_KERNELS)
 def test_logits_ignore_block_table_entries_past_the_rows(layout, kernel):
     """Block-table entries past the last page a request's rows reach hold
     an out-of-pool page id: no kernel uses them (no range flag, logits as
@@ -165,7 +165,7 @@ def test_logits_ignore_block_table_entries_past_the_rows(layout, kernel):
         b.block_table[r, need:] = 1 << 30
     print(f"case: junk past the pages, layout {layout}, kernel {kernel}",
           flush=True)
-    binding.dsa_set_option("logits_kernel", kernel)
+    parity.set_logits_kernel(kernel)
     _, _, lg, _ = parity.run_gpu(b)
     assert binding.dsa_device_error_flags(reset=True) == 0
     g = lg.cpu().numpy()

@@ -11,11 +11,11 @@ from oracle import chunking, indexer
 
 def test_printed_figures(golden):
     g = golden("logits_budget_example.json")
-    assert chunking.BYTES_PER_ELEM == g["bytes_per_elem"]
-    assert chunking.STATIC_SKIP_ELEMS == g["static_skip_elems"]
-    assert chunking.TOTAL_MEM_FRACTION == g["total_mem_fraction"]
-    assert chunking.ROW_ALIGN_ELEMS * 4 == g["row_stride_bytes"]
-    assert g["context_1m"] * chunking.BYTES_PER_ELEM == g["row_bytes_1m"]
+    assert chunking.FP32_BYTES == g["bytes_per_elem"]
+    assert chunking.UNCHECKED_BELOW_ELEMS == g["static_skip_elems"]
+    assert chunking.DEVICE_SHARE == g["total_mem_fraction"]
+    assert chunking.ROW_COLUMNS_ALIGN * 4 == g["row_stride_bytes"]
+    assert g["context_1m"] * chunking.FP32_BYTES == g["row_bytes_1m"]
     assert g["row_bytes_1m"] == 4 << 20                          # "4MB"
     assert g["prefill_rows_32k"] * g["row_bytes_1m"] == \
         g["prefill_bytes_32k_by_1m"] == 128 << 30                  # "128GB"
