@@ -93,6 +93,11 @@ def parse():
                     help="per-dispatch FETCH_SIZE / WRITE_SIZE of the logits "
                          "kernel from two rocprofv3 --pmc CSV directories, "
                          "scaled by the 256 MiB calibration copy (no GPU)")
+    ap.add_argument("--mfma-summary", metavar="DIR",
+                    help="per-dispatch MFMA counters (SQ_VALU_MFMA_BUSY_"
+                         "CYCLES, SQ_INSTS_VALU_MFMA_MOPS_F8, ..., "
+                         "GRBM_GUI_ACTIVE) of the logits kernel from one "
+                         "rocprofv3 --pmc CSV directory (no GPU)")
     ap.add_argument("--bench-log", help="bench JSON line of the profiled run")
     ap.add_argument("--command", action="append", default=[],
                     help="command line(s) that produced the profile")
@@ -326,6 +331,78 @@ def pmc_summary(args):
             bench["roofline"]["algorithmic_bytes"] if bench else None,
         "commands": args.command,
     }
+    print(json.dumps(out, indent=1))
+
+
+SIMDS = 4 * 256               # MI355X: 256 compute units x 4 SIMDs
+
+
+def mfma_summary(args):
+    """Average per dispatch of each counter of a multi-counter --pmc run,
+    for the workload's logits kernel at its largest grid (the workload's own
+    launch), with the MFMA busy fraction SQ_VALU_MFMA_BUSY_CYCLES /
+    (GRBM_GUI_ACTIVE x SIMDs) and the FP8 MFMA work the counters saw
+    (SQ_INSTS_VALU_MFMA_MOPS_F8 x 512 FLOP) beside the algorithmic FLOPs."""
+    rows = _csv_rows(args.mfma_summary, "counter_collection.csv")
+    # GRBM_GUI_ACTIVE comes summed over the XCDs (each counts the cycles
+    # the GPU is busy): per XCD it is the dispatch's active cycles
+    xcc = 8
+    for a in glob.glob(os.path.join(args.mfma_summary, "*agent_info.csv")):
+        with open(a, newline="") as f:
+            for r in csv.DictReader(f):
+                if r.get("Agent_Type") == "GPU" and r.get("Num_Xcc"):
+                    xcc = int(r["Num_Xcc"])
+    per, grid = {}, {}
+    for r in rows:
+        key = r["Dispatch_Id"]
+        d = per.setdefault(key, {"name": r["Kernel_Name"],
+                                 "grid": int(r["Grid_Size"]), "c": {},
+                                 "ns": None})
+        c = r["Counter_Name"]
+        d["c"][c] = d["c"].get(c, 0.0) + float(r["Counter_Value"])
+        if r.get("End_Timestamp") and r.get("Start_Timestamp"):
+            d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        b = _base_name(d["name"])
+        grid[b] = max(grid.get(b, 0), d["grid"])
+    is_dom = _matcher(args.config)
+    dom = [d for d in per.values() if is_dom(d["name"]) and
+           d["grid"] == grid[_base_name(d["name"])]]
+    if not dom:
+        raise SystemExit("no logits dispatch in the counter run")
+    names = sorted({c for d in dom for c in d["c"]})
+    avg = {c: sum(d["c"].get(c, 0.0) for d in dom) / len(dom) for c in names}
+    b = make_batch(args.config)
+    _, flops = logits_work(b)
+    out = {"config": args.config,
+           "kernel": sorted({d["name"] for d in dom}),
+           "sources_digest": logits_sources_digest(),
+           "dispatches": len(dom),
+           "counters_per_dispatch": {c: round(v, 1) for c, v in avg.items()},
+           "simds": SIMDS,
+           "algorithmic_fp8_flops": flops,
+           "commands": args.command}
+    out["xcds"] = xcc
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and avg.get("GRBM_GUI_ACTIVE"):
+        active = avg["GRBM_GUI_ACTIVE"] / xcc
+        out["active_cycles_per_dispatch"] = round(active, 1)
+        out["mfma_busy_frac"] = round(avg["SQ_VALU_MFMA_BUSY_CYCLES"] /
+                                      (active * SIMDS), 4)
+        ns = [d["ns"] for d in dom if d["ns"]]
+        if ns:
+            dur = sorted(ns)[len(ns) // 2] * 1e-9
+            out["median_dispatch_ms"] = round(dur * 1e3, 4)
+            out["clock_ghz"] = round(active / dur / 1e9, 3)
+    if "SQ_INSTS_VALU_MFMA_MOPS_F8" in avg:
+        out["counted_fp8_flops"] = avg["SQ_INSTS_VALU_MFMA_MOPS_F8"] * 512
+        out["counted_over_algorithmic"] = round(
+            out["counted_fp8_flops"] / flops, 4)
+    if args.bench_log:
+        with open(args.bench_log) as f:
+            for line in f:
+                if line.startswith("{") and '"metric"' in line:
+                    bl = json.loads(line)
+                    out["bench_logits_ms"] = bl["kernels_ms"]["logits"]
+                    out["bench_roofline_frac"] = bl["roofline"]["frac"]
     print(json.dumps(out, indent=1))
 
 
@@ -601,6 +678,8 @@ def main():
         return trace_summary(args)
     if args.pmc_summary:
         return pmc_summary(args)
+    if args.mfma_summary:
+        return mfma_summary(args)
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; "
                                    "--gpus N > 1 is not supported"}))

@@ -136,3 +136,32 @@ def test_pmc_summary_refuses_a_foreign_largest_copy(tmp_path):
     r = _run("--config", "tiny", "--pmc-summary", f, w)
     assert r.returncode != 0
     assert "calibration" in r.stderr
+
+
+def test_mfma_summary(tmp_path):
+    """Multi-counter run: per-dispatch averages of the logits kernel at its
+    largest grid only, the busy fraction over GRBM_GUI_ACTIVE x 1024 SIMDs
+    and the FP8 work the counters saw (MOPS x 512) against the algorithm's."""
+    rows, d = [], 0
+    for grid, busy, gui, mops in ((1 << 20, 600.0, 1.0, 10.0),
+                                  (1 << 20, 400.0, 1.0, 10.0),
+                                  (1 << 16, 1.0, 1.0, 1.0)):
+        d += 1
+        for name, v in (("SQ_VALU_MFMA_BUSY_CYCLES", busy),
+                        ("GRBM_GUI_ACTIVE", gui),
+                        ("SQ_INSTS_VALU_MFMA_MOPS_F8", mops)):
+            rows.append(dict(Dispatch_Id=d, Kernel_Name=TILE, Grid_Size=grid,
+                             Counter_Name=name, Counter_Value=v))
+    p = tmp_path / "m"
+    p.mkdir()
+    _write(p / "x_counter_collection.csv", rows)
+    r = _run("--config", "tiny", "--mfma-summary", str(p),
+             "--command", "rocprofv3 --pmc ... -- python3 bench.py")
+    assert r.returncode == 0, r.stderr
+    out = json.loads(r.stdout)
+    assert out["dispatches"] == 2
+    assert out["counters_per_dispatch"]["SQ_VALU_MFMA_BUSY_CYCLES"] == 500.0
+    assert out["xcds"] == 8                      # no agent file: MI355X's
+    assert out["mfma_busy_frac"] == round(500.0 / (1.0 / 8 * 1024), 4)
+    assert out["counted_fp8_flops"] == 10.0 * 512
+    assert out["commands"] == ["rocprofv3 --pmc ... -- python3 bench.py"]

@@ -67,13 +67,14 @@ def _check_run(batches, ref, mask, snaps, k, rows_per_layer=None, dev=None):
         rows = range(b.T) if rows_per_layer is None else rows_per_layer
         rows = list(rows)
         ora = parity.oracle_logits(b, rows=rows)
+        mag = parity.magnitude(b, rows=rows)
         lg_rows = lg[rows].cpu().numpy()
         for i, t in enumerate(rows):
             p = int(b.positions[t])
             parity.check_topk_row(snaps[l][t], ora[i, : p + 1], k,
                                   f"layer {l} row {t}")
             parity.check_logits_row(lg_rows[i], ora[i], p,
-                                    f"layer {l} row {t}")
+                                    f"layer {l} row {t}", mag[i])
 
 
 @pytest.mark.parametrize("cfg", [dict(freq=4, offset=2),

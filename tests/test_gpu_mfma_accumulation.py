@@ -1,20 +1,23 @@
-"""How exactly the FP8 MFMA sums its 128 products, measured through the
-logits entry point on inputs where every other step is exact.
+"""How exactly the FP8 MFMA (v_mfma_f32_16x16x128_f8f6f4) sums its 128
+products, measured through the logits entry point on inputs where every
+other step is exact.
 
 With one head, weight 2, a q block whose largest element is 448 (so its
 scale is exactly 1 and its codes are its values) and K scales of 1, the
 logit of token s is 2 * max(d_s, 0) with d_s the MFMA's fp32 output for the
 dot product of the q codes with the key codes: the weight folding (w * s_q /
 2 = 1), the ReLU, the head sum (the other heads have weight 0) and the K
-scale are all exact.  The exact dot is an integer multiple of 2^-18 (e4m3
-values are multiples of 2^-9), summed exactly in float64 here.
+scale are all exact.  The exact dot is a multiple of 2^-18 (e4m3 values are
+multiples of 2^-9), summed exactly in float64 here.
 
-The logits tolerance of the parity tests assumes the error of one such dot
-stays below 2^-16 of the sum of the magnitudes of its products; this test
-measures the error on random and on cancelling dot products and checks that
-assumption, and prints how far the result is from a correctly rounded fp32
-sum (plain fp32 accumulation would be within about 2^-24 relative of the
-dot itself)."""
+Measured on gfx950 (and pinned below): the MFMA does not return the
+correctly rounded fp32 sum -- most dots differ from it -- and its error
+grows with the spread of the products' magnitudes.  On codes drawn like the
+workloads' (absmax-scaled normal values) it stays below 2^-16 of the sum of
+the products' magnitudes, the absolute term of the parity tests' logits
+tolerance; on codes spread over the whole e4m3 range it reaches about
+2^-12.4 of it.  A plain fp32 sum of the same products (any order) would be
+within about 2^-24 * 128 of that sum."""
 
 import math
 import sys
@@ -34,27 +37,39 @@ DEC = fp8.decode(np.arange(256, dtype=np.uint8)).astype(np.float64)
 FINITE = np.array([c for c in range(256) if np.isfinite(DEC[c])], np.uint8)
 
 
-def _case(seed, R, n, cancel):
+def _codes_like_workload(rng, shape):
+    """e4m3 codes of N(0,1) vectors scaled by their absmax to 448 (the
+    workloads' quantisation; torch's cast rounds to nearest even)."""
+    x = rng.standard_normal(shape).astype(np.float32)
+    s = np.max(np.abs(x), axis=-1, keepdims=True) / np.float32(448.0)
+    y = np.clip(x / s, -448, 448).astype(np.float32)
+    return torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8) \
+        .numpy()
+
+
+def _case(seed, R, n, kind):
     rng = np.random.Generator(np.random.PCG64(seed))
-    # q: e4m3 values (exact in bf16), element 0 = 448 so the scale is 1
-    q_codes = rng.choice(FINITE, size=(R, 128))
-    q_codes[:, 0] = 0x7E
-    if cancel:                        # halves equal: see the K codes below
+    if kind == "workload":
+        q_codes = _codes_like_workload(rng, (R, 128))
+        k_codes = _codes_like_workload(rng, (R, n, 128))
+    else:
+        q_codes = rng.choice(FINITE, size=(R, 128))
+        k_codes = rng.choice(FINITE, size=(R, n, 128))
+    q_codes[:, 0] = 0x7E                # largest q element 448: scale 1
+    if kind == "cancel":
+        # halves of q equal, second half of each key the negated first
+        # half with 5 % of the codes nudged by one step: dots small
+        # against their magnitudes
         q_codes[:, 64:] = q_codes[:, :64]
-    qv = DEC[q_codes]
-    # K codes: random finite e4m3; "cancel" flips signs to pair products so
-    # that the dots are small against their magnitudes
-    k_codes = rng.choice(FINITE, size=(R, n, 128))
-    if cancel:
         k_codes[:, :, 64:] = k_codes[:, :, :64] ^ 0x80
         k_codes[:, :, 64:] ^= (rng.random((R, n, 64)) < 0.05).astype(
-            np.uint8) * 0x01                       # near, not exact, cancel
+            np.uint8) * 0x01
         k_codes[(k_codes & 0x7F) == 0x7F] ^= 0x02  # NaN code -> 0x7D / 0xFD
+    qv = DEC[q_codes]
     kv = DEC[k_codes]
     pages_per = (n + 63) // 64
     pool = R * pages_per
-    perm = rng.permutation(pool).astype(np.int32)
-    bt = perm.reshape(R, pages_per)
+    bt = rng.permutation(pool).astype(np.int32).reshape(R, pages_per)
     kc = np.zeros((pool, 8448), np.uint8)
     for r in range(R):
         codes = np.zeros((pages_per * 64, 128), np.uint8)
@@ -70,16 +85,21 @@ def _case(seed, R, n, cancel):
     return q, kc, bt, exact, mag
 
 
-@pytest.mark.parametrize("cancel", [False, True])
-def test_fp8_mfma_dot_error(cancel):
+# kind -> the bound on |d - exact| / sum|products| that the hardware keeps
+BOUNDS = {"workload": 2.0 ** -16, "full_range": 2.0 ** -11,
+          "cancel": 2.0 ** -11}
+
+
+@pytest.mark.parametrize("kind", sorted(BOUNDS))
+def test_fp8_mfma_dot_error(kind):
     R, n = 16, 4096
-    print(f"case: MFMA accumulation, {R} rows x {n} keys, cancel={cancel}",
+    print(f"case: MFMA accumulation, {R} rows x {n} keys, {kind} codes",
           flush=True)
     sys.stdout.flush()
-    q, kc, bt, exact, mag = _case(123 + int(cancel), R, n, cancel)
+    q, kc, bt, exact, mag = _case(123 + sorted(BOUNDS).index(kind), R, n,
+                                  kind)
     dev = "cuda"
-    q = q.to(dev)
-    q8, qs = binding.dsa_quantize_q(q)
+    q8, qs = binding.dsa_quantize_q(q.to(dev))
     assert torch.all(qs == 1.0)
     w = torch.full((R, 1), 2.0, dtype=torch.float32, device=dev)
     qsl = torch.arange(R + 1, dtype=torch.int32, device=dev)
@@ -91,19 +111,19 @@ def test_fp8_mfma_dot_error(cancel):
     torch.cuda.synchronize()
     assert binding.dsa_device_error_flags(reset=True) == 0
     g = lg[:, :n].cpu().numpy().astype(np.float64) / 2.0
-    pos_ = exact > 0
-    err = np.abs(g[pos_] - exact[pos_])
-    rel_m = err / mag[pos_]
-    rn32 = exact[pos_].astype(np.float32).astype(np.float64)
-    not_rn = float(np.mean(g[pos_] != rn32))
-    rel_d = err / exact[pos_]
-    q_m = np.quantile(rel_m, [0.5, 0.99, 1.0])
-    print(f"MFMA dot error / sum|products|: median 2^{math.log2(q_m[0] + 1e-300):.1f}"
-          f", p99 2^{math.log2(q_m[1] + 1e-300):.1f}, max 2^{math.log2(q_m[2] + 1e-300):.1f}; "
-          f"relative to the dot: max {rel_d.max():.3g}; "
-          f"{100 * not_rn:.1f} % of {pos_.sum()} positive dots differ from "
-          f"the correctly rounded fp32 sum", flush=True)
-    # negative dots are clamped to exactly 0
-    assert np.all(g[~pos_ & (exact < 0)] == 0.0)
-    # the premise of the parity tolerance
-    assert np.all(err <= 2.0 ** -16 * mag[pos_])
+    # compare where the MFMA's ReLU input is known to be positive: the
+    # exact dot above the error bound (below it the clamp may go either way)
+    bound = BOUNDS[kind]
+    sure = exact > bound * mag
+    err = np.abs(g[sure] - exact[sure])
+    rel = err / mag[sure]
+    rn32 = exact[sure].astype(np.float32).astype(np.float64)
+    not_rn = float(np.mean(g[sure] != rn32))
+    qq = np.quantile(rel, [0.5, 0.99, 1.0])
+    print(f"{kind}: error / sum|products| median 2^{math.log2(qq[0] + 1e-300):.1f}, "
+          f"p99 2^{math.log2(qq[1] + 1e-300):.1f}, max 2^{math.log2(qq[2] + 1e-300):.1f}; "
+          f"{100 * not_rn:.1f} % of {int(sure.sum())} dots differ from the "
+          "correctly rounded fp32 sum", flush=True)
+    assert np.all(err <= bound * mag[sure])
+    # a dot clearly below zero is clamped to exactly 0 by the ReLU
+    assert np.all(g[exact < -bound * mag] == 0.0)
