@@ -60,6 +60,9 @@ _SIGNATURES = {
     "dsa_indexer_forward": (_I, [_P, _P, _P, _L, _P, _L, _P, _P, _L, _I, _I,
                                  _I, _I, _P, _L, _I, _P, _L, _P, _S, _P]),
     "dsa_forward_workspace_size": (_S, [_L, _I, _L, _I]),
+    "dsa_indexer_forward_noalloc": (_I, [_P, _P, _P, _L, _P, _L, _P, _P, _L,
+                                         _I, _I, _I, _I, _P, _L, _I, _P, _L,
+                                         _P]),
     "dsa_logits_budget_bytes": (_S, [_S, ctypes.c_double, ctypes.c_double]),
     "dsa_logits_chunk_rows": (_L, [_L, _L, _S]),
     "dsa_indexer_forward_chunked": (_I, [_P, _P, _P, _L, _P, _L, _P, _P, _L,
@@ -262,6 +265,43 @@ def dsa_indexer_forward(q_bf16, weights, k_cache, block_table,
             logits.shape[1], k, _dev_ptr(out, torch.int32, "out"),
             out.shape[1], _dev_ptr(workspace, torch.uint8, "workspace"),
             workspace.numel(), _stream(stream, dev)))
+    return logits, out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def dsa_indexer_forward_noalloc(q_bf16, weights, k_cache, block_table,
+                                query_start_loc, positions, logits, out,
+                                k=None, stream=None):
+    """dsa_indexer_forward without a workspace: the library's own fixed
+    scratch array is used (no device allocation in the call).  ``logits``
+    (fp32 [>= T, ld]) and ``out`` (int32 [>= T, >= k]) are the caller's;
+    k defaults to out's width.  Returns (logits, out)."""
+    T, H, D = q_bf16.shape
+    R = block_table.shape[0]
+    dev = q_bf16.device
+    k = out.shape[1] if k is None else int(k)
+    if k_cache.dim() != 2 or k_cache.shape[1] != PAGE_BYTES:
+        raise ValueError("k_cache must be uint8 [num_pages, 8448]")
+    if query_start_loc.numel() != R + 1:
+        raise ValueError("query_start_loc must have R + 1 entries")
+    _shape(weights, (T, H), "weights")
+    _shape(positions, (T,), "positions")
+    _rows_at_least(logits, T, "logits")
+    _rows_at_least(out, T, "out", k)
+    with torch.cuda.device(dev):
+        _check(lib().dsa_indexer_forward_noalloc(
+            _dev_ptr(q_bf16, torch.bfloat16, "q_bf16"),
+            _dev_ptr(weights, torch.float32, "weights"),
+            _dev_ptr(k_cache, torch.uint8, "k_cache"), k_cache.shape[0],
+            _dev_ptr(block_table, torch.int32, "block_table"),
+            block_table.shape[1],
+            _dev_ptr(query_start_loc, torch.int32, "query_start_loc"),
+            _dev_ptr(positions, torch.int32, "positions"), T, R, H, D,
+            PAGE_TOKENS, _dev_ptr(logits, torch.float32, "logits"),
+            logits.shape[1], k, _dev_ptr(out, torch.int32, "out"),
+            out.shape[1], _stream(stream, dev)))
     return logits, out
 
 

@@ -179,6 +179,32 @@ int dsa_indexer_forward(const void* q_bf16, const float* weights,
 size_t dsa_forward_workspace_size(int64_t T, int H, int64_t ld, int k);
 
 /*
+ * dsa_indexer_forward_noalloc -- dsa_indexer_forward for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments (without the workspace),
+ * same kernels, same results bit for bit.  Its scratch (q codes and scales,
+ * top-k scratch) is one fixed array of DSA_NOALLOC_SCRATCH_BYTES inside the
+ * library per device, held from the first call on that device until the
+ * process ends; nothing in it needs to start at zero.  A batch whose
+ * dsa_forward_workspace_size(T, H, ld, k) exceeds that limit is rejected
+ * with DSA_ERR_WORKSPACE before anything is enqueued (for example the
+ * 8192-row prefill chunk at H = 64: use dsa_indexer_forward).  Allocates
+ * nothing and calls no allocating routine.  Every call on a device uses that
+ * device's one array: calls that overlap on one device (two streams, or two
+ * threads without ordering) race and give undefined results.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+int dsa_indexer_forward_noalloc(const void* q_bf16, const float* weights,
+                                const uint8_t* k_cache, int64_t num_pages,
+                                const int32_t* block_table, int64_t bt_stride,
+                                const int32_t* query_start_loc,
+                                const int32_t* positions, int64_t T, int R,
+                                int H, int head_dim, int page_size,
+                                float* logits, int64_t ld, int k, int32_t* out,
+                                int64_t out_ld, void* stream);
+
+/*
  * dsa_logits_budget_bytes -- the logits memory budget ([KVB] section on
  * SGLang's logits budget): 30 % of the device's total_mem bytes; when a
  * static memory fraction is set (mem_fraction_static >= 0; pass a negative
