@@ -135,9 +135,11 @@ def logits_work(b):
 
 
 def dominant_kernel(b):
-    """Name prefix of the step's logits kernel, as the profiler prints it."""
+    """(Name prefix, name part) of the step's logits kernel as the profiler
+    prints it: a decode batch's forward scores with its page schedule (the
+    instance whose last template argument is true)."""
     if b.T <= 128 and b.T <= 2 * b.R:
-        return "logits_balanced_kernel<", ""
+        return "logits_balanced_kernel<", ", true>"
     if b.T <= 2 * b.R:
         return "logits_row_prefetch_kernel<", ""
     return "logits_tile16_kernel<", ""
@@ -572,11 +574,23 @@ def measure_workload(args, name, K, W, extras=False, cpu=True,
                 NK, R)
     kl = _timed(torch, lambda r: binding.dsa_indexer_logits(
         q8, qsc, ws_in[r], kcs[r], bt, qsl, pos, ld, logits), NK, R)
+    # decode batches: the step scores with the page schedule its
+    # quantisation launch builds; time that kernel (one schedule, built
+    # once: it depends only on the batch's metadata)
+    sched = binding.dsa_logits_schedule(bt, qsl, pos, ld) \
+        if dominant_kernel(b)[1] else None
+    kl_plain = kl
+    if sched is not None:
+        kl = _timed(torch, lambda r: binding.dsa_indexer_logits_scheduled(
+            q8, qsc, ws_in[r], kcs[r], bt, qsl, pos, ld, sched, logits),
+            NK, R)
     kt = _timed(torch, lambda r: binding.dsa_indexer_topk(
         logits, pos, k, buf, tws), NK, R)
     kf = _timed(torch, forward, NK, R)
     kernels = {"quantize_q": round(kq, 5), "logits": round(kl, 5),
                "topk": round(kt, 5), "forward": round(kf, 5)}
+    if sched is not None:
+        kernels["logits_without_schedule"] = round(kl_plain, 5)
     rec = {}
     if extras:
         # Row-chunked forward under a 256 MiB logits budget.

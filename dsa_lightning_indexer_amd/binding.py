@@ -57,6 +57,11 @@ _SIGNATURES = {
                                 _I, _I, _I, _P, _L, _P]),
     "dsa_indexer_topk": (_I, [_P, _L, _P, _L, _I, _P, _L, _P, _S, _P]),
     "dsa_topk_workspace_size": (_S, [_L, _L, _I]),
+    "dsa_logits_schedule_size": (_S, [_L, _L]),
+    "dsa_logits_schedule": (_I, [_P, _L, _P, _P, _L, _I, _L, _P, _S, _P]),
+    "dsa_indexer_logits_scheduled": (_I, [_P, _P, _P, _P, _L, _P, _L, _P, _P,
+                                          _L, _I, _I, _I, _I, _P, _L, _P,
+                                          _P]),
     "dsa_indexer_forward": (_I, [_P, _P, _P, _L, _P, _L, _P, _P, _L, _I, _I,
                                  _I, _I, _P, _L, _I, _P, _L, _P, _S, _P]),
     "dsa_forward_workspace_size": (_S, [_L, _I, _L, _I]),
@@ -195,6 +200,72 @@ def dsa_indexer_logits(q_fp8, q_scale, weights, k_cache, block_table,
             _dev_ptr(positions, torch.int32, "positions"), T, R, H, D,
             PAGE_TOKENS, _dev_ptr(logits, torch.float32, "logits"),
             logits.shape[1], _stream(stream, dev)))
+    return logits
+
+
+def dsa_logits_schedule_size(T, ld):
+    return lib().dsa_logits_schedule_size(T, ld)
+
+
+def dsa_logits_schedule(block_table, query_start_loc, positions, ld,
+                        schedule=None, stream=None):
+    """Decode page schedule (int32 device buffer) of a batch for
+    dsa_indexer_logits_scheduled; None when the batch takes none."""
+    T = positions.shape[0]
+    R = block_table.shape[0]
+    dev = positions.device
+    if query_start_loc.numel() != R + 1:
+        raise ValueError("query_start_loc must have R + 1 entries")
+    need = dsa_logits_schedule_size(T, ld)
+    if need == 0:
+        return None
+    if schedule is None:
+        schedule = torch.empty((need // 4,), dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().dsa_logits_schedule(
+            _dev_ptr(block_table, torch.int32, "block_table"),
+            block_table.shape[1],
+            _dev_ptr(query_start_loc, torch.int32, "query_start_loc"),
+            _dev_ptr(positions, torch.int32, "positions"), T, R, ld,
+            _dev_ptr(schedule, torch.int32, "schedule"),
+            schedule.numel() * 4, _stream(stream, dev)))
+    return schedule
+
+
+def dsa_indexer_logits_scheduled(q_fp8, q_scale, weights, k_cache,
+                                 block_table, query_start_loc, positions, ld,
+                                 schedule, logits=None, stream=None):
+    """dsa_indexer_logits with a schedule from dsa_logits_schedule (same
+    results)."""
+    T, H, D = q_fp8.shape
+    R = block_table.shape[0]
+    dev = q_fp8.device
+    if logits is None:
+        logits = torch.empty((T, ld), dtype=torch.float32, device=dev)
+    if k_cache.dim() != 2 or k_cache.shape[1] != PAGE_BYTES:
+        raise ValueError("k_cache must be uint8 [num_pages, 8448]")
+    if query_start_loc.numel() != R + 1:
+        raise ValueError("query_start_loc must have R + 1 entries")
+    _shape(q_scale, (T, H), "q_scale")
+    _shape(weights, (T, H), "weights")
+    _shape(positions, (T,), "positions")
+    _rows_at_least(logits, T, "logits")
+    if schedule is not None and \
+            schedule.numel() * 4 < dsa_logits_schedule_size(T, ld):
+        raise ValueError("schedule smaller than dsa_logits_schedule_size")
+    with torch.cuda.device(dev):
+        _check(lib().dsa_indexer_logits_scheduled(
+            _dev_ptr(q_fp8, torch.uint8, "q_fp8"),
+            _dev_ptr(q_scale, torch.float32, "q_scale"),
+            _dev_ptr(weights, torch.float32, "weights"),
+            _dev_ptr(k_cache, torch.uint8, "k_cache"), k_cache.shape[0],
+            _dev_ptr(block_table, torch.int32, "block_table"),
+            block_table.shape[1],
+            _dev_ptr(query_start_loc, torch.int32, "query_start_loc"),
+            _dev_ptr(positions, torch.int32, "positions"), T, R, H, D,
+            PAGE_TOKENS, _dev_ptr(logits, torch.float32, "logits"),
+            logits.shape[1], _dev_ptr(schedule, torch.int32, "schedule"),
+            _stream(stream, dev)))
     return logits
 
 

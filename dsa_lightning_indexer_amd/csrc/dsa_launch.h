@@ -52,7 +52,17 @@ struct ForwardArgs {
   float* q_scale;               // lg.q_scale
   LogitsArgs lg;
   TopkArgs tk;                  // tk.logits == lg.logits
+  // decode page schedule (logits_schedule_bytes(T, ld) bytes), or null;
+  // build_sched false: it already holds the schedule of this batch's
+  // positions, query_start_loc and block table (IndexCache F layers)
+  int32_t* sched = nullptr;
+  bool build_sched = true;
 };
+// Bytes of the decode page schedule of a T-row batch with ld-column logits
+// (0 when no schedule is used for such a batch).
+size_t logits_schedule_bytes(int64_t T, int64_t ld);
+hipError_t launch_logits_schedule(const LogitsArgs& a, int32_t* sched,
+                                  hipStream_t stream);
 
 // Kernel-choice knobs (dsa_set_option); 0 = automatic.  Kept per device as
 // atomics; options() is a snapshot of the calling thread's current device.
@@ -99,7 +109,8 @@ enum class LogitsPlan {
 LogitsPlan logits_plan(int64_t T, int R);
 int device_cu_count();            // compute units of the current device
 hipError_t launch_logits(const LogitsArgs& a, hipStream_t stream,
-                         LogitsPlan plan = LogitsPlan::Auto);
+                         LogitsPlan plan = LogitsPlan::Auto,
+                         const int32_t* sched = nullptr);
 // The forward pass over row chunks [a, a + rows) that reuse one logits
 // buffer: q quantised once, then per chunk query_start_loc rebased into
 // qsl_chunk, logits of the chunk's rows (the class of the whole batch) and

@@ -37,10 +37,10 @@ __device__ __forceinline__ void raise_flag(unsigned f) {
 //   amax = max |q|;  s = amax / 448 (IEEE fp32 division; s = 1 if amax == 0)
 //   code = e4m3fn(q / s) (IEEE fp32 division, RNE, saturating)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void quantize_q_kernel(
+__device__ __forceinline__ void quantize_q_blocks(
     const uint16_t* __restrict__ q, int64_t blocks, uint8_t* __restrict__ q8,
-    float* __restrict__ q_scale) {
-  const int64_t blk = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    float* __restrict__ q_scale, int64_t wg) {
+  const int64_t blk = wg * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
   if (blk >= blocks) return;                 // whole 16-lane groups exit
   const uint4 raw = *reinterpret_cast<const uint4*>(q + blk * 128 + sub * 8);
@@ -65,6 +65,12 @@ __global__ __launch_bounds__(256) void quantize_q_kernel(
   for (int i = 0; i < 4; ++i) hi |= e4m3fn_encode(f[4 + i] / s) << (8 * i);
   *reinterpret_cast<uint2*>(q8 + blk * 128 + sub * 8) = make_uint2(lo, hi);
   if (sub == 0) q_scale[blk] = s;
+}
+
+__global__ __launch_bounds__(256) void quantize_q_kernel(
+    const uint16_t* __restrict__ q, int64_t blocks, uint8_t* __restrict__ q8,
+    float* __restrict__ q_scale) {
+  quantize_q_blocks(q, blocks, q8, q_scale, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -184,8 +190,10 @@ __device__ __forceinline__ float head_reduce_abs(const f32x4 (&acc)[MT],
 
 // ---------------------------------------------------------------------------
 // Request of row t: the number of requests r < R with qsl[r] <= t, minus 1
-// (query_start_loc is non-decreasing).  64 entries per wave-wide load and
-// ballot, so the lookup costs one memory round trip for R <= 64.
+// (query_start_loc is non-decreasing), and 0 for a row before qsl[0] (no
+// request holds it: a caller error, kept in bounds as request_of_row
+// does).  64 entries per wave-wide load and ballot, so the lookup costs one
+// memory round trip for R <= 64.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int request_of_row_wave(const int32_t* qsl, int R,
                                                    int64_t t) {
@@ -198,7 +206,7 @@ __device__ __forceinline__ int request_of_row_wave(const int32_t* qsl, int R,
     count += __popcll(m);
     if (m != ~0ull) break;                     // later entries are > t
   }
-  return count - 1;
+  return max(count - 1, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -437,22 +445,86 @@ __device__ __forceinline__ RowSpan balanced_span(const LogitsArgs& a, int D,
   return sp;
 }
 
+// ---------------------------------------------------------------------------
+// Decode page schedule, built once per batch.  The balanced waves' spans
+// depend only on the positions, query_start_loc and block table, which a
+// forward pass shares with every F layer of an IndexCache run, so they are
+// computed ahead of the logits launch -- by extra workgroups of the
+// q-quantisation launch, whose own work is latency-bound -- and a logits
+// wave then issues its K loads after one scalar load of its entry instead of
+// a chain of three metadata round trips (positions, spans, block table).
+// Entry of logits wave w, kSchedInts int32: row (-1: no work), position,
+// first page, end page, request, physical pages of its first kSchedPages
+// pages (-1 past the range).  The spans are balanced_span's without head
+// waves, so each (row, page) is scored by the same code as without the
+// schedule: the logits are bit-identical.
+// ---------------------------------------------------------------------------
+constexpr int kSchedInts = 8;
+constexpr int kSchedPages = 3;
+
+template <int NCH>
+__global__ __launch_bounds__(256) void quantize_q_sched_kernel(
+    const uint16_t* __restrict__ q, int64_t blocks, uint8_t* __restrict__ q8,
+    float* __restrict__ q_scale, int qgrid, LogitsArgs a, int D, int per_xcd,
+    int nwaves, int32_t* __restrict__ sched) {
+  if ((int)blockIdx.x < qgrid) {
+    quantize_q_blocks(q, blocks, q8, q_scale, blockIdx.x);
+    return;
+  }
+  const int w = ((int)blockIdx.x - qgrid) * 4 + (int)(threadIdx.x >> 6);
+  if (w >= nwaves) return;
+  const int lane = lane_id();
+  const RowSpan sp = balanced_span<NCH>(a, D, per_xcd, w, 0);
+  int v = -1;
+  if (sp.row >= 0) {
+    const int r = wave_uniform(request_of_row_wave(a.qsl, a.R, sp.row));
+    const int last = (int)a.bt_stride - 1;
+    const int j = sp.jb + (lane - 5);
+    const int page = a.block_table[(int64_t)r * a.bt_stride +
+                                   min(max(j, 0), last)];
+    v = lane == 0 ? sp.row : lane == 1 ? sp.p : lane == 2 ? sp.jb
+        : lane == 3 ? sp.je : lane == 4 ? r : (j < sp.je ? page : -1);
+  }
+  if (lane < kSchedInts) sched[(int64_t)w * kSchedInts + lane] = v;
+}
+
 // head_waves > 0: the first head_waves workgroups are head waves: wave
 // (t, i) = (b / HW, b % HW) takes pages [i D, i D + D) of row t, known
 // without the positions, so its block-table, q and position loads go out
 // together and its K loads one round trip before the balanced waves'
 // (which first need every row's position); the balanced waves share the
 // pages from HW D on.  head_waves is a multiple of 8 (XCD parity).
-template <int MT, bool FULL, int D, int NCH>
-__global__ __launch_bounds__(64) void logits_balanced_kernel(LogitsArgs a,
-                                                             int per_xcd,
-                                                             int hw,
-                                                             int head_waves) {
+//
+// SCHED: the spans come from the page schedule (no head waves): wave b
+// reads entry b -- row, position, range, request and its first pages -- in
+// one scalar load and issues its K loads right after it.
+template <int MT, bool FULL, int D, int NCH, bool SCHED>
+__global__ __launch_bounds__(64) void logits_balanced_kernel(
+    LogitsArgs a, int per_xcd, int hw, int head_waves,
+    const int32_t* __restrict__ sched) {
+  static_assert(!SCHED || D <= kSchedPages, "schedule holds 3 pages");
   const int lane = lane_id();
   const int i16 = lane & 15, g = lane >> 4;
-  const bool head = (int)blockIdx.x < head_waves;
+  const bool head = !SCHED && (int)blockIdx.x < head_waves;
   RowSpan sp;
-  if (head) {
+  int sched_r = 0;
+  int sched_pages[kSchedPages];
+  if (SCHED) {
+    typedef __attribute__((address_space(4))) const i32x8 const_i32x8;
+    const i32x8 e = ((const_i32x8*)(sched))[blockIdx.x];
+    sp = RowSpan{e[0], e[2], e[3], e[1]};
+    // an entry the builder did not write for this batch (a knob changed
+    // in between) must still keep every access in bounds
+    if (sp.row < 0 || sp.row >= a.T || sp.p < 0 || sp.p >= a.ld ||
+        (int64_t)(sp.p >> 6) >= a.bt_stride || sp.jb < 0)
+      return;
+    sp.je = min(sp.je, (sp.p >> 6) + 1);
+    if (sp.jb >= sp.je) return;
+    sched_r = min(max(e[4], 0), a.R - 1);
+    sched_pages[0] = e[5];
+    sched_pages[1] = e[6];
+    sched_pages[2] = e[7];
+  } else if (head) {
     const int hb = (int)blockIdx.x;
     sp = RowSpan{hb / hw, (hb % hw) * D, (hb % hw) * D + D, 0};
     if (sp.row >= a.T) return;
@@ -467,14 +539,16 @@ __global__ __launch_bounds__(64) void logits_balanced_kernel(LogitsArgs a,
   if (head) p = load_uniform(a.positions, t);
 
   // request guess r = t (one query row per request), checked below; the
-  // page ids of the first chunk are fetched with it
-  int r = (int)min<int64_t>(t, a.R - 1);
-  const int q0 = load_uniform(a.qsl, r), q1 = load_uniform(a.qsl, r + 1);
+  // page ids of the first chunk are fetched with it (the schedule has both)
+  int r = SCHED ? sched_r : (int)min<int64_t>(t, a.R - 1);
+  const int q0 = SCHED ? 0 : load_uniform(a.qsl, r);
+  const int q1 = SCHED ? 1 : load_uniform(a.qsl, r + 1);
   const int32_t* btr = a.block_table + (int64_t)r * a.bt_stride;
   const int last = (int)a.bt_stride - 1;
   int pages[D];
 #pragma unroll
-  for (int q = 0; q < D; ++q) pages[q] = load_uniform(btr, min(jb + q, last));
+  for (int q = 0; q < D; ++q)
+    pages[q] = SCHED ? sched_pages[q] : load_uniform(btr, min(jb + q, last));
   i32x8 qa[MT];
   load_q_frags<MT, FULL>(a.q8 + t * a.H * kHeadDim, a.H, qa);
   float w[MT][4];
@@ -487,7 +561,7 @@ __global__ __launch_bounds__(64) void logits_balanced_kernel(LogitsArgs a,
     je = min(je, (p >> 6) + 1);
     if (jb >= je) return;
   }
-  if (!(q0 <= t && t < q1)) {                 // rows are not one per request
+  if (!SCHED && !(q0 <= t && t < q1)) {      // rows are not one per request
     r = wave_uniform(request_of_row_wave(a.qsl, a.R, t));
     btr = a.block_table + (int64_t)r * a.bt_stride;
 #pragma unroll
@@ -1360,36 +1434,78 @@ LogitsPlan logits_plan(int64_t T, int R) {
                                                        : LogitsPlan::Rowwise;
 }
 
+// Grid of the balanced decode kernel: D pages per wave; enough waves that a
+// batch whose rows all reach max_pages still gets about D pages per wave;
+// with the page schedule no head waves.
+struct BalancedGeometry {
+  int D;
+  int64_t per_xcd;
+  int hw;                 // head waves per row
+  int64_t head_waves;
+  int64_t waves;          // grid size (one wave per workgroup)
+};
+
+static BalancedGeometry balanced_geometry(int64_t T, int64_t max_pages,
+                                          const Options& o, bool sched) {
+  BalancedGeometry g{};
+  int D = o.row_pages_per_wave;
+  D = D <= 0 ? 3 : std::min(D, 4);
+  if (D == 1) D = 2;
+  g.D = D;
+  const int64_t pmax = T * max_pages;
+  const int64_t part = (pmax + 7) / 8;
+  g.per_xcd =
+      std::max<int64_t>(1, std::min<int64_t>((part + D - 1) / D, 1 << 13));
+  // one head wave per row (measured: 10.54 -> 10.39 us on the decode
+  // batch; more head waves gain nothing, the balanced waves' chain of three
+  // round trips still ends the kernel); option value 1 + n sets n.  The
+  // schedule removes that chain: no head waves.
+  g.hw = sched ? 0 : (o.row_head_waves > 0 ? o.row_head_waves - 1 : 1);
+  g.head_waves = g.hw ? (T * g.hw + 7) / 8 * 8 : 0;
+  g.waves = g.head_waves + 8 * (g.per_xcd + T);
+  return g;
+}
+
+// The page schedule serves decode launches of the balanced class whose D
+// fits an entry.
+static bool schedule_applies(int64_t T, int64_t max_pages, const Options& o) {
+  return T >= 1 && T <= kBalancedMaxRows &&
+         balanced_geometry(T, max_pages, o, true).D <= kSchedPages;
+}
+
+size_t logits_schedule_bytes(int64_t T, int64_t ld) {
+  if (T < 1 || T > kBalancedMaxRows || ld < 1) return 0;
+  // the most waves any option value gives: D = 2, max_pages = ld / 64
+  Options o{};
+  o.row_pages_per_wave = 2;
+  const int64_t w = balanced_geometry(T, (ld + 63) / 64, o, true).waves;
+  return (size_t)w * kSchedInts * sizeof(int32_t);
+}
+
 template <int MT, bool FULL>
 static hipError_t launch_logits_mt(const LogitsArgs& a, hipStream_t stream,
-                                   LogitsPlan plan, int64_t max_pages) {
+                                   LogitsPlan plan, int64_t max_pages,
+                                   const int32_t* sched) {
   const Options& o = options();
   const bool tiled = plan == LogitsPlan::Tiled;
   if (plan == LogitsPlan::Balanced && a.T <= kBalancedMaxRows) {
-    // D pages per wave; enough waves that a batch whose rows all reach
-    // max_pages still gets about D pages per wave
-    int D = o.row_pages_per_wave;
-    D = D <= 0 ? 3 : std::min(D, 4);
-    if (D == 1) D = 2;
-    const int64_t pmax = a.T * max_pages;
-    const int64_t part = (pmax + 7) / 8;
-    const int64_t per_xcd =
-        std::max<int64_t>(1, std::min<int64_t>((part + D - 1) / D, 1 << 13));
-    // one head wave per row (measured: 10.54 -> 10.39 us on the decode
-    // batch; more head waves gain nothing, the balanced waves' chain of
-    // three round trips still ends the kernel); option value 1 + n sets n
-    const int hw = o.row_head_waves > 0 ? o.row_head_waves - 1 : 1;
-    const int64_t head_waves = hw ? (a.T * hw + 7) / 8 * 8 : 0;
-    const dim3 grid((unsigned)(head_waves + 8 * (per_xcd + a.T)));
+    const bool use_sched = sched && schedule_applies(a.T, max_pages, o);
+    const BalancedGeometry bg = balanced_geometry(a.T, max_pages, o, use_sched);
+    const dim3 grid((unsigned)bg.waves);
     const bool two = a.T > 64;
-#define DSA_BAL(DD)                                                          \
-    if (two) hipLaunchKernelGGL((logits_balanced_kernel<MT, FULL, DD, 2>),    \
-                                grid, dim3(64), 0, stream, a, (int)per_xcd,   \
-                                hw, (int)head_waves);                         \
-    else hipLaunchKernelGGL((logits_balanced_kernel<MT, FULL, DD, 1>),        \
-                            grid, dim3(64), 0, stream, a, (int)per_xcd, hw,   \
-                            (int)head_waves);
-    if (D == 2) { DSA_BAL(2) } else if (D == 3) { DSA_BAL(3) } else { DSA_BAL(4) }
+    const int per_xcd = (int)bg.per_xcd, hw = bg.hw, hwv = (int)bg.head_waves;
+#define DSA_BAL(DD, SC)                                                      \
+    if (two) hipLaunchKernelGGL((logits_balanced_kernel<MT, FULL, DD, 2, SC>),\
+                                grid, dim3(64), 0, stream, a, per_xcd, hw,    \
+                                hwv, sched);                                  \
+    else hipLaunchKernelGGL((logits_balanced_kernel<MT, FULL, DD, 1, SC>),    \
+                            grid, dim3(64), 0, stream, a, per_xcd, hw, hwv,   \
+                            sched);
+    if (use_sched) {
+      if (bg.D == 2) { DSA_BAL(2, true) } else { DSA_BAL(3, true) }
+    } else if (bg.D == 2) { DSA_BAL(2, false) }
+    else if (bg.D == 3) { DSA_BAL(3, false) }
+    else { DSA_BAL(4, false) }
 #undef DSA_BAL
   } else if (!tiled) {
     int ppw = o.row_pages_per_wave;
@@ -1469,32 +1585,89 @@ static hipError_t launch_logits_mt(const LogitsArgs& a, hipStream_t stream,
   return hipGetLastError();
 }
 
+static int64_t logits_max_pages(const LogitsArgs& a) {
+  return std::min<int64_t>(a.bt_stride, a.ld / kPageTokens);
+}
+
 hipError_t launch_logits(const LogitsArgs& a, hipStream_t stream,
-                         LogitsPlan plan) {
+                         LogitsPlan plan, const int32_t* sched) {
   if (a.T <= 0) return hipSuccess;
-  const int64_t max_pages = std::min<int64_t>(a.bt_stride, a.ld / kPageTokens);
+  const int64_t max_pages = logits_max_pages(a);
   if (plan == LogitsPlan::Auto) plan = logits_plan(a.T, a.R);
   switch (a.H) {
-    case 16: return launch_logits_mt<1, true>(a, stream, plan, max_pages);
-    case 32: return launch_logits_mt<2, true>(a, stream, plan, max_pages);
-    case 48: return launch_logits_mt<3, true>(a, stream, plan, max_pages);
-    case 64: return launch_logits_mt<4, true>(a, stream, plan, max_pages);
+    case 16: return launch_logits_mt<1, true>(a, stream, plan, max_pages, sched);
+    case 32: return launch_logits_mt<2, true>(a, stream, plan, max_pages, sched);
+    case 48: return launch_logits_mt<3, true>(a, stream, plan, max_pages, sched);
+    case 64: return launch_logits_mt<4, true>(a, stream, plan, max_pages, sched);
     default: break;
   }
   switch ((a.H + 15) / 16) {
-    case 1: return launch_logits_mt<1, false>(a, stream, plan, max_pages);
-    case 2: return launch_logits_mt<2, false>(a, stream, plan, max_pages);
-    case 3: return launch_logits_mt<3, false>(a, stream, plan, max_pages);
-    default: return launch_logits_mt<4, false>(a, stream, plan, max_pages);
+    case 1: return launch_logits_mt<1, false>(a, stream, plan, max_pages, sched);
+    case 2: return launch_logits_mt<2, false>(a, stream, plan, max_pages, sched);
+    case 3: return launch_logits_mt<3, false>(a, stream, plan, max_pages, sched);
+    default: return launch_logits_mt<4, false>(a, stream, plan, max_pages, sched);
   }
 }
 
-// One layer's hot path: q quantisation, logits, top-k.
+// q quantisation plus, in the same launch, the decode page schedule of the
+// logits launch that follows (extra 4-wave workgroups, one wave per entry).
+static hipError_t launch_quantize_q_sched(const ForwardArgs& f,
+                                          int64_t max_pages,
+                                          hipStream_t stream) {
+  const int64_t blocks = f.lg.T * f.lg.H;
+  const int64_t qgrid = (blocks + 15) / 16;
+  const BalancedGeometry bg =
+      balanced_geometry(f.lg.T, max_pages, options(), true);
+  const int64_t sgrid = (bg.waves + 3) / 4;
+  const dim3 grid((unsigned)(qgrid + sgrid));
+  if (f.lg.T > 64)
+    hipLaunchKernelGGL(quantize_q_sched_kernel<2>, grid, dim3(256), 0, stream,
+                       f.q_bf16, blocks, f.q8, f.q_scale, (int)qgrid, f.lg,
+                       bg.D, (int)bg.per_xcd, (int)bg.waves, f.sched);
+  else
+    hipLaunchKernelGGL(quantize_q_sched_kernel<1>, grid, dim3(256), 0, stream,
+                       f.q_bf16, blocks, f.q8, f.q_scale, (int)qgrid, f.lg,
+                       bg.D, (int)bg.per_xcd, (int)bg.waves, f.sched);
+  return hipGetLastError();
+}
+
+// The page schedule alone (dsa_logits_schedule): the builder workgroups of
+// the launch above, no quantisation.
+hipError_t launch_logits_schedule(const LogitsArgs& a, int32_t* sched,
+                                  hipStream_t stream) {
+  if (a.T <= 0 || a.T > kBalancedMaxRows) return hipSuccess;
+  const BalancedGeometry bg =
+      balanced_geometry(a.T, logits_max_pages(a), options(), true);
+  const dim3 grid((unsigned)((bg.waves + 3) / 4));
+  if (a.T > 64)
+    hipLaunchKernelGGL(quantize_q_sched_kernel<2>, grid, dim3(256), 0, stream,
+                       nullptr, (int64_t)0, nullptr, nullptr, 0, a, bg.D,
+                       (int)bg.per_xcd, (int)bg.waves, sched);
+  else
+    hipLaunchKernelGGL(quantize_q_sched_kernel<1>, grid, dim3(256), 0, stream,
+                       nullptr, (int64_t)0, nullptr, nullptr, 0, a, bg.D,
+                       (int)bg.per_xcd, (int)bg.waves, sched);
+  return hipGetLastError();
+}
+
+// One layer's hot path: q quantisation, logits, top-k.  A decode batch of
+// the balanced class with a schedule buffer builds its page schedule in the
+// quantisation launch (build_sched; otherwise the buffer already holds the
+// schedule of the same positions, query_start_loc and block table) and the
+// logits launch reads it.
 hipError_t launch_forward(const ForwardArgs& f, hipStream_t stream) {
   if (f.lg.T <= 0) return hipSuccess;
-  hipError_t e = launch_quantize_q(f.q_bf16, f.lg.T * f.lg.H, f.q8, f.q_scale,
-                                   stream);
-  if (e == hipSuccess) e = launch_logits(f.lg, stream);
+  const int64_t max_pages = logits_max_pages(f.lg);
+  const LogitsPlan plan = logits_plan(f.lg.T, f.lg.R);
+  const bool sched = f.sched && plan == LogitsPlan::Balanced &&
+                     schedule_applies(f.lg.T, max_pages, options());
+  hipError_t e;
+  if (sched && f.build_sched)
+    e = launch_quantize_q_sched(f, max_pages, stream);
+  else
+    e = launch_quantize_q(f.q_bf16, f.lg.T * f.lg.H, f.q8, f.q_scale, stream);
+  if (e == hipSuccess)
+    e = launch_logits(f.lg, stream, plan, sched ? f.sched : nullptr);
   if (e == hipSuccess) e = launch_topk(f.tk, stream);
   return e;
 }

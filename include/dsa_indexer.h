@@ -131,6 +131,46 @@ int dsa_indexer_logits(const uint8_t* q_fp8, const float* q_scale,
                        void* stream);
 
 /*
+ * dsa_logits_schedule -- the decode page schedule of a batch, for
+ * dsa_indexer_logits_scheduled: which wave scores which row's page range,
+ * with the request and the first physical pages of each range resolved
+ * through block_table ([HBM] 2.3, 4.2).  It depends only on block_table,
+ * query_start_loc, positions, T, R and ld, so one schedule serves every
+ * layer of a batch (the IndexCache F layers of a pass share them).  Built
+ * only for batches of at most 128 rows (dsa_logits_schedule_size gives 0
+ * otherwise: nothing to build, no error).
+ *   schedule  device, out: dsa_logits_schedule_size(T, ld) bytes.
+ * A position outside the logits or block-table row raises
+ * DSA_DEVERR_POSITION_OUT_OF_RANGE and gives that row no range.
+ */
+size_t dsa_logits_schedule_size(int64_t T, int64_t ld);
+
+int dsa_logits_schedule(const int32_t* block_table, int64_t bt_stride,
+                        const int32_t* query_start_loc,
+                        const int32_t* positions, int64_t T, int R,
+                        int64_t ld, int32_t* schedule, size_t sched_bytes,
+                        void* stream);
+
+/*
+ * dsa_indexer_logits_scheduled -- dsa_indexer_logits with a page schedule
+ * built by dsa_logits_schedule for the same block_table, query_start_loc,
+ * positions, T, R and ld (and the same dsa_set_option knobs), enqueued
+ * before it: each decode wave then starts its K loads after one load of its
+ * schedule entry.  Arguments and results as for dsa_indexer_logits, bit for
+ * bit; schedule == NULL, or a batch the schedule does not serve (more than
+ * 128 rows, rows sharing a request's keys), runs dsa_indexer_logits.
+ */
+int dsa_indexer_logits_scheduled(const uint8_t* q_fp8, const float* q_scale,
+                                 const float* weights, const uint8_t* k_cache,
+                                 int64_t num_pages, const int32_t* block_table,
+                                 int64_t bt_stride,
+                                 const int32_t* query_start_loc,
+                                 const int32_t* positions, int64_t T, int R,
+                                 int H, int head_dim, int page_size,
+                                 float* logits, int64_t ld,
+                                 const int32_t* schedule, void* stream);
+
+/*
  * dsa_indexer_topk -- per-row causal top-k into the shared index buffer
  * ([IC] 2: rows cleared to -1, then the top-k scattered in; [KVB] top-k
  * buffer: int32 [max_num_batched_tokens, index_topk]).
@@ -162,8 +202,11 @@ size_t dsa_topk_workspace_size(int64_t T, int64_t ld, int k);
  *   workspace  device, dsa_forward_workspace_size(T, H, ld, k) bytes (q
  *              codes and scales, top-k scratch); contents on entry do not
  *              matter.
- * The three kernels run in turn on `stream`; the result equals the three
- * separate calls bit for bit, except that a row whose position is past its
+ * The three kernels run in turn on `stream` (a decode batch of at most 128
+ * rows builds its page schedule in the quantisation launch, as
+ * dsa_logits_schedule would, and scores with it); the result equals the
+ * three separate calls bit for bit, except that a row whose position is past
+ * its
  * block-table row (p / 64 >= bt_stride; flagged, logits not written) gets a
  * top-k row of -1.
  */
