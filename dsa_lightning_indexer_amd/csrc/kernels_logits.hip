@@ -1168,12 +1168,15 @@ __global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
       const float val = (s <= prow && pok[h]) ? (pt[h] + lv) * ks : -INFINITY;
       // the page's 64 logits as a buffer, empty for a padding row, a page
       // past the range or past the row's own last page (a shorter row of
-      // the tile): an unconditional store, no 64-bit address math
+      // the tile): an unconditional store, no 64-bit address math;
+      // non-temporal (nt), so the logits stream does not fill the caches
+      // with lines the kernel never reads (measured 1-2 % faster on the
+      // prefill chunk and the 1M-token tail)
       const __amdgpu_buffer_rsrc_t ro = make_rsrc(
           orow + (int64_t)min(pj, npages - 1) * kPageTokens,
           prow >= 0 && pj < je && pj <= (prow >> 6) ? kPageTokens * 4 : 0);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, 4 * tok,
-                                            0, 0);
+                                            0, 2);
     }
   };
 

@@ -473,8 +473,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(
 // ---------------------------------------------------------------------------
 template <int NT, int S>
 struct RegTopkShared {
-  uint32_t hist[kHistBins];
-  uint32_t hist2[kHistBins];
+  __align__(16) uint32_t hist[kHistBins];
+  __align__(16) uint32_t hist2[kHistBins];
   uint32_t tot[S * (NT / 64)];                 // packed per (slice, wave)
   uint32_t wave_sum[NT / 64];
   uint32_t sel_digit, sel_above, sel_count;
@@ -497,13 +497,89 @@ struct RegKeys {
   }
 };
 
+// Clears the two histograms reg_threshold expects zero (16-byte stores);
+// the caller then passes a barrier before calling it.
+template <int NT, int S>
+__device__ __forceinline__ void reg_clear(RegTopkShared<NT, S>& sh) {
+  for (int b = 4 * (int)threadIdx.x; b < kHistBins; b += 4 * NT) {
+    *reinterpret_cast<uint4*>(&sh.hist[b]) = make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4*>(&sh.hist2[b]) = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// The bin of the k_rem-th largest key of a 4096-bin histogram (bins taken
+// from the top), found by every wave itself after one barrier: thread t
+// owns bins 4095 - B t down to 4096 - B (t + 1) (B = 4096 / NT); each wave
+// scans its bins and publishes its total; after the barrier every wave
+// scans the totals, finds the wave that owns the bin, reads that wave's
+// bins from LDS and scans them again -- so the result (d, the count of keys
+// above it, its count) is in registers of every wave without a second
+// barrier.  k_rem must not exceed the histogram's total.
+template <int NT>
+__device__ __forceinline__ void select_bin_all(const uint32_t* hist,
+                                               uint32_t k_rem,
+                                               uint32_t* wave_sum, uint32_t& d,
+                                               uint32_t& above,
+                                               uint32_t& count) {
+  constexpr int B = kHistBins / NT;
+  constexpr int NW = NT / 64;
+  static_assert(B * NT == kHistBins && NW <= 64, "bins per thread");
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  uint32_t local = 0u;
+  {
+    const int top = kHistBins - 1 - B * (int)threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < B; ++j) local += hist[top - j];
+  }
+  const uint32_t incl = wave_inclusive_scan(local);
+  if (lane == 63) wave_sum[wave] = incl;
+  __syncthreads();
+  const uint32_t wt = lane < NW ? wave_sum[lane] : 0u;
+  const uint32_t wincl = wave_inclusive_scan(wt);
+  const int ws =
+      __builtin_ctzll(__ballot(lane < NW && wincl >= k_rem));
+  const uint32_t above_w =
+      __builtin_amdgcn_readlane(wincl - wt, ws);
+  uint32_t c[B];
+  uint32_t l2 = 0u;
+  const int top = kHistBins - 1 - B * (64 * ws + lane);
+#pragma unroll
+  for (int j = 0; j < B; ++j) {
+    c[j] = hist[top - j];
+    l2 += c[j];
+  }
+  const uint32_t i2 = wave_inclusive_scan(l2);
+  uint32_t a = above_w + i2 - l2;
+  const int ls = __builtin_ctzll(__ballot(a < k_rem && a + l2 >= k_rem));
+  int jj = 0;
+  uint32_t ab = 0u, cn = 0u;
+  bool found = false;
+#pragma unroll
+  for (int j = 0; j < B; ++j) {
+    if (!found && a + c[j] >= k_rem) {
+      found = true;
+      jj = j;
+      ab = a;
+      cn = c[j];
+    }
+    a += c[j];
+  }
+  d = (uint32_t)(kHistBins - 1 - B * (64 * ws + ls) -
+                 __builtin_amdgcn_readlane(jj, ls));
+  above = __builtin_amdgcn_readlane(ab, ls);
+  count = __builtin_amdgcn_readlane(cn, ls);
+}
+
 // Threshold of the k largest valid keys (k < number of valid keys): a key
 // is selected when (key & mask) > thr, or (key & mask) == thr and it is
 // among the k_tie lowest-position such keys.  Up to three LDS histograms
 // (top 12 key bits over the list; bits 19..8 over the keys of the chosen
-// bin; bits 7..0 over the keys matching the 24-bit prefix), each followed
-// by the two-barrier bin search.  sh.hist and sh.hist2 must be zero and a
-// barrier passed before the call.  Call from all NT threads.
+// bin; bits 7..0 over the keys matching the 24-bit prefix).  The first bin
+// search is select_bin_all (one barrier) for instances of up to 4 slices;
+// wider ones keep their registers for the keys and use the two-barrier
+// search throughout.  reg_clear and a barrier must precede the call.  Call
+// from all NT threads.
 template <int NT, int S>
 __device__ void reg_threshold(const RegKeys<S, NT>& r, int k,
                               RegTopkShared<NT, S>& sh, uint32_t& mask,
@@ -515,11 +591,18 @@ __device__ void reg_threshold(const RegKeys<S, NT>& r, int k,
     for (int j = 0; j < 4; ++j)
       if (r.ok(s, j)) atomicAdd(&sh.hist[r.key[s][j] >> 20], 1u);
   __syncthreads();
-  topk_select_bin<kHistBins, NT>(sh.hist, (uint32_t)k, sh);
-  const uint32_t d = sh.sel_digit;
-  const uint32_t k_rem = (uint32_t)k - sh.sel_above;
+  uint32_t d, above, count;
+  if constexpr (S <= 4) {
+    select_bin_all<NT>(sh.hist, (uint32_t)k, sh.wave_sum, d, above, count);
+  } else {
+    topk_select_bin<kHistBins, NT>(sh.hist, (uint32_t)k, sh);
+    d = sh.sel_digit;
+    above = sh.sel_above;
+    count = sh.sel_count;
+  }
+  const uint32_t k_rem = (uint32_t)k - above;
   mask = 0xfff00000u; thr = d << 20; k_tie = k_rem;
-  if (k_rem < sh.sel_count) {
+  if (k_rem < count) {
     // pass 2: bits 19..8 of the keys in bin d; bins 0..255 of hist are
     // cleared for pass 3 (the barrier after pass 2 orders the clear)
     for (int b = tid; b < 256; b += NT) sh.hist[b] = 0u;
@@ -581,9 +664,12 @@ __device__ void reg_emit(const RegKeys<S, NT>& r, int k, uint32_t mask,
     if (lane == 63) sh.tot[s * NW + wave] = incl;
   }
   __syncthreads();
-  // exclusive scan of the S * NW (slice, wave) totals, in place, by wave 0
-  if (wave == 0) {
-    constexpr int kPer = (S * NW + 63) / 64;
+  // every wave scans the S * NW (slice, wave) totals itself (exclusive, in
+  // (slice, wave) order; lane l holds entries kPer l ..), then takes the
+  // entry of (s, its wave) from the lane holding it: no second barrier
+  constexpr int kPer = (S * NW + 63) / 64;
+  uint32_t ex[kPer];
+  {
     uint32_t v[kPer], local = 0u;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -594,12 +680,18 @@ __device__ void reg_emit(const RegKeys<S, NT>& r, int k, uint32_t mask,
     uint32_t run = wave_inclusive_scan(local) - local;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int idx = lane * kPer + i;
-      if (idx < S * NW) sh.tot[idx] = run;
+      ex[i] = run;
       run += v[i];
     }
   }
-  __syncthreads();
+  auto base_of = [&](int s) {
+    const int idx = s * NW + wave;            // wave-uniform
+    uint32_t x = ex[0];
+#pragma unroll
+    for (int i = 1; i < kPer; ++i)
+      if (idx % kPer == i) x = ex[i];
+    return __builtin_amdgcn_readlane(x, idx / kPer);
+  };
   // 4 tid through an empty asm: the column indices below are then computed
   // where they are used instead of being hoisted out of a caller's row loop
   // as S x 4 loop-invariant registers
@@ -614,7 +706,7 @@ __device__ void reg_emit(const RegKeys<S, NT>& r, int k, uint32_t mask,
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(orow, k * 4);
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    const uint32_t before = sh.tot[s * NW + wave] + excl[s];
+    const uint32_t before = base_of(s) + excl[s];
     uint32_t gt_b = before & 0xffffu, eq_b = before >> 16;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -727,10 +819,7 @@ __device__ void topk_row_registers(const float* row, int64_t ld, int n, int k,
                                    int32_t* orow, RegTopkShared<NT, S>& sh) {
   constexpr int kSlice = 4 * NT;
   const int tid = threadIdx.x;
-  for (int b = tid; b < kHistBins; b += NT) {
-    sh.hist[b] = 0u;
-    sh.hist2[b] = 0u;
-  }
+  reg_clear(sh);
   RegKeys<S, NT> r;
   r.n = n;
 #pragma unroll
@@ -807,10 +896,7 @@ __global__ __launch_bounds__(NT, 4) void topk_reg_kernel(
       topk_row_short<NT>(n, k, orow);
       return;
     }
-    for (int b = tid; b < kHistBins; b += NT) {
-      sh.hist[b] = 0u;
-      sh.hist2[b] = 0u;
-    }
+    reg_clear(sh);
     RegKeys<S, NT> r;
     r.n = n;
 #pragma unroll
@@ -1331,10 +1417,7 @@ __global__ __launch_bounds__(kTopkThreads) void ss_sample_kernel(
   const int n = row_len(positions, t, ws.plim);
   if (n <= kSsCandMax || n <= k) return;
   const int tid = threadIdx.x;
-  for (int b = tid; b < kHistBins; b += kTopkThreads) {
-    sh.hist[b] = 0u;
-    sh.hist2[b] = 0u;
-  }
+  reg_clear(sh);
   const uint32_t* samp = ws.samp + t * kSsSample;
   RegKeys<4> r;
   r.n = kSsSample;
@@ -1487,10 +1570,7 @@ __global__ __launch_bounds__(kTopkThreads) void ss_select_kernel(
     topk_radix_rest(keys, n, k, orow, sh.full);
     return;
   }
-  for (int b = tid; b < kHistBins; b += kTopkThreads) {
-    sh.reg.hist[b] = 0u;
-    sh.reg.hist2[b] = 0u;
-  }
+  reg_clear(sh.reg);
   // gather: item x (list order = column order) lives in chunk q with
   // s_pre[q] <= x < s_pre[q + 1]
   RegKeys<4> r;
