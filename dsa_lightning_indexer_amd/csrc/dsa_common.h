@@ -18,6 +18,9 @@ constexpr int kHeadDim = 128;
 constexpr int kPageKeyBytes = kPageTokens * kHeadDim;       // 8192
 constexpr int kPageBytes = kPageKeyBytes + kPageTokens * 4;  // 8448
 constexpr int kMaxHeads = 64;
+// Rows of a tile of the tiled logits kernels: tiles of 16 consecutive rows
+// from each request's first row.
+constexpr int kTileRows = 16;
 constexpr float kE4M3Max = 448.0f;
 
 // Device error flags (sticky, cleared by dsa_device_error_flags(reset=1)).
@@ -69,6 +72,11 @@ __device__ __forceinline__ uint32_t float_to_ordered(float f) {
   uint32_t u = __float_as_uint(f);
   if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inverse of float_to_ordered (-0 comes back as +0).
+__device__ __forceinline__ float ordered_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }

@@ -27,6 +27,23 @@ struct LogitsArgs {
   int H;
   float* logits;                // [T, ld]
   int64_t ld;
+  // 16-row tile kernel only: score logical pages j = 0, 1, .. of the real
+  // pages j * page_stride (the fused forward's sample pass) and write row t
+  // at logits + t * out_ld (0: ld), page j at columns 64 j ..
+  int page_stride = 1;
+  int64_t out_ld = 0;
+};
+
+// Candidate mode of the 16-row tile kernel (fused forward): instead of its
+// logits, workgroup (tile, split x) appends the (ordered key, column) of
+// every logit of row t at or above tlo[t] to cand[(t * splits + x) * cap
+// ..], in ascending column order, and writes how many there were (possibly
+// more than cap) to count[t * splits + x].
+struct FusedTile {
+  const uint32_t* tlo = nullptr;
+  uint2* cand = nullptr;
+  uint32_t* count = nullptr;
+  int cap = 0;
 };
 
 struct TopkArgs {
@@ -73,6 +90,9 @@ struct Options {
   int row_head_waves = 0;       // decode: 1 + head waves per row (0: one)
   int topk_kernel = 0;          // 0/1 register rows, 2 LDS-cached rows, 3 long rows by multi-WG radix, register rows: 0 two 512-thread workgroups per CU when rows outnumber CUs, else one 1024-thread, 1 always 1024, 4 always 512
   int tile_pages_per_step = 0;  // 16-row tile kernel: pages per copy step (0 auto, 2 or 4)
+  int fused_sample_stride = 0;  // fused forward: sample every n-th page (0: 32; 16, 32, 64)
+  int fused_cand_cap = 0;       // fused forward: candidates per (row, split) slot (0 auto; n: at most n)
+  int fused_force_rescue = 0;   // fused forward: 1 re-scores every row of more than k columns
 };
 Options options();
 
@@ -122,6 +142,25 @@ struct ChunkedForwardArgs {
 };
 hipError_t launch_forward_chunked(const ChunkedForwardArgs& c,
                                   hipStream_t stream);
+// Fused forward, tile passes (the default tiled class).  Sample pass: the
+// logits of every page_stride-th page of each row into samp (row t at samp
+// + t * ld_s, logical page j at columns 64 j ..).  Candidate pass: every
+// page scored, logits at or above each row's threshold appended to ft
+// (FusedTile) over gx page splits per tile -- gx must be
+// fused_candidate_splits(a), which the caller sizes ft by.
+int64_t fused_candidate_splits(const LogitsArgs& a);
+hipError_t launch_logits_sample(const LogitsArgs& a, int page_stride,
+                                float* samp, int64_t ld_s, hipStream_t stream);
+hipError_t launch_logits_candidates(const LogitsArgs& a, const FusedTile& ft,
+                                    int64_t gx, hipStream_t stream);
+// The fused forward of a tiled batch: q quantisation into f.q8 / f.q_scale,
+// then scoring and exact top-k into f.tk.out without a logits buffer
+// (f.lg.logits and f.tk.logits unused); ws holds fused_workspace_bytes(T,
+// ld, k) bytes.  The top-k equals launch_forward's with the default tiled
+// logits kernel.
+size_t fused_workspace_bytes(int64_t T, int64_t ld, int k);
+hipError_t launch_forward_fused(const ForwardArgs& f, void* ws,
+                                hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 size_t topk_workspace_bytes(int64_t T, int64_t ld, int k);
 hipError_t read_error_flags(unsigned* flags, bool reset);

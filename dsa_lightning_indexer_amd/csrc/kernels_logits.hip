@@ -23,6 +23,7 @@
 
 #include "dsa_common.h"
 #include "dsa_launch.h"
+#include "dsa_score.h"
 
 namespace dsa {
 
@@ -73,120 +74,6 @@ __global__ __launch_bounds__(256) void quantize_q_kernel(
   quantize_q_blocks(q, blocks, q8, q_scale, blockIdx.x);
 }
 
-// ---------------------------------------------------------------------------
-// MFMA operand layout used below (v_mfma_f32_16x16x128_f8f6f4, wave64):
-//   A (16 x 128): lane l holds row (l % 16), 32 bytes of K-chunk (l / 16);
-//   B (128 x 16): lane l holds column (l % 16), the same 32-byte K-chunk;
-//   C (16 x 16):  lane l holds rows 4*(l/16) + j, j = 0..3, column (l % 16).
-// A and B place the 128-long reduction index identically, so loading q rows
-// and K rows with the same byte pattern gives the exact dot products.
-// Rows of A are heads (16 per M-tile), columns of B are tokens (16 per
-// N-tile); a 64-token page is 4 N-tiles.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ i32x8 load_frag_global(const uint8_t* row32) {
-  const uint4 x = *reinterpret_cast<const uint4*>(row32);
-  const uint4 y = *reinterpret_cast<const uint4*>(row32 + 16);
-  i32x8 v = {(int)x.x, (int)x.y, (int)x.z, (int)x.w,
-             (int)y.x, (int)y.y, (int)y.z, (int)y.w};
-  return v;
-}
-
-// A fragments of one query row (MT M-tiles of 16 heads; heads >= H are 0).
-// FULL (H == 16 * MT): plain loads.  Otherwise the head index is clamped so
-// every load stays in bounds and is issued unconditionally (no divergent
-// branch, so the loads overlap), and padded heads are zeroed afterwards.
-template <int MT, bool FULL>
-__device__ __forceinline__ void load_q_frags(const uint8_t* q8_row, int H,
-                                             i32x8 (&qa)[MT]) {
-  const int lane = lane_id();
-  const int i16 = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    const int head = 16 * m + i16;
-    const int hh = FULL ? head : min(head, H - 1);
-    qa[m] = load_frag_global(q8_row + hh * kHeadDim + 32 * g);
-    if (!FULL && head >= H) qa[m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-  }
-}
-
-// The same fragments in the chunk-major K order of the 16-row tile kernel:
-// lane l holds bytes [16 (l / 16), + 16) and [64 + 16 (l / 16), + 16) of its
-// row (a permutation of the 128-long reduction index; A and B use the same
-// one, so the dot products are unchanged).
-template <int MT, bool FULL>
-__device__ __forceinline__ void load_q_frags_cm(const uint8_t* q8_row, int H,
-                                                i32x8 (&qa)[MT]) {
-  const int lane = lane_id();
-  const int i16 = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    const int head = 16 * m + i16;
-    const int hh = FULL ? head : min(head, H - 1);
-    const uint8_t* row = q8_row + hh * kHeadDim + 16 * g;
-    const uint4 x = *reinterpret_cast<const uint4*>(row);
-    const uint4 y = *reinterpret_cast<const uint4*>(row + 64);
-    qa[m] = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w,
-                  (int)y.x, (int)y.y, (int)y.z, (int)y.w};
-    if (!FULL && head >= H) qa[m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-  }
-}
-
-// Per-lane effective head weights w[h] * s_q[h] / 2 for the C rows this
-// lane holds: head 16*m + 4*(lane/16) + j, j = 0..3 (4 consecutive heads,
-// one 16-byte load each when FULL).  The 1/2 belongs to head_reduce's ReLU.
-template <int MT, bool FULL>
-__device__ __forceinline__ void load_head_weights(const float* w_row,
-                                                  const float* s_row, int H,
-                                                  float (&w)[MT][4]) {
-  const int g = lane_id() >> 4;
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    if (FULL) {
-      const float4 wv = *reinterpret_cast<const float4*>(w_row + 16 * m + 4 * g);
-      const float4 sv = *reinterpret_cast<const float4*>(s_row + 16 * m + 4 * g);
-      w[m][0] = 0.5f * (wv.x * sv.x); w[m][1] = 0.5f * (wv.y * sv.y);
-      w[m][2] = 0.5f * (wv.z * sv.z); w[m][3] = 0.5f * (wv.w * sv.w);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int head = 16 * m + 4 * g + j;
-        const int hh = min(head, H - 1);
-        const float x = 0.5f * (w_row[hh] * s_row[hh]);
-        w[m][j] = head < H ? x : 0.f;
-      }
-    }
-  }
-}
-
-// sum over this lane's heads of w * ReLU(dot) for one N-tile.  ReLU is
-// written as (x + |x|) / 2 with the 1/2 folded into the weights: one add
-// with an abs source modifier and one FMA per MFMA output (a plain fmaxf
-// costs an extra NaN-canonicalising max on gfx950).
-template <int MT>
-__device__ __forceinline__ float head_reduce(const f32x4 (&acc)[MT],
-                                             const float (&w_half)[MT][4]) {
-  float v = 0.f;
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      v = fmaf(w_half[m][j], acc[m][j] + fabsf(acc[m][j]), v);
-  return v;
-}
-
-// The same sum without the linear part: sum over this lane's heads of
-// w * |dot| (one FMA with an abs source modifier per MFMA output).  The
-// tile kernels add sum_h w * dot, computed once for four rows, afterwards.
-template <int MT>
-__device__ __forceinline__ float head_reduce_abs(const f32x4 (&acc)[MT],
-                                                 const float (&w_half)[MT][4]) {
-  float v = 0.f;
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v = fmaf(w_half[m][j], fabsf(acc[m][j]), v);
-  return v;
-}
 
 // ---------------------------------------------------------------------------
 // Request of row t: the number of requests r < R with qsl[r] <= t, minus 1
@@ -634,7 +521,6 @@ __global__ __launch_bounds__(64) void logits_balanced_kernel(
 // all 8 waves; wave w scores rows 2w and 2w+1.  Grid: x = page split,
 // y = tile (tiles of request r are numbered after those of requests < r).
 // ---------------------------------------------------------------------------
-constexpr int kTileRows = 16;
 constexpr int kTileWaves = 8;
 constexpr int kLdsRow = 144;
 
@@ -804,141 +690,6 @@ __global__ __launch_bounds__(512) void logits_tile_kernel(LogitsArgs a,
   }
 }
 
-// ---------------------------------------------------------------------------
-// Linear part of the head reduction, shared by four rows (tile kernel).
-// With ReLU written as (x + |x|) / 2 and the 1/2 folded into the weights,
-//   sum_h w_h (x_h + |x_h|) = L + sum_h w_h |x_h|,
-//   L = sum_h w_h x_h = qlin . code_k,   qlin = sum_h w_h code_q[h, :],
-// so the per-output epilogue is a single FMA, and L costs one more FP8
-// MFMA per 16 keys for four rows together.  qlin (fp32) is split into
-// kLinPieces FP8 pieces, qlin ~= sum_p s_p c_p: s_p an fp32 scale, c_p the
-// e4m3 rounding of what the earlier pieces left over.  Each piece shrinks
-// the largest residual at least 28-fold (half an e4m3 step at the top of
-// the range is 1/28 of it), so four pieces leave at most ~1.6e-6 max|qlin|
-// per element, far inside the fp32 accumulation error of the dot products.
-// The A operand of that MFMA has rows 4 q + p = (row q of the group, piece
-// p), so lane group q of its output holds the four pieces of row q.
-// ---------------------------------------------------------------------------
-constexpr int kLinPieces = 4;
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(
-      __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-
-// One reduce-scatter step over v[0..N): lanes paired by the DPP pattern
-// CTRL differ in `bit`; a lane keeps half `bit` of the list and adds the
-// partner's copy of that half.
-template <int CTRL, int N>
-__device__ __forceinline__ void rs_step(float* v, bool bit) {
-#pragma unroll
-  for (int j = 0; j < N / 2; ++j) {
-    const float send = bit ? v[j] : v[j + N / 2];
-    const float keep = bit ? v[j + N / 2] : v[j];
-    v[j] = keep + dpp_f<CTRL>(send);
-  }
-}
-
-// Maximum over the wave of x >= 0 (wave-uniform result).
-__device__ __forceinline__ float wave_max_nonneg(float x) {
-  x = fmaxf(x, dpp_f<0xB1>(x));    // quad_perm [1,0,3,2]
-  x = fmaxf(x, dpp_f<0x4E>(x));    // quad_perm [2,3,0,1]
-  x = fmaxf(x, dpp_f<0x141>(x));   // row_half_mirror
-  x = fmaxf(x, dpp_f<0x140>(x));   // row_mirror
-  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
-  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
-  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
-  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
-  return fmaxf(fmaxf(a, b), fmaxf(c, d));
-}
-
-// qlin of one row from its chunk-major A fragments (lane l: head 16 m +
-// l % 16; byte j of qa[m] is dim 16 (l / 16) + j for j < 16 and 64 + 16 (l
-// / 16) + j - 16 after; wa[m] the folded weight of that head), summed over
-// the 16 lanes of each lane row by a reduce-scatter (row_mirror,
-// row_half_mirror, then two quad permutations): lane l ends with bytes
-// 2 (l % 16) and + 1 of that list.  The hardware fp8 -> f32 conversion
-// decodes e4m3fn exactly.
-template <int MT>
-__device__ __forceinline__ float2 row_qlin(const i32x8 (&qa)[MT],
-                                           const float (&wa)[MT]) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  float v[32];
-#pragma unroll
-  for (int j = 0; j < 32; ++j) v[j] = 0.f;
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(qa[m][k], false);
-      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(qa[m][k], true);
-      v[4 * k + 0] = fmaf(wa[m], lo[0], v[4 * k + 0]);
-      v[4 * k + 1] = fmaf(wa[m], lo[1], v[4 * k + 1]);
-      v[4 * k + 2] = fmaf(wa[m], hi[0], v[4 * k + 2]);
-      v[4 * k + 3] = fmaf(wa[m], hi[1], v[4 * k + 3]);
-    }
-  const int i16 = lane_id() & 15;
-  rs_step<0x140, 32>(v, (i16 >> 3) & 1);
-  rs_step<0x141, 16>(v, (i16 >> 2) & 1);
-  rs_step<0x4E, 8>(v, (i16 >> 1) & 1);
-  rs_step<0xB1, 4>(v, i16 & 1);
-  return make_float2(v[0], v[1]);
-}
-
-// Splits qlin (this lane's dims d, d + 1 as left by row_qlin) into
-// kLinPieces e4m3 pieces, A row a = 4 q + p of the group's operand (q = the
-// row within the group), stored chunk-major like the keys: byte d of A row
-// a at group[(d / 64) * 1024 + (d / 16 % 4) * 256 + a * 16 + d % 16], so
-// lane l reads its fragment at group + 16 l (+ 1024).  The scale of piece p
-// goes to scales[p].  qlin is first brought to max|qlin| in [1, 2) by a
-// power of two (exact), so a residual below 2^-60 -- nothing left that
-// matters -- ends the split without dividing by a denormal.
-__device__ __forceinline__ void split_pieces(float r0, float r1, int q,
-                                             uint8_t* group, float* scales) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const int lane = lane_id();
-  const int i16 = lane & 15, g = lane >> 4;
-  const int d = (i16 < 8 ? 16 * g : 64 + 16 * g - 16) + 2 * i16;
-  const float amax0 = wave_max_nonneg(fmaxf(fabsf(r0), fabsf(r1)));
-  int e = 0;
-  if (amax0 > 0.f) (void)frexpf(amax0, &e);
-  const int E = amax0 > 0.f ? 1 - e : 0;          // amax0 * 2^E in [1, 2)
-  r0 = __builtin_amdgcn_ldexpf(r0, E);
-  r1 = __builtin_amdgcn_ldexpf(r1, E);
-#pragma unroll
-  for (int p = 0; p < kLinPieces; ++p) {
-    const float amax = wave_max_nonneg(fmaxf(fabsf(r0), fabsf(r1)));
-    const bool live = amax > 0x1p-60f;
-    const float inv = live ? kE4M3Max / amax : 0.f;
-    const float sc = live ? amax / kE4M3Max : 0.f;
-    const uint32_t c0 = e4m3fn_encode(r0 * inv);
-    const uint32_t c1 = e4m3fn_encode(r1 * inv);
-    const uint32_t pk = c0 | (c1 << 8);
-    const f32x2 dec = __builtin_amdgcn_cvt_pk_f32_fp8((int)pk, false);
-    r0 = fmaf(-sc, dec[0], r0);
-    r1 = fmaf(-sc, dec[1], r1);
-    *reinterpret_cast<uint16_t*>(group + (d >> 6) * 1024 + ((d >> 4) & 3) * 256 +
-                                 (4 * q + p) * 16 + (d & 15)) = (uint16_t)pk;
-    if (lane == 0) scales[p] = __builtin_amdgcn_ldexpf(sc, -E);
-  }
-}
-
-// Folded weights w[h] * s_q[h] / 2 of the A-fragment heads of this lane:
-// head 16 m + l % 16 (0 for heads >= H).
-template <int MT, bool FULL>
-__device__ __forceinline__ void load_a_weights(const float* w_row,
-                                               const float* s_row, int H,
-                                               float (&wa)[MT]) {
-  const int i16 = lane_id() & 15;
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    const int head = 16 * m + i16;
-    const int hh = FULL ? head : min(head, H - 1);
-    const float x = 0.5f * (w_row[hh] * s_row[hh]);
-    wa[m] = (FULL || head < H) ? x : 0.f;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Tiled logits, one row per wave.  A workgroup of 16 waves owns a tile of 16
@@ -1008,10 +759,20 @@ __device__ __forceinline__ void lds_copy(const void* base, int bytes,
 #pragma clang diagnostic pop
 }
 
-template <int MT, bool FULL, bool LIN, int PP, bool PF>
+//
+// a.page_stride > 1 (the fused forward's sample pass, LIN only): the tile's
+// pages are the logical pages j = 0, 1, .. of real page j * page_stride; a
+// row sees logical page j when j * page_stride <= p / 64, its logits go to
+// columns 64 j .. of row t at a.logits + t * a.out_ld.
+// CAND (LIN only): no logits are written; every visible logit of row t at
+// or above ft.tlo[t] (as an ordered key) is appended as (key, column) to
+// this workgroup's slot of the row in ascending column order, and the
+// count to ft.count (FusedTile).
+template <int MT, bool FULL, bool LIN, int PP, bool PF, bool CAND>
 __global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
-    LogitsArgs a, int pages_per_split, int min_pages) {
+    LogitsArgs a, int pages_per_split, int min_pages, FusedTile ft) {
   static_assert(PP == 2 || PP == 4, "pages per step");
+  static_assert(LIN || !CAND, "candidate mode has the linear-term epilogue");
   constexpr int kLs = PP * kPageTokens + 16;     // s_lin row stride (banks)
   // two key buffers [page of the step][8192 key bytes, chunk-major], as two
   // objects so the compiler can tell the reads of one from the direct-to-LDS
@@ -1050,10 +811,12 @@ __global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
     s_pos[tid] = p;
   }
   __syncthreads();
+  const int SSt = LIN ? a.page_stride : 1;
   int maxp = -1;
 #pragma unroll
   for (int i = 0; i < kTileRows; ++i) maxp = max(maxp, s_pos[i]);
-  const int npages = (maxp >> 6) + 1;        // 0 when no valid row
+  // (logical) pages of the tile; 0 when no valid row
+  const int npages = maxp < 0 ? 0 : (maxp >> 6) / SSt + 1;
   // pages_per_split > 0: fixed ranges; otherwise this tile's pages are cut
   // into gridDim.x equal ranges of at least min_pages (the splits of a
   // tile then take the same time whatever its length)
@@ -1062,7 +825,12 @@ __global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
                       : max(min_pages, (npages + (int)gridDim.x - 1) / (int)gridDim.x);
   const int jb = blockIdx.x * per;
   const int je = min(jb + per, npages);
-  if (jb >= je) return;
+  if (jb >= je) {
+    // a split past the tile's pages: its rows found no candidates here
+    if (CAND && tid < kTileRows && s_pos[tid] >= 0)
+      ft.count[(row0 + tid) * gridDim.x + blockIdx.x] = 0u;
+    return;
+  }
 
   const int32_t* bt = a.block_table + (int64_t)r * a.bt_stride;
   const int i16 = lane & 15, g = lane >> 4;
@@ -1081,7 +849,7 @@ __global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
   bool bad_page = false;
   const int last = (int)a.bt_stride - 1;
   auto page_id = [&](int jp) {
-    const int page = load_uniform(bt, min(jp, last));
+    const int page = load_uniform(bt, min(jp * SSt, last));
     return jp < je ? page : -1;
   };
   auto fetch = [&](int jp, auto buf_, int sbuf) {
@@ -1144,7 +912,17 @@ __global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) w[m][j] = 0.f;
   }
-  float* orow = a.logits + t * a.ld;
+  float* orow = a.logits + t * (a.out_ld > 0 ? a.out_ld : a.ld);
+  // candidate mode: this row's threshold and slot, the running count
+  const uint32_t cthr =
+      (CAND && prow >= 0) ? load_uniform(reinterpret_cast<const int32_t*>(
+                                             ft.tlo), t)
+                          : 0u;
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(
+      CAND ? ft.cand + (t * gridDim.x + blockIdx.x) * (int64_t)ft.cap
+           : nullptr,
+      CAND && prow >= 0 ? ft.cap * 8 : 0);
+  uint32_t cbase = 0u;
 
   // LIN: wave 4 G + wq takes the N-tiles of a page in the order wq, wq + 1,
   // ... (mod 4), so the tile it computes L for is always its first one and
@@ -1162,10 +940,33 @@ __global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
 #pragma unroll
     for (int h = 0; h < PP; ++h) {
       const int pj = pjp + h;
-      const int s = pj * kPageTokens + tok;
+      const int s = pj * SSt * kPageTokens + tok;      // real column
       const float lv = s_lin[pbuf][wave][kPageTokens * h + tok];
       const float ks = s_scale[psbuf][h][tok];
       const float val = (s <= prow && pok[h]) ? (pt[h] + lv) * ks : -INFINITY;
+      if (CAND) {
+        // lane group g holds token group (wq + g) & 3: rotating the lane
+        // mask by 16 wq bits gives the mask in token order, so a lane's
+        // slot is the number of selected tokens before its own
+        const bool vis = prow >= 0 && pj < je && s <= prow;
+        const uint32_t key = float_to_ordered(val);
+        const bool sel = vis && key >= (uint32_t)cthr;
+        const uint64_t lm = __ballot(sel);
+        if (lm) {
+          const uint64_t tm = __builtin_rotateleft64(lm, 16 * wq);
+          const uint32_t rank =
+              (uint32_t)__popcll(tm & ((1ull << tok) - 1ull));
+          const uint32_t slot = cbase + rank;
+          // slots past cap fall outside the buffer and are dropped
+          const int off = sel && slot < (uint32_t)ft.cap ? (int)slot * 8
+                                                          : ft.cap * 8;
+          typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{key, (uint32_t)s}, crs,
+                                                off, 0, 0);
+          cbase += (uint32_t)__popcll(lm);
+        }
+        continue;
+      }
       // the page's 64 logits as a buffer, empty for a padding row, a page
       // past the range or past the row's own last page (a shorter row of
       // the tile): an unconditional store, no 64-bit address math;
@@ -1174,7 +975,8 @@ __global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
       // prefill chunk and the 1M-token tail)
       const __amdgpu_buffer_rsrc_t ro = make_rsrc(
           orow + (int64_t)min(pj, npages - 1) * kPageTokens,
-          prow >= 0 && pj < je && pj <= (prow >> 6) ? kPageTokens * 4 : 0);
+          prow >= 0 && pj < je && pj * SSt <= (prow >> 6) ? kPageTokens * 4
+                                                           : 0);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, 4 * tok,
                                             0, 2);
     }
@@ -1273,6 +1075,8 @@ __global__ __launch_bounds__(kT16Threads) void logits_tile16_kernel(
     __syncthreads();
     complete();
   }
+  if (CAND && prow >= 0 && lane == 0)
+    ft.count[t * gridDim.x + blockIdx.x] = cbase;
   // each half of the workgroup checks the pages it copies
   if (bad_page && lane == 0) raise_flag(kErrPageOutOfRange);
 }
@@ -1485,6 +1289,57 @@ size_t logits_schedule_bytes(int64_t T, int64_t ld) {
   return (size_t)w * kSchedInts * sizeof(int32_t);
 }
 
+// Grid of the tiled logits kernels: gx page splits per tile (the 16-row
+// kernel re-cuts each tile's own pages into gx equal ranges unless the
+// split size is forced: pps16 > 0), tiles workgroup rows (an upper bound:
+// grid rows past the last tile exit at once).
+struct TileGeometry {
+  int64_t gx, tiles;
+  int pps, pps16;
+  bool deep;                    // four pages per copy step
+};
+
+static TileGeometry tile_geometry(int64_t T, int R, int64_t max_pages,
+                                  const Options& o) {
+  TileGeometry g{};
+  g.tiles = (T + kTileRows - 1) / kTileRows + R;
+  int pps = o.tile_pages_per_split;
+  if (pps <= 0) {
+    const int64_t real_tiles = (T + kTileRows - 1) / kTileRows;
+    int64_t splits = (2048 + real_tiles - 1) / real_tiles;
+    splits = std::max<int64_t>(1, std::min<int64_t>(splits, max_pages));
+    // at least 64 pages per workgroup: a 16-wave workgroup has a
+    // noticeable start (tile lookup, q fragments, first page pair); the
+    // 1M-token tail (one tile) measured best at 64 (256 workgroups)
+    pps = (int)std::max<int64_t>(64, (max_pages + splits - 1) / splits);
+    // One 16-wave workgroup fills a compute unit, so the grid runs in
+    // rounds of `cus` workgroups and a last round that is barely used
+    // costs a whole round (a 103-tile launch with 10 splits is 4 rounds
+    // and 6 workgroups).  Among 1/2 .. 1 times the splits chosen above,
+    // take the one with the fewest rounds per unit of work, the nearest
+    // to that choice on a tie.
+    const int64_t g0 = (max_pages + pps - 1) / pps;
+    const int64_t cus = device_cu_count();
+    int64_t best = g0, br = (g0 * real_tiles + cus - 1) / cus;
+    for (int64_t g = g0 - 1; g >= (g0 + 1) / 2; --g) {
+      const int64_t r = (g * real_tiles + cus - 1) / cus;
+      if (r * best < br * g) { best = g; br = r; }   // r / g < br / best
+    }
+    if (best != g0) pps = (int)((max_pages + best - 1) / best);
+  }
+  g.pps = pps;
+  g.gx = std::max<int64_t>(1, (max_pages + pps - 1) / pps);
+  g.pps16 = o.tile_pages_per_split > 0 ? pps : 0;
+  // four pages per copy step (twice the lookahead) when the workgroups
+  // take more than two rounds of the compute units: measured faster on
+  // the prefill chunk (8 rounds); on the 1M tail (2 rounds) the step was
+  // slower
+  g.deep = o.tile_pages_per_step == 4 ||
+           (o.tile_pages_per_step == 0 &&
+            g.gx * g.tiles > 2 * (int64_t)device_cu_count());
+  return g;
+}
+
 template <int MT, bool FULL>
 static hipError_t launch_logits_mt(const LogitsArgs& a, hipStream_t stream,
                                    LogitsPlan plan, int64_t max_pages,
@@ -1530,52 +1385,23 @@ static hipError_t launch_logits_mt(const LogitsArgs& a, hipStream_t stream,
                          dim3((unsigned)a.T, (unsigned)gy), dim3(256), 0,
                          stream, a, ppw);
   } else {
-    const int64_t tiles = (a.T + kTileRows - 1) / kTileRows + a.R;
-    int pps = o.tile_pages_per_split;
-    if (pps <= 0) {
-      const int64_t real_tiles = (a.T + kTileRows - 1) / kTileRows;
-      int64_t splits = (2048 + real_tiles - 1) / real_tiles;
-      splits = std::max<int64_t>(1, std::min<int64_t>(splits, max_pages));
-      // at least 64 pages per workgroup: a 16-wave workgroup has a
-      // noticeable start (tile lookup, q fragments, first page pair); the
-      // 1M-token tail (one tile) measured best at 64 (256 workgroups)
-      pps = (int)std::max<int64_t>(64, (max_pages + splits - 1) / splits);
-      // One 16-wave workgroup fills a compute unit, so the grid runs in
-      // rounds of `cus` workgroups and a last round that is barely used
-      // costs a whole round (a 103-tile launch with 10 splits is 4 rounds
-      // and 6 workgroups).  Among 1/2 .. 1 times the splits chosen above,
-      // take the one with the fewest rounds per unit of work, the nearest
-      // to that choice on a tie.
-      const int64_t g0 = (max_pages + pps - 1) / pps;
-      const int64_t cus = device_cu_count();
-      int64_t best = g0, br = (g0 * real_tiles + cus - 1) / cus;
-      for (int64_t g = g0 - 1; g >= (g0 + 1) / 2; --g) {
-        const int64_t r = (g * real_tiles + cus - 1) / cus;
-        if (r * best < br * g) { best = g; br = r; }   // r / g < br / best
-      }
-      if (best != g0) pps = (int)((max_pages + best - 1) / best);
-    }
-    const int64_t gx = (max_pages + pps - 1) / pps;
-    // the 16-row kernel re-cuts each tile's own pages into gx equal ranges
-    // unless the split size is forced
-    const int pps16 = o.tile_pages_per_split > 0 ? pps : 0;
+    const TileGeometry tg = tile_geometry(a.T, a.R, max_pages, o);
+    const int64_t tiles = tg.tiles, gx = tg.gx;
+    const int pps = tg.pps, pps16 = tg.pps16;
+    const bool deep = tg.deep;
     const dim3 g3((unsigned)gx, (unsigned)tiles);
-    // four pages per copy step (twice the lookahead) when the workgroups
-    // take more than two rounds of the compute units: measured faster on
-    // the prefill chunk (8 rounds); on the 1M tail (2 rounds) the step was
-    // slower
-    const bool deep = o.tile_pages_per_step == 4 ||
-                      (o.tile_pages_per_step == 0 &&
-                       gx * tiles > 2 * (int64_t)device_cu_count());
     if (o.logits_kernel == 5)
-      hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL, false, 2, false>), g3,
-                         dim3(kT16Threads), 0, stream, a, pps16, 64);
+      hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL, false, 2, false, false>),
+                         g3, dim3(kT16Threads), 0, stream, a, pps16, 64,
+                         FusedTile{});
     else if (o.logits_kernel != 2 && o.logits_kernel != 3 && deep)
-      hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL, true, 4, true>), g3,
-                         dim3(kT16Threads), 0, stream, a, pps16, 64);
+      hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL, true, 4, true, false>),
+                         g3, dim3(kT16Threads), 0, stream, a, pps16, 64,
+                         FusedTile{});
     else if (o.logits_kernel != 2 && o.logits_kernel != 3)
-      hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL, true, 2, true>), g3,
-                         dim3(kT16Threads), 0, stream, a, pps16, 64);
+      hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL, true, 2, true, false>),
+                         g3, dim3(kT16Threads), 0, stream, a, pps16, 64,
+                         FusedTile{});
     else if (o.logits_kernel == 3)
       hipLaunchKernelGGL((logits_tile_direct_kernel<MT, FULL>),
                          dim3((unsigned)gx, (unsigned)tiles),
@@ -1610,6 +1436,78 @@ hipError_t launch_logits(const LogitsArgs& a, hipStream_t stream,
     case 3: return launch_logits_mt<3, false>(a, stream, plan, max_pages, sched);
     default: return launch_logits_mt<4, false>(a, stream, plan, max_pages, sched);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Tile passes of the fused forward (the default 16-row class with the
+// linear-term epilogue, whatever logits_kernel says).
+// ---------------------------------------------------------------------------
+template <typename F>
+static hipError_t with_heads(int H, F f) {
+  switch (H) {
+    case 16: return f(std::integral_constant<int, 1>(), std::true_type());
+    case 32: return f(std::integral_constant<int, 2>(), std::true_type());
+    case 48: return f(std::integral_constant<int, 3>(), std::true_type());
+    case 64: return f(std::integral_constant<int, 4>(), std::true_type());
+    default: break;
+  }
+  switch ((H + 15) / 16) {
+    case 1: return f(std::integral_constant<int, 1>(), std::false_type());
+    case 2: return f(std::integral_constant<int, 2>(), std::false_type());
+    case 3: return f(std::integral_constant<int, 3>(), std::false_type());
+    default: return f(std::integral_constant<int, 4>(), std::false_type());
+  }
+}
+
+int64_t fused_candidate_splits(const LogitsArgs& a) {
+  return tile_geometry(a.T, a.R, logits_max_pages(a), options()).gx;
+}
+
+hipError_t launch_logits_sample(const LogitsArgs& a, int page_stride,
+                                float* samp, int64_t ld_s,
+                                hipStream_t stream) {
+  if (a.T <= 0) return hipSuccess;
+  LogitsArgs s = a;
+  s.logits = samp;
+  s.out_ld = ld_s;
+  s.page_stride = page_stride;
+  const int64_t lp = (logits_max_pages(a) + page_stride - 1) / page_stride;
+  const int64_t real_tiles = (a.T + kTileRows - 1) / kTileRows;
+  // about two workgroups per compute unit, at least two logical pages each
+  const int64_t cus = device_cu_count();
+  const int64_t gx = std::max<int64_t>(
+      1, std::min<int64_t>((2 * cus + real_tiles - 1) / real_tiles,
+                           (lp + 1) / 2));
+  const dim3 g3((unsigned)gx, (unsigned)(real_tiles + a.R));
+  return with_heads(a.H, [&](auto mt, auto full) {
+    constexpr int MT = decltype(mt)::value;
+    constexpr bool FULL = decltype(full)::value;
+    hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL, true, 2, true, false>),
+                       g3, dim3(kT16Threads), 0, stream, s, 0, 2, FusedTile{});
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_logits_candidates(const LogitsArgs& a, const FusedTile& ft,
+                                    int64_t gx, hipStream_t stream) {
+  if (a.T <= 0) return hipSuccess;
+  const TileGeometry tg =
+      tile_geometry(a.T, a.R, logits_max_pages(a), options());
+  if (tg.gx != gx) return hipErrorInvalidValue;   // options changed between
+  const dim3 g3((unsigned)tg.gx, (unsigned)tg.tiles);
+  return with_heads(a.H, [&](auto mt, auto full) {
+    constexpr int MT = decltype(mt)::value;
+    constexpr bool FULL = decltype(full)::value;
+    if (tg.deep)
+      hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL, true, 4, true, true>),
+                         g3, dim3(kT16Threads), 0, stream, a, tg.pps16, 64,
+                         ft);
+    else
+      hipLaunchKernelGGL((logits_tile16_kernel<MT, FULL, true, 2, true, true>),
+                         g3, dim3(kT16Threads), 0, stream, a, tg.pps16, 64,
+                         ft);
+    return hipGetLastError();
+  });
 }
 
 // q quantisation plus, in the same launch, the decode page schedule of the

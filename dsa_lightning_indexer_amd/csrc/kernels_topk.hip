@@ -30,11 +30,13 @@
 // the row is longer than the bitmaps cover, the row falls back to a full
 // 12+12+8-bit radix select over the row.
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <type_traits>
 
 #include "dsa_common.h"
 #include "dsa_launch.h"
+#include "dsa_score.h"
 
 namespace dsa {
 
@@ -1600,6 +1602,821 @@ __global__ __launch_bounds__(kTopkThreads) void ss_select_kernel(
   reg_threshold<kTopkThreads, 4>(r, k, sh.reg, mask, thr, k_tie);
   reg_emit<kTopkThreads, 4>(r, k, mask, thr, k_tie, orow, sh.reg,
                             [&](int s, int j, int) { return (int)col[s][j]; });
+}
+
+// ---------------------------------------------------------------------------
+// Fused forward: logits and exact top-k without the [T, ld] logits buffer
+// (the GLM-5.3 cache-budget article's logits budget, section on SGLang's
+// logits budget: a score buffer of rows x columns fp32 that grows with the
+// context; here the rows never materialise).  The same lower-bound idea as
+// the sample select above, with the sample scored instead of read:
+//   sample    the tile kernel scores every SS-th page of each row (SS >= 16)
+//             into a compact buffer (logits_tile16_kernel, page_stride);
+//   threshold one workgroup per row takes the m-th largest sampled key as
+//             T_lo, m = e + 4 sqrt(e) + 16 with e = k n_s / n the expected
+//             number of sampled keys among the row's k largest (n_s sampled
+//             visible columns);
+//   score     the tile kernel scores every page again and appends every
+//             logit >= T_lo, as (key, column), to its (row, split) slot in
+//             ascending column order, with the slot's count
+//             (logits_tile16_kernel, CAND);
+//   select    one workgroup per row gathers its slots (column order) into
+//             registers and runs the register top-k on them;
+//   rescue    rows whose candidates cannot hold the answer (fewer than k,
+//             a slot overflowed, more than 16384) are re-scored whole into
+//             a per-workgroup scratch row with the tile kernel's arithmetic
+//             and ranked by the exact radix select.
+// Every key above the k-th largest is >= T_lo once the candidates number k
+// or more, and every key equal to it is a candidate too, so the selection
+// (ties lowest column first) is the exact top-k of the row's logits: the
+// sample decides the speed only.  The logits themselves are those of the
+// default tiled kernel bit for bit (same operations per logit), so the
+// result equals dsa_indexer_forward's for such a batch.
+// ---------------------------------------------------------------------------
+constexpr int kFusedMaxSplits = 2048;
+constexpr int kFusedCandMax = 4 * 4 * kTopkThreads;    // RegKeys<4>
+constexpr int kFusedMinStride = 16;
+constexpr int kFusedMaxSampledPages = 256;             // n_s <= 16384
+constexpr int kFusedRescueSlots = 64;
+
+// One sample workgroup of NT threads per row (up to 16 NT sampled
+// columns): T_lo[t] (0xffffffff for a row of at most k columns: nothing to
+// collect); workgroup 0 also clears the rescue count.
+template <int NT, int S>
+__global__ __launch_bounds__(NT) void fused_threshold_kernel(
+    const float* __restrict__ samp, int64_t ld_s,
+    const int32_t* __restrict__ positions, int plim, int SS, int k,
+    uint32_t* __restrict__ tlo, uint32_t* __restrict__ fail) {
+  __shared__ RegTopkShared<NT, S> sh;
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (t == 0 && tid == 0) fail[0] = 0u;
+  const int n = row_len_of(positions[t], plim);
+  if (n <= k) {
+    if (tid == 0) tlo[t] = 0xffffffffu;
+    return;
+  }
+  // logical pages 0..lp-1 hold real pages 0, SS, 2 SS, ..: all full but
+  // the last, whose real page may be the row's partial one
+  const int lp = ((n - 1) >> 6) / SS + 1;
+  const int ns = kPageTokens * lp;
+  const int nreal =
+      kPageTokens * (lp - 1) + min(kPageTokens, n - kPageTokens * (lp - 1) * SS);
+  const float e = (float)k * (float)nreal / (float)n;
+  const int m = min(nreal - 1, (int)(e + 4.f * sqrtf(e)) + 16);
+  if (m < 1) {                               // take every logit
+    if (tid == 0) tlo[t] = 0u;
+    return;
+  }
+  reg_clear(sh);
+  RegKeys<S, NT> r;
+  r.n = ns;                                  // the -inf tail ranks last
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(samp + t * ld_s, ns * 4);
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+        rs, 16 * tid, s * 16 * NT, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      r.key[s][j] = float_to_ordered(__uint_as_float(v[j]));
+  }
+  __syncthreads();
+  uint32_t mask, thr, k_tie;
+  reg_threshold<NT, S>(r, m, sh, mask, thr, k_tie);
+  if (tid == 0) tlo[t] = thr & mask;
+}
+
+// One workgroup per row: the row's candidate slots -> top-k, or the row
+// goes on the rescue list.
+__global__ __launch_bounds__(kTopkThreads) void fused_select_kernel(
+    const int32_t* __restrict__ positions, const int32_t* __restrict__ qsl,
+    int R, int plim, int k,
+    int32_t* __restrict__ out, int64_t out_ld,
+    const uint32_t* __restrict__ count, const uint2* __restrict__ cand,
+    int gx, int cap, int force_rescue, uint32_t* __restrict__ fail) {
+  __shared__ RegTopkShared<kTopkThreads, 4> sh;
+  __shared__ uint32_t s_pre[kFusedMaxSplits + 1];
+  __shared__ uint32_t s_flag[2];
+  const int64_t t = blockIdx.x;
+  // a row outside query_start_loc's rows is in no tile: a row of -1
+  const bool in_batch =
+      t >= load_uniform(qsl, 0) && t < load_uniform(qsl, R);
+  const int n = in_batch ? row_len_of(positions[t], plim) : 0;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  int32_t* orow = out + t * out_ld;
+  if (n <= k) {
+    topk_row_short<kTopkThreads>(n, k, orow);
+    return;
+  }
+  // slot counts -> exclusive prefix over the gx splits (two per thread)
+  const uint32_t* crow = count + t * gx;
+  const uint32_t c0 = 2 * tid < gx ? crow[2 * tid] : 0u;
+  const uint32_t c1 = 2 * tid + 1 < gx ? crow[2 * tid + 1] : 0u;
+  if (tid == 0) { s_flag[0] = 0u; s_flag[1] = 0u; }
+  __syncthreads();
+  if (c0 > (uint32_t)cap || c1 > (uint32_t)cap) s_flag[0] = 1u;  // overflow
+  const uint32_t cc = c0 + c1;
+  const uint32_t wi = wave_inclusive_scan(cc);
+  if (lane == 63) sh.wave_sum[wave] = wi;
+  __syncthreads();
+  uint32_t before = wi - cc;
+  for (int w = 0; w < wave; ++w) before += sh.wave_sum[w];
+  if (2 * tid < gx) s_pre[2 * tid] = before;
+  if (2 * tid + 1 < gx) s_pre[2 * tid + 1] = before + c0;
+  if (tid == kTopkThreads - 1) s_flag[1] = before + cc;
+  __syncthreads();
+  const uint32_t total = s_flag[1];
+  const bool rescue = force_rescue || s_flag[0] != 0u ||
+                      total < (uint32_t)k || total > (uint32_t)kFusedCandMax;
+  if (rescue) {
+    if (tid == 0) fail[1 + atomicAdd(fail, 1u)] = (uint32_t)t;
+    return;
+  }
+  reg_clear(sh);
+  // item x (list order = column order) lives in split q with s_pre[q] <= x
+  // < s_pre[q + 1]; every count is <= cap, so x - s_pre[q] < cap
+  RegKeys<4> r;
+  r.n = (int)total;
+  uint32_t col[4][4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t x = (uint32_t)(s * 4 * kTopkThreads + 4 * tid + j);
+      r.key[s][j] = 0u;
+      col[s][j] = 0u;
+      if (x < total) {
+        int lo = 0, hi = gx - 1;              // last split with s_pre <= x
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_pre[mid] <= x) lo = mid; else hi = mid - 1;
+        }
+        const uint2 e =
+            cand[(t * gx + lo) * (int64_t)cap + (x - s_pre[lo])];
+        r.key[s][j] = e.x;
+        col[s][j] = e.y;
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t mask, thr, k_tie;
+  reg_threshold<kTopkThreads, 4>(r, k, sh, mask, thr, k_tie);
+  reg_emit<kTopkThreads, 4>(r, k, mask, thr, k_tie, orow, sh,
+                            [&](int s, int j, int) { return (int)col[s][j]; });
+}
+
+// ---------------------------------------------------------------------------
+// One wave per row (sample thresholds and candidate lists of up to a few
+// thousand items): the items in registers, item x = 64 j + lane (j < KPL),
+// and a radix select with 8-bit digits over a 256-bin LDS histogram of the
+// wave's own -- no workgroup barrier, and a few hundred bytes of LDS per
+// row, so a compute unit holds many rows at once.
+// ---------------------------------------------------------------------------
+constexpr int kWaveRowsPerWg = 4;
+constexpr int kWaveMaxSplits = 16;
+
+// Maximum / minimum over the wave (every lane gets the result).
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xf, 0xf, false));
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)x, 0),
+                 (uint32_t)__builtin_amdgcn_readlane((int)x, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)x, 32),
+                 (uint32_t)__builtin_amdgcn_readlane((int)x, 48)));
+}
+__device__ __forceinline__ uint32_t wave_umin(uint32_t x) {
+  return ~wave_umax(~x);
+}
+
+// The k-th largest of the n valid items' keys (1 <= k <= n): thr, and
+// k_tie, how many of the items equal to it belong to the k largest (the
+// lowest-x ones).  Each round bins the keys of the items still in play by
+// (key - lo) >> s over [lo, hi], their smallest and largest key, in at most
+// 256 bins of a 256-bin LDS histogram of the wave's own (bins follow the
+// keys' actual spread, so few items share an LDS address: atomics to one
+// address serialise); the bin holding the k-th largest becomes the next
+// range, narrowed again to its items' smallest and largest key.
+template <int KPL>
+__device__ __forceinline__ void wave_kth_key(const uint32_t (&key)[KPL], int n, uint32_t k,
+                             uint32_t* hist, uint32_t& thr, uint32_t& k_tie) {
+  const int lane = lane_id();
+  const int jn = (n + 63) >> 6;
+  uint32_t lo = 0u, hi = 0xffffffffu, k_rem = k;
+#pragma unroll 1
+  for (int round = 0; round < 8; ++round) {
+    uint32_t a = 0xffffffffu, z = 0u;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      if (j >= jn) continue;
+      if (64 * j + lane < n && key[j] - lo <= hi - lo) {
+        a = min(a, key[j]);
+        z = max(z, key[j]);
+      }
+    }
+    lo = wave_umin(a);
+    hi = wave_umax(z);
+    thr = lo; k_tie = k_rem;
+    if (lo == hi) return;                      // every item in play is equal
+    const uint32_t range = hi - lo;
+    const int s = max(0, 24 - __builtin_clz(range));   // range >> s < 256
+    // (LDS accesses of one wave take effect in program order)
+    *reinterpret_cast<uint4*>(&hist[4 * lane]) = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      if (j >= jn) continue;
+      if (64 * j + lane < n && key[j] - lo <= range)
+        atomicAdd(&hist[(key[j] - lo) >> s], 1u);
+    }
+    // lane l holds bins 255 - 4 l down to 252 - 4 l
+    const uint4 h = *reinterpret_cast<const uint4*>(&hist[252 - 4 * lane]);
+    const uint32_t c[4] = {h.w, h.z, h.y, h.x};
+    const uint32_t local = c[0] + c[1] + c[2] + c[3];
+    const uint32_t incl = wave_inclusive_scan(local);
+    const int ls = __builtin_ctzll(__ballot(incl >= k_rem));
+    uint32_t acc = incl - local, ab = 0u, cn = 0u;
+    int jj = 0;
+    bool found = false;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (!found && acc + c[q] >= k_rem) {
+        found = true;
+        jj = q;
+        ab = acc;
+        cn = c[q];
+      }
+      acc += c[q];
+    }
+    const uint32_t b = 255u - 4u * (uint32_t)ls -
+                       (uint32_t)__builtin_amdgcn_readlane(jj, ls);
+    const uint32_t above = __builtin_amdgcn_readlane(ab, ls);
+    const uint32_t count = __builtin_amdgcn_readlane(cn, ls);
+    k_rem -= above;
+    const uint32_t blo = lo + (b << s);
+    const uint32_t bhi = s == 0 ? blo : min(hi, blo + ((1u << s) - 1u));
+    if (count == k_rem) {
+      // the whole bin is taken: keys > thr, and all k_rem ties at thr
+      // ... expressed with the bin's smallest key as thr
+      lo = blo; hi = bhi;
+      uint32_t a2 = 0xffffffffu;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        if (j >= jn) continue;
+        if (64 * j + lane < n && key[j] - lo <= hi - lo) a2 = min(a2, key[j]);
+      }
+      thr = wave_umin(a2);
+      // items equal to thr are all in the bin: all of them are taken
+      k_tie = k_rem;
+      return;
+    }
+    lo = blo; hi = bhi;
+  }
+}
+
+// Writes the selected items' col_of(j, taken) in item order (ascending x;
+// of the items equal to thr the k_tie lowest-x ones) to orow[0..k).
+// col_of is called for every j in turn, on every lane (taken: whether this
+// lane's item is written).
+template <int KPL, typename ColOf>
+__device__ __forceinline__ void wave_emit(const uint32_t (&key)[KPL], int n, uint32_t thr,
+                          uint32_t k_tie, int k, int32_t* orow, ColOf col_of) {
+  const int lane = lane_id();
+  const uint64_t below = (1ull << lane) - 1ull;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(orow, k * 4);
+  uint32_t pos = 0u, eq_seen = 0u;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    if (64 * j >= n) continue;
+    const bool ok = 64 * j + lane < n;
+    const bool gt = ok && key[j] > thr;
+    const bool eq = ok && key[j] == thr;
+    const uint64_t eqm = __ballot(eq);
+    const uint32_t er = eq_seen + (uint32_t)__popcll(eqm & below);
+    const bool take = gt || (eq && er < k_tie);
+    const uint64_t tm = __ballot(take);
+    const uint32_t slot = pos + (uint32_t)__popcll(tm & below);
+    const uint32_t col = (uint32_t)col_of(j, take);
+    __builtin_amdgcn_raw_buffer_store_b32(col, ro,
+                                          take ? (int)(4 * slot) : 4 * k, 0,
+                                          0);
+    pos += (uint32_t)__popcll(tm);
+    eq_seen += (uint32_t)__popcll(eqm);
+  }
+}
+
+// Sample thresholds, one wave per row (rows of at most 64 KPL sampled
+// columns); see fused_threshold_kernel.  Only a lower bound of the m-th
+// largest sample is needed, found on the values: a 256-bin histogram over
+// [min, max] of the finite samples, a second one over the bin holding the
+// m-th largest, and the smallest sample of the sub-bin holding it (the bin
+// of a value is a non-decreasing function of the value, so that sub-bin's
+// smallest sample is at most the m-th largest).
+template <int KPL>
+__global__ __launch_bounds__(64 * kWaveRowsPerWg) void fused_threshold_wave_kernel(
+    const float* __restrict__ samp, int64_t ld_s,
+    const int32_t* __restrict__ positions, int64_t T, int plim, int SS, int k,
+    uint32_t* __restrict__ tlo, uint32_t* __restrict__ fail) {
+  __shared__ __align__(16) uint32_t s_hist[kWaveRowsPerWg][256];
+  const int lane = lane_id();
+  const int wave = wave_uniform(threadIdx.x >> 6);
+  const int64_t t = (int64_t)blockIdx.x * kWaveRowsPerWg + wave;
+  if (blockIdx.x == 0 && threadIdx.x == 0) fail[0] = 0u;
+  if (t >= T) return;
+  const int n = row_len_of(load_uniform(positions, t), plim);
+  if (n <= k) {
+    if (lane == 0) tlo[t] = 0xffffffffu;
+    return;
+  }
+  const int lp = ((n - 1) >> 6) / SS + 1;
+  const int ns = kPageTokens * lp;
+  const int nreal =
+      kPageTokens * (lp - 1) + min(kPageTokens, n - kPageTokens * (lp - 1) * SS);
+  const float e = (float)k * (float)nreal / (float)n;
+  const int m = min(nreal - 1, (int)(e + 4.f * sqrtf(e)) + 16);
+  // the sample order does not matter here: 16-byte loads, item (j4, q) =
+  // column 256 j4 + 4 lane + q; columns past ns count as -inf
+  const int j4n = (ns + 255) >> 8;
+  float v[KPL];
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(samp + t * ld_s, ns * 4);
+#pragma unroll
+  for (int j4 = 0; j4 < KPL / 4; ++j4) {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane,
+                                                         j4 * 1024, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[4 * j4 + q] = 256 * j4 + 4 * lane + q < ns ? __uint_as_float(x[q])
+                                                   : -INFINITY;
+  }
+  uint32_t* hist = s_hist[wave];
+  float mx = -INFINITY, mn = INFINITY;
+  uint32_t nfin = 0u;
+  bool nan = false;
+#pragma unroll
+  for (int j4 = 0; j4 < KPL / 4; ++j4) {
+    if (j4 >= j4n) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float y = v[4 * j4 + q];
+      nan |= y != y;
+      if (fabsf(y) <= 3.402823466e38f) {
+        mx = fmaxf(mx, y);
+        mn = fminf(mn, y);
+        ++nfin;
+      }
+    }
+  }
+  nfin = __builtin_amdgcn_readlane(wave_inclusive_scan(nfin), 63);
+  // (ordered keys: a max / min over them is one over the values)
+  const uint32_t kmx = wave_umax(float_to_ordered(mx));
+  const uint32_t kmn = wave_umin(float_to_ordered(mn));
+  if (m < 1 || __ballot(nan) != 0ull || (uint32_t)m >= nfin) {
+    if (lane == 0) tlo[t] = 0u;                 // take every logit
+    return;
+  }
+  if (kmx == kmn) {                             // all finite samples equal
+    if (lane == 0) tlo[t] = kmn;
+    return;
+  }
+  mx = ordered_to_float(kmx);
+  mn = ordered_to_float(kmn);
+  const float scale = 256.f / (mx - mn);       // 0 if the span overflows
+  auto bin1 = [&](float y) { return min(255, (int)((y - mn) * scale)); };
+  uint32_t k_rem = (uint32_t)m, above = 0u;
+  int b1 = 0;
+  // pass 1 over the finite samples, pass 2 over those of bin b1
+#pragma unroll 1
+  for (int pass = 0; pass < 2; ++pass) {
+    *reinterpret_cast<uint4*>(&hist[4 * lane]) = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int j4 = 0; j4 < KPL / 4; ++j4) {
+      if (j4 >= j4n) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float y = v[4 * j4 + q];
+        if (!(fabsf(y) <= 3.402823466e38f)) continue;
+        const int c1 = bin1(y);
+        if (pass == 0) {
+          atomicAdd(&hist[c1], 1u);
+        } else if (c1 == b1) {
+          const int c2 =
+              min(255, max(0, (int)(((y - mn) * scale - (float)b1) * 256.f)));
+          atomicAdd(&hist[c2], 1u);
+        }
+      }
+    }
+    const uint4 h = *reinterpret_cast<const uint4*>(&hist[252 - 4 * lane]);
+    const uint32_t c[4] = {h.w, h.z, h.y, h.x};
+    const uint32_t local = c[0] + c[1] + c[2] + c[3];
+    const uint32_t incl = wave_inclusive_scan(local);
+    const int ls = __builtin_ctzll(__ballot(incl >= k_rem));
+    uint32_t acc = incl - local, ab = 0u;
+    int jj = 0;
+    bool found = false;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (!found && acc + c[q] >= k_rem) {
+        found = true;
+        jj = q;
+        ab = acc;
+      }
+      acc += c[q];
+    }
+    const int b = 255 - 4 * ls - __builtin_amdgcn_readlane(jj, ls);
+    above = __builtin_amdgcn_readlane(ab, ls);
+    k_rem -= above;
+    if (pass == 0) {
+      b1 = b;
+    } else {
+      // the smallest sample of sub-bin b of bin b1
+      float lowest = INFINITY;
+#pragma unroll
+      for (int j4 = 0; j4 < KPL / 4; ++j4) {
+        if (j4 >= j4n) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float y = v[4 * j4 + q];
+          if (!(fabsf(y) <= 3.402823466e38f) || bin1(y) != b1) continue;
+          const int c2 =
+              min(255, max(0, (int)(((y - mn) * scale - (float)b1) * 256.f)));
+          if (c2 == b) lowest = fminf(lowest, y);
+        }
+      }
+      const uint32_t kl = wave_umin(float_to_ordered(lowest));
+      if (lane == 0) tlo[t] = kl;
+    }
+  }
+}
+
+// Candidate item x of a row: in split q, the last q with pre[q] <= x (a
+// fixed four-step search over at most 16 splits).
+static_assert(kWaveMaxSplits <= 16, "four search steps");
+__device__ __forceinline__ const uint2* wave_item(const uint2* crow,
+                                                  const uint32_t* pre, int gx,
+                                                  int cap, uint32_t x) {
+  int q = 0;
+#pragma unroll
+  for (int st = 8; st >= 1; st >>= 1)
+    if (q + st < gx && pre[q + st] <= x) q += st;
+  return crow + (int64_t)q * cap + (x - pre[q]);
+}
+
+// Candidate select, one wave per row (candidate lists of at most 64 KPL
+// items, at most kWaveMaxSplits splits); see fused_select_kernel.
+template <int KPL>
+__global__ __launch_bounds__(64 * kWaveRowsPerWg) void fused_select_wave_kernel(
+    const int32_t* __restrict__ positions, const int32_t* __restrict__ qsl,
+    int R, int64_t T, int plim, int k, int32_t* __restrict__ out,
+    int64_t out_ld, const uint32_t* __restrict__ count,
+    const uint2* __restrict__ cand, int gx, int cap, int force_rescue,
+    uint32_t* __restrict__ fail) {
+  __shared__ __align__(16) uint32_t s_hist[kWaveRowsPerWg][256];
+  __shared__ uint32_t s_pre[kWaveRowsPerWg][kWaveMaxSplits + 1];
+  const int lane = lane_id();
+  const int wave = wave_uniform(threadIdx.x >> 6);
+  const int64_t t = (int64_t)blockIdx.x * kWaveRowsPerWg + wave;
+  if (t >= T) return;
+  const bool in_batch =
+      t >= load_uniform(qsl, 0) && t < load_uniform(qsl, R);
+  const int n = in_batch ? row_len_of(load_uniform(positions, t), plim) : 0;
+  int32_t* orow = out + t * out_ld;
+  if (n <= k) {
+    for (int i = lane; i < k; i += 64) orow[i] = i < n ? i : -1;
+    return;
+  }
+  // slot counts -> prefix (lane l: splits 4 l .. 4 l + 3)
+  uint32_t c[4], local = 0u;
+  bool over = false;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int x = 4 * lane + q;
+    c[q] = x < gx ? count[t * gx + x] : 0u;
+    over |= c[q] > (uint32_t)cap;
+    local += c[q];
+  }
+  const uint32_t incl = wave_inclusive_scan(local);
+  uint32_t run = incl - local;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (4 * lane + q < gx) s_pre[wave][4 * lane + q] = run;
+    run += c[q];
+  }
+  const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
+  if (force_rescue || __ballot(over) != 0ull || total < (uint32_t)k ||
+      total > 64u * KPL) {
+    if (lane == 0) fail[1 + atomicAdd(fail, 1u)] = (uint32_t)t;
+    return;
+  }
+  // (a taken item's column could be read again at the end instead of kept
+  // in registers: measured slower, the reads then wait one by one)
+  const uint2* crow = cand + t * gx * (int64_t)cap;
+  const uint32_t* pre = s_pre[wave];
+  uint32_t key[KPL], col[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const uint32_t x = (uint32_t)(64 * j + lane);
+    key[j] = 0u;
+    col[j] = 0u;
+    if (x < total) {
+      const uint2 e = *wave_item(crow, pre, gx, cap, x);
+      key[j] = e.x;
+      col[j] = e.y;
+    }
+  }
+  uint32_t thr, k_tie;
+  wave_kth_key<KPL>(key, (int)total, (uint32_t)k, s_hist[wave], thr, k_tie);
+  wave_emit<KPL>(key, (int)total, thr, k_tie, k, orow,
+                 [&](int j, bool) { return col[j]; });
+}
+
+// Rescue: workgroup b takes rows fail[1 + b], fail[1 + b + gridDim.x], ..
+// of the list's fail[0].  Each of its 16 waves scores pages w, w + 16, ..
+// of the row into the workgroup's scratch row with the operations the
+// 16-row tile kernel applies to that row.  The row's place in its tile
+// (wave w of the tile, w = row - tile start, tiles of 16 rows from the
+// request's first row) fixes the order of the N-tiles in the head
+// reduction; the linear term's MFMA gets the same A operand as in the tile
+// -- the pieces of all four rows of the row's group of four (rows of the
+// tile past its end, or with a position the tile does not score, are zero
+// there as in the tile), since its outputs are not bit-independent of the
+// other A rows.  Then the exact radix select over the scratch row.
+template <int MT, bool FULL>
+__global__ __launch_bounds__(kTopkThreads) void fused_rescue_kernel(
+    LogitsArgs a, int plim, int k, int32_t* __restrict__ out, int64_t out_ld,
+    const uint32_t* __restrict__ fail, float* __restrict__ scratch) {
+  __shared__ TopkShared sh;
+  __shared__ __align__(16) uint8_t s_alin[2048];
+  __shared__ __align__(16) float s_asc[4][kLinPieces];
+  __shared__ float s_lv[kTopkWaves][kPageTokens];
+  const uint32_t nf = fail[0];
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = wave_uniform(tid >> 6);
+  const int i16 = lane & 15, g = lane >> 4;
+  float* srow = scratch + (int64_t)blockIdx.x * a.ld;
+  for (uint32_t i = blockIdx.x; i < nf; i += gridDim.x) {
+    const int64_t t = wave_uniform((int)fail[1 + i]);
+    int32_t* orow = out + t * out_ld;
+    const int n = row_len_of(a.positions[t], plim);
+    // the request holding row t: the last r with qsl[r] <= t
+    int lo = 0, hi = a.R - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (load_uniform(a.qsl, mid) <= t) lo = mid; else hi = mid - 1;
+    }
+    const int q0 = load_uniform(a.qsl, lo);
+    const int q1 = load_uniform(a.qsl, lo + 1);
+    if (n <= k || t < q0 || t >= q1) {
+      // not a row the tile kernel scores: no candidates to rank
+      for (int j = tid; j < k; j += kTopkThreads) orow[j] = -1;
+      continue;
+    }
+    const int p = n - 1;
+    const int64_t row0 = q0 + (t - q0) / kTileRows * kTileRows;
+    const int tw = (int)(t - row0);            // the row's wave in its tile
+    const int wq = tw & 3;
+    // the group's linear-term operand: waves 0..3 split the pieces of rows
+    // 4 (tw / 4) + wave of the tile
+    if (tid < 128)
+      *reinterpret_cast<uint4*>(&s_alin[16 * tid]) = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    if (wave < 4) {
+      const int gw = (tw & ~3) + wave;
+      const int64_t tg = row0 + gw;
+      bool valid = gw < q1 - row0 && tg < a.T;
+      if (valid) {
+        const int pg = load_uniform(a.positions, tg);
+        valid = !(pg < 0 || pg >= a.ld || (int64_t)(pg >> 6) >= a.bt_stride);
+      }
+      if (valid) {
+        i32x8 qg[MT];
+        load_q_frags_cm<MT, FULL>(a.q8 + tg * a.H * kHeadDim, a.H, qg);
+        float wa[MT];
+        load_a_weights<MT, FULL>(a.weights + tg * a.H, a.q_scale + tg * a.H,
+                                 a.H, wa);
+        const float2 ql = row_qlin<MT>(qg, wa);
+        split_pieces(ql.x, ql.y, wave, &s_alin[0], &s_asc[wave][0]);
+      }
+    }
+    __syncthreads();
+    i32x8 alin;
+    {
+      const uint4 x = *reinterpret_cast<const uint4*>(&s_alin[16 * lane]);
+      const uint4 y = *reinterpret_cast<const uint4*>(&s_alin[16 * lane + 1024]);
+      alin = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w,
+                   (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+    }
+    const float4 lsc = *reinterpret_cast<const float4*>(&s_asc[wq][0]);
+    i32x8 qa[MT];
+    load_q_frags_cm<MT, FULL>(a.q8 + t * a.H * kHeadDim, a.H, qa);
+    float w[MT][4];
+    load_head_weights<MT, FULL>(a.weights + t * a.H, a.q_scale + t * a.H,
+                                a.H, w);
+    const int tok = 16 * ((wq + g) & 3) + i16;
+    const int32_t* bt = a.block_table + (int64_t)lo * a.bt_stride;
+    for (int jp = wave; jp <= (p >> 6); jp += kTopkWaves) {
+      const int page = load_uniform(bt, jp);
+      const bool ok = page >= 0 && (int64_t)page < a.num_pages;
+      const uint8_t* pg = a.k_cache + (int64_t)(ok ? page : 0) * kPageBytes;
+      // N-tile (wq + nt) mod 4 in turn (a rolled loop: few registers live);
+      // its head sum, the same FMA chain as head_reduce_abs, into v[nt]
+      float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
+#pragma unroll 1
+      for (int nt = 0; nt < 4; ++nt) {
+        const int nn = (wq + nt) & 3;
+        const uint8_t* src = pg + (16 * nn + i16) * kHeadDim + 16 * g;
+        const uint4 x = *reinterpret_cast<const uint4*>(src);
+        const uint4 y = *reinterpret_cast<const uint4*>(src + 64);
+        const i32x8 kb = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w,
+                               (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+        float vv = 0.f;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const f32x4 acc =
+              mfma16x16x128_fp8(qa[m], kb, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int j = 0; j < 4; ++j) vv = fmaf(w[m][j], fabsf(acc[j]), vv);
+        }
+        const f32x4 lin =
+            mfma16x16x128_fp8(alin, kb, f32x4{0.f, 0.f, 0.f, 0.f});
+        const float lval = fmaf(lsc.w, lin[3],
+                           fmaf(lsc.z, lin[2],
+                           fmaf(lsc.y, lin[1], lsc.x * lin[0])));
+        if (g == wq) s_lv[wave][16 * nn + i16] = lval;
+        v0 = nt == 0 ? vv : v0;
+        v1 = nt == 1 ? vv : v1;
+        v2 = nt == 2 ? vv : v2;
+        v3 = nt == 3 ? vv : v3;
+      }
+      const float tot = reduce_scatter4(v0, v1, v2, v3);
+      const float lv = s_lv[wave][tok];
+      const float ks =
+          ok ? *reinterpret_cast<const float*>(pg + kPageKeyBytes + 4 * tok)
+             : 0.f;
+      const int s = jp * kPageTokens + tok;
+      srow[s] = (s <= p && ok) ? (tot + lv) * ks : -INFINITY;
+    }
+    // the row's logits, written by every wave, become visible to all
+    __threadfence();
+    __syncthreads();
+    const RowKeys keys{srow, nullptr, 0};
+    radix_pass<kHistBins>(keys, n, 0u, 0u, 20, (uint32_t)k, sh);
+    topk_radix_rest(keys, n, k, orow, sh);
+    __syncthreads();
+  }
+}
+
+// Workspace of the fused forward after the q codes and scales.
+struct FusedLayout {
+  int64_t gxm;          // page splits per tile the slots are sized for
+  int64_t ld_s;         // sampled columns per row
+  int cap;              // candidates per (row, split) slot
+  int slots;            // rescue scratch rows
+  size_t samp, tlo, count, cand, fail, scr, total;    // byte offsets
+};
+
+static FusedLayout fused_layout(int64_t T, int64_t ld, int k) {
+  FusedLayout L{};
+  const int64_t P = ld / kPageTokens;
+  const int64_t rt = (T + kTileRows - 1) / kTileRows;
+  // the candidate pass's splits never exceed this (tile grid rule)
+  L.gxm = std::max<int64_t>(
+      1, std::min<int64_t>((2048 + rt - 1) / rt, (P + 63) / 64));
+  L.ld_s = (int64_t)kPageTokens *
+           std::min<int64_t>(kFusedMaxSampledPages,
+                             (P + kFusedMinStride - 1) / kFusedMinStride);
+  // a split covers at least 64 pages; a row's candidates number about k
+  // plus a few standard deviations, all of them in one split for a row no
+  // longer than it
+  const int64_t split_cols =
+      (int64_t)kPageTokens * std::max<int64_t>(64, (P + L.gxm - 1) / L.gxm);
+  const int64_t want = std::max<int64_t>(2048, ((2 * (int64_t)k + 255) / 256) * 256);
+  // (more than kFusedCandMax candidates in a row go to the rescue anyway)
+  L.cap = (int)std::min<int64_t>(std::min<int64_t>(split_cols, want),
+                                 kFusedCandMax);
+  L.slots = (int)std::min<int64_t>(T, kFusedRescueSlots);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  L.samp = take((size_t)T * L.ld_s * 4);
+  L.tlo = take((size_t)T * 4);
+  L.count = take((size_t)T * L.gxm * 4);
+  L.cand = take((size_t)T * L.gxm * L.cap * 8);
+  L.fail = take((size_t)(T + 1) * 4);
+  L.scr = take((size_t)L.slots * ld * 4);
+  L.total = off;
+  return L;
+}
+
+size_t fused_workspace_bytes(int64_t T, int64_t ld, int k) {
+  if (T <= 0 || ld <= 0) return 0;
+  return fused_layout(T, ld, k).total;
+}
+
+hipError_t launch_forward_fused(const ForwardArgs& f, void* ws,
+                                hipStream_t stream) {
+  const LogitsArgs& a = f.lg;
+  const int64_t T = a.T;
+  if (T <= 0) return hipSuccess;
+  const int k = f.tk.k;
+  const FusedLayout L = fused_layout(T, a.ld, k);
+  char* base = static_cast<char*>(ws);
+  float* samp = reinterpret_cast<float*>(base + L.samp);
+  uint32_t* tlo = reinterpret_cast<uint32_t*>(base + L.tlo);
+  uint32_t* count = reinterpret_cast<uint32_t*>(base + L.count);
+  uint2* cand = reinterpret_cast<uint2*>(base + L.cand);
+  uint32_t* fail = reinterpret_cast<uint32_t*>(base + L.fail);
+  float* scr = reinterpret_cast<float*>(base + L.scr);
+  const Options o = options();
+  const int64_t max_pages = std::min<int64_t>(a.bt_stride, a.ld / kPageTokens);
+  // every 32nd page unless set: about 1/32 of the scoring, and about
+  // k + 48 * 32 candidates per long row (the sample rule below)
+  int64_t SS = o.fused_sample_stride > 0 ? o.fused_sample_stride
+                                         : 2 * kFusedMinStride;
+  SS = std::max<int64_t>(SS, (max_pages + kFusedMaxSampledPages - 1) /
+                                 kFusedMaxSampledPages);
+  const int64_t gx = fused_candidate_splits(a);
+  if (gx < 1 || gx > L.gxm) return hipErrorInvalidValue;
+  int cap = L.cap;
+  if (o.fused_cand_cap > 0) cap = std::min(cap, o.fused_cand_cap);
+  const int plim = pos_limit(f.tk);
+
+  hipError_t e = launch_quantize_q(f.q_bf16, T * a.H, f.q8, f.q_scale, stream);
+  if (e == hipSuccess)
+    e = launch_logits_sample(a, (int)SS, samp, L.ld_s, stream);
+  if (e != hipSuccess) return e;
+  const unsigned wgs = (unsigned)((T + kWaveRowsPerWg - 1) / kWaveRowsPerWg);
+  // sampled columns of the longest row: 64 * ceil(max_pages / SS)
+  const int64_t ns_max =
+      (int64_t)kPageTokens * ((max_pages + SS - 1) / SS);
+#define DSA_THR_WAVE(KPL)                                                     \
+    hipLaunchKernelGGL(fused_threshold_wave_kernel<KPL>, dim3(wgs),           \
+                       dim3(64 * kWaveRowsPerWg), 0, stream, samp, L.ld_s,    \
+                       a.positions, T, plim, (int)SS, k, tlo, fail);
+  if (ns_max <= 64 * 16) { DSA_THR_WAVE(16) }
+  else if (ns_max <= 64 * 40) { DSA_THR_WAVE(40) }
+  else if (ns_max <= 64 * 64) { DSA_THR_WAVE(64) }
+#undef DSA_THR_WAVE
+  else
+    hipLaunchKernelGGL((fused_threshold_kernel<kTopkThreads, 4>),
+                       dim3((unsigned)T), dim3(kTopkThreads), 0, stream, samp,
+                       L.ld_s, a.positions, plim, (int)SS, k, tlo, fail);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  FusedTile ft;
+  ft.tlo = tlo;
+  ft.cand = cand;
+  ft.count = count;
+  ft.cap = cap;
+  if ((e = launch_logits_candidates(a, ft, gx, stream)) != hipSuccess)
+    return e;
+  // a row's candidates number about k + (4 sqrt(k / SS) + 16) SS (the
+  // sample rule; 4 standard deviations and more below the wave kernels'
+  // capacity)
+  const double c_est =
+      k + (4.0 * std::sqrt((double)k / (double)SS) + 16.0) * (double)SS;
+  const int force = o.fused_force_rescue ? 1 : 0;
+  // (the wave kernel finds an item's split by a binary search over the
+  // splits: for few splits only)
+  if (gx <= kWaveMaxSplits && c_est <= 0.8 * 64 * 64)
+    hipLaunchKernelGGL(fused_select_wave_kernel<64>, dim3(wgs),
+                       dim3(64 * kWaveRowsPerWg), 0, stream, a.positions,
+                       a.qsl, a.R, T, plim, k, f.tk.out, f.tk.out_ld, count,
+                       cand, (int)gx, cap, force, fail);
+  else if (gx <= kWaveMaxSplits && c_est <= 0.8 * 64 * 80)
+    hipLaunchKernelGGL(fused_select_wave_kernel<80>, dim3(wgs),
+                       dim3(64 * kWaveRowsPerWg), 0, stream, a.positions,
+                       a.qsl, a.R, T, plim, k, f.tk.out, f.tk.out_ld, count,
+                       cand, (int)gx, cap, force, fail);
+  else
+    hipLaunchKernelGGL(fused_select_kernel, dim3((unsigned)T),
+                       dim3(kTopkThreads), 0, stream, a.positions, a.qsl, a.R,
+                       plim, k, f.tk.out, f.tk.out_ld, count, cand, (int)gx,
+                       cap, force, fail);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const dim3 rg((unsigned)L.slots);
+  auto rescue = [&](auto mt, auto full) {
+    constexpr int MT = decltype(mt)::value;
+    constexpr bool FULL = decltype(full)::value;
+    hipLaunchKernelGGL((fused_rescue_kernel<MT, FULL>), rg,
+                       dim3(kTopkThreads), 0, stream, a, plim, k, f.tk.out,
+                       f.tk.out_ld, fail, scr);
+  };
+  switch (a.H) {
+    case 16: rescue(std::integral_constant<int, 1>(), std::true_type()); break;
+    case 32: rescue(std::integral_constant<int, 2>(), std::true_type()); break;
+    case 48: rescue(std::integral_constant<int, 3>(), std::true_type()); break;
+    case 64: rescue(std::integral_constant<int, 4>(), std::true_type()); break;
+    default:
+      switch ((a.H + 15) / 16) {
+        case 1: rescue(std::integral_constant<int, 1>(), std::false_type()); break;
+        case 2: rescue(std::integral_constant<int, 2>(), std::false_type()); break;
+        case 3: rescue(std::integral_constant<int, 3>(), std::false_type()); break;
+        default: rescue(std::integral_constant<int, 4>(), std::false_type()); break;
+      }
+  }
+  return hipGetLastError();
 }
 
 size_t topk_workspace_bytes(int64_t T, int64_t ld, int k) {

@@ -299,6 +299,45 @@ size_t dsa_forward_chunked_workspace_size(int64_t T, int R, int H, int64_t ld,
                                           int k, int64_t rows_per_chunk);
 
 /*
+ * dsa_indexer_forward_fused -- the forward pass without a logits buffer
+ * ([KVB], SGLang logits budget: the fp32 score buffer of rows x columns that
+ * the budget bounds is never written; the context is cut into page splits,
+ * each keeps only its candidates for the row's top-k, and the candidates
+ * are merged and ranked).  Arguments as for dsa_indexer_forward, except:
+ *   (no logits argument)
+ *   workspace  device, dsa_forward_fused_workspace_size(T, R, H, ld, k)
+ *              bytes; contents on entry do not matter.
+ * A tiled batch (T > 2 R: prefill chunks, query rows over long contexts) is
+ * scored twice by the default tiled kernel: once over every 32nd page (the
+ * fused_sample_stride option: 16, 32 or 64; sparser when a row would have
+ * more than 256 sampled pages), whose logits give each
+ * row a lower bound of its k-th largest logit, then over every page, keeping
+ * only the (logit, position) pairs at or above that bound, per row and page
+ * split in position order.  The row's top-k is then selected from those
+ * pairs.  When they cannot hold the answer (fewer than k, a split's slot
+ * full, more than 16384), the row is scored again whole, with the same
+ * arithmetic, into a scratch row of the workspace, and ranked from there.
+ * Either way out holds exactly the top-k of the logits the default tiled
+ * kernel computes: dsa_indexer_forward's rows bit for bit, when that call
+ * uses the default kernel for the batch.  Other batches (T <= 2 R) run
+ * dsa_indexer_forward with the logits in the workspace.  Errors as for
+ * dsa_indexer_forward; DSA_ERR_UNSUPPORTED when the tile_pages_per_split
+ * option cuts the pages into more splits than the workspace was sized for.
+ * Rows outside query_start_loc's rows get -1.
+ */
+int dsa_indexer_forward_fused(const void* q_bf16, const float* weights,
+                              const uint8_t* k_cache, int64_t num_pages,
+                              const int32_t* block_table, int64_t bt_stride,
+                              const int32_t* query_start_loc,
+                              const int32_t* positions, int64_t T, int R,
+                              int H, int head_dim, int page_size, int64_t ld,
+                              int k, int32_t* out, int64_t out_ld,
+                              void* workspace, size_t ws_bytes, void* stream);
+
+size_t dsa_forward_fused_workspace_size(int64_t T, int R, int H, int64_t ld,
+                                        int k);
+
+/*
  * dsa_index_cache_mask -- IndexCache layer rule ([IC] 3, 4, 5.3), host only.
  *   pattern            host, nullable: one 'F'/'S' per DSA layer; overrides
  *                      freq when non-NULL; layers past its end are F.
@@ -503,7 +542,12 @@ int dsa_device_error_flags(int reset);
  * workgroups per compute unit when the rows outnumber the compute units; 1
  * always the former, 4 always the latter; 2 keys cached in LDS; rows longer
  * than 65536 columns: 3 multi-workgroup radix select instead of sample
- * select).
+ * select), and for dsa_indexer_forward_fused "fused_sample_stride" (sample
+ * every 16th, 32nd or 64th page, default 32; more sparsely when a row would
+ * have more than 256 sampled pages), "fused_cand_cap" (n: at most n candidates per
+ * row and page split; rows that overflow are re-scored) and
+ * "fused_force_rescue" (1: every row of more than k columns is re-scored;
+ * the result must not change).
  */
 int dsa_set_option(const char* key, int value);
 
