@@ -16,7 +16,9 @@ adds one record per other workload of the metric: ``prefill`` (8192 queries
 against a 40960-token cache: the FP8-MFMA-bound chunk), ``long`` (16 rows
 at the end of a 1M-token cache) and ``index_cache`` (61-layer stacks at
 freq 4, a seeded pattern and freq 1); ``--only`` measures the chosen
-``--config`` alone.
+``--config`` alone.  The tiled workloads (prefill, long) also time the fused
+forward (dsa_indexer_forward_fused: no logits buffer), after checking that
+its top-k equals the forward's bit for bit.
 
 Timing: inputs are resident in HBM before the timed region.  R copies of the
 K cache (and of q / weights) rotate across steps so that consecutive steps do
@@ -633,6 +635,41 @@ def measure_workload(args, name, K, W, extras=False, cpu=True,
         rec["topk_mask_gbs"] = round(T * ld * 4 / (kmask * 1e-3) / 1e9, 1)
         rec["k_write_gbs"] = round(T * (2 * 128 + 8 + 132) /
                                    (kkw * 1e-3) / 1e9, 1)
+    if T > 2 * b.R:
+        # The fused forward (no logits buffer) on the same batch: its top-k
+        # must equal the forward's bit for bit; then a graph of K fused
+        # steps, timed like the forward's.
+        fu_ws = torch.empty(binding.dsa_forward_fused_workspace_size(
+            T, b.R, H, ld, k), dtype=torch.uint8, device=dev)
+        fu_out = torch.empty((T, k), dtype=torch.int32, device=dev)
+
+        def fused(r):
+            binding.dsa_indexer_forward_fused(
+                qs_in[r], ws_in[r], kcs[r], bt, qsl, pos, ld, k, out=fu_out,
+                workspace=fu_ws)
+
+        def fused_step(r):
+            binding.dsa_index_cache_mask(1)
+            fused(r)
+
+        forward(0)
+        fused(0)
+        torch.cuda.synchronize()
+        if not torch.equal(fu_out, buf):
+            raise SystemExit("fused forward differs from the forward")
+        ms_fused, again_fused = _graph_steps(torch, fused_step, K, R, W,
+                                             fu_out, fused_step)
+        kernels["forward_fused"] = round(_timed(torch, fused, NK, R), 5)
+        rec["fused"] = {
+            "ms_per_step": round(ms_fused, 5),
+            "ms_per_step_more_replays": again_fused,
+            "value": round(T / (ms_fused * 1e-3), 1),
+            "unit": "query-rows/s",
+            "speedup_vs_forward": round(ms_step / ms_fused, 4),
+            "topk_equal_to_forward": True,
+            "workspace_bytes": int(fu_ws.numel()),
+            "logits_bytes_not_written": int(T * ld * 4)}
+        del fu_ws
     assert binding.dsa_device_error_flags(reset=True) == 0
 
     alg_bytes, flops = logits_work(b)

@@ -93,6 +93,7 @@ struct Options {
   int fused_sample_stride = 0;  // fused forward: sample every n-th page (0: 32; 16, 32, 64)
   int fused_cand_cap = 0;       // fused forward: candidates per (row, split) slot (0 auto; n: at most n)
   int fused_force_rescue = 0;   // fused forward: 1 re-scores every row of more than k columns
+  int fused_select = 0;         // fused forward: candidate select kernel (0 auto, 1/2 one wave per row with 64/80 items per lane (16 splits or fewer), 3 1024-thread workgroup per row)
 };
 Options options();
 

@@ -2377,14 +2377,19 @@ hipError_t launch_forward_fused(const ForwardArgs& f, void* ws,
   const double c_est =
       k + (4.0 * std::sqrt((double)k / (double)SS) + 16.0) * (double)SS;
   const int force = o.fused_force_rescue ? 1 : 0;
-  // (the wave kernel finds an item's split by a binary search over the
-  // splits: for few splits only)
-  if (gx <= kWaveMaxSplits && c_est <= 0.8 * 64 * 64)
+  // one wave per row (its items found by a four-step search over at most
+  // 16 splits) when the list fits 80 % of its capacity, else the
+  // 1024-thread workgroup (measured on the prefill chunk: 0.12-0.16 ms
+  // against 0.27 ms; a 256-thread workgroup per row with the wave kernel's
+  // range-adaptive digits measured 0.24 ms)
+  const int qsel = o.fused_select;
+  const bool wave_ok = gx <= kWaveMaxSplits;
+  if (wave_ok && (qsel == 1 || (qsel == 0 && c_est <= 0.8 * 64 * 64)))
     hipLaunchKernelGGL(fused_select_wave_kernel<64>, dim3(wgs),
                        dim3(64 * kWaveRowsPerWg), 0, stream, a.positions,
                        a.qsl, a.R, T, plim, k, f.tk.out, f.tk.out_ld, count,
                        cand, (int)gx, cap, force, fail);
-  else if (gx <= kWaveMaxSplits && c_est <= 0.8 * 64 * 80)
+  else if (wave_ok && (qsel == 2 || (qsel == 0 && c_est <= 0.8 * 64 * 80)))
     hipLaunchKernelGGL(fused_select_wave_kernel<80>, dim3(wgs),
                        dim3(64 * kWaveRowsPerWg), 0, stream, a.positions,
                        a.qsl, a.R, T, plim, k, f.tk.out, f.tk.out_ld, count,

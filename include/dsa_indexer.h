@@ -545,9 +545,12 @@ int dsa_device_error_flags(int reset);
  * select), and for dsa_indexer_forward_fused "fused_sample_stride" (sample
  * every 16th, 32nd or 64th page, default 32; more sparsely when a row would
  * have more than 256 sampled pages), "fused_cand_cap" (n: at most n candidates per
- * row and page split; rows that overflow are re-scored) and
+ * row and page split; rows that overflow are re-scored),
  * "fused_force_rescue" (1: every row of more than k columns is re-scored;
- * the result must not change).
+ * the result must not change) and "fused_select" (candidate selection: 1
+ * or 2 one wave per row with up to 4096 / 5120 candidates, when the batch
+ * has at most 16 page splits per tile; 3 one 1024-thread workgroup per
+ * row).
  */
 int dsa_set_option(const char* key, int value);
 

@@ -20,7 +20,7 @@ pytestmark = [pytest.mark.gpu,
                                  reason="needs a GPU")]
 
 FUSED_OPTIONS = ("fused_sample_stride", "fused_cand_cap",
-                 "fused_force_rescue")
+                 "fused_force_rescue", "fused_select")
 
 
 def _say(msg):
@@ -74,8 +74,11 @@ VARIANTS = {
     "candidates": {},
     "forced_rescue": {"fused_force_rescue": 1},
     "slot_overflow": {"fused_cand_cap": 8},
-    "stride32": {"fused_sample_stride": 32},
+    "stride16": {"fused_sample_stride": 16},
     "stride64": {"fused_sample_stride": 64},
+    "select_wave64": {"fused_select": 1},
+    "select_wave80": {"fused_select": 2},
+    "select_block": {"fused_select": 3},
 }
 
 
@@ -186,15 +189,21 @@ def test_workspace_is_smaller_than_the_logits_it_replaces():
 
 
 def test_full_size_prefill():
-    """The 8192 x 40960 prefill chunk: candidate path and forced rescue both
-    bit-identical to the forward; 16 evenly spaced rows against the
-    oracle."""
+    """The 8192 x 40960 prefill chunk: candidate path (every select kernel,
+    sample strides 16 and 64) and forced rescue all bit-identical to the
+    forward; 16 evenly spaced rows against the oracle."""
     _say("case: fused full-size prefill")
     b = synth.prefill()
     d = parity.upload(b)
     ref = _forward(d, b)
     out = _fused(d, b)
     assert torch.equal(out, ref)
+    for sel in (1, 2, 3):
+        _say(f"case: fused full-size prefill, select kernel {sel}")
+        assert torch.equal(_fused(d, b, fused_select=sel), ref)
+    for ss in (16, 64):
+        _say(f"case: fused full-size prefill, sample stride {ss}")
+        assert torch.equal(_fused(d, b, fused_sample_stride=ss), ref)
     _say("case: fused full-size prefill, forced rescue")
     assert torch.equal(_fused(d, b, fused_force_rescue=1), ref)
     assert binding.dsa_device_error_flags(reset=True) == 0
