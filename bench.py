@@ -139,12 +139,14 @@ def logits_work(b):
 def dominant_kernel(b):
     """(Name prefix, name part) of the step's logits kernel as the profiler
     prints it: a decode batch's forward scores with its page schedule (the
-    instance whose last template argument is true)."""
+    instance whose last template argument is true); a tiled batch's forward
+    with the tile kernel that writes logits (last template argument false:
+    true is the fused forward's candidate pass)."""
     if b.T <= 128 and b.T <= 2 * b.R:
         return "logits_balanced_kernel<", ", true>"
     if b.T <= 2 * b.R:
         return "logits_row_prefetch_kernel<", ""
-    return "logits_tile16_kernel<", ""
+    return "logits_tile16_kernel<", ", false>"
 
 
 def host_cpu():
@@ -309,6 +311,31 @@ def pmc_summary(args):
     f_cal, w_cal = calib(fetch), calib(write)
     f_ff = CALIBRATION_BYTES / (f_cal * 1024.0)
     w_ff = CALIBRATION_BYTES / (w_cal * 1024.0)
+
+    def every_kernel(directory):
+        # per (kernel, grid): dispatches and average KiB per dispatch
+        acc = {}
+        per = {}
+        for r in _csv_rows(directory, "counter_collection.csv"):
+            k = (r["Dispatch_Id"], r["Kernel_Name"], int(r["Grid_Size"]))
+            per[k] = per.get(k, 0.0) + float(r["Counter_Value"])
+        for (_, name, g), v in per.items():
+            if "dsa::" not in name:
+                continue
+            a = acc.setdefault((name, g), [0, 0.0])
+            a[0] += 1
+            a[1] += v
+        return {k: (n, v / n) for k, (n, v) in acc.items()}
+
+    ef, ew = every_kernel(args.pmc_summary[0]), every_kernel(args.pmc_summary[1])
+    kernels_kib = []
+    for (name, g) in sorted(ef, key=lambda x: -ef[x][1]):
+        n, fk = ef[(name, g)]
+        wk = ew.get((name, g), (0, 0.0))[1]
+        kernels_kib.append({
+            "kernel": name, "grid": g, "dispatches": n, "fetch_kib": round(fk, 1),
+            "write_kib": round(wk, 1),
+            "hbm_bytes": int(round(fk * 1024 * f_ff + wk * 1024 * w_ff))})
     f_kib, nf, names = logits(fetch)
     w_kib, nw, _ = logits(write)
     bench = None
@@ -333,6 +360,7 @@ def pmc_summary(args):
                                               w_kib * 1024 * w_ff)),
         "algorithmic_bytes_per_launch":
             bench["roofline"]["algorithmic_bytes"] if bench else None,
+        "every_kernel_per_dispatch": kernels_kib,
         "commands": args.command,
     }
     print(json.dumps(out, indent=1))
@@ -454,6 +482,33 @@ def trace_summary(args):
                   f"leg): `{n}`, "
                   f"{len(d)} dispatches, average {sum(d) / len(d):.3f} us, "
                   f"median {d[len(d) // 2]:.3f} us."]
+    # back-to-back dispatches of the dominant kernel (the per-kernel event
+    # loop): the idle time from one's end to the next one's start, which a
+    # HIP-event average over the loop includes and a dispatch duration not
+    seq = sorted(trace, key=lambda r: int(r["Start_Timestamp"]))
+
+    def grid_of(r):
+        return (int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) *
+                int(r["Grid_Size_Z"]))
+
+    pairs = []
+    for a_, b_ in zip(seq, seq[1:]):
+        if (is_dom(a_["Kernel_Name"]) and a_["Kernel_Name"] == b_["Kernel_Name"]
+                and grid_of(a_) == grid_of(b_) ==
+                top.get(_base_name(a_["Kernel_Name"]), -1)):
+            dur = (int(a_["End_Timestamp"]) - int(a_["Start_Timestamp"])) / 1e3
+            gap = (int(b_["Start_Timestamp"]) - int(a_["End_Timestamp"])) / 1e3
+            pairs.append((dur, gap))
+    if pairs:
+        gaps = sorted(g for _, g in pairs)
+        per = sorted(d + g for d, g in pairs)
+        lines += ["", f"Back-to-back dispatches of the dominant kernel at its "
+                  f"largest grid: {len(pairs)} pairs; gap from one dispatch's "
+                  f"end to the next one's start: median "
+                  f"{gaps[len(gaps) // 2]:.3f} us (min {gaps[0]:.3f}, max "
+                  f"{gaps[-1]:.3f}); duration + gap: median "
+                  f"{per[len(per) // 2]:.3f} us (what a HIP-event average "
+                  f"over back-to-back launches measures)."]
     if args.bench_log:
         with open(args.bench_log) as f:
             for line in f:

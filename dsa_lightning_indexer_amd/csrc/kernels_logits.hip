@@ -724,39 +724,24 @@ constexpr int kT16Waves = 16;
 constexpr int kT16Threads = 64 * kT16Waves;
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Direct-to-LDS buffer loads (lane l's SIZE bytes from base + voff land at
-// LDS address lds + SIZE * l), issued through inline assembly so that the
-// compiler does not track them: it cannot tell a copy into one LDS buffer
-// from reads of the other and would wait for the copy before every read.
-// The caller makes the data visible itself (vmcnt(0), then a barrier).
-// base, bytes and lds are wave-uniform; reads at or past `bytes` return 0.
+// LDS address lds + SIZE * l) through the compiler's builtin, which sets m0
+// itself.  (An earlier inline-assembly version wrote m0 behind the
+// compiler's back; the builtin measured as fast, logits bit-identical.)  The
+// caller makes the data visible itself (vmcnt(0), then a barrier).  base,
+// bytes and lds are wave-uniform; reads at or past `bytes` return 0.
 template <int SIZE>
 __device__ __forceinline__ void lds_copy(const void* base, int bytes,
                                          const void* lds, int voff) {
   static_assert(SIZE == 4 || SIZE == 16, "copy size");
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  u32x4 d;                                   // raw buffer resource
-  d[0] = __builtin_amdgcn_readfirstlane((uint32_t)b);
-  d[1] = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xffffu);
-  d[2] = __builtin_amdgcn_readfirstlane((uint32_t)bytes);
-  d[3] = 0x00020000u;
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const lds_u8*)lds);
-  // m0 is a reserved register, so the compiler warns that the clobber below
-  // may be ignored: it would then assume m0 unchanged.  The kernels that use
-  // this copy contain no compiler-generated read of m0 (their only m0
-  // writes are these, each read by the copy in the same statement).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-  if (SIZE == 16)
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(d), "s"(m0) : "memory", "m0");
+  typedef __attribute__((address_space(3))) void lds_void;
+  lds_void* dst = (lds_void*)(const lds_u8*)lds;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(base, bytes);
+  if constexpr (SIZE == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
   else
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(d), "s"(m0) : "memory", "m0");
-#pragma clang diagnostic pop
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, voff, 0, 0, 0);
 }
 
 //

@@ -14,7 +14,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
-TILE = "void dsa::logits_tile16_kernel<1, false, true, 2, true>(dsa::LogitsArgs, int, int)"
+TILE = ("void dsa::logits_tile16_kernel<1, false, true, 2, true, false>"
+        "(dsa::LogitsArgs, int, int, dsa::FusedTile)")
+# the fused forward's candidate pass: the same kernel and grid, not the
+# forward's logits launch
+CAND = ("void dsa::logits_tile16_kernel<1, false, true, 2, true, true>"
+        "(dsa::LogitsArgs, int, int, dsa::FusedTile)")
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -54,6 +59,9 @@ def _pmc_dir(tmp, name, cal_kib, big, small):
                 rows.append(dict(Dispatch_Id=d, Kernel_Name=TILE,
                                  Grid_Size=grid, Counter_Name="X",
                                  Counter_Value=v * half))
+    d += 1
+    rows.append(dict(Dispatch_Id=d, Kernel_Name=CAND, Grid_Size=1 << 20,
+                     Counter_Name="X", Counter_Value=1e6))
     p = tmp / name
     p.mkdir()
     _write(p / "x_counter_collection.csv", rows)
@@ -73,6 +81,9 @@ def test_pmc_summary_takes_the_largest_grid_and_scales(tmp_path):
     assert d["fetch_scale"] == 2.0 and d["write_scale"] == 1.0
     assert d["traffic_bytes_per_launch"] == 200 * 1024 * 2 + 40 * 1024
     assert d["sources_digest"] == bench.logits_sources_digest()
+    # every dsa kernel, per (kernel, grid), in the side table
+    cand = [e for e in d["every_kernel_per_dispatch"] if e["kernel"] == CAND]
+    assert len(cand) == 1 and cand[0]["fetch_kib"] == 1e6
 
 
 def test_trace_summary_reports_the_workload_launch(tmp_path):
