@@ -263,18 +263,16 @@ def _base_name(name):
 
 def _per_dispatch(rows):
     """{dispatch id: (kernel name, summed counter value in KiB)}; only the
-    dispatches at the largest grid of their kernel (any instance) are kept
-    (the workload's own launch: the chunked leg launches the same kernels
-    on smaller grids)."""
+    dispatches at the largest grid of their kernel instance are kept (the
+    workload's own launch: the chunked leg and the fused forward's sample
+    pass launch the same instance on smaller grids)."""
     out, grid = {}, {}
     for r in rows:
         key = r["Dispatch_Id"]
         name, v, g = out.get(key, (r["Kernel_Name"], 0.0, int(r["Grid_Size"])))
         out[key] = (name, v + float(r["Counter_Value"]), g)
-        b = _base_name(name)
-        grid[b] = max(grid.get(b, 0), g)
-    return {k: (n, v) for k, (n, v, g) in out.items()
-            if g == grid[_base_name(n)]}
+        grid[name] = max(grid.get(name, 0), g)
+    return {k: (n, v, g) for k, (n, v, g) in out.items() if g == grid[n]}
 
 
 def _matcher(config):
@@ -290,7 +288,7 @@ def pmc_summary(args):
 
     def calib(d):
         # the calibration copies are the largest copy dispatches
-        v = sorted((x for n, x in d.values() if "copyBuffer" in n),
+        v = sorted((x for n, x, _ in d.values() if "copyBuffer" in n),
                    reverse=True)[:3]
         if not v:
             raise SystemExit("no calibration copy in the counter run")
@@ -302,8 +300,11 @@ def pmc_summary(args):
     is_dom = _matcher(args.config)
 
     def logits(d):
-        v = [x for n, x in d.values() if is_dom(n)]
-        names = sorted({n for n, _ in d.values() if is_dom(n)})
+        # the matching instance at the largest grid: the workload's own
+        # logits launch (a fused sample pass is a smaller launch)
+        top = max((g for n, _, g in d.values() if is_dom(n)), default=0)
+        v = [x for n, x, g in d.values() if is_dom(n) and g == top]
+        names = sorted({n for n, _, g in d.values() if is_dom(n) and g == top})
         if not v:
             raise SystemExit("no logits dispatch in the counter run")
         return sum(v) / len(v), len(v), names
@@ -394,11 +395,11 @@ def mfma_summary(args):
         d["c"][c] = d["c"].get(c, 0.0) + float(r["Counter_Value"])
         if r.get("End_Timestamp") and r.get("Start_Timestamp"):
             d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
-        b = _base_name(d["name"])
-        grid[b] = max(grid.get(b, 0), d["grid"])
+        grid[d["name"]] = max(grid.get(d["name"], 0), d["grid"])
     is_dom = _matcher(args.config)
-    dom = [d for d in per.values() if is_dom(d["name"]) and
-           d["grid"] == grid[_base_name(d["name"])]]
+    top = max((d["grid"] for d in per.values() if is_dom(d["name"])),
+              default=0)
+    dom = [d for d in per.values() if is_dom(d["name"]) and d["grid"] == top]
     if not dom:
         raise SystemExit("no logits dispatch in the counter run")
     names = sorted({c for d in dom for c in d["c"]})
@@ -543,6 +544,25 @@ def _timed(torch, fn, launches, rotate):
     return a.elapsed_time(z) / launches
 
 
+def _in_step(torch, before, kernel, after, K, R, warmup):
+    """Average duration (ms) of ``kernel`` inside eager steps: before(r),
+    event, kernel(r), event, after(r) for K steps (after ``warmup`` steps),
+    so that the kernel runs between the step's other kernels as it does in
+    the timed graph rather than back to back with itself."""
+    for i in range(warmup):
+        before(i % R); kernel(i % R); after(i % R)
+    torch.cuda.synchronize()
+    ev = [_events(torch) for _ in range(K)]
+    for i in range(K):
+        before(i % R)
+        ev[i][0].record()
+        kernel(i % R)
+        ev[i][1].record()
+        after(i % R)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(z) for a, z in ev) / K
+
+
 def _graph_steps(torch, step, K, R, warmup, check_buf, ref_step):
     """W eager warm-up steps, then a HIP graph of exactly K steps (step i on
     copy i mod R), checked bit-exactly against the eager result of its last
@@ -635,7 +655,7 @@ def measure_workload(args, name, K, W, extras=False, cpu=True,
     # quantisation launch builds; time that kernel (one schedule, built
     # once: it depends only on the batch's metadata)
     sched = binding.dsa_logits_schedule(bt, qsl, pos, ld) \
-        if dominant_kernel(b)[1] else None
+        if b.T <= 128 and b.T <= 2 * b.R else None
     kl_plain = kl
     if sched is not None:
         kl = _timed(torch, lambda r: binding.dsa_indexer_logits_scheduled(
@@ -643,8 +663,21 @@ def measure_workload(args, name, K, W, extras=False, cpu=True,
             NK, R)
     kt = _timed(torch, lambda r: binding.dsa_indexer_topk(
         logits, pos, k, buf, tws), NK, R)
+    # the logits kernel between the step's quantisation and top-k (as in the
+    # timed graph; back to back with itself the chip runs it at a lower
+    # clock: see the kernel traces)
+    kl_step = _in_step(
+        torch, lambda r: binding.dsa_quantize_q(qs_in[r], q8, qsc),
+        (lambda r: binding.dsa_indexer_logits_scheduled(
+            q8, qsc, ws_in[r], kcs[r], bt, qsl, pos, ld, sched, logits))
+        if sched is not None else
+        (lambda r: binding.dsa_indexer_logits(
+            q8, qsc, ws_in[r], kcs[r], bt, qsl, pos, ld, logits)),
+        lambda r: binding.dsa_indexer_topk(logits, pos, k, buf, tws),
+        NK, R, 4)
     kf = _timed(torch, forward, NK, R)
     kernels = {"quantize_q": round(kq, 5), "logits": round(kl, 5),
+               "logits_in_step": round(kl_step, 5),
                "topk": round(kt, 5), "forward": round(kf, 5)}
     if sched is not None:
         kernels["logits_without_schedule"] = round(kl_plain, 5)
@@ -743,6 +776,11 @@ def measure_workload(args, name, K, W, extras=False, cpu=True,
     roof["algorithmic_bytes"] = int(alg_bytes)
     roof["algorithmic_flops"] = flops
     roof["kernel_ms"] = round(kl, 5)
+    # the same kernel timed between the step's other kernels
+    roof["kernel_ms_in_step"] = round(kl_step, 5)
+    roof["frac_in_step"] = round(
+        (flops / (kl_step * 1e-3) / 1e12 / FP8_PEAK_TFLOPS) if T > 2 * b.R
+        else (alg_bytes / (kl_step * 1e-3) / 1e9 / HBM_PEAK_GBS), 4)
     roof["hbm_gbs"] = round(gbs, 1)
     roof["fp8_tflops"] = round(tfl, 2)
     rec.update({
