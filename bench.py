@@ -31,8 +31,11 @@ queued behind a GPU sleep so that no host gap falls inside a bracket.
 
 Prints ONE JSON line.  ``roofline`` is for the dominant kernel (the logits
 kernel): achieved = algorithmic bytes (or FLOPs) per launch / its average
-duration; ``cpu_baseline`` times the CPU oracle (numpy) on a bounded sample
-of the same workload on this host.
+duration, against the published peaks and against the rates this box
+measures in the same run (a 1 GiB device copy; the library's pure FP8 MFMA
+loop); ``ms_per_step_quantiles`` are over the timed replay and 16 more;
+``cpu_baseline`` times the CPU oracle (numpy) on a bounded sample of the same
+workload on this host (every workload's record has one).
 """
 
 import argparse
@@ -161,6 +164,12 @@ def host_cpu():
     except OSError:
         pass
     return model, len(os.sched_getaffinity(0))
+
+
+# Rows of the oracle's CPU sample per workload (evenly spaced; the whole batch
+# when absent): the prefill chunk's 8192 rows and the 1M-token tail's 16 rows
+# of 1M columns would take minutes to hours in numpy.
+CPU_SAMPLE_ROWS = {"prefill": 256, "long": 1}
 
 
 def cpu_baseline(b, seconds, max_rows=None):
@@ -567,7 +576,7 @@ def _graph_steps(torch, step, K, R, warmup, check_buf, ref_step):
     """W eager warm-up steps, then a HIP graph of exactly K steps (step i on
     copy i mod R), checked bit-exactly against the eager result of its last
     step, replayed once for the timed region.  Returns (ms per step, [ms per
-    step of 4 more replays])."""
+    step of 16 more replays])."""
     for i in range(warmup):
         step(i % R)
     last = (K - 1) % R
@@ -594,7 +603,7 @@ def _graph_steps(torch, step, K, R, warmup, check_buf, ref_step):
     torch.cuda.synchronize()
     ms = a.elapsed_time(z) / K
     again = []
-    for _ in range(4):
+    for _ in range(16):
         a, z = _events(torch)
         a.record()
         graph.replay()
@@ -605,6 +614,14 @@ def _graph_steps(torch, step, K, R, warmup, check_buf, ref_step):
         raise SystemExit("graph replay differs from the eager result")
     del graph
     return ms, again
+
+
+def _quantiles(vals):
+    """p10 / p50 / p90 (nearest rank) of per-replay step times."""
+    v = sorted(vals)
+    pick = lambda q: v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
+    return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9),
+            "replays": len(v)}
 
 
 def measure_workload(args, name, K, W, extras=False, cpu=True,
@@ -753,6 +770,8 @@ def measure_workload(args, name, K, W, extras=False, cpu=True,
         rec["fused"] = {
             "ms_per_step": round(ms_fused, 5),
             "ms_per_step_more_replays": again_fused,
+            "ms_per_step_quantiles": _quantiles([round(ms_fused, 5)] +
+                                                again_fused),
             "value": round(T / (ms_fused * 1e-3), 1),
             "unit": "query-rows/s",
             "speedup_vs_forward": round(ms_step / ms_fused, 4),
@@ -789,6 +808,7 @@ def measure_workload(args, name, K, W, extras=False, cpu=True,
         "workload": WORKLOADS[name],
         "value": round(T / (ms_step * 1e-3), 1), "unit": "query-rows/s",
         "ms_per_step": round(ms_step, 5), "ms_per_step_more_replays": again,
+        "ms_per_step_quantiles": _quantiles([round(ms_step, 5)] + again),
         "rows": T, "heads": H, "index_topk": k,
         "visible_pairs": b.visible_pairs, "kcache_copies_rotated": R,
         "kernels_ms": kernels, "roofline": roof})
@@ -816,6 +836,40 @@ def copy_rate(torch):
     del c_src, c_dst
     torch.cuda.empty_cache()
     return 2 * (1 << 30) * 5 / (a.elapsed_time(z) * 1e-3) / 1e9
+
+
+def mfma_rate(torch):
+    """Attainable FP8 MFMA rate on this machine: the library's pure MFMA loop
+    (no memory traffic) at the clock the chip holds under it, TFLOP/s."""
+    from dsa_lightning_indexer_amd import binding
+    iters = 4000
+    binding.dsa_fp8_mfma_rate_probe(iters)
+    a, z = _events(torch)
+    torch.cuda.synchronize()
+    a.record()
+    flops = sum(binding.dsa_fp8_mfma_rate_probe(iters) for _ in range(5))
+    z.record()
+    torch.cuda.synchronize()
+    return flops / (a.elapsed_time(z) * 1e-3) / 1e12
+
+
+def add_measured_peaks(roof, copy_gbs, mfma_tflops):
+    """The roofline against the box's measured rates as well as the
+    published peaks."""
+    if copy_gbs is not None:
+        roof["copy_gbs_measured"] = round(copy_gbs, 1)
+        if roof["bound"] == "hbm":
+            roof["frac_of_measured_copy"] = round(roof["achieved"] / copy_gbs,
+                                                  4)
+    if mfma_tflops is not None:
+        roof["fp8_mfma_measured_tflops"] = round(mfma_tflops, 1)
+        if roof["bound"] == "mfma":
+            roof["frac_of_measured_mfma"] = round(
+                roof["achieved"] / mfma_tflops, 4)
+            if "kernel_ms_in_step" in roof:
+                roof["frac_of_measured_mfma_in_step"] = round(
+                    roof["algorithmic_flops"] / (roof["kernel_ms_in_step"] *
+                                                 1e-3) / 1e12 / mfma_tflops, 4)
 
 
 def main():
@@ -855,17 +909,14 @@ def main():
         return
 
     head = args.config
-    cpu_rows = 256 if head == "prefill" else None
-    main_rec = measure_workload(args, head, K, W, extras=True,
-                                cpu=head != "long", cpu_rows=cpu_rows)
+    main_rec = measure_workload(args, head, K, W, extras=True, cpu=True,
+                                cpu_rows=CPU_SAMPLE_ROWS.get(head))
     roof = main_rec.pop("roofline")
     # Not in counter runs: their scale comes from the largest copies, which
     # must be the 256 MiB calibration copies.
-    if not args.copy_calibration:
-        cg = copy_rate(torch)
-        roof["copy_gbs_measured"] = round(cg, 1)
-        if roof["bound"] == "hbm":
-            roof["frac_of_measured_copy"] = round(roof["achieved"] / cg, 4)
+    cg = None if args.copy_calibration else copy_rate(torch)
+    mt = mfma_rate(torch)
+    add_measured_peaks(roof, cg, mt)
     out = {
         "metric": METRIC, "value": main_rec.pop("value"),
         "unit": main_rec.pop("unit"), "n_gpus": 1, "steps": K, "warmup": W,
@@ -893,8 +944,9 @@ def main():
                 continue
             try:
                 out[name] = measure_workload(
-                    args, name, K, W, cpu=name == "prefill",
-                    cpu_rows=256 if name == "prefill" else None)
+                    args, name, K, W, cpu=True,
+                    cpu_rows=CPU_SAMPLE_ROWS.get(name))
+                add_measured_peaks(out[name]["roofline"], cg, mt)
             except Exception as e:                    # pragma: no cover
                 out[name] = {"error": repr(e)}
         try:

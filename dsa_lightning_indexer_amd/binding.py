@@ -92,6 +92,8 @@ _SIGNATURES = {
     "dsa_topk_to_slots": (_I, [_P, _L, _I, _L, _P, _L, _P, _I, _P, _P]),
     "dsa_topk_mask": (_I, [_P, _L, _I, _L, _P, _L, _P]),
     "dsa_device_error_flags": (_I, [_I]),
+    "dsa_fp8_mfma_rate_probe": (_I, [_I, ctypes.POINTER(ctypes.c_double),
+                                     _P]),
     "dsa_set_option": (_I, [ctypes.c_char_p, _I]),
 }
 
@@ -673,6 +675,19 @@ def dsa_topk_mask(topk, ld, mask=None, stream=None, k=None):
 
 def dsa_device_error_flags(reset=True):
     return _check(lib().dsa_device_error_flags(1 if reset else 0))
+
+
+def dsa_fp8_mfma_rate_probe(iters, stream=None, device=None):
+    """Enqueue one pure FP8 MFMA loop launch on the current (or given)
+    device (measurement helper); returns the FP8 operations it performs
+    (time it with events on the stream)."""
+    dev = torch.device("cuda", torch.cuda.current_device()) \
+        if device is None else torch.device(device)
+    flops = ctypes.c_double(0.0)
+    with torch.cuda.device(dev):
+        _check(lib().dsa_fp8_mfma_rate_probe(int(iters), ctypes.byref(flops),
+                                             _stream(stream, dev)))
+    return flops.value
 
 
 def dsa_set_option(key, value):

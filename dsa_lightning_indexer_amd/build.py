@@ -20,7 +20,8 @@ LIB = os.path.join(LIBDIR, "libdsa_indexer.so")
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "kernels_logits.hip", "kernels_topk.hip",
-           "kernels_kwrite.hip", "kernels_handoff.hip", "kernels_chunk.hip"]
+           "kernels_kwrite.hip", "kernels_handoff.hip", "kernels_chunk.hip",
+           "kernels_calib.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -523,6 +523,19 @@ int dsa_topk_mask(const int32_t* topk, int64_t T, int k, int64_t topk_ld,
 int dsa_device_error_flags(int reset);
 
 /*
+ * dsa_fp8_mfma_rate_probe -- measurement helper, not a step of the hot
+ * path: enqueues on `stream` one launch in which every wave (two per SIMD)
+ * runs `iters` rounds of 8 independent 16x16x128 FP8 MFMAs on register
+ * operands -- no memory traffic -- and stores in *flops the FP8 operations
+ * that launch performs.  Timed by the caller (events on the same stream), it
+ * gives the FP8 matrix rate this device reaches at the clock it holds under
+ * such a load, the measured counterpart of the published dense peak that
+ * the logits kernels' rate is read against.  iters in [1, 1 << 24];
+ * DSA_ERR_INVALID_ARG otherwise or for flops == NULL.
+ */
+int dsa_fp8_mfma_rate_probe(int iters, double* flops, void* stream);
+
+/*
  * dsa_set_option -- tuning/testing knobs; returns the previous value or
  * DSA_ERR_INVALID_ARG for an unknown key or value.  Knobs are kept per
  * device (the calling thread's current HIP device) in atomics: concurrent

@@ -281,6 +281,16 @@ def test_workspace_sizes():
         full
 
 
+def test_mfma_rate_probe_rejects_bad_arguments():
+    L = binding.lib()
+    flops = ctypes.c_double(0.0)
+    for iters in (0, -5, (1 << 24) + 1):
+        assert L.dsa_fp8_mfma_rate_probe(iters, ctypes.byref(flops),
+                                         None) == binding.DSA_ERR_INVALID_ARG
+    assert L.dsa_fp8_mfma_rate_probe(16, None, None) == \
+        binding.DSA_ERR_INVALID_ARG
+
+
 def test_set_option_roundtrip():
     prev = binding.dsa_set_option("logits_kernel", 2)
     assert binding.dsa_set_option("logits_kernel", prev) == 2

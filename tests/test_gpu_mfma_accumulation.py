@@ -127,3 +127,24 @@ def test_fp8_mfma_dot_error(kind):
     assert np.all(err <= bound * mag[sure])
     # a dot clearly below zero is clamped to exactly 0 by the ReLU
     assert np.all(g[exact < -bound * mag] == 0.0)
+
+
+def test_fp8_mfma_rate_probe_counts_and_runs():
+    """The measurement helper: its FLOP count is two 4-wave workgroups per
+    compute unit x iters x 8 MFMAs x 2*16*16*128, and the launch it enqueues
+    runs (a positive rate no higher than the chip's unit count allows)."""
+    print("case: fp8 mfma rate probe", flush=True)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 2000
+    binding.dsa_fp8_mfma_rate_probe(iters)               # warm
+    a = torch.cuda.Event(enable_timing=True)
+    z = torch.cuda.Event(enable_timing=True)
+    a.record()
+    flops = binding.dsa_fp8_mfma_rate_probe(iters)
+    z.record()
+    torch.cuda.synchronize()
+    assert flops == 2 * cus * 4 * iters * 8 * 2 * 16 * 16 * 128
+    rate = flops / (a.elapsed_time(z) * 1e-3)
+    # at most one 16x16x128 FP8 MFMA per 16 cycles per SIMD at 3 GHz
+    assert 0 < rate < cus * 4 * (2 * 16 * 16 * 128 / 16) * 3e9
+
