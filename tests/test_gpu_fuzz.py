@@ -170,3 +170,53 @@ def test_random_chunked_forward(seed):
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
     assert chunking.pieces(b.T, rows)[-1][1] == b.T
+
+
+FUSED_KNOBS = ("fused_sample_stride", "fused_select", "fused_cand_cap")
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_fused_forward(seed):
+    """The fused forward (no logits buffer) on random tiled batches -- rows
+    in any order with repeated positions, every head count, k from 1 to past
+    the context, spare columns -- with a random sample stride, select kernel
+    and (sometimes) a tiny slot capacity: the forward's top-k, bit for bit."""
+    rng = np.random.Generator(np.random.PCG64(5000 + seed))
+    R = int(rng.integers(1, 5))
+    ctx, pos = [], []
+    for _ in range(R):
+        L = int(rng.integers(1, 6000))
+        ctx.append(L)
+        m = min(L, int(rng.integers(1, 70)))
+        pos.append(rng.integers(0, L, m).tolist() if seed % 2 else
+                   sorted(rng.choice(L, m, replace=False).tolist()))
+    H = HEADS[seed % len(HEADS)]
+    k = int(rng.choice([1, 7, 64, 300, 2048]))
+    b = synth.build_batch(rng, ctx, pos, H=H, k=k,
+                          boost_frac=0.02 if seed % 3 == 0 else 0.0)
+    if seed % 4 == 3:
+        b.ld += 256
+    knobs = {"fused_sample_stride": int(rng.choice([0, 16, 32, 64])),
+             "fused_select": int(rng.integers(0, 4)),
+             "fused_cand_cap": int(rng.choice([0, 0, 0, 4]))}
+    print(f"case: seed {seed}: R={b.R} T={b.T} H={b.H} k={b.k} ld={b.ld} "
+          f"{knobs}", flush=True)
+    sys.stdout.flush()
+    d = parity.upload(b)
+    binding.dsa_device_error_flags(reset=True)
+    _, ref = binding.dsa_indexer_forward(
+        d["q_bf16"], d["weights"], d["k_cache"], d["block_table"], d["qsl"],
+        d["positions"], b.ld, b.k)
+    torch.cuda.synchronize()
+    try:
+        for key, v in knobs.items():
+            binding.dsa_set_option(key, v)
+        out = binding.dsa_indexer_forward_fused(
+            d["q_bf16"], d["weights"], d["k_cache"], d["block_table"],
+            d["qsl"], d["positions"], b.ld, b.k)
+        torch.cuda.synchronize()
+    finally:
+        for key in FUSED_KNOBS:
+            binding.dsa_set_option(key, 0)
+    assert torch.equal(out, ref)
+    assert binding.dsa_device_error_flags(reset=True) == 0
