@@ -127,6 +127,48 @@ __device__ __forceinline__ float head_reduce_abs(const f32x4 (&acc)[MT],
 }
 
 // ---------------------------------------------------------------------------
+// One 64-token page of the decode kernels, K read straight into the MFMA B
+// operand: N-tile nt (tokens 16 nt .. 16 nt + 15) of lane l is token 16 nt
+// + l % 16, bytes 32 (l / 16) .. + 31 of its key; lane l also takes the
+// scale of token l.  rs covers the page's 8448 bytes (zero size for a page
+// that is not scored: every load returns 0 without touching memory).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void load_k_page_regs(__amdgpu_buffer_rsrc_t rs,
+                                                 i32x8 (&kb)[4], float& ks) {
+  const int lane = lane_id();
+  const int i16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int off = (16 * nt + i16) * kHeadDim + 32 * g;
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    const auto y = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0);
+    kb[nt] = i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3],
+                   (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+  }
+  ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+      rs, kPageKeyBytes + 4 * lane, 0, 0));
+}
+
+// Head-weighted ReLU sum of one page for one query row, before the K scale:
+// lane l ends with token l's sum over the H heads (16 MFMAs for H = 64, the
+// head reduction of each N-tile, then the lane-group reduce-scatter).
+template <int MT>
+__device__ __forceinline__ float decode_page_sum(const i32x8 (&qa)[MT],
+                                                 const i32x8 (&kb)[4],
+                                                 const float (&w)[MT][4]) {
+  float v[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    f32x4 acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      acc[m] = mfma16x16x128_fp8(qa[m], kb[nt], f32x4{0.f, 0.f, 0.f, 0.f});
+    v[nt] = head_reduce<MT>(acc, w);
+  }
+  return reduce_scatter4(v[0], v[1], v[2], v[3]);
+}
+
+// ---------------------------------------------------------------------------
 // Linear part of the head reduction, shared by four rows (tile kernel).
 // With ReLU written as (x + |x|) / 2 and the 1/2 folded into the weights,
 //   sum_h w_h (x_h + |x_h|) = L + sum_h w_h |x_h|,

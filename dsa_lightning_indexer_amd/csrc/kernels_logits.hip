@@ -391,7 +391,6 @@ __global__ __launch_bounds__(64) void logits_balanced_kernel(
     const int32_t* __restrict__ sched) {
   static_assert(!SCHED || D <= kSchedPages, "schedule holds 3 pages");
   const int lane = lane_id();
-  const int i16 = lane & 15, g = lane >> 4;
   const bool head = !SCHED && (int)blockIdx.x < head_waves;
   RowSpan sp;
   int sched_r = 0;
@@ -468,19 +467,10 @@ __global__ __launch_bounds__(64) void logits_balanced_kernel(
     for (int q = 0; q < D; ++q) {
       ok[q] = c + q < je && pages[q] >= 0 && (int64_t)pages[q] < a.num_pages;
       bad_page |= c + q < je && !ok[q];
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(
-          a.k_cache + (int64_t)(ok[q] ? pages[q] : 0) * kPageBytes,
-          ok[q] ? kPageBytes : 0);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int off = (16 * nt + i16) * kHeadDim + 32 * g;
-        const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
-        const auto y = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0);
-        kb[q][nt] = i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3],
-                          (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
-      }
-      ks[q] = __uint_as_float(
-          __builtin_amdgcn_raw_buffer_load_b32(rs, kPageKeyBytes + 4 * lane, 0, 0));
+      load_k_page_regs(
+          make_rsrc(a.k_cache + (int64_t)(ok[q] ? pages[q] : 0) * kPageBytes,
+                    ok[q] ? kPageBytes : 0),
+          kb[q], ks[q]);
     }
     // keep every load of the chunk ahead of the first MFMA
     __builtin_amdgcn_sched_barrier(0);
@@ -489,16 +479,7 @@ __global__ __launch_bounds__(64) void logits_balanced_kernel(
       const int jp = c + q;
       float res = -INFINITY;
       if (ok[q]) {
-        float v[4];
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          f32x4 acc[MT];
-#pragma unroll
-          for (int m = 0; m < MT; ++m)
-            acc[m] = mfma16x16x128_fp8(qa[m], kb[q][nt], f32x4{0.f, 0.f, 0.f, 0.f});
-          v[nt] = head_reduce<MT>(acc, w);
-        }
-        const float tot = reduce_scatter4(v[0], v[1], v[2], v[3]);
+        const float tot = decode_page_sum<MT>(qa, kb[q], w);
         if (jp * kPageTokens + lane <= p) res = tot * ks[q];
       }
       const __amdgpu_buffer_rsrc_t ro = make_rsrc(

@@ -348,6 +348,40 @@ def test_topk_row_lengths(ld, kernel):
                                               f"ld {ld} row {t}")
 
 
+@pytest.mark.parametrize("kernel", [1, 2, 4])
+@pytest.mark.parametrize("ld", [4096, 8192, 16384])
+def test_topk_threshold_among_huge_negative_logits(ld, kernel):
+    """Rows whose k-th largest logit is below -2^96 or -inf, so the bin it
+    falls in is one of the lowest 256 of the first pass and the second and
+    third passes run: distinct huge negative values, values that agree in
+    their top 24 key bits, -inf with a few finite values, and negative
+    values in a band narrower than a first-pass bin."""
+    _say(f"case: top-k threshold among huge negative logits, ld {ld}, "
+         f"top-k kernel {kernel}")
+    binding.dsa_set_option("topk_kernel", kernel)
+    k = 2048
+    rng = np.random.default_rng(ld + 7 * kernel)
+    T = 6
+    lg = np.empty((T, ld), np.float32)
+    lg[0] = -(1e30 * (1.0 + rng.random(ld))).astype(np.float32)
+    lg[0, : k // 2] = rng.standard_normal(k // 2)      # fewer than k finite
+    base = np.float32(-3e30).view(np.uint32)
+    lg[1] = (base + rng.integers(0, 256, ld).astype(np.uint32)).view(
+        np.float32)                                    # one 24-bit prefix
+    lg[1, ::5] = rng.standard_normal(len(lg[1, ::5]))
+    lg[2] = -np.inf
+    lg[2, rng.choice(ld, k // 4, replace=False)] = 1.0
+    lg[3] = -np.inf
+    lg[4] = -(2.0 ** 100) * (1.0 + rng.random(ld) * 1e-3).astype(np.float32)
+    lg[5] = -(1e35 * rng.random(ld)).astype(np.float32)
+    pos = np.array([ld - 1, ld - 1, ld - 1, ld - 1, ld - 2, ld - 1], np.int32)
+    g = binding.dsa_indexer_topk(torch.from_numpy(lg).cuda(),
+                                 torch.from_numpy(pos).cuda(), k).cpu().numpy()
+    for t in range(T):
+        parity.check_topk_exact_on_gpu_logits(g[t], lg[t], int(pos[t]), k,
+                                              f"huge negative row {t}")
+
+
 @pytest.mark.parametrize("kernel", [0, 1])
 @pytest.mark.parametrize("k", [512, 2048])
 def test_topk_rows_looped_per_workgroup(k, kernel):
