@@ -804,6 +804,18 @@ def measure_workload(args, name, K, W, extras=False, cpu=True,
             flops / (kl_step * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4)
     roof["hbm_gbs"] = round(gbs, 1)
     roof["fp8_tflops"] = round(tfl, 2)
+    if roof["bound"] == "hbm":
+        # the attainable floor on this machine: a bare read of exactly the K
+        # pages the batch's rows reach (the library's page-read helper: no
+        # metadata lookups, no compute), timed like the logits kernel
+        ids = torch.from_numpy(visible_page_ids(b)).to(dev)
+        kr = _timed(torch, lambda r: binding.dsa_page_read_probe(kcs[r], ids),
+                    NK, R)
+        rb = int(ids.numel()) * 8448
+        roof["bare_read_ms"] = round(kr, 5)
+        roof["bare_read_bytes"] = rb
+        roof["bare_read_gbs"] = round(rb / (kr * 1e-3) / 1e9, 1)
+        roof["frac_of_bare_read"] = round(kr / kl, 4)
     rec.update({
         "workload": WORKLOADS[name],
         "value": round(T / (ms_step * 1e-3), 1), "unit": "query-rows/s",
@@ -817,6 +829,15 @@ def measure_workload(args, name, K, W, extras=False, cpu=True,
         rec["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds, cpu_rows)
     torch.cuda.empty_cache()
     return rec
+
+
+def visible_page_ids(b):
+    """Physical ids of the K pages the batch's rows reach (page j of row t's
+    request for j <= p_t / 64), row by row."""
+    req = np.searchsorted(b.query_start_loc, np.arange(b.T), side="right") - 1
+    ids = [b.block_table[int(req[t]), : int(b.positions[t]) // 64 + 1]
+           for t in range(b.T)]
+    return np.concatenate(ids).astype(np.int32)
 
 
 def copy_rate(torch):

@@ -94,6 +94,7 @@ _SIGNATURES = {
     "dsa_device_error_flags": (_I, [_I]),
     "dsa_fp8_mfma_rate_probe": (_I, [_I, ctypes.POINTER(ctypes.c_double),
                                      _P]),
+    "dsa_page_read_probe": (_I, [_P, _L, _P, _L, _P]),
     "dsa_set_option": (_I, [ctypes.c_char_p, _I]),
 }
 
@@ -688,6 +689,22 @@ def dsa_fp8_mfma_rate_probe(iters, stream=None, device=None):
         _check(lib().dsa_fp8_mfma_rate_probe(int(iters), ctypes.byref(flops),
                                              _stream(stream, dev)))
     return flops.value
+
+
+def dsa_page_read_probe(k_cache, page_ids, stream=None):
+    """Enqueue one bare read of the K pages page_ids (int32 [n]) of k_cache
+    (uint8 [num_pages, 8448]) on the current stream (measurement helper;
+    time it with events on the stream)."""
+    if k_cache.dim() != 2 or k_cache.shape[1] != PAGE_BYTES:
+        raise ValueError("k_cache must be uint8 [num_pages, 8448]")
+    if page_ids.dim() != 1:
+        raise ValueError("page_ids must be int32 [n]")
+    dev = k_cache.device
+    with torch.cuda.device(dev):
+        _check(lib().dsa_page_read_probe(
+            _dev_ptr(k_cache, torch.uint8, "k_cache"), k_cache.shape[0],
+            _dev_ptr(page_ids, torch.int32, "page_ids"), page_ids.numel(),
+            _stream(stream, dev)))
 
 
 def dsa_set_option(key, value):

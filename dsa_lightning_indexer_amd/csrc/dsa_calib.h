@@ -1,4 +1,4 @@
-// Host-side launcher of the library's measurement helper (internal; the
+// Host-side launchers of the library's measurement helpers (internal; the
 // public C ABI is include/dsa_indexer.h).
 #pragma once
 
@@ -9,5 +9,10 @@ namespace dsa {
 // One launch of a pure FP8 MFMA loop (iters rounds per wave, two waves per
 // SIMD); *flops = the FP8 operations it performs.
 hipError_t launch_fp8_mfma_rate(int iters, double* flops, hipStream_t stream);
+
+// One launch reading the n K pages whose ids are ids[0 .. n) whole (ids
+// outside [0, num_pages) read nothing), three pages per wave, no compute.
+hipError_t launch_page_read(const uint8_t* k_cache, int64_t num_pages,
+                            const int32_t* ids, int64_t n, hipStream_t stream);
 
 }  // namespace dsa

@@ -1,7 +1,8 @@
-// Measurement helper of the gfx950 library (not a step of the indexer hot
+// Measurement helpers of the gfx950 library (not steps of the indexer hot
 // path): the FP8 matrix-core rate this device reaches at the clock it holds
-// under a pure MFMA load.  The logits kernels' FP8 rate is then read against
-// both the published dense peak and this measured one.
+// under a pure MFMA load, and the time a bare read of a batch's K pages
+// takes.  The logits kernels' rates are read against the published peaks
+// and against these measured ones.
 #include "dsa_calib.h"
 #include "dsa_common.h"
 #include "dsa_launch.h"
@@ -36,6 +37,56 @@ __global__ __launch_bounds__(256) void fp8_mfma_rate_kernel(int iters) {
 #pragma unroll
   for (int j = 0; j < kCalibChains; ++j) s += c[j][0] + c[j][1] + c[j][2] + c[j][3];
   g_calib_sink[lane] = s;
+}
+
+constexpr int kReadPagesPerWave = 3;
+
+// Wave w reads pages ids[3 w .. 3 w + 2] whole (8448 bytes each: 8 loads of
+// 1 KB contiguous per page, then its 256 scale bytes), all before the first
+// result is used; an id outside [0, num_pages) reads nothing.  The words are
+// folded into one value, kept only so that the loads are not dropped.
+__global__ __launch_bounds__(64) void page_read_kernel(
+    const uint8_t* __restrict__ k_cache, int64_t num_pages,
+    const int32_t* __restrict__ ids, int64_t n) {
+  const int lane = lane_id();
+  const int64_t w = blockIdx.x;
+  uint32_t acc = 0u;
+  uint4 v[kReadPagesPerWave][8];
+  uint32_t sc[kReadPagesPerWave];
+#pragma unroll
+  for (int q = 0; q < kReadPagesPerWave; ++q) {
+    const int64_t i = w * kReadPagesPerWave + q;
+    const int page = i < n ? load_uniform(ids, i) : -1;
+    const bool ok = page >= 0 && (int64_t)page < num_pages;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(
+        k_cache + (int64_t)(ok ? page : 0) * kPageBytes, ok ? kPageBytes : 0);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const auto x =
+          __builtin_amdgcn_raw_buffer_load_b128(rs, 1024 * c + 16 * lane, 0, 0);
+      v[q][c] = make_uint4(x[0], x[1], x[2], x[3]);
+    }
+    sc[q] = __builtin_amdgcn_raw_buffer_load_b32(rs, kPageKeyBytes + 4 * lane,
+                                                 0, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < kReadPagesPerWave; ++q) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      acc ^= v[q][c].x ^ v[q][c].y ^ v[q][c].z ^ v[q][c].w;
+    acc ^= sc[q];
+  }
+  if (acc == 0x9e3779b9u) g_calib_sink[lane] = (float)acc;
+}
+
+hipError_t launch_page_read(const uint8_t* k_cache, int64_t num_pages,
+                            const int32_t* ids, int64_t n,
+                            hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t waves = (n + kReadPagesPerWave - 1) / kReadPagesPerWave;
+  hipLaunchKernelGGL(page_read_kernel, dim3((unsigned)waves), dim3(64), 0,
+                     stream, k_cache, num_pages, ids, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_fp8_mfma_rate(int iters, double* flops, hipStream_t stream) {

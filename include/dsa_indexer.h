@@ -536,6 +536,23 @@ int dsa_device_error_flags(int reset);
 int dsa_fp8_mfma_rate_probe(int iters, double* flops, void* stream);
 
 /*
+ * dsa_page_read_probe -- measurement helper, not a step of the hot path:
+ * enqueues on `stream` one launch that reads the n K pages whose ids are
+ * page_ids[0 .. n) (device, int32) from k_cache (device, [num_pages, 8448]
+ * bytes, the layout of [KVB] SGLang buffer shape) whole -- 8 KB of keys and
+ * 256 B of scales each, in 1 KB contiguous loads, three pages per wave --
+ * and does nothing with the bytes.  Timed by the caller (events on the same
+ * stream) over the pages a decode batch's rows reach, it gives the time a
+ * bare read of exactly the bytes the decode logits kernel reads takes on
+ * this device, with no metadata lookups and no compute: the attainable
+ * floor that kernel's time is read against.  An id outside [0, num_pages)
+ * reads nothing.  Errors: DSA_ERR_INVALID_ARG for n < 0, num_pages < 1 or a
+ * null pointer with n > 0; DSA_ERR_UNSUPPORTED for n > 2^31.
+ */
+int dsa_page_read_probe(const uint8_t* k_cache, int64_t num_pages,
+                        const int32_t* page_ids, int64_t n, void* stream);
+
+/*
  * dsa_set_option -- tuning/testing knobs; returns the previous value or
  * DSA_ERR_INVALID_ARG for an unknown key or value.  Knobs are kept per
  * device (the calling thread's current HIP device) in atomics: concurrent

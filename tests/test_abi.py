@@ -291,6 +291,22 @@ def test_mfma_rate_probe_rejects_bad_arguments():
         binding.DSA_ERR_INVALID_ARG
 
 
+def test_page_read_probe_rejects_bad_arguments():
+    L = binding.lib()
+    dummy = ctypes.c_void_p(0x1000)
+    assert L.dsa_page_read_probe(dummy, 16, dummy, -1, None) == \
+        binding.DSA_ERR_INVALID_ARG
+    assert L.dsa_page_read_probe(dummy, 0, dummy, 4, None) == \
+        binding.DSA_ERR_INVALID_ARG
+    assert L.dsa_page_read_probe(None, 16, dummy, 4, None) == \
+        binding.DSA_ERR_INVALID_ARG
+    assert L.dsa_page_read_probe(dummy, 16, None, 4, None) == \
+        binding.DSA_ERR_INVALID_ARG
+    assert L.dsa_page_read_probe(dummy, 16, dummy, (1 << 31) + 1, None) == \
+        binding.DSA_ERR_UNSUPPORTED
+    assert L.dsa_page_read_probe(None, 16, None, 0, None) == binding.DSA_OK
+
+
 def test_set_option_roundtrip():
     prev = binding.dsa_set_option("logits_kernel", 2)
     assert binding.dsa_set_option("logits_kernel", prev) == 2

@@ -176,3 +176,22 @@ def test_mfma_summary(tmp_path):
     assert out["mfma_busy_frac"] == round(500.0 / (1.0 / 8 * 1024), 4)
     assert out["counted_fp8_flops"] == 10.0 * 512
     assert out["commands"] == ["rocprofv3 --pmc ... -- python3 bench.py"]
+
+
+def test_visible_page_ids_match_a_walk_over_the_rows():
+    """The bare-read floor reads the pages of every row up to its own
+    position, through its own request's block-table row (rows of one
+    request repeat its pages, as the logits kernel reads them)."""
+    import numpy as np
+    from dsa_lightning_indexer_amd import synth
+    rng = np.random.Generator(np.random.PCG64(9))
+    b = synth.build_batch(rng, [300, 64, 1000, 1], [[299], [0, 63], [],
+                                                    [0]], H=4, k=8)
+    want = []
+    for r in range(b.R):
+        for t in range(int(b.query_start_loc[r]),
+                       int(b.query_start_loc[r + 1])):
+            for j in range(int(b.positions[t]) // 64 + 1):
+                want.append(int(b.block_table[r, j]))
+    got = bench.visible_page_ids(b)
+    assert got.dtype == np.int32 and got.tolist() == want

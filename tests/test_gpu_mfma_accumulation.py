@@ -148,3 +148,23 @@ def test_fp8_mfma_rate_probe_counts_and_runs():
     # at most one 16x16x128 FP8 MFMA per 16 cycles per SIMD at 3 GHz
     assert 0 < rate < cus * 4 * (2 * 16 * 16 * 128 / 16) * 3e9
 
+
+
+def test_page_read_probe_runs_on_any_ids():
+    """The bare-read measurement helper reads the pages it is given, and ids
+    outside the pool (negative, past the end) read nothing: no fault, no
+    flag, and the cache is left as it was."""
+    print("case: page read probe", flush=True)
+    num_pages = 300
+    cache = torch.randint(0, 255, (num_pages, 8448), dtype=torch.uint8,
+                          device="cuda")
+    before = cache.clone()
+    ids = torch.tensor(list(range(0, num_pages, 7)) +
+                       [-1, num_pages, num_pages + 5, -(1 << 30),
+                        (1 << 31) - 1, 0], dtype=torch.int32, device="cuda")
+    for n in (1, 2, 3, 4, ids.numel()):
+        binding.dsa_page_read_probe(cache, ids[:n])
+    binding.dsa_page_read_probe(cache, ids[:0])
+    torch.cuda.synchronize()
+    assert torch.equal(cache, before)
+    assert binding.dsa_device_error_flags(reset=True) == 0
