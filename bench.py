@@ -999,6 +999,9 @@ def bench_index_cache(args, K, W):
         layers.append({"q_bf16": b.q_bf16.to(dev),
                        "weights": torch.from_numpy(b.weights).to(dev),
                        "k_cache": torch.from_numpy(b.k_cache).to(dev)})
+    # host inputs of the freq-4 stack's F layers, for the CPU oracle's pass
+    host_f4 = {l: layers_np[l] for l, sk in enumerate(
+        binding.dsa_index_cache_mask(L, freq=4, offset=2)) if not sk}
     del layers_np
     bt = torch.from_numpy(ref.block_table).to(dev)
     qsl = torch.from_numpy(ref.query_start_loc).to(dev)
@@ -1054,7 +1057,11 @@ def bench_index_cache(args, K, W):
     per_layer_bytes = 132 * T * 16384 + T * H * 136 + 4 * T * k
     del layers, ws, q8s
     torch.cuda.empty_cache()
-    return {
+    cpu_rec = None
+    if not args.no_cpu_baseline:
+        cpu_rec = cpu_baseline_index_cache(host_f4, ref, L, args.cpu_seconds)
+    del host_f4
+    rec = {
         "metric": "IndexCache stack forward (61 DSA layers)",
         "value": round(T / (res["freq4"] * 1e-3), 1), "unit": "query-rows/s",
         "steps": K, "warmup": W, "ms_per_step": round(res["freq4"], 4),
@@ -1082,6 +1089,50 @@ def bench_index_cache(args, K, W):
                           4),
             "algorithmic_bytes": per_layer_bytes},
     }
+    if cpu_rec is not None:
+        rec["cpu_baseline"] = cpu_rec
+    return rec
+
+
+def cpu_baseline_index_cache(host_layers, ref, L, seconds):
+    """Time the CPU oracle's layer loop over the freq-4 / offset-2 stack of
+    L layers (quantise q, logits and top-k on every F layer, the shared
+    buffer kept on every S layer) for the whole batch, in whole passes
+    repeated until ``seconds`` of work.  ``host_layers`` maps each F layer
+    to its host inputs; BLAS threads = the usable cores."""
+    from oracle import index_cache as oic
+    model, cores = host_cpu()
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores)
+    except Exception:                                   # pragma: no cover
+        limiter = None
+    mask = oic.skip_mask(L, freq=4, offset=2)
+    layers = [None if mask[l] else
+              {"q": host_layers[l].q_bf16.float().numpy(),
+               "weights": host_layers[l].weights,
+               "k_cache": host_layers[l].k_cache} for l in range(L)]
+    buf = np.full((ref.T, ref.k), -1, np.int32)
+    try:
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            oic.run(layers, ref.block_table, ref.query_start_loc,
+                    ref.positions, ref.ld, ref.k, buf, freq=4, offset=2)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    finally:
+        if limiter is not None:
+            limiter.unregister()
+    n_f = int(sum(1 for m in mask if not m))
+    return {"value": reps * ref.T / el, "unit": "query-rows/s",
+            "cores": int(cores), "kind": "oracle", "cpu_model": model,
+            "sample": f"whole batch ({ref.T} rows), the freq-4 stack of {L} "
+                      f"layers ({n_f} F), {reps} pass(es) in {el:.1f} s "
+                      "(numpy fp64 oracle layer loop: quantise q, logits, "
+                      "sort-based top-k per F layer)"}
 
 
 if __name__ == "__main__":

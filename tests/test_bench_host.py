@@ -195,3 +195,21 @@ def test_visible_page_ids_match_a_walk_over_the_rows():
                 want.append(int(b.block_table[r, j]))
     got = bench.visible_page_ids(b)
     assert got.dtype == np.int32 and got.tolist() == want
+
+
+def test_index_cache_cpu_baseline_runs_the_oracle_stack():
+    """The IndexCache CPU leg runs the oracle's layer loop over a freq-4
+    stack: on a small stack it completes whole passes and reports rows/s
+    for the whole batch."""
+    from dsa_lightning_indexer_amd import synth
+    from oracle import index_cache as oic
+    L = 6
+    full = [l for l, s in enumerate(oic.skip_mask(L, freq=4, offset=2))
+            if not s]
+    host = synth.index_cache_layers(full, R=3, context=300, H=4, k=16,
+                                    workers=1)
+    ref = host[full[0]]
+    rec = bench.cpu_baseline_index_cache(host, ref, L, 0.0)
+    assert rec["kind"] == "oracle" and rec["unit"] == "query-rows/s"
+    assert rec["value"] > 0 and rec["cores"] >= 1
+    assert f"({len(full)} F)" in rec["sample"] and "1 pass(es)" in rec["sample"]
