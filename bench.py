@@ -223,7 +223,8 @@ def cpu_baseline(b, seconds, max_rows=None):
 # ----------------------------------------------------------------------------
 LOGITS_SOURCES = ("dsa_lightning_indexer_amd/csrc/kernels_logits.hip",
                   "dsa_lightning_indexer_amd/csrc/dsa_common.h",
-                  "dsa_lightning_indexer_amd/csrc/dsa_launch.h")
+                  "dsa_lightning_indexer_amd/csrc/dsa_launch.h",
+                  "dsa_lightning_indexer_amd/csrc/dsa_score.h")
 CALIBRATION_BYTES = 1 << 28
 
 

@@ -361,10 +361,17 @@ __global__ __launch_bounds__(256) void quantize_q_sched_kernel(
   const int w = ((int)blockIdx.x - qgrid) * 4 + (int)(threadIdx.x >> 6);
   if (w >= nwaves) return;
   const int lane = lane_id();
+  // query_start_loc of the first 64 requests, loaded while the span is
+  // computed from the positions: the request of a row among them then
+  // needs no further round trip before the block-table load
+  const int q_first = lane < a.R ? a.qsl[lane] : 0;
   const RowSpan sp = balanced_span<NCH>(a, D, per_xcd, w, 0);
   int v = -1;
   if (sp.row >= 0) {
-    const int r = wave_uniform(request_of_row_wave(a.qsl, a.R, sp.row));
+    const uint64_t le = __ballot(lane < a.R && q_first <= sp.row);
+    const int r = wave_uniform(le != ~0ull
+                                   ? max(__popcll(le) - 1, 0)
+                                   : request_of_row_wave(a.qsl, a.R, sp.row));
     const int last = (int)a.bt_stride - 1;
     const int j = sp.jb + (lane - 5);
     const int page = a.block_table[(int64_t)r * a.bt_stride +
