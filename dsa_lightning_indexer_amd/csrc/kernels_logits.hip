@@ -489,11 +489,16 @@ __global__ __launch_bounds__(64) void logits_balanced_kernel(
         const float tot = decode_page_sum<MT>(qa, kb[q], w);
         if (jp * kPageTokens + lane <= p) res = tot * ks[q];
       }
+      // device-scope (sc1) store: written through this XCD's L2, so the
+      // end of the launch has no dirty logits lines left to write back
+      // before the top-k launch reads them from another XCD (measured
+      // 0.15-0.2 us faster per decode forward; non-temporal stores were
+      // 0.25 us slower)
       const __amdgpu_buffer_rsrc_t ro = make_rsrc(
           out + (int64_t)min(jp, last) * kPageTokens,
           jp < je ? kPageTokens * 4 : 0);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(res), ro, 4 * lane,
-                                            0, 0);
+                                            0, 16);
     }
   }
   if (bad_page && lane == 0) raise_flag(kErrPageOutOfRange);
