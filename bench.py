@@ -1044,19 +1044,23 @@ def bench_index_cache(args, K, W):
         res[name] = a.elapsed_time(z) / K
         del g
     # one F layer's logits kernel alone, rotating over the 16 freq-4 F
-    # layers' inputs (each launch reads a cache the previous ones did not)
+    # layers' inputs (each launch reads a cache the previous ones did not),
+    # with the page schedule built once for all of them, as
+    # dsa_index_cache_run builds it once per pass
     full4 = [l for l, sk in enumerate(binding.dsa_index_cache_mask(
         L, freq=4, offset=2)) if not sk]
     q8s = [binding.dsa_quantize_q(layers[l]["q_bf16"]) for l in full4]
     lg = torch.empty((T, ld), dtype=torch.float32, device=dev)
-    kl = _timed(torch, lambda i: binding.dsa_indexer_logits(
+    sch = binding.dsa_logits_schedule(bt, qsl, pos, ld)
+    kl = _timed(torch, lambda i: binding.dsa_indexer_logits_scheduled(
         q8s[i][0], q8s[i][1], layers[full4[i]]["weights"],
-        layers[full4[i]]["k_cache"], bt, qsl, pos, ld, lg), 64, len(full4))
+        layers[full4[i]]["k_cache"], bt, qsl, pos, ld, sch, lg), 64,
+        len(full4))
     assert binding.dsa_device_error_flags(reset=True) == 0
     # algorithmic bytes of one F layer (as for decode): K pages, q fp8 +
     # scales + weights, top-k indices written; no logits round trip
     per_layer_bytes = 132 * T * 16384 + T * H * 136 + 4 * T * k
-    del layers, ws, q8s
+    del layers, ws, q8s, sch
     torch.cuda.empty_cache()
     cpu_rec = None
     if not args.no_cpu_baseline:
