@@ -59,10 +59,17 @@ def test_quantize_q_bit_exact():
     q[2, 1, :] = 0.0
     q[2, 1, 0] = -448.0
     q[2, 1, 1:1 + 26] = -mids[60:86]
+    # the reciprocal path's edges: s just above 2^-100 (amax 2^-91) and
+    # just below (amax 2^-92, exact division); a block holding +inf (s =
+    # inf: exact division, codes 0 and NaN)
+    q[3, 0] *= 2.0 ** -91 / np.abs(q[3, 0]).max()
+    q[3, 1] *= 2.0 ** -92 / np.abs(q[3, 1]).max()
+    q[3, 2, 7] = np.inf
     qb = _bf16(q)
     q8, qs = binding.dsa_quantize_q(qb.cuda())
     torch.cuda.synchronize()
-    codes, s = oi.quantize_q(qb.float().numpy())
+    with np.errstate(invalid="ignore"):                  # inf / inf
+        codes, s = oi.quantize_q(qb.float().numpy())
     assert np.array_equal(qs.cpu().numpy().view(np.uint32), s.view(np.uint32))
     assert np.array_equal(q8.cpu().numpy(), codes)
 
