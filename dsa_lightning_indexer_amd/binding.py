@@ -95,6 +95,7 @@ _SIGNATURES = {
     "dsa_fp8_mfma_rate_probe": (_I, [_I, ctypes.POINTER(ctypes.c_double),
                                      _P]),
     "dsa_page_read_probe": (_I, [_P, _L, _P, _L, _P]),
+    "dsa_fp8_code_check": (_I, [_P, _P]),
     "dsa_set_option": (_I, [ctypes.c_char_p, _I]),
 }
 
@@ -705,6 +706,20 @@ def dsa_page_read_probe(k_cache, page_ids, stream=None):
             _dev_ptr(k_cache, torch.uint8, "k_cache"), k_cache.shape[0],
             _dev_ptr(page_ids, torch.int32, "page_ids"), page_ids.numel(),
             _stream(stream, dev)))
+
+
+def dsa_fp8_code_check(device=None, stream=None):
+    """Run the exhaustive FP8 code check of the q quantisation's fast path
+    on ``device``; returns the three mismatch counts (hardware conversion vs
+    integer encoder, corrected quotient vs IEEE quotient, codes of the two
+    quotients).  Synchronises."""
+    dev = torch.device("cuda", 0) if device is None else torch.device(device)
+    counts = torch.zeros(3, dtype=torch.int64, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib().dsa_fp8_code_check(counts.data_ptr(),
+                                        _stream(stream, dev)))
+        torch.cuda.synchronize(dev)
+    return [int(x) for x in counts.cpu().tolist()]
 
 
 def dsa_set_option(key, value):

@@ -15,4 +15,9 @@ hipError_t launch_fp8_mfma_rate(int iters, double* flops, hipStream_t stream);
 hipError_t launch_page_read(const uint8_t* k_cache, int64_t num_pages,
                             const int32_t* ids, int64_t n, hipStream_t stream);
 
+// Zeroes counts[0..2], then counts the FP8 code mismatches described at
+// fp8_cvt_check_kernel / fp8_quotient_check_kernel (device counters).
+hipError_t launch_fp8_code_check(unsigned long long* counts,
+                                 hipStream_t stream);
+
 }  // namespace dsa

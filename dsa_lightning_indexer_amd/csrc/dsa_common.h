@@ -66,6 +66,19 @@ __device__ __forceinline__ uint32_t e4m3fn_encode(float x) {
   return code | sign;
 }
 
+// q / s for an FP8 block scale s (= amax / 448) and r = 1 / s, both IEEE
+// float32: the reciprocal product with one FMA correction -- y = q r, then
+// e = q - s y (exact), y + e r; y itself when e = 0 (keeps the sign of a
+// zero).  For a finite block of bf16 values with s >= 2^-100 its FP8 code
+// (hardware e4m3 conversion) equals the integer encoder's code of the IEEE
+// quotient q / s for every q with |q| <= amax: dsa_fp8_code_check counts the
+// pairs where it does not (none on gfx950).
+__device__ __forceinline__ float div_by_scale(float q, float s, float r) {
+  const float y0 = q * r;
+  const float e = fmaf(-y0, s, q);
+  return e == 0.f ? y0 : fmaf(e, r, y0);
+}
+
 // Order-preserving map of an fp32 value to uint32 (larger float -> larger
 // key); -0 is folded onto +0 first so the two compare equal.
 __device__ __forceinline__ uint32_t float_to_ordered(float f) {

@@ -1,7 +1,8 @@
-// Measurement helpers of the gfx950 library (not steps of the indexer hot
-// path): the FP8 matrix-core rate this device reaches at the clock it holds
-// under a pure MFMA load, and the time a bare read of a batch's K pages
-// takes.  The logits kernels' rates are read against the published peaks
+// Measurement and check helpers of the gfx950 library (not steps of the
+// indexer hot path): the FP8 matrix-core rate this device reaches at the
+// clock it holds under a pure MFMA load, the time a bare read of a batch's K
+// pages takes, and an exhaustive check of the FP8 code arithmetic the q
+// quantisation's fast path relies on.  The logits kernels' rates are read against the published peaks
 // and against these measured ones.
 #include "dsa_calib.h"
 #include "dsa_common.h"
@@ -86,6 +87,76 @@ hipError_t launch_page_read(const uint8_t* k_cache, int64_t num_pages,
   const int64_t waves = (n + kReadPagesPerWave - 1) / kReadPagesPerWave;
   hipLaunchKernelGGL(page_read_kernel, dim3((unsigned)waves), dim3(64), 0,
                      stream, k_cache, num_pages, ids, n);
+  return hipGetLastError();
+}
+
+// FP8 code checks behind the q quantisation's fast path (counts[0..2]):
+// [0] fp32 values with |x| < 464 (all a quotient q / s with |q| <= amax can
+// round to) whose hardware e4m3 conversion differs from e4m3fn_encode;
+// [1] bf16 pairs (q, amax), amax finite and positive, |q| <= amax, s =
+// amax / 448 >= 2^-100, where div_by_scale differs from the IEEE quotient;
+// [2] those pairs where the hardware code of div_by_scale differs from the
+// integer code of the IEEE quotient (the one that matters).
+// Thread t of workgroup b checks the 16 bit patterns base + 16 (256 b + t)
+// + 0..15.
+constexpr int kCvtPerThread = 16;
+__global__ __launch_bounds__(256) void fp8_cvt_check_kernel(
+    uint64_t base, unsigned long long* counts) {
+  const uint64_t i0 = base + ((uint64_t)blockIdx.x * blockDim.x + threadIdx.x) *
+                                 kCvtPerThread;
+  unsigned long long n = 0;
+  for (int k = 0; k < kCvtPerThread; ++k) {
+    const uint64_t i = i0 + k;
+    const uint32_t bits = (uint32_t)i;
+    const uint32_t a = bits & 0x7fffffffu;
+    if (i >= (1ull << 32) || a >= 0x43e80000u) continue;  // |x| >= 464, NaN
+    const float x = __uint_as_float(bits);
+    const uint32_t hw =
+        (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false) & 0xffu;
+    n += hw != e4m3fn_encode(x) ? 1 : 0;
+  }
+  if (n) atomicAdd(&counts[0], n);
+}
+
+// Workgroup y: amax = bf16 bits (amax0 + y); thread t: q bits t, t + 256, ..
+__global__ __launch_bounds__(256) void fp8_quotient_check_kernel(
+    uint32_t amax0, unsigned long long* counts) {
+  const uint32_t ah = amax0 + blockIdx.x;
+  if (ah == 0u || ah > 0x7f7fu) return;                // positive finite
+  const float amax = __uint_as_float(ah << 16);
+  const float s = amax / kE4M3Max;
+  if (!(s >= 0x1p-100f)) return;
+  const float r = 1.0f / s;
+  unsigned long long nq = 0, nc = 0;
+  for (uint32_t qh = threadIdx.x; qh < 65536u; qh += 256u) {
+    const float q = __uint_as_float(qh << 16);
+    if (!(fabsf(q) <= amax)) continue;                 // also drops NaN
+    const float ref = q / s;
+    const float y = div_by_scale(q, s, r);
+    nq += __float_as_uint(y) != __float_as_uint(ref) ? 1 : 0;
+    const uint32_t hw =
+        (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.f, 0, false) & 0xffu;
+    nc += hw != e4m3fn_encode(ref) ? 1 : 0;
+  }
+  if (nq) atomicAdd(&counts[1], nq);
+  if (nc) atomicAdd(&counts[2], nc);
+}
+
+__global__ void zero_counts_kernel(unsigned long long* counts, int n) {
+  if ((int)threadIdx.x < n) counts[threadIdx.x] = 0ull;
+}
+
+hipError_t launch_fp8_code_check(unsigned long long* counts,
+                                 hipStream_t stream) {
+  hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(64), 0, stream, counts,
+                     3);
+  const uint64_t chunk = 1ull << 30;
+  for (uint64_t b = 0; b < (1ull << 32); b += chunk)
+    hipLaunchKernelGGL(fp8_cvt_check_kernel,
+                       dim3((unsigned)(chunk / (256 * kCvtPerThread))),
+                       dim3(256), 0, stream, b, counts);
+  hipLaunchKernelGGL(fp8_quotient_check_kernel, dim3(0x7f80u), dim3(256), 0,
+                     stream, 0u, counts);
   return hipGetLastError();
 }
 

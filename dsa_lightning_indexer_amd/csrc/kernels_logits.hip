@@ -68,19 +68,14 @@ __device__ __forceinline__ void quantize_q_blocks(
   uint32_t lo = 0, hi = 0;
   if (abits < 0x7f800000u && s >= 0x1p-100f) {
     // all finite, scale not tiny: q / s from the reciprocal with one FMA
-    // correction (y = q r, e = q - s y exactly; y + e r, or y when e = 0)
-    // and the hardware e4m3 conversion -- the same code as the IEEE
-    // quotient and the integer encoder below for every pair of bf16 values
-    // |q| <= amax (checked exhaustively on the GPU), at a fraction of the
+    // correction and the hardware e4m3 conversion -- the same code as the
+    // IEEE quotient and the integer encoder below for every pair of bf16
+    // values |q| <= amax (dsa_fp8_code_check), at a fraction of the
     // instructions
     const float r = 1.0f / s;
     float y[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float y0 = f[i] * r;
-      const float e = fmaf(-y0, s, f[i]);
-      y[i] = e == 0.f ? y0 : fmaf(e, r, y0);
-    }
+    for (int i = 0; i < 8; ++i) y[i] = div_by_scale(f[i], s, r);
     lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
         y[2], y[3], __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false),
         true);

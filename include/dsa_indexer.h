@@ -553,6 +553,23 @@ int dsa_page_read_probe(const uint8_t* k_cache, int64_t num_pages,
                         const int32_t* page_ids, int64_t n, void* stream);
 
 /*
+ * dsa_fp8_code_check -- check helper, not a step of the hot path: enqueues
+ * on `stream` an exhaustive check of the FP8 arithmetic dsa_quantize_q's
+ * fast path uses for a finite block with scale s = amax / 448 >= 2^-100
+ * (the q quantisation's e4m3fn code of fp32(q / s), [RFC] 2.1.3 FP8
+ * indexer) and writes three mismatch counts to counts (device, uint64 [3],
+ * zeroed first): [0] fp32 values with |x| < 464 whose hardware e4m3
+ * conversion differs from the library's integer round-to-nearest-even
+ * encoder; [1] bf16 pairs (q, amax) with amax finite and positive, |q| <=
+ * amax and s >= 2^-100 whose reciprocal-with-one-FMA quotient differs from
+ * the IEEE quotient; [2] such pairs whose hardware code of that quotient
+ * differs from the integer code of the IEEE quotient.  [2] == 0 is what the
+ * fast path needs.  About 6.6 G cases; a few milliseconds.
+ * DSA_ERR_INVALID_ARG for counts == NULL.
+ */
+int dsa_fp8_code_check(uint64_t* counts, void* stream);
+
+/*
  * dsa_set_option -- tuning/testing knobs; returns the previous value or
  * DSA_ERR_INVALID_ARG for an unknown key or value.  Knobs are kept per
  * device (the calling thread's current HIP device) in atomics: concurrent

@@ -392,3 +392,8 @@ def test_product_and_oracle_share_no_code():
         if name.endswith(".py"):
             for m in _imports(os.path.join(root, "oracle", name)):
                 assert m.split(".")[0] != "dsa_lightning_indexer_amd", (name, m)
+
+
+def test_fp8_code_check_rejects_null_counts():
+    L = binding.lib()
+    assert L.dsa_fp8_code_check(None, None) == binding.DSA_ERR_INVALID_ARG

@@ -74,6 +74,19 @@ def test_quantize_q_bit_exact():
     assert np.array_equal(q8.cpu().numpy(), codes)
 
 
+def test_fp8_code_check_finds_no_mismatch():
+    """The q quantisation's fast path (reciprocal with one FMA correction,
+    hardware e4m3 conversion) gives the integer encoder's code of the IEEE
+    quotient for every pair of bf16 values it is used on, and the hardware
+    conversion equals the integer encoder for every fp32 below 464 in
+    magnitude: an exhaustive device-side count, no mismatch allowed."""
+    _say("case: exhaustive FP8 code check")
+    cvt, quotient, codes = binding.dsa_fp8_code_check()
+    print(f"fp8 code check: conversion {cvt}, quotient {quotient}, "
+          f"codes {codes} mismatches", flush=True)
+    assert cvt == 0 and codes == 0
+
+
 def test_quantize_q_bit_exact_decode_shape():
     _say("case: quantize_q decode batch")
     b = synth.decode()
