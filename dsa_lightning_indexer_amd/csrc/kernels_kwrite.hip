@@ -64,8 +64,9 @@ __global__ __launch_bounds__(256) void compressed_slot_mapping_kernel(
 
 // 16 lanes per token, 8 bf16 values per lane (one 16-byte load):
 //   amax = max |k|, s = amax / 448 (IEEE fp32 division), code = e4m3fn(k / s)
-//   (IEEE division, round to nearest even, saturating); an all-zero key
-//   stores s = 0 and zero codes.
+//   (round to nearest even, saturating; for a finite key with s >= 2^-100
+//   from the reciprocal quotient and the hardware conversion, which give the
+//   IEEE quotient's codes); an all-zero key stores s = 0 and zero codes.
 // Lane i of the token's group writes key bytes 8 i .. 8 i + 7 (the group
 // writes the 128-byte row in one coalesced store) and lane 0 the scale.  A
 // negative slot writes nothing; a slot past the pool raises the page flag.
@@ -86,11 +87,17 @@ __global__ __launch_bounds__(256) void k_write_kernel(
     f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
   }
   float amax = 0.f;
+  uint32_t abits = 0u;                       // largest |k| bit pattern
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  for (int i = 0; i < 8; ++i) {
+    amax = fmaxf(amax, fabsf(f[i]));
+    abits = max(abits, __float_as_uint(f[i]) & 0x7fffffffu);
+  }
 #pragma unroll
-  for (int off = 8; off >= 1; off >>= 1)
+  for (int off = 8; off >= 1; off >>= 1) {
     amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+    abits = max(abits, (uint32_t)__shfl_xor((int)abits, off, 16));
+  }
   if (slot < 0) return;                      // padding token (group-uniform)
   if (slot >= num_pages * kPageTokens) {
     if (sub == 0) atomicOr(&g_err_kwrite, kErrPageOutOfRange);
@@ -98,7 +105,21 @@ __global__ __launch_bounds__(256) void k_write_kernel(
   }
   const float s = amax / kE4M3Max;
   uint32_t lo = 0, hi = 0;
-  if (s > 0.f) {
+  if (abits < 0x7f800000u && s >= 0x1p-100f) {
+    // finite key, scale not tiny: the reciprocal quotient and the hardware
+    // conversion give the same codes as the IEEE quotient and the integer
+    // encoder (dsa_fp8_code_check)
+    const float r = 1.0f / s;
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = div_by_scale(f[i], s, r);
+    lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+        y[2], y[3], __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false),
+        true);
+    hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+        y[6], y[7], __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false),
+        true);
+  } else if (s > 0.f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) lo |= e4m3fn_encode(f[i] / s) << (8 * i);
 #pragma unroll
