@@ -187,11 +187,14 @@ __device__ __forceinline__ void select_bin_all(const uint32_t* hist,
 // bin search is select_bin_all (one barrier) for instances of up to 4
 // slices; wider ones keep their registers for the keys and use the
 // two-barrier search throughout.  reg_clear and a barrier must precede the
-// call.  Call from all NT threads.
+// call.  Call from all NT threads.  n_eq (optional) receives the number of
+// valid keys equal to thr under mask; k_tie == n_eq means every tied key is
+// selected.
 template <int NT, int S>
 __device__ void reg_threshold(const RegKeys<S, NT>& r, int k,
                               RegTopkShared<NT, S>& sh, uint32_t& mask,
-                              uint32_t& thr, uint32_t& k_tie) {
+                              uint32_t& thr, uint32_t& k_tie,
+                              uint32_t* n_eq = nullptr) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int s = 0; s < S; ++s)
@@ -210,6 +213,7 @@ __device__ void reg_threshold(const RegKeys<S, NT>& r, int k,
   }
   const uint32_t k_rem = (uint32_t)k - above;
   mask = 0xfff00000u; thr = d << 20; k_tie = k_rem;
+  if (n_eq) *n_eq = count;
   if (k_rem < count) {
     // pass 2: bits 19..8 of the keys in bin d (hist2; hist may still be
     // read by waves finishing the first bin search, so pass 3 has its own
@@ -224,8 +228,10 @@ __device__ void reg_threshold(const RegKeys<S, NT>& r, int k,
     topk_select_bin<kHistBins, NT>(sh.hist2, k_rem, sh);
     const uint32_t p24 = (d << 12) | sh.sel_digit;
     const uint32_t k2 = k_rem - sh.sel_above;
+    const uint32_t c2 = sh.sel_count;
     mask = 0xffffff00u; thr = p24 << 8; k_tie = k2;
-    if (k2 < sh.sel_count) {
+    if (n_eq) *n_eq = c2;
+    if (k2 < c2) {
       // pass 3: bits 7..0 of the keys matching the 24-bit prefix
 #pragma unroll
       for (int s = 0; s < S; ++s)
@@ -237,6 +243,7 @@ __device__ void reg_threshold(const RegKeys<S, NT>& r, int k,
       topk_select_bin<256, NT>(sh.hist3, k2, sh);
       mask = 0xffffffffu; thr = (p24 << 8) | sh.sel_digit;
       k_tie = k2 - sh.sel_above;
+      if (n_eq) *n_eq = sh.sel_count;
     }
   }
 }
@@ -361,7 +368,8 @@ __device__ void reg_emit(const RegKeys<S, NT>& r, int k, uint32_t mask,
 template <int NT, int S>
 __device__ void reg_emit_columns(const RegKeys<S, NT>& r, int k, uint32_t mask,
                                  uint32_t thr, uint32_t k_tie, int32_t* orow,
-                                 RegTopkShared<NT, S>& sh) {
+                                 RegTopkShared<NT, S>& sh,
+                                 bool all_ties = false) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
@@ -372,21 +380,37 @@ __device__ void reg_emit_columns(const RegKeys<S, NT>& r, int k, uint32_t mask,
     return x;
   };
   const int sh4 = 4 * (tid & 7);
+  if (all_ties) {
+    // every tied key taken: one bitmap of the keys at or above the
+    // threshold, no tie words
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
-    uint32_t sel = 0u, tie = 0u;
+    for (int s = 0; s < S; ++s) {
+      uint32_t sel = 0u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bool ok = r.ok(s, j);
-      const uint32_t km = r.key[s][j] & mask;
-      sel |= (ok && km > thr) ? (1u << j) : 0u;
-      tie |= (ok && km == thr) ? (1u << j) : 0u;
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = r.ok(s, j);
+        sel |= (ok && (r.key[s][j] & mask) >= thr) ? (1u << j) : 0u;
+      }
+      sel = or8(sel << sh4);
+      if ((tid & 7) == 0) sh.selw[s * (NT / 8) + (tid >> 3)] = sel;
     }
-    sel = or8(sel << sh4);
-    tie = or8(tie << sh4);
-    if ((tid & 7) == 0) {
-      sh.selw[s * (NT / 8) + (tid >> 3)] = sel;
-      sh.tiew[s * (NT / 8) + (tid >> 3)] = tie;
+  } else {
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      uint32_t sel = 0u, tie = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = r.ok(s, j);
+        const uint32_t km = r.key[s][j] & mask;
+        sel |= (ok && km > thr) ? (1u << j) : 0u;
+        tie |= (ok && km == thr) ? (1u << j) : 0u;
+      }
+      sel = or8(sel << sh4);
+      tie = or8(tie << sh4);
+      if ((tid & 7) == 0) {
+        sh.selw[s * (NT / 8) + (tid >> 3)] = sel;
+        sh.tiew[s * (NT / 8) + (tid >> 3)] = tie;
+      }
     }
   }
   __syncthreads();
@@ -402,7 +426,10 @@ __device__ void reg_emit_columns(const RegKeys<S, NT>& r, int k, uint32_t mask,
   for (int h = 0; h < WPT; ++h) {
     sw_[h] = 0u;
     tw_[h] = 0u;
-    if (w0 + h < nw) { sw_[h] = sh.selw[w0 + h]; tw_[h] = sh.tiew[w0 + h]; }
+    if (w0 + h < nw) {
+      sw_[h] = sh.selw[w0 + h];
+      tw_[h] = all_ties ? 0u : sh.tiew[w0 + h];
+    }
     n_sel += (uint32_t)__builtin_popcount(sw_[h]);
     n_tie += (uint32_t)__builtin_popcount(tw_[h]);
   }

@@ -470,10 +470,13 @@ __global__ __launch_bounds__(NT, 4) void topk_reg_kernel(
       r.key[s][3] = float_to_ordered(v[s].w);
     }
     __syncthreads();
-    uint32_t mask, thr, k_tie;
-    reg_threshold<NT, S>(r, k, sh, mask, thr, k_tie);
+    uint32_t mask, thr, k_tie, n_eq;
+    reg_threshold<NT, S>(r, k, sh, mask, thr, k_tie, BITMAP ? &n_eq : nullptr);
     if (BITMAP)
-      reg_emit_columns<NT, S>(r, k, mask, thr, k_tie, orow, sh);
+      // the usual case (distinct values at the threshold): every tied key
+      // is selected and the bitmaps carry no tie words
+      reg_emit_columns<NT, S>(r, k, mask, thr, k_tie, orow, sh,
+                              k_tie == n_eq);
     else
       reg_emit<NT, S>(r, k, mask, thr, k_tie, orow, sh,
                       [](int, int, int pos) { return pos; });
