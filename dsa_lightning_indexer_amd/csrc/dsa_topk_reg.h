@@ -382,16 +382,18 @@ __device__ void reg_emit_columns(const RegKeys<S, NT>& r, int k, uint32_t mask,
   const int sh4 = 4 * (tid & 7);
   if (all_ties) {
     // every tied key taken: one bitmap of the keys at or above the
-    // threshold, no tie words
+    // threshold, no tie words.  thr is zero below the bits mask keeps, so
+    // (key & mask) >= thr is key >= thr; a thread's valid keys of a slice
+    // are a prefix of its four
 #pragma unroll
     for (int s = 0; s < S; ++s) {
+      const int lim = r.n - s * 4 * NT - 4 * tid;
+      const uint32_t valid =
+          lim >= 4 ? 0xfu : (lim <= 0 ? 0u : (1u << lim) - 1u);
       uint32_t sel = 0u;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool ok = r.ok(s, j);
-        sel |= (ok && (r.key[s][j] & mask) >= thr) ? (1u << j) : 0u;
-      }
-      sel = or8(sel << sh4);
+      for (int j = 0; j < 4; ++j) sel |= r.key[s][j] >= thr ? (1u << j) : 0u;
+      sel = or8((sel & valid) << sh4);
       if ((tid & 7) == 0) sh.selw[s * (NT / 8) + (tid >> 3)] = sel;
     }
   } else {
