@@ -28,23 +28,23 @@ def golden():
 
 
 # ----------------------------------------------------------------------------
-# Survey logits criterion (G11) bookkeeping: tests.parity.check_logits_row
+# Floor-criterion bookkeeping: tests.parity.check_logits_row
 # records every row it checks; each record is tagged with its test here and
 # the session summary prints the totals per test function (and writes them
-# as JSON to $DSA_G11_JSON when that is set).
+# as JSON to $DSA_FLOOR_JSON when that is set).
 # ----------------------------------------------------------------------------
 @pytest.hookimpl(hookwrapper=True)
 def pytest_runtest_call(item):
     mod = sys.modules.get("tests.parity")
-    n0 = len(mod.G11_LOG) if mod else 0
+    n0 = len(mod.FLOOR_LOG) if mod else 0
     yield
     mod = sys.modules.get("tests.parity")
     if mod:
-        for rec in mod.G11_LOG[n0:]:
+        for rec in mod.FLOOR_LOG[n0:]:
             rec.setdefault("test", item.nodeid)
 
 
-def _g11_totals(log):
+def _floor_totals(log):
     per = {}
     for r in log:
         key = r.get("test", "?")
@@ -67,9 +67,9 @@ def _g11_totals(log):
 def pytest_terminal_summary(terminalreporter):
     import json
     mod = sys.modules.get("tests.parity")
-    if not mod or not mod.G11_LOG:
+    if not mod or not mod.FLOOR_LOG:
         return
-    per = _g11_totals(mod.G11_LOG)
+    per = _floor_totals(mod.FLOOR_LOG)
     funcs = {}
     for key, a in per.items():
         f = funcs.setdefault(key.split("[")[0], {"rows": 0, "cols": 0,
@@ -81,12 +81,12 @@ def pytest_terminal_summary(terminalreporter):
         f["max_ratio"] = max(f["max_ratio"], a["max_ratio"])
         f["max_abs"] = max(f["max_abs"], a["viol_cols_max_abs_over_S"])
     tr = terminalreporter
-    tr.write_sep("-", "logits criterion 2e-3 * max(|o|, 1e-2 S_t) (G11)")
+    tr.write_sep("-", "logits criterion 2e-3 * max(|o|, 1e-2 S_t)")
     for name, f in sorted(funcs.items()):
         tr.write_line(f"{name}: {f['viol']} of {f['cols']} columns over "
                       f"({f['rows']} rows), max ratio {f['max_ratio']:.3g}, "
                       f"largest |o|/S_t among them {f['max_abs']:.3g}")
-    path = os.environ.get("DSA_G11_JSON")
+    path = os.environ.get("DSA_FLOOR_JSON")
     if path:
         with open(path, "w") as fh:
             json.dump({"per_test": per, "per_function": funcs}, fh, indent=1)

@@ -106,15 +106,15 @@ def magnitude(b, rows=None):
     return out
 
 
-# The survey's logits criterion (the north star's "max relative error 2e-3"
-# with a floor for logits near zero): |g - o| <= 2e-3 * max(|o|, 1e-2 S_t),
+# The floor criterion (a relative error of at most 2e-3, with a floor for
+# logits near zero): |g - o| <= 2e-3 * max(|o|, 1e-2 S_t),
 # S_t = max |o| over the row's visible columns.  Every check_logits_row call
 # evaluates it on every visible column and appends one record here; the
 # session summary (tests/conftest.py) reports the totals.
-G11_LOG = []
+FLOOR_LOG = []
 
 
-def g11_ratios(g, o):
+def floor_ratios(g, o):
     """|g - o| / (2e-3 max(|o|, 1e-2 S_t)) per column (0 where both the
     error and the bound are 0)."""
     o = np.asarray(o, dtype=np.float64)
@@ -128,8 +128,8 @@ def g11_ratios(g, o):
 
 def check_logits_row(g, o, p, what="", m=None):
     """Logit tolerance on columns 0..p (``m`` = magnitude row; without it
-    only the relative term applies).  Also evaluates the survey criterion
-    (G11_LOG).  Returns the max relative error over columns with |o| >=
+    only the relative term applies).  Also evaluates the floor criterion
+    (FLOOR_LOG).  Returns the max relative error over columns with |o| >=
     1e-2 * max|o|."""
     o = np.asarray(o[: p + 1], dtype=np.float64)
     g = np.asarray(g[: p + 1], dtype=np.float64)
@@ -143,7 +143,7 @@ def check_logits_row(g, o, p, what="", m=None):
         f"gpu={g[bad[0]]!r} oracle={o[bad[0]]!r} tol={tol[bad[0]]!r}")
     S = float(np.max(np.abs(o))) if o.size else 0.0
     big = np.abs(o) >= LOGIT_FLOOR * S
-    r = g11_ratios(g, o)
+    r = floor_ratios(g, o)
     rec = {"what": what, "cols": int(o.size), "viol": int(np.sum(r > 1)),
            "max_ratio": float(r.max()) if r.size else 0.0,
            "viol_cols_max_abs_over_S": float(np.max(np.abs(o[r > 1])) / S)
@@ -151,7 +151,7 @@ def check_logits_row(g, o, p, what="", m=None):
     if m is not None and np.any(r > 1):
         mm = np.asarray(m[: p + 1], dtype=np.float64)
         rec["viol_max_err_over_M"] = float(np.max(err[r > 1] / mm[r > 1]))
-    G11_LOG.append(rec)
+    FLOOR_LOG.append(rec)
     return float(np.max(err[big] / np.abs(o[big]))) if big.any() else 0.0
 
 
