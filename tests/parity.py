@@ -155,8 +155,12 @@ def check_logits_row(g, o, p, what="", m=None):
     return float(np.max(err[big] / np.abs(o[big]))) if big.any() else 0.0
 
 
-def check_topk_row(gpu_row, oracle_visible, k, what=""):
-    """G10 comparison of one GPU top-k row with the oracle's logits."""
+def check_topk_row(gpu_row, oracle_visible, k, what="", m=None):
+    """One GPU top-k row against the oracle's logits: the GPU's set equals
+    the oracle's except for indices whose oracle logit lies within the tie
+    window of the k-th value (TOPK_TIE relative, floored at LOGIT_FLOOR of
+    the row maximum) or, given the magnitude row m, within the two logits'
+    combined logits tolerance of it."""
     gpu_row = np.asarray(gpu_row)
     o = np.asarray(oracle_visible, dtype=np.float64)
     n = o.shape[0]
@@ -174,7 +178,16 @@ def check_topk_row(gpu_row, oracle_visible, k, what=""):
         vk = np.sort(o)[-k]
         S = float(np.max(np.abs(o)))
         win = TOPK_TIE * max(abs(vk), LOGIT_FLOOR * S)
-        far = diff[np.abs(o[diff] - vk) > win]
+        gap = np.abs(o[diff] - vk)
+        if m is not None:
+            # two logits closer than the sum of their logits tolerances
+            # (LOGIT_RTOL |o| + LOGIT_ABS m) may swap order within the error
+            # the logits check permits: such an index is a tie as well
+            mm = np.asarray(m[:n], dtype=np.float64)
+            kth = int(np.argsort(o, kind="stable")[-k])
+            tol = LOGIT_RTOL * np.abs(o) + LOGIT_ABS * mm
+            win = np.maximum(win, tol[diff] + tol[kth])
+        far = diff[gap > win]
         assert far.size == 0, (
             f"{what}: {far.size} indices differ beyond the tie window "
             f"(first {far[0]}, logit {o[far[0]]!r}, v_k {vk!r})")

@@ -51,7 +51,10 @@ def _case(seed):
     return b
 
 
-@pytest.mark.parametrize("seed", range(120))
+# 2770 and 3722: rows (H = 4) whose oracle top-k differs from the GPU's by
+# two logits closer than their combined logits tolerance -- one pair 0.23 %
+# apart, one set of exact zeros against logits a few 1e-4 below zero
+@pytest.mark.parametrize("seed", list(range(120)) + [2770, 3722])
 def test_random_configuration(seed):
     b = _case(seed)
     print(f"case: seed {seed}: R={b.R} T={b.T} H={b.H} k={b.k} ld={b.ld}",
@@ -67,7 +70,7 @@ def test_random_configuration(seed):
         parity.check_logits_row(lg[t], ora[t], p, f"seed {seed} row {t}",
                                 mag[t])
         parity.check_topk_row(tk[t], ora[t, : p + 1], b.k,
-                              f"seed {seed} row {t}")
+                              f"seed {seed} row {t}", mag[t])
         parity.check_topk_exact_on_gpu_logits(tk[t], lg[t], p, b.k,
                                               f"seed {seed} row {t}")
     assert binding.dsa_device_error_flags(reset=True) == 0
